@@ -1,0 +1,154 @@
+"""Benchmark of the tiled GEMM hot path on one MI355X.
+
+A "step" is one C = alpha*A.B + beta*C through the C ABI over the resident
+synthetic inputs of the workload (default: bf16 A, B, fp32 C, M = N = K = 8192,
+N(0,1) inputs rounded to bf16, beta = 0).  W untimed warm-up steps, then K
+timed steps between two synchronisations, timed with HIP events on the stream
+the kernel is launched on.  Prints one JSON line.
+
+  python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+The CPU-baseline leg times the fp64 oracle (test infrastructure, untuned) on a
+bounded band of output rows of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3}   # MI355X dense MFMA
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="c2_bf16_8192")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU-baseline duration")
+    ap.add_argument("--config", type=int, default=0, help="force a tile configuration (tg_config)")
+    ap.add_argument("--pipeline-depth", type=int, default=0)
+    ap.add_argument("--swizzle", type=int, default=0)
+    ap.add_argument("--block-order", type=int, default=0)
+    return ap.parse_args()
+
+
+def cpu_baseline(p, seconds):
+    """The oracle on rows [0, R) of the workload's output, R grown until ~`seconds` of work."""
+    import numpy as np
+
+    import oracle
+    from workloads import Problem
+    threads = oracle.max_threads()
+    rows_done, flops, t_total = 0, 0.0, 0.0
+    band = 8
+    while t_total < seconds and rows_done < p.M:
+        r = min(band, p.M - rows_done)
+        sub = Problem("band", p.dtype, r, p.N, p.K, lda=p.lda, ldb=p.ldb, ldc=p.ldc, alpha=p.alpha, beta=p.beta)
+        A = np.ascontiguousarray(p.A[rows_done * p.lda: rows_done * p.lda + r * p.lda])
+        C0 = None
+        if p.beta != 0:
+            C0 = np.ascontiguousarray(p.C0[rows_done * p.ldc: rows_done * p.ldc + r * p.ldc])
+        t = time.perf_counter()
+        oracle.gemm(r, p.N, p.K, p.dtype, A, p.lda, p.B, p.ldb, C0=C0, ldc=p.ldc, alpha=p.alpha, beta=p.beta)
+        t_total += time.perf_counter() - t
+        rows_done += r
+        flops += 2.0 * r * p.N * p.K
+        band = min(band * 2, 256)
+    return {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"output rows 0..{rows_done - 1} of {p.name} ({rows_done}x{p.N}x{p.K}, batch 0), "
+                      f"fp64 triple loop, {t_total:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the path has no multi-GPU mode)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import tile_scheduled_dense_amd as tg
+    import workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.cuda.current_device()
+    props = torch.cuda.get_device_properties(dev)
+
+    p = workloads.config(args.workload)
+    print(f"# workload {p.name}: {p.batch}x{p.M}x{p.N}x{p.K} {p.dtype}", file=sys.stderr, flush=True)
+    to_dev = lambda a: torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).to("cuda")
+    A, B = to_dev(p.A), to_dev(p.B)
+    C = to_dev(p.C0.copy()) if p.beta != 0 else torch.zeros(p.sizeC(), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    opts = dict(config=args.config, pipeline_depth=args.pipeline_depth, swizzle=args.swizzle,
+                block_order=args.block_order)
+    plan = tg.tile_gemm_plan(p.batch, p.M, p.N, p.K, p.dtype, **opts)
+
+    def step():
+        tg.tile_gemm_ex(p.batch, p.M, p.N, p.K, p.dtype, A, p.lda, p.strideA, B, p.ldb, p.strideB,
+                        C, p.ldc, p.strideC, p.alpha, p.beta, stream, **opts)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_total = start.elapsed_time(end)
+    ms_step = ms_total / args.steps
+    print(f"# {args.steps} steps: {ms_total:.3f} ms on the stream, {wall * 1e3:.3f} ms wall",
+          file=sys.stderr, flush=True)
+
+    tflops = p.flops / (ms_step * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[p.dtype]
+    bytes_alg = p.compulsory_bytes()
+    gbs = bytes_alg / (ms_step * 1e-3) / 1e9
+    # Each step is exactly one launch of the GEMM kernel, so the event time per
+    # step is the kernel's average launch duration (plus launch gaps).
+    roofline = {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(tflops / peak, 4), "traffic": None,
+                "algorithmic_flops_per_launch": p.flops, "avg_launch_us": round(ms_step * 1e3, 2),
+                "algorithmic_bytes_per_launch": bytes_alg, "achieved_GBps": round(gbs, 1)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(p, args.cpu_seconds)
+
+    line = {
+        "metric": "GEMM TFLOP/s and % of MI355X MFMA peak, square + ragged extents, 1 GPU",
+        "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": p.dtype, "data": "synthetic",
+        "config": {"workload": p.name, "M": p.M, "N": p.N, "K": p.K, "batch": p.batch,
+                   "lda": p.lda, "ldb": p.ldb, "ldc": p.ldc, "alpha": p.alpha, "beta": p.beta,
+                   "inputs": f"{p.dist} seed {p.seed}", "accumulate": "fp32", "output": "fp32",
+                   "tile": f"{plan['block_m']}x{plan['block_n']}x{plan['block_k']}",
+                   "pipeline_depth": plan["pipeline_depth"], "grid": plan["grid"]},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "device": {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
+                   "cus": props.multi_processor_count},
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

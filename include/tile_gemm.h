@@ -1,0 +1,197 @@
+/*
+ * tile_gemm.h -- C ABI of the MI355X (gfx950) tiled dense contraction.
+ *
+ *     C[b] <- alpha * A[b] . B[b] + beta * C[b]          (row-major, any extents)
+ *
+ * The operation is the matmul micro-kernel d[i,j] += a[i,k] * b[k,j] that the
+ * OCANNL "Module Ir.Schedule" page tensorizes (Tensorize paragraph: operands
+ * row-major in their last two axes, not transposed), equivalently
+ * acc = mma(a, b, acc) over a reduce region in LuisaCompute "Execution Nests and
+ * coordinates" (structured-region calculus; logical anchor and frontier).  The
+ * schedule it is built with -- pad-to-tile, partition into interior and fringe
+ * blocks, staging through a swizzled on-chip tile, a window-2 software pipeline
+ * over K, tensorized multiply-accumulate -- changes how the value is reached,
+ * not the value, except that the k sum may be regrouped (the Interchange
+ * paragraph of the OCANNL page; reduce's regrouping permission on the
+ * LuisaCompute page).
+ *
+ * Conventions shared by every entry point
+ *  - Element (i, k) of A is A[i*lda + k]; (k, j) of B is B[k*ldb + j]; (i, j) of
+ *    C is C[i*ldc + j].  Leading dimensions and batch strides count ELEMENTS.
+ *  - A and B have the same dtype (fp32, bf16 or fp16).  C is always fp32, and
+ *    the products are accumulated in fp32.
+ *  - beta == 0: C is write-only (it is not read, so NaN in C does not leak).
+ *  - M == 0, N == 0 or batch == 0: nothing is launched, TG_OK.
+ *    K == 0: C <- beta * C (zeros when beta == 0).
+ *  - No alignment requirement: any lda/ldb/ldc, and A/B pointers need only be
+ *    aligned to their element size, C to 4 bytes.
+ *  - Device pointers.  The caller owns every buffer; the library never
+ *    allocates, frees or keeps a pointer past the call.  Work is enqueued
+ *    asynchronously on `stream` (a hipStream_t passed as void*, 0 = the null
+ *    stream); buffers must stay alive until the stream reaches the work.
+ *  - C must not overlap A or B (the source of a staged tile must not be
+ *    written by the routine: OCANNL Stage paragraph).  Overlap is checked on
+ *    the address ranges and rejected.
+ *  - Errors are returned, never printed, and no C++ exception crosses the ABI.
+ *    Argument errors are detected before any device work.  A device fault
+ *    surfaces, as usual in HIP, at the caller's next synchronisation.
+ *  - The library is stateless apart from a lazily filled, lock-protected cache
+ *    of per-device properties; it is safe to call from several host threads.
+ */
+#ifndef TILE_GEMM_H
+#define TILE_GEMM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TILE_GEMM_ABI_VERSION 1
+
+typedef enum { TG_F32 = 0, TG_BF16 = 1, TG_F16 = 2 } tg_dtype;
+
+typedef enum {
+    TG_OK = 0,
+    TG_ERR_INVALID_ARG = 1,  /* extents, strides, pointers, dtype or overlap rejected */
+    TG_ERR_UNSUPPORTED = 2,  /* no visible gfx950 device, or an option this build lacks */
+    TG_ERR_LAUNCH = 3,       /* the HIP runtime refused the launch */
+    TG_ERR_INTERNAL = 4      /* unexpected failure inside the library */
+} tg_status;
+
+/*
+ * C = alpha * A . B + beta * C for one M x N x K problem.
+ * A: M x K (lda >= max(1, K)); B: K x N (ldb >= max(1, N)); C: M x N fp32
+ * (ldc >= max(1, N)).  Pointers may be NULL only where their extent is empty.
+ */
+tg_status tile_gemm(int64_t M, int64_t N, int64_t K, tg_dtype dtype,
+                    const void *A, int64_t lda, const void *B, int64_t ldb,
+                    float *C, int64_t ldc, float alpha, float beta, void *stream);
+
+/*
+ * `batch` independent problems in one launch: problem b uses A + b*strideA,
+ * B + b*strideB and C + b*strideC (element strides, >= 0).  The C ranges of
+ * distinct b must not overlap each other (checked).  A stride of 0 shares an
+ * operand across the batch.
+ */
+tg_status tile_gemm_strided_batched(int64_t batch, int64_t M, int64_t N, int64_t K, tg_dtype dtype,
+                                    const void *A, int64_t lda, int64_t strideA,
+                                    const void *B, int64_t ldb, int64_t strideB,
+                                    float *C, int64_t ldc, int64_t strideC,
+                                    float alpha, float beta, void *stream);
+
+/* Schedule knobs, for tests and measurements; zero-initialise for defaults. */
+typedef enum {
+    TG_CFG_AUTO = 0,
+    TG_CFG_256x256 = 1,     /* 16-bit inputs: 256x256 block tile, 8 waves        */
+    TG_CFG_128x128 = 2,     /* 16-bit inputs: 128x128 block tile, 4 waves        */
+    TG_CFG_64x64 = 3,       /* 16-bit inputs: 64x64 block tile, 4 waves          */
+    TG_CFG_F32_64x64 = 4    /* fp32 inputs: 64x64 block tile, 4 waves            */
+} tg_config;
+
+typedef struct {
+    int struct_size;     /* sizeof(tg_options); a smaller value is rejected         */
+    int config;          /* tg_config; TG_CFG_AUTO picks by dtype and shape           */
+    int pipeline_depth;  /* 0 = default (2); 1 = unpipelined; 2 = window-2 pipeline  */
+    int swizzle;         /* 0 = default (XOR); 1 = none (row-major tile); 2 = XOR   */
+    int block_order;     /* 0 = default (XCD-grouped); 1 = plain row-major          */
+} tg_options;
+
+/* tile_gemm_strided_batched with explicit schedule knobs (opt may be NULL).
+ * Every combination computes the same value; options a build lacks return
+ * TG_ERR_UNSUPPORTED. */
+tg_status tile_gemm_ex(int64_t batch, int64_t M, int64_t N, int64_t K, tg_dtype dtype,
+                       const void *A, int64_t lda, int64_t strideA,
+                       const void *B, int64_t ldb, int64_t strideB,
+                       float *C, int64_t ldc, int64_t strideC,
+                       float alpha, float beta, void *stream, const tg_options *opt);
+
+/* ---- host-side introspection: no device needed, nothing launched ---------- */
+
+/* The plan a call would launch (pure host arithmetic). */
+typedef struct {
+    int config;           /* tg_config actually chosen                             */
+    int block_m, block_n, block_k;
+    int waves, threads;
+    int pipeline_depth, swizzle, block_order;
+    int64_t tiles_m, tiles_n;     /* ceil(M / block_m), ceil(N / block_n)          */
+    int64_t grid;                 /* tiles_m * tiles_n * batch workgroups          */
+    int64_t interior_blocks;      /* blocks with no M/N fringe, per problem        */
+    int64_t fringe_blocks;        /* blocks whose tile crosses M or N, per problem */
+    int64_t k_tiles;              /* ceil(K / block_k)                             */
+    int64_t k_tail;               /* K mod block_k (0: no peeled tail tile)        */
+    int lds_bytes;                /* LDS per workgroup, all pipeline copies        */
+} tg_plan_info;
+
+tg_status tile_gemm_plan(int64_t batch, int64_t M, int64_t N, int64_t K, tg_dtype dtype,
+                         const tg_options *opt, tg_plan_info *out);
+
+/*
+ * Tile layouts in the TileLayout / SwizzleLayout model of the Apache TVM TIRx
+ * "Tensor Layout" page (TileLayout, Forward mapping, SwizzleLayout and
+ * ComposeLayout sections): a logical index is flattened row-major, split over
+ * the shard iters, each component scaled by its stride onto its axis, the
+ * offset added, and every replica combination added; a swizzle, if present,
+ * then permutes the coordinate on the memory axis m:
+ *     addr(m) = f(m >> M) * 2^M + (m mod 2^M),  f(x) = x ^ ((x & ((2^B-1) << S)) >> S).
+ */
+#define TG_LAYOUT_MAX_ITERS 12
+#define TG_LAYOUT_MAX_RANK 6
+
+typedef enum { TG_AXIS_M = 0, TG_AXIS_LANE = 1, TG_AXIS_WAVE = 2, TG_AXIS_PID = 3,
+               TG_AXIS_TLANE = 4, TG_AXIS_TCOL = 5, TG_AXIS_COUNT = 6 } tg_axis;
+
+typedef struct { int64_t extent; int64_t stride; int32_t axis; int32_t pad_; } tg_iter;
+
+typedef struct {
+    int32_t rank;                             /* logical rank                      */
+    int32_t n_shard;                          /* D iters                           */
+    int32_t n_replica;                        /* R iters                           */
+    int32_t swizzle;                          /* 0: none; 1: (M, B, S) below on m   */
+    int64_t shape[TG_LAYOUT_MAX_RANK];        /* logical shape                     */
+    tg_iter shard[TG_LAYOUT_MAX_ITERS];
+    tg_iter replica[TG_LAYOUT_MAX_ITERS];
+    int64_t offset[TG_AXIS_COUNT];            /* O, one integer per axis           */
+    int32_t swz_m, swz_b, swz_s, pad_;
+} tg_layout;
+
+/*
+ * Evaluate L(x) for the logical coordinate x[0..rank).  Writes up to max_out
+ * coordinates (each TG_AXIS_COUNT int64s, row-major into out) and returns the
+ * number of coordinates in L(x), or -1 if x or the layout is invalid (shape
+ * not admitted: product of shape != product of shard extents).
+ */
+int64_t tg_layout_eval(const tg_layout *L, const int64_t *x, int64_t *out, int64_t max_out);
+
+/* Layouts the kernels use, described as tg_layouts:
+ *   TG_LAYOUT_LDS_A / _B : operand tile element (row, k) -> swizzled LDS element
+ *                          offset within one pipeline copy (B is held as
+ *                          [n][k], i.e. transposed, so both operands are
+ *                          read as k-contiguous 16-byte fragments);
+ *   TG_LAYOUT_ACC        : block accumulator element (row, col) -> (lane, wave,
+ *                          register slot m) of the MFMA register tiles;
+ *   TG_LAYOUT_COPY_A     : A tile 16-byte chunk (row, chunk) -> (lane, wave, m)
+ *                          of the thread and the load slot m that copies it. */
+typedef enum { TG_LAYOUT_LDS_A = 0, TG_LAYOUT_LDS_B = 1, TG_LAYOUT_ACC = 2,
+               TG_LAYOUT_COPY_A = 3 } tg_layout_kind;
+
+tg_status tile_gemm_describe_layout(int config, int swizzle, int kind, tg_layout *out);
+
+/* The LDS element offset the kernel itself computes for (row, k) of an operand
+ * tile (operand 0 = A, 1 = B), from the same inline function the device code
+ * calls; -1 for an invalid request.  For checking the kernel against its layout. */
+int64_t tile_gemm_lds_offset(int config, int swizzle, int operand, int64_t row, int64_t k);
+
+/* The accumulator (row, col) inside the block tile that (wave, lane, slot) of
+ * the kernel's register tiles holds, as the epilogue computes it; returns 0,
+ * or -1 for an invalid request. */
+int tile_gemm_acc_coord(int config, int wave, int lane, int slot, int64_t *row, int64_t *col);
+
+const char *tile_gemm_status_string(tg_status s);
+int tile_gemm_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TILE_GEMM_H */

@@ -1,0 +1,125 @@
+"""The C ABI on the CPU: the library loads, exports what the header declares,
+validates arguments before any device work and plans blocks as documented.
+No kernel is launched here (there is no GPU in this container)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import tile_scheduled_dense_amd as tg
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tile_gemm.h")
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", text)) - {"sizeof"})
+
+
+def test_exports_every_declared_symbol():
+    lib = ctypes.CDLL(tg.library_path())
+    declared = header_functions()
+    assert set(declared) == set(tg.EXPORTED), declared
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_abi_version_and_status_strings():
+    assert tg.abi_version() == 1
+    for s in range(5):
+        assert tg.STATUS_NAMES[s] in tg.status_string(s)
+
+
+FAKE = 0x10000  # never dereferenced: every case below fails validation or has no GPU
+
+
+def call(batch=1, M=64, N=64, K=64, dtype=tg.TG_BF16, A=FAKE, lda=None, sA=0, B=FAKE * 64, ldb=None, sB=0,
+         C=FAKE * 4096, ldc=None, sC=0, alpha=1.0, beta=0.0):
+    lda = K if lda is None else lda
+    ldb = N if ldb is None else ldb
+    ldc = N if ldc is None else ldc
+    return tg.tile_gemm_status("tile_gemm_strided_batched", batch, M, N, K, dtype, A, lda, sA, B, ldb, sB,
+                               C, ldc, sC, alpha, beta, 0)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(M=-1), dict(N=-2), dict(K=-3), dict(batch=-1),
+    dict(lda=63), dict(ldb=10), dict(ldc=63), dict(dtype=7),
+    dict(A=0), dict(B=0), dict(C=0),
+    dict(A=FAKE + 1), dict(C=FAKE * 4096 + 2),
+    dict(sA=-1), dict(batch=2, sC=64 * 63),            # batch entries of C overlap
+    dict(C=FAKE),                                      # C overlaps A
+    dict(C=FAKE * 64 + 64),                            # C overlaps B
+])
+def test_invalid_arguments_rejected_without_device(kw):
+    assert call(**kw) == tg.TG_ERR_INVALID_ARG
+
+
+def test_empty_problems_are_ok_without_device():
+    assert call(M=0) == tg.TG_OK
+    assert call(N=0, ldb=1, ldc=1) == tg.TG_OK
+    assert call(batch=0) == tg.TG_OK
+    assert call(M=0, A=0, B=0, C=0) == tg.TG_OK
+
+
+def test_no_gpu_is_unsupported():
+    # valid arguments: the only failure left is the missing gfx950 device
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is visible")
+    assert call() == tg.TG_ERR_UNSUPPORTED
+    assert call(K=0, lda=1) == tg.TG_ERR_UNSUPPORTED     # K == 0 still launches (C = beta*C)
+
+
+def test_options_validation():
+    opt = tg.Options(ctypes.sizeof(tg.Options) - 4, 0, 0, 0, 0)
+    info = tg.PlanInfo()
+    lib = tg._lib()
+    assert lib.tile_gemm_plan(1, 8, 8, 8, tg.TG_BF16, ctypes.byref(opt), ctypes.byref(info)) == tg.TG_ERR_INVALID_ARG
+    with pytest.raises(tg.TileGemmError):
+        tg.tile_gemm_plan(1, 8, 8, 8, "bf16", pipeline_depth=3)
+    with pytest.raises(tg.TileGemmError):
+        tg.tile_gemm_plan(1, 8, 8, 8, "f32", config=tg.TG_CFG_256x256)   # fp32 has its own tile
+    with pytest.raises(tg.TileGemmError):
+        tg.tile_gemm_plan(1, 8, 8, 8, "bf16", swizzle=5)
+
+
+# Block classes of the five measured problems (pad-to-tile + partition).
+@pytest.mark.parametrize("args,expect", [
+    ((1, 67, 45, 53, "f32"), dict(config=tg.TG_CFG_F32_64x64, tiles_m=2, tiles_n=1, interior_blocks=0,
+                                  fringe_blocks=2, k_tiles=2, k_tail=21)),
+    ((1, 8192, 8192, 8192, "bf16"), dict(config=tg.TG_CFG_256x256, tiles_m=32, tiles_n=32, grid=1024,
+                                         interior_blocks=1024, fringe_blocks=0, k_tiles=128, k_tail=0,
+                                         lds_bytes=131072)),
+    ((1, 8191, 8193, 8190, "bf16"), dict(config=tg.TG_CFG_256x256, tiles_m=32, tiles_n=33, grid=1056,
+                                         interior_blocks=31 * 32, fringe_blocks=1056 - 992, k_tiles=128,
+                                         k_tail=62)),
+    ((512, 257, 129, 1000, "f16"), dict(tiles_m=5, tiles_n=3, interior_blocks=8, fringe_blocks=7,
+                                        grid=15 * 512, k_tiles=16, k_tail=40)),
+    ((1, 512, 512, 131072, "bf16"), dict(k_tiles=2048, k_tail=0, fringe_blocks=0)),
+])
+def test_plan_block_classes(args, expect):
+    kw = {}
+    if args[1] == 257:
+        kw["config"] = tg.TG_CFG_64x64
+    info = tg.tile_gemm_plan(*args, **kw)
+    for k, v in expect.items():
+        assert info[k] == v, (k, info)
+
+
+def test_plan_depth_changes_lds_only():
+    a = tg.tile_gemm_plan(1, 1000, 1000, 1000, "bf16", config=tg.TG_CFG_128x128, pipeline_depth=1)
+    b = tg.tile_gemm_plan(1, 1000, 1000, 1000, "bf16", config=tg.TG_CFG_128x128, pipeline_depth=2)
+    assert b["lds_bytes"] == 2 * a["lds_bytes"] == 2 * (128 * 64 * 2 * 2)
+    assert {k: v for k, v in a.items() if k not in ("lds_bytes", "pipeline_depth")} == \
+           {k: v for k, v in b.items() if k not in ("lds_bytes", "pipeline_depth")}
+
+
+def test_lds_budget():
+    # every configuration's two pipeline copies fit the 160 KiB LDS of a gfx950 CU
+    for cfg, dt in [(1, "bf16"), (2, "bf16"), (3, "bf16"), (4, "f32")]:
+        info = tg.tile_gemm_plan(1, 4096, 4096, 4096, dt, config=cfg)
+        assert info["lds_bytes"] <= 160 * 1024

@@ -1,0 +1,243 @@
+"""tile_scheduled_dense_amd -- Python binding of the gfx950 tiled GEMM library.
+
+C = alpha * A . B + beta * C, row-major, any extents; A/B fp32, bf16 or fp16,
+C fp32.  Every step runs in the HIP kernels of ``libtile_gemm.so`` (built
+in-tree by ``build_lib.py``); this module only marshals arguments into its C
+ABI (``include/tile_gemm.h``), with the same entry-point names.  There is no
+CPU fallback: if the library is missing, every call raises.
+
+Pointers are device addresses (ints) or torch tensors (their ``data_ptr()``);
+``stream`` is a ``hipStream_t`` as an int, a ``torch.cuda.Stream``, or None for
+torch's current stream on the current device.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libtile_gemm.so")
+
+TG_F32, TG_BF16, TG_F16 = 0, 1, 2
+DTYPES = {"f32": TG_F32, "bf16": TG_BF16, "f16": TG_F16}
+
+TG_OK, TG_ERR_INVALID_ARG, TG_ERR_UNSUPPORTED, TG_ERR_LAUNCH, TG_ERR_INTERNAL = range(5)
+STATUS_NAMES = {0: "TG_OK", 1: "TG_ERR_INVALID_ARG", 2: "TG_ERR_UNSUPPORTED", 3: "TG_ERR_LAUNCH",
+                4: "TG_ERR_INTERNAL"}
+
+TG_CFG_AUTO, TG_CFG_256x256, TG_CFG_128x128, TG_CFG_64x64, TG_CFG_F32_64x64 = range(5)
+SWZ_DEFAULT, SWZ_NONE, SWZ_XOR = 0, 1, 2
+
+LAYOUT_LDS_A, LAYOUT_LDS_B, LAYOUT_ACC, LAYOUT_COPY_A = range(4)
+AXIS_M, AXIS_LANE, AXIS_WAVE, AXIS_PID, AXIS_TLANE, AXIS_TCOL = range(6)
+AXIS_COUNT = 6
+LAYOUT_MAX_ITERS = 12
+LAYOUT_MAX_RANK = 6
+
+# every symbol include/tile_gemm.h declares
+EXPORTED = ["tile_gemm", "tile_gemm_strided_batched", "tile_gemm_ex", "tile_gemm_plan",
+            "tg_layout_eval", "tile_gemm_describe_layout", "tile_gemm_lds_offset",
+            "tile_gemm_acc_coord", "tile_gemm_status_string", "tile_gemm_abi_version"]
+
+
+class TileGemmError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)}")
+
+
+class Options(ctypes.Structure):
+    _fields_ = [("struct_size", ctypes.c_int), ("config", ctypes.c_int), ("pipeline_depth", ctypes.c_int),
+                ("swizzle", ctypes.c_int), ("block_order", ctypes.c_int)]
+
+
+class PlanInfo(ctypes.Structure):
+    _fields_ = [("config", ctypes.c_int), ("block_m", ctypes.c_int), ("block_n", ctypes.c_int),
+                ("block_k", ctypes.c_int), ("waves", ctypes.c_int), ("threads", ctypes.c_int),
+                ("pipeline_depth", ctypes.c_int), ("swizzle", ctypes.c_int), ("block_order", ctypes.c_int),
+                ("tiles_m", ctypes.c_int64), ("tiles_n", ctypes.c_int64), ("grid", ctypes.c_int64),
+                ("interior_blocks", ctypes.c_int64), ("fringe_blocks", ctypes.c_int64),
+                ("k_tiles", ctypes.c_int64), ("k_tail", ctypes.c_int64), ("lds_bytes", ctypes.c_int)]
+
+    def as_dict(self):
+        return {f: getattr(self, f) for f, _ in self._fields_}
+
+
+class Iter(ctypes.Structure):
+    _fields_ = [("extent", ctypes.c_int64), ("stride", ctypes.c_int64), ("axis", ctypes.c_int32),
+                ("pad_", ctypes.c_int32)]
+
+
+class Layout(ctypes.Structure):
+    _fields_ = [("rank", ctypes.c_int32), ("n_shard", ctypes.c_int32), ("n_replica", ctypes.c_int32),
+                ("swizzle", ctypes.c_int32), ("shape", ctypes.c_int64 * LAYOUT_MAX_RANK),
+                ("shard", Iter * LAYOUT_MAX_ITERS), ("replica", Iter * LAYOUT_MAX_ITERS),
+                ("offset", ctypes.c_int64 * AXIS_COUNT), ("swz_m", ctypes.c_int32), ("swz_b", ctypes.c_int32),
+                ("swz_s", ctypes.c_int32), ("pad_", ctypes.c_int32)]
+
+
+_lib_handle = None
+
+
+def library_path() -> str:
+    return LIB_PATH
+
+
+def _lib():
+    global _lib_handle
+    if _lib_handle is not None:
+        return _lib_handle
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python -m tile_scheduled_dense_amd.build_lib` "
+                          "(or __graft_entry__.build())")
+    lib = ctypes.CDLL(LIB_PATH)
+    i64, f32, vp, ci = ctypes.c_int64, ctypes.c_float, ctypes.c_void_p, ctypes.c_int
+    lib.tile_gemm.argtypes = [i64, i64, i64, ci, vp, i64, vp, i64, vp, i64, f32, f32, vp]
+    lib.tile_gemm.restype = ci
+    lib.tile_gemm_strided_batched.argtypes = [i64, i64, i64, i64, ci, vp, i64, i64, vp, i64, i64,
+                                              vp, i64, i64, f32, f32, vp]
+    lib.tile_gemm_strided_batched.restype = ci
+    lib.tile_gemm_ex.argtypes = [i64, i64, i64, i64, ci, vp, i64, i64, vp, i64, i64, vp, i64, i64,
+                                 f32, f32, vp, ctypes.POINTER(Options)]
+    lib.tile_gemm_ex.restype = ci
+    lib.tile_gemm_plan.argtypes = [i64, i64, i64, i64, ci, ctypes.POINTER(Options), ctypes.POINTER(PlanInfo)]
+    lib.tile_gemm_plan.restype = ci
+    lib.tg_layout_eval.argtypes = [ctypes.POINTER(Layout), ctypes.POINTER(i64), ctypes.POINTER(i64), i64]
+    lib.tg_layout_eval.restype = i64
+    lib.tile_gemm_describe_layout.argtypes = [ci, ci, ci, ctypes.POINTER(Layout)]
+    lib.tile_gemm_describe_layout.restype = ci
+    lib.tile_gemm_lds_offset.argtypes = [ci, ci, ci, i64, i64]
+    lib.tile_gemm_lds_offset.restype = i64
+    lib.tile_gemm_acc_coord.argtypes = [ci, ci, ci, ci, ctypes.POINTER(i64), ctypes.POINTER(i64)]
+    lib.tile_gemm_acc_coord.restype = ci
+    lib.tile_gemm_status_string.argtypes = [ci]
+    lib.tile_gemm_status_string.restype = ctypes.c_char_p
+    lib.tile_gemm_abi_version.restype = ci
+    _lib_handle = lib
+    return lib
+
+
+def _addr(x) -> Optional[int]:
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    if hasattr(x, "data_ptr"):
+        return int(x.data_ptr())
+    raise TypeError(f"expected a device address or a tensor, got {type(x)!r}")
+
+
+def _stream(s) -> int:
+    if s is None:
+        import torch
+        return int(torch.cuda.current_stream().cuda_stream) if torch.cuda.is_available() else 0
+    if isinstance(s, int):
+        return s
+    if hasattr(s, "cuda_stream"):
+        return int(s.cuda_stream)
+    raise TypeError(f"expected a stream, got {type(s)!r}")
+
+
+def _dtype(d) -> int:
+    return DTYPES[d] if isinstance(d, str) else int(d)
+
+
+def _options(config=0, pipeline_depth=0, swizzle=0, block_order=0) -> Options:
+    return Options(ctypes.sizeof(Options), int(config), int(pipeline_depth), int(swizzle), int(block_order))
+
+
+def _check(status: int, where: str):
+    if status != TG_OK:
+        raise TileGemmError(status, where)
+
+
+def status_string(status: int) -> str:
+    return _lib().tile_gemm_status_string(int(status)).decode()
+
+
+def abi_version() -> int:
+    return int(_lib().tile_gemm_abi_version())
+
+
+def tile_gemm(M, N, K, dtype, A, lda, B, ldb, C, ldc, alpha=1.0, beta=0.0, stream=None) -> None:
+    _check(_lib().tile_gemm(M, N, K, _dtype(dtype), _addr(A), lda, _addr(B), ldb, _addr(C), ldc,
+                            alpha, beta, _stream(stream)), "tile_gemm")
+
+
+def tile_gemm_strided_batched(batch, M, N, K, dtype, A, lda, strideA, B, ldb, strideB, C, ldc, strideC,
+                              alpha=1.0, beta=0.0, stream=None) -> None:
+    _check(_lib().tile_gemm_strided_batched(batch, M, N, K, _dtype(dtype), _addr(A), lda, strideA,
+                                            _addr(B), ldb, strideB, _addr(C), ldc, strideC, alpha, beta,
+                                            _stream(stream)), "tile_gemm_strided_batched")
+
+
+def tile_gemm_ex(batch, M, N, K, dtype, A, lda, strideA, B, ldb, strideB, C, ldc, strideC,
+                 alpha=1.0, beta=0.0, stream=None, config=0, pipeline_depth=0, swizzle=0,
+                 block_order=0) -> None:
+    opt = _options(config, pipeline_depth, swizzle, block_order)
+    _check(_lib().tile_gemm_ex(batch, M, N, K, _dtype(dtype), _addr(A), lda, strideA, _addr(B), ldb, strideB,
+                               _addr(C), ldc, strideC, alpha, beta, _stream(stream), ctypes.byref(opt)),
+           "tile_gemm_ex")
+
+
+def tile_gemm_status(fn: str, *args) -> int:
+    """Call an entry point and return its raw status instead of raising (argument-error tests)."""
+    return int(getattr(_lib(), fn)(*args))
+
+
+def tile_gemm_plan(batch, M, N, K, dtype, config=0, pipeline_depth=0, swizzle=0, block_order=0) -> dict:
+    info = PlanInfo()
+    opt = _options(config, pipeline_depth, swizzle, block_order)
+    _check(_lib().tile_gemm_plan(batch, M, N, K, _dtype(dtype), ctypes.byref(opt), ctypes.byref(info)),
+           "tile_gemm_plan")
+    return info.as_dict()
+
+
+def make_layout(shape, shard, replica=(), offset=None, swizzle=None) -> Layout:
+    """Build a tg_layout: shard/replica are (extent, stride, axis) triples."""
+    L = Layout()
+    L.rank = len(shape)
+    for d, e in enumerate(shape):
+        L.shape[d] = e
+    L.n_shard = len(shard)
+    for k, (e, s, a) in enumerate(shard):
+        L.shard[k] = Iter(e, s, a, 0)
+    L.n_replica = len(replica)
+    for k, (e, s, a) in enumerate(replica):
+        L.replica[k] = Iter(e, s, a, 0)
+    for a, v in (offset or {}).items():
+        L.offset[a] = v
+    if swizzle is not None:
+        L.swizzle = 1
+        L.swz_m, L.swz_b, L.swz_s = swizzle
+    return L
+
+
+def tg_layout_eval(layout: Layout, x) -> list:
+    """All coordinates of L(x), each a tuple of AXIS_COUNT ints."""
+    xs = (ctypes.c_int64 * len(x))(*x)
+    n = _lib().tg_layout_eval(ctypes.byref(layout), xs, None, 0)
+    if n < 0:
+        raise ValueError("invalid layout or coordinate")
+    out = (ctypes.c_int64 * (AXIS_COUNT * max(n, 1)))()
+    _lib().tg_layout_eval(ctypes.byref(layout), xs, out, n)
+    return [tuple(out[r * AXIS_COUNT:(r + 1) * AXIS_COUNT]) for r in range(n)]
+
+
+def tile_gemm_describe_layout(config, swizzle, kind) -> Layout:
+    L = Layout()
+    _check(_lib().tile_gemm_describe_layout(config, swizzle, kind, ctypes.byref(L)), "tile_gemm_describe_layout")
+    return L
+
+
+def tile_gemm_lds_offset(config, swizzle, operand, row, k) -> int:
+    return int(_lib().tile_gemm_lds_offset(config, swizzle, operand, row, k))
+
+
+def tile_gemm_acc_coord(config, wave, lane, slot):
+    r, c = ctypes.c_int64(), ctypes.c_int64()
+    rc = _lib().tile_gemm_acc_coord(config, wave, lane, slot, ctypes.byref(r), ctypes.byref(c))
+    if rc != 0:
+        raise ValueError("invalid accumulator slot")
+    return int(r.value), int(c.value)

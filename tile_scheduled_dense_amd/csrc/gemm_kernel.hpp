@@ -1,0 +1,379 @@
+// gemm_kernel.hpp -- the gfx950 kernel family for C = alpha * A.B + beta * C.
+//
+// One workgroup computes one BM x BN tile of C (a Split of the M and N loops,
+// OCANNL "Module Ir.Schedule", Split; the workgroups are LuisaCompute's
+// independent `parallel` children, "Execution Nests and coordinates",
+// structured-region calculus, so they write disjoint tiles with no atomics).
+//
+// Per workgroup:
+//  1. block order: the hardware hands consecutive workgroup ids to the eight
+//     XCDs in turn; the id is remapped so each XCD receives a contiguous run of
+//     tiles, walked in groups of GROUP_M tile rows, so tiles that share A and B
+//     panels are resident on one XCD's L2 at the same time (the ParallelMap
+//     "reshape, permute or swizzle child coordinates" of the LuisaCompute page).
+//  2. pad-to-tile + partition (OCANNL Pad and Partition paragraphs): the
+//     extents are padded to the tile; a block whose tile lies inside M x N runs
+//     the guard-free instantiation, a block crossing M or N runs the one whose
+//     copies guard rows/columns.  The K loop is partitioned at the last whole
+//     tile: every tile but a ragged last one uses unguarded loads; the tail tile
+//     zero-fills k >= K in both operands (a NaN in A's lda padding times a zero
+//     of B would otherwise poison C).  Row/column masks of the output sit only
+//     on the accumulator store-back.
+//  3. staging (OCANNL Stage paragraph, shared + cooperative): each element of
+//     the A and B tiles is copied by exactly one thread with 16-byte global
+//     loads; the A and B copies form one phase with no barrier between them.
+//     B is transposed in registers on its way to LDS so both operands are held
+//     k-contiguous.  Placement: the XOR swizzle in tile_config.hpp.
+//  4. window-2 pipeline (OCANNL pipeline_depth = 2; LuisaCompute "Pipelines and
+//     stage boundaries", window = 2): a prologue copies tile 0 into LDS copy 0;
+//     iteration k issues the global loads of tile k+1, multiplies tile k from
+//     copy k mod 2, then writes tile k+1 into copy (k+1) mod 2, and closes with
+//     one barrier -- N + 1 barriers for N tiles.  The barrier is the release of
+//     the copy read in iteration k before iteration k+1 overwrites it (issue,
+//     completion and release are distinct events: a slot is reused only after
+//     every reader is done).  Depth 1 (2 barriers per tile) is kept as an option
+//     and reads the same values in the same order, so it is bitwise identical.
+//  5. tensorized multiply-accumulate (OCANNL Tensorize; Privatize): MFMA
+//     32x32x16 for bf16/fp16, 16x16x4 for fp32, over the wave's TM x TN
+//     register tiles, accumulators privatised in registers from +0.
+//  6. fused epilogue (OCANNL epilogue fusion): C = fma(alpha, acc, beta * C0)
+//     (alpha * acc when beta == 0, C0 not read), one store per element.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "tile_config.hpp"
+
+namespace tg {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+struct GemmParams {
+    const char *A;
+    const char *B;
+    float *C;
+    int64_t M, N, K;
+    int64_t lda, ldb, ldc;
+    int64_t sA, sB, sC;          // batch strides, elements
+    int64_t tiles_m, tiles_n, batch;
+    float alpha, beta;
+    int block_order;             // 0: XCD-grouped, 1: plain
+    int group_m;                 // tile rows per group in the grouped order
+};
+
+template <class C>
+struct AccT {
+    typedef typename std::conditional<C::MT == 32, f32x16, f32x4>::type type;
+};
+
+// ---- block order -----------------------------------------------------------
+__device__ __forceinline__ void block_coords(const GemmParams &p, int64_t &b, int64_t &tm, int64_t &tn) {
+    // The grid is below 2^31 workgroups (checked on the host): 32-bit math.
+    const uint32_t tiles_m = (uint32_t)p.tiles_m, tiles_n = (uint32_t)p.tiles_n;
+    const uint32_t per_batch = tiles_m * tiles_n;
+    const uint32_t total = per_batch * (uint32_t)p.batch;
+    const uint32_t w = blockIdx.x;
+    uint32_t lid = w;
+    if (p.block_order == 0) {
+        // Undo the round-robin over 8 XCDs: XCD x = w % 8 gets the x-th
+        // contiguous run of logical tiles.
+        const uint32_t per = total / 8, rem = total % 8;
+        const uint32_t x = w % 8, j = w / 8;
+        lid = x * per + (x < rem ? x : rem) + j;
+    }
+    b = lid / per_batch;
+    const uint32_t t = lid % per_batch;
+    if (p.block_order == 0) {
+        const uint32_t gm = (uint32_t)p.group_m;
+        const uint32_t group = t / (gm * tiles_n);
+        const uint32_t first_m = group * gm;
+        const uint32_t rows = (tiles_m - first_m) < gm ? (tiles_m - first_m) : gm;
+        const uint32_t in_g = t % (gm * tiles_n);
+        tm = first_m + in_g % rows;
+        tn = in_g / rows;
+    } else {
+        tm = t / tiles_n;
+        tn = t % tiles_n;
+    }
+}
+
+// ---- 16-byte chunk loads -----------------------------------------------------
+// Tile copies go through buffer loads: a 128-bit resource (base pointer, size
+// limit) in scalar registers plus one 32-bit byte offset per lane, so a thread
+// needs a single address register however many chunks it copies.  Rows need
+// not be 16-byte aligned (odd lda, packed batches): gfx950 serves an unaligned
+// 128-bit load as one instruction.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const char *base) {
+    // The base is the same for the whole workgroup; say so, so the resource
+    // lives in scalar registers.
+    const uint64_t a = (uint64_t)base;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    const char *u = (const char *)(((uint64_t)hi << 32) | lo);
+    // stride 0 (raw buffer), offsets up to 2^31 - 1 bytes, gfx9 data format word
+    return __builtin_amdgcn_make_buffer_rsrc((void *)u, (short)0, 0x7fffffff, 0x00020000);
+}
+
+__device__ __forceinline__ u32x4 bload16(rsrc_t r, int voff, int soff) {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+
+// A chunk of which only the first n elements exist (0 <= n <= CHUNK); the
+// rest is +0 -- the zero fill of a staged tile's fringe.
+template <int ELEM>
+__device__ __forceinline__ u32x4 bload16_n(rsrc_t r, int voff, int soff, int n) {
+    constexpr int CHUNK = 16 / ELEM;
+    if (n >= CHUNK) return bload16(r, voff, soff);
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (ELEM == 4) {
+#pragma unroll
+        for (int e = 0; e < 3; ++e)
+            if (e < n) v[e] = __builtin_amdgcn_raw_buffer_load_b32(r, voff + 4 * e, soff, 0);
+    } else {
+#pragma unroll
+        for (int e = 0; e < 7; ++e) {
+            if (e < n) {
+                const uint32_t h = __builtin_amdgcn_raw_buffer_load_b16(r, voff + 2 * e, soff, 0);
+                v[e >> 1] |= (e & 1) ? (h << 16) : h;
+            }
+        }
+    }
+    return v;
+}
+
+// Transpose a CHUNK x CHUNK square held as CHUNK rows of 16 bytes: on return
+// out[c] holds column c, i.e. the CHUNK k-values of one n.
+template <int ELEM>
+__device__ __forceinline__ void transpose_square(const u32x4 *in, u32x4 *out) {
+    if (ELEM == 4) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+            out[c] = u32x4{in[0][c], in[1][c], in[2][c], in[3][c]};
+    } else {
+        // in[r][w] packs elements (r, 2w) (low half) and (r, 2w+1) (high half).
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            u32x4 ev, od;
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {
+                const uint32_t lo = in[2 * h][w], hi = in[2 * h + 1][w];
+                ev[h] = (lo & 0xffffu) | (hi << 16);            // column 2w, k = 2h, 2h+1
+                od[h] = (lo >> 16) | (hi & 0xffff0000u);        // column 2w+1
+            }
+            out[2 * w] = ev;
+            out[2 * w + 1] = od;
+        }
+    }
+}
+
+// ---- MFMA ---------------------------------------------------------------------
+template <int DT>
+__device__ __forceinline__ void mfma_chunk(const u32x4 &a, const u32x4 &b, f32x16 &acc) {
+    if constexpr (DT == DT_BF16) {
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                       __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
+    } else {
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                      __builtin_bit_cast(f16x8, b), acc, 0, 0, 0);
+    }
+}
+
+template <int DT>
+__device__ __forceinline__ void mfma_chunk(const u32x4 &a, const u32x4 &b, f32x4 &acc) {
+    // four 16x16x4 fp32 MFMAs; element e of both chunks is the same k.
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__builtin_bit_cast(float, a[e]),
+                                                   __builtin_bit_cast(float, b[e]), acc, 0, 0, 0);
+}
+
+// ---- one workgroup tile ----------------------------------------------------------
+template <class C, int DEPTH, int SWZ, bool FRINGE>
+__device__ __forceinline__ void gemm_tile(const GemmParams &p, char *smem, int64_t b, int64_t tm, int64_t tn) {
+    using Acc = typename AccT<C>::type;
+    constexpr int E = C::ELEM;
+    constexpr int NST = C::A_PER_THREAD > C::B_PER_THREAD * C::CHUNK ? C::A_PER_THREAD
+                                                                     : C::B_PER_THREAD * C::CHUNK;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const bool a_loader = tid < C::LOADERS;           // wave-uniform
+    const int lt = a_loader ? tid : tid - C::LOADERS;  // loader-local thread id
+
+    const int64_t M = p.M, N = p.N, K = p.K;
+    const int64_t m0 = tm * C::BM, n0 = tn * C::BN;
+    const int lda = (int)p.lda, ldb = (int)p.ldb, ldc = (int)p.ldc;
+    const char *Ablk = p.A + (b * p.sA + m0 * p.lda) * E;   // A[b][m0][0]
+    const char *Bblk = p.B + (b * p.sB + n0) * E;           // B[b][0][n0]
+    const int64_t nk = (K + C::BK - 1) / C::BK;
+    const bool ragged_k = (K % C::BK) != 0;
+
+    Acc acc[C::TM][C::TN];
+#pragma unroll
+    for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::TN; ++j)
+            acc[i][j] = Acc{};
+
+    u32x4 st[NST];
+
+    // -- global -> registers for K tile kt (guard only where the tile needs it)
+    auto gload = [&](int64_t kt) {
+        const int64_t k0 = kt * C::BK;
+        const bool guard = FRINGE || (ragged_k && kt == nk - 1);
+        if (a_loader) {
+            const rsrc_t ra = make_rsrc(Ablk + k0 * E);
+#pragma unroll
+            for (int q = 0; q < C::A_PER_THREAD; ++q) {
+                int row, ch;
+                copy_a_chunk<C>(lt, q, row, ch);
+                const int off = (row * lda + ch * C::CHUNK) * E;
+                if (!guard) {
+                    st[q] = bload16(ra, off, 0);
+                } else {
+                    const int64_t left = K - (k0 + ch * C::CHUNK);
+                    const bool row_ok = !FRINGE || (m0 + row < M);
+                    const int n = !row_ok || left <= 0 ? 0 : (left >= C::CHUNK ? C::CHUNK : (int)left);
+                    st[q] = bload16_n<E>(ra, off, 0, n);
+                }
+            }
+        } else {
+            const rsrc_t rb = make_rsrc(Bblk + k0 * p.ldb * E);
+#pragma unroll
+            for (int u = 0; u < C::B_PER_THREAD; ++u) {
+                int kb, nb;
+                copy_b_unit<C>(lt, u, kb, nb);
+                const int64_t cols_left = N - (n0 + nb * C::CHUNK);
+                const int ncol = !FRINGE ? C::CHUNK
+                                 : (cols_left <= 0 ? 0 : (cols_left >= C::CHUNK ? C::CHUNK : (int)cols_left));
+#pragma unroll
+                for (int r = 0; r < C::CHUNK; ++r) {
+                    const int krow = kb * C::CHUNK + r;
+                    const int off = (krow * ldb + nb * C::CHUNK) * E;
+                    if (!guard) {
+                        st[u * C::CHUNK + r] = bload16(rb, off, 0);
+                    } else {
+                        const int n = k0 + krow < K ? ncol : 0;
+                        st[u * C::CHUNK + r] = bload16_n<E>(rb, off, 0, n);
+                    }
+                }
+            }
+        }
+    };
+
+    // -- registers -> LDS copy `buf`
+    auto lstore = [&](int buf) {
+        char *sA = smem + buf * C::STAGE_BYTES;
+        char *sB = sA + C::A_TILE_BYTES;
+        if (a_loader) {
+#pragma unroll
+            for (int q = 0; q < C::A_PER_THREAD; ++q) {
+                int row, ch;
+                copy_a_chunk<C>(lt, q, row, ch);
+                *(u32x4 *)(sA + lds_chunk_byte<C>(row, ch, SWZ)) = st[q];
+            }
+        } else {
+#pragma unroll
+            for (int u = 0; u < C::B_PER_THREAD; ++u) {
+                int kb, nb;
+                copy_b_unit<C>(lt, u, kb, nb);
+                u32x4 col[C::CHUNK];
+                transpose_square<E>(&st[u * C::CHUNK], col);
+#pragma unroll
+                for (int c = 0; c < C::CHUNK; ++c)
+                    *(u32x4 *)(sB + lds_chunk_byte<C>(nb * C::CHUNK + c, kb, SWZ)) = col[c];
+            }
+        }
+    };
+
+    // -- MFMA over LDS copy `buf`
+    const int wrow = (wave / C::WAVES_N) * C::WTM;
+    const int wcol = (wave % C::WAVES_N) * C::WTN;
+    auto compute = [&](int buf) {
+        const char *sA = smem + buf * C::STAGE_BYTES;
+        const char *sB = sA + C::A_TILE_BYTES;
+#pragma unroll
+        for (int s = 0; s < C::KSTEPS; ++s) {
+            const int ch = frag_chunk<C>(s, lane);
+            u32x4 af[C::TM], bfr[C::TN];
+#pragma unroll
+            for (int i = 0; i < C::TM; ++i)
+                af[i] = *(const u32x4 *)(sA + lds_chunk_byte<C>(wrow + i * C::MT + lane % C::MT, ch, SWZ));
+#pragma unroll
+            for (int j = 0; j < C::TN; ++j)
+                bfr[j] = *(const u32x4 *)(sB + lds_chunk_byte<C>(wcol + j * C::MT + lane % C::MT, ch, SWZ));
+#pragma unroll
+            for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+                for (int j = 0; j < C::TN; ++j)
+                    mfma_chunk<C::DT>(af[i], bfr[j], acc[i][j]);
+        }
+    };
+
+    if (nk > 0) {
+        // prologue: tile 0 -> copy 0
+        gload(0);
+        lstore(0);
+        __syncthreads();
+        if (DEPTH == 2) {
+            for (int64_t kt = 0; kt < nk; ++kt) {
+                const int cur = (int)(kt & 1);
+                const bool more = kt + 1 < nk;
+                if (more) gload(kt + 1);      // prefetch issued before the compute that hides it
+                compute(cur);
+                if (more) lstore(cur ^ 1);
+                __syncthreads();             // publishes copy cur^1, releases copy cur
+            }
+        } else {
+            for (int64_t kt = 0; kt < nk; ++kt) {
+                compute(0);
+                if (kt + 1 < nk) {
+                    __syncthreads();         // every reader of copy 0 is done
+                    gload(kt + 1);
+                    lstore(0);
+                    __syncthreads();         // copy 0 holds tile kt+1
+                }
+            }
+        }
+    }
+
+    // -- epilogue: fused alpha/beta store-back, masks only here
+    float *Cblk = p.C + b * p.sC + m0 * p.ldc + n0;
+    const float alpha = p.alpha, beta = p.beta;
+#pragma unroll
+    for (int i = 0; i < C::TM; ++i) {
+#pragma unroll
+        for (int j = 0; j < C::TN; ++j) {
+#pragma unroll
+            for (int v = 0; v < C::ACC_PER_MFMA; ++v) {
+                int row, col;
+                acc_coord<C>(wave, lane, (i * C::TN + j) * C::ACC_PER_MFMA + v, row, col);
+                if (FRINGE && !(m0 + row < M && n0 + col < N)) continue;
+                float *dst = Cblk + (row * ldc + col);
+                const float a = acc[i][j][v];
+                *dst = beta != 0.0f ? __builtin_fmaf(alpha, a, beta * *dst) : alpha * a;
+            }
+        }
+    }
+}
+
+template <class C, int DEPTH, int SWZ>
+__global__ __launch_bounds__(C::THREADS, 1) void gemm_kernel(GemmParams p) {
+    __shared__ __attribute__((aligned(16))) char smem[(DEPTH == 2 ? 2 : 1) * C::STAGE_BYTES];
+    int64_t b, tm, tn;
+    block_coords(p, b, tm, tn);
+    const bool interior = (tm + 1) * C::BM <= p.M && (tn + 1) * C::BN <= p.N;
+    if (interior) gemm_tile<C, DEPTH, SWZ, false>(p, smem, b, tm, tn);
+    else gemm_tile<C, DEPTH, SWZ, true>(p, smem, b, tm, tn);
+}
+
+}  // namespace tg

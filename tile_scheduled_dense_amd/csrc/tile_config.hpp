@@ -1,0 +1,164 @@
+// tile_config.hpp -- compile-time tile configurations and the index maps the
+// kernels use, as __host__ __device__ functions so the host can evaluate
+// exactly what the device computes.
+//
+// Vocabulary follows the OCANNL "Module Ir.Schedule" page: a block tile is a
+// Split of the M and N loops, the K loop is Split by BK and Staged through a
+// workgroup-shared tile with an XOR swizzle, the per-wave register tile is the
+// materialised Unroll of the MFMA loop nest (register blocktiling), and the
+// accumulator is Privatized into registers.
+#pragma once
+
+#include <stdint.h>
+
+#if defined(__HIPCC__)
+#define TG_HD __host__ __device__ __forceinline__
+#else
+#define TG_HD inline
+#endif
+
+namespace tg {
+
+enum DType : int { DT_F32 = 0, DT_BF16 = 1, DT_F16 = 2 };
+
+// One configuration of the kernel family.
+//  * BK is chosen so one tile row is 128 bytes -- exactly one LDS bank line of
+//    32 x 4-byte banks, the row width for which the TIRx "Tensor Layout" page
+//    (Worked example; Choosing the parameters) shows an 8-row, 16-byte column
+//    read is conflict-free under Swizzle(M, 3, 3).
+//  * Both operands are staged k-contiguous: A as [BM][BK], B transposed as
+//    [BN][BK], so every MFMA operand fragment is one 16-byte LDS read.
+template <int DT_, int BM_, int BN_, int WAVES_M_, int WAVES_N_>
+struct TileCfg {
+    static constexpr int DT = DT_;
+    static constexpr int ELEM = DT_ == DT_F32 ? 4 : 2;       // bytes per input element
+    static constexpr int BM = BM_, BN = BN_;
+    static constexpr int BK = 128 / ELEM;                    // 64 (16-bit) or 32 (fp32)
+    static constexpr int CHUNK = 16 / ELEM;                  // elements per 16-byte chunk
+    static constexpr int CPR = BK / CHUNK;                   // chunks per tile row (8)
+    static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
+    static constexpr int WAVES = WAVES_M_ * WAVES_N_;
+    static constexpr int THREADS = 64 * WAVES;
+    // MFMA shape: 32x32x16 for bf16/fp16, 16x16x4 for fp32.
+    static constexpr int MT = DT_ == DT_F32 ? 16 : 32;       // MFMA tile edge (rows = cols)
+    static constexpr int ACC_PER_MFMA = MT * MT / 64;        // accumulators per lane per MFMA tile
+    static constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;   // wave tile
+    static constexpr int TM = WTM / MT, TN = WTN / MT;       // MFMA tiles per wave
+    static constexpr int LANE_GROUPS = 64 / MT;              // lanes sharing a row: 2 or 4
+    static constexpr int KSTEPS = CPR / LANE_GROUPS;         // fragment reads per K tile
+    // Global -> LDS copy: the first half of the threads copy A, the second B.
+    static constexpr int LOADERS = THREADS / 2;
+    static constexpr int A_CHUNKS = BM * CPR;                // 16-byte chunks in an A tile
+    static constexpr int A_PER_THREAD = A_CHUNKS / LOADERS;
+    static constexpr int B_UNITS = (BK / CHUNK) * (BN / CHUNK);   // CHUNK x CHUNK squares
+    static constexpr int B_PER_THREAD = B_UNITS / LOADERS;
+    static constexpr int A_TILE_BYTES = BM * BK * ELEM;
+    static constexpr int B_TILE_BYTES = BN * BK * ELEM;
+    static constexpr int STAGE_BYTES = A_TILE_BYTES + B_TILE_BYTES;
+
+    static_assert(BM % (WAVES_M * MT) == 0 && BN % (WAVES_N * MT) == 0, "wave tiling");
+    static_assert(CPR == 8, "tile rows are one 128-byte bank line");
+    static_assert(A_CHUNKS % LOADERS == 0 && A_PER_THREAD >= 1, "A copy split");
+    static_assert(B_UNITS % LOADERS == 0 && B_PER_THREAD >= 1, "B copy split");
+};
+
+// The shipped configurations (ids match tg_config in tile_gemm.h).
+template <int DT> using Cfg256 = TileCfg<DT, 256, 256, 2, 4>;  // 8 waves, wave tile 128 x 64
+template <int DT> using Cfg128 = TileCfg<DT, 128, 128, 2, 2>;  // 4 waves, wave tile 64 x 64
+template <int DT> using Cfg64 = TileCfg<DT, 64, 64, 1, 2>;     // 2 waves, wave tile 64 x 32
+using CfgF32 = TileCfg<DT_F32, 64, 64, 2, 2>;                  // 4 waves, wave tile 32 x 32 (16x16 MFMA)
+
+enum Swz : int { SWZ_NONE = 1, SWZ_XOR = 2 };
+
+// ---------------------------------------------------------------------------
+// LDS placement of one operand tile (rows x BK, k contiguous).
+//
+// The tile layout S[(rows, BK):(BK@m, 1@m)] gives the row-major element
+// address m = row*BK + k; the swizzle of the TIRx page then permutes it:
+//     addr(m) = f(m >> M) * 2^M + (m mod 2^M),   f(x) = x ^ ((x & (7 << 3)) >> 3)
+// with M = log2(elements per 16 bytes) (3 for 16-bit, 2 for fp32), B = 3 and
+// S = 3.  With 8 chunks per row, f XORs the row's low three bits into the
+// chunk index: a per-row bijection of 16-byte units (the Swizzle_b128 flavour
+// of the OCANNL Stage paragraph), so each 16-byte fragment stays contiguous.
+// ---------------------------------------------------------------------------
+TG_HD int64_t swizzle_apply(int64_t m, int M, int B, int S) {
+    int64_t x = m >> M;
+    int64_t f = x ^ ((x & (((int64_t(1) << B) - 1) << S)) >> S);
+    return (f << M) + (m & ((int64_t(1) << M) - 1));
+}
+
+template <class C>
+TG_HD int lds_elem(int row, int k, int swz) {
+    int m = row * C::BK + k;
+    if (swz == SWZ_NONE) return m;
+    constexpr int M = C::ELEM == 2 ? 3 : 2;
+    return (int)swizzle_apply(m, M, 3, 3);
+}
+
+// Byte offset of 16-byte chunk `chunk` of tile row `row` (the unit every
+// LDS write and fragment read moves).
+template <class C>
+TG_HD int lds_chunk_byte(int row, int chunk, int swz) {
+    int c = swz == SWZ_NONE ? chunk : (chunk ^ (row & 7));
+    return (row * C::CPR + c) * 16;
+}
+
+// ---------------------------------------------------------------------------
+// MFMA register tiles.  Wave w owns the wave tile at
+//   (w / WAVES_N) * WTM, (w % WAVES_N) * WTN
+// split into TM x TN MFMA tiles; accumulator slot
+//   s = (i * TN + j) * ACC_PER_MFMA + v
+// of lane l holds element (row, col) of MFMA tile (i, j) with
+//   32x32 (16-bit):  col = l % 32, row = 8 * (v / 4) + 4 * (l / 32) + v % 4
+//   16x16 (fp32):    col = l % 16, row = 4 * (l / 16) + v
+// ---------------------------------------------------------------------------
+template <class C>
+TG_HD void acc_coord(int wave, int lane, int slot, int &row, int &col) {
+    int tile = slot / C::ACC_PER_MFMA, v = slot % C::ACC_PER_MFMA;
+    int i = tile / C::TN, j = tile % C::TN;
+    int r, c;
+    if (C::MT == 32) {
+        c = lane % 32;
+        r = 8 * (v / 4) + 4 * (lane / 32) + v % 4;
+    } else {
+        c = lane % 16;
+        r = 4 * (lane / 16) + v;
+    }
+    row = (wave / C::WAVES_N) * C::WTM + i * C::MT + r;
+    col = (wave % C::WAVES_N) * C::WTN + j * C::MT + c;
+}
+
+// Fragment read: for K sub-step s, lane l reads 16-byte chunk
+//   LANE_GROUPS * s + l / MT
+// of tile row (wave row base + i*MT + l % MT).  For 16-bit inputs the chunk's
+// 8 consecutive k are the lane's MFMA operand; for fp32 the chunk's 4 k feed 4
+// consecutive 16x16x4 MFMAs (element e to MFMA e).  A and B lanes use the same
+// k assignment, so every k of the tile meets its partner exactly once.
+template <class C>
+TG_HD int frag_chunk(int s, int lane) { return C::LANE_GROUPS * s + lane / C::MT; }
+
+// Copy ownership of the A tile: loader thread t (0 <= t < LOADERS) copies
+// chunks q = t + LOADERS * p, p < A_PER_THREAD, i.e. row q / 8, chunk q % 8:
+// eight consecutive lanes cover one 128-byte row (a coalesced global read and
+// eight distinct swizzled LDS slots).
+template <class C>
+TG_HD void copy_a_chunk(int t, int p, int &row, int &chunk) {
+    int q = t + C::LOADERS * p;
+    row = q / C::CPR;
+    chunk = q % C::CPR;
+}
+
+// Copy ownership of the B tile: loader thread t copies the CHUNK x CHUNK
+// square kb = u % 8, nb = u / 8 with u = t + LOADERS * p: CHUNK global rows of
+// 16 bytes each, transposed in registers into CHUNK k-contiguous chunks (one
+// per column n = nb*CHUNK + c), written to LDS row n, chunk kb.  Eight
+// consecutive lanes take eight different kb, so their writes of one column
+// index c land on eight distinct swizzled slots.
+template <class C>
+TG_HD void copy_b_unit(int t, int p, int &kb, int &nb) {
+    int u = t + C::LOADERS * p;
+    kb = u % C::CPR;
+    nb = u / C::CPR;
+}
+
+}  // namespace tg

@@ -1,0 +1,315 @@
+// tile_gemm.hip -- the C ABI: argument validation, planning, kernel selection
+// and launch on the caller's stream.  Declarations and contracts are in
+// include/tile_gemm.h.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstring>
+#include <mutex>
+#include <new>
+
+#include "gemm_kernel.hpp"
+#include "tile_gemm.h"
+
+using namespace tg;
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+
+struct DeviceState {
+    bool probed = false;
+    bool gfx950 = false;
+};
+
+std::mutex g_mutex;
+DeviceState g_devices[kMaxDevices];
+
+// gfx950 check for the current device, cached per device.
+tg_status current_device_ok() {
+    int count = 0;
+    if (hipGetDeviceCount(&count) != hipSuccess || count <= 0) {
+        (void)hipGetLastError();
+        return TG_ERR_UNSUPPORTED;
+    }
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        (void)hipGetLastError();
+        return TG_ERR_UNSUPPORTED;
+    }
+    std::lock_guard<std::mutex> lock(g_mutex);
+    DeviceState &d = g_devices[dev];
+    if (!d.probed) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+            (void)hipGetLastError();
+            return TG_ERR_UNSUPPORTED;
+        }
+        d.gfx950 = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+        d.probed = true;
+    }
+    return d.gfx950 ? TG_OK : TG_ERR_UNSUPPORTED;
+}
+
+struct CfgDims {
+    int bm, bn, bk, waves;
+};
+
+CfgDims cfg_dims(int config) {
+    switch (config) {
+        case TG_CFG_256x256: return {Cfg256<DT_BF16>::BM, Cfg256<DT_BF16>::BN, Cfg256<DT_BF16>::BK, Cfg256<DT_BF16>::WAVES};
+        case TG_CFG_128x128: return {Cfg128<DT_BF16>::BM, Cfg128<DT_BF16>::BN, Cfg128<DT_BF16>::BK, Cfg128<DT_BF16>::WAVES};
+        case TG_CFG_64x64: return {Cfg64<DT_BF16>::BM, Cfg64<DT_BF16>::BN, Cfg64<DT_BF16>::BK, Cfg64<DT_BF16>::WAVES};
+        case TG_CFG_F32_64x64: return {CfgF32::BM, CfgF32::BN, CfgF32::BK, CfgF32::WAVES};
+        default: return {0, 0, 0, 0};
+    }
+}
+
+int stage_bytes(int config) {
+    switch (config) {
+        case TG_CFG_256x256: return Cfg256<DT_BF16>::STAGE_BYTES;
+        case TG_CFG_128x128: return Cfg128<DT_BF16>::STAGE_BYTES;
+        case TG_CFG_64x64: return Cfg64<DT_BF16>::STAGE_BYTES;
+        case TG_CFG_F32_64x64: return CfgF32::STAGE_BYTES;
+        default: return 0;
+    }
+}
+
+inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Default choice: the largest tile that still gives the chip (256 CUs) at
+// least about one workgroup per CU; fp32 has one configuration.
+int choose_config(int64_t batch, int64_t M, int64_t N, tg_dtype dtype) {
+    if (dtype == TG_F32) return TG_CFG_F32_64x64;
+    const int64_t big = cdiv(M, 256) * cdiv(N, 256) * batch;
+    if (big >= 240) return TG_CFG_256x256;
+    const int64_t mid = cdiv(M, 128) * cdiv(N, 128) * batch;
+    if (mid >= 240) return TG_CFG_128x128;
+    return TG_CFG_64x64;
+}
+
+struct Plan {
+    tg_plan_info info;
+};
+
+tg_status make_plan(int64_t batch, int64_t M, int64_t N, int64_t K, tg_dtype dtype,
+                    const tg_options *opt, Plan &out) {
+    if (batch < 0 || M < 0 || N < 0 || K < 0) return TG_ERR_INVALID_ARG;
+    if (dtype != TG_F32 && dtype != TG_BF16 && dtype != TG_F16) return TG_ERR_INVALID_ARG;
+    tg_options o{};
+    if (opt) {
+        if (opt->struct_size < (int)sizeof(tg_options)) return TG_ERR_INVALID_ARG;
+        o = *opt;
+    }
+    int config = o.config ? o.config : choose_config(batch, M, N, dtype);
+    if (config < TG_CFG_256x256 || config > TG_CFG_F32_64x64) return TG_ERR_INVALID_ARG;
+    if ((dtype == TG_F32) != (config == TG_CFG_F32_64x64)) return TG_ERR_UNSUPPORTED;
+    const int depth = o.pipeline_depth ? o.pipeline_depth : 2;
+    if (depth != 1 && depth != 2) return TG_ERR_UNSUPPORTED;
+    const int swz = o.swizzle ? o.swizzle : SWZ_XOR;
+    if (swz != SWZ_NONE && swz != SWZ_XOR) return TG_ERR_UNSUPPORTED;
+    const int order = o.block_order;
+    if (order != 0 && order != 1) return TG_ERR_UNSUPPORTED;
+
+    const CfgDims d = cfg_dims(config);
+    tg_plan_info &p = out.info;
+    std::memset(&p, 0, sizeof p);
+    p.config = config;
+    p.block_m = d.bm;
+    p.block_n = d.bn;
+    p.block_k = d.bk;
+    p.waves = d.waves;
+    p.threads = 64 * d.waves;
+    p.pipeline_depth = depth;
+    p.swizzle = swz;
+    p.block_order = order;
+    p.tiles_m = cdiv(M, d.bm);
+    p.tiles_n = cdiv(N, d.bn);
+    p.grid = p.tiles_m * p.tiles_n * batch;
+    const int64_t full_m = M / d.bm, full_n = N / d.bn;
+    p.interior_blocks = full_m * full_n;
+    p.fringe_blocks = p.tiles_m * p.tiles_n - p.interior_blocks;
+    p.k_tiles = cdiv(K, d.bk);
+    p.k_tail = K % d.bk;
+    p.lds_bytes = depth * stage_bytes(config);
+    return TG_OK;
+}
+
+// Byte extent [lo, hi) touched by a strided-batched row-major operand.
+struct Range {
+    uintptr_t lo, hi;
+};
+
+Range span(const void *p, int64_t batch, int64_t rows, int64_t cols, int64_t ld, int64_t stride, int esz) {
+    if (batch == 0 || rows == 0 || cols == 0) return {0, 0};
+    const uintptr_t base = reinterpret_cast<uintptr_t>(p);
+    const int64_t last = (batch - 1) * stride + (rows - 1) * ld + cols;   // one past the last element
+    return {base, base + static_cast<uintptr_t>(last) * esz};
+}
+
+bool overlaps(Range a, Range b) { return a.lo < a.hi && b.lo < b.hi && a.lo < b.hi && b.lo < a.hi; }
+
+tg_status validate(int64_t batch, int64_t M, int64_t N, int64_t K, tg_dtype dtype,
+                   const void *A, int64_t lda, int64_t sA, const void *B, int64_t ldb, int64_t sB,
+                   const float *C, int64_t ldc, int64_t sC) {
+    if (batch < 0 || M < 0 || N < 0 || K < 0) return TG_ERR_INVALID_ARG;
+    if (dtype != TG_F32 && dtype != TG_BF16 && dtype != TG_F16) return TG_ERR_INVALID_ARG;
+    if (lda < (K > 1 ? K : 1) || ldb < (N > 1 ? N : 1) || ldc < (N > 1 ? N : 1)) return TG_ERR_INVALID_ARG;
+    if (sA < 0 || sB < 0 || sC < 0) return TG_ERR_INVALID_ARG;
+    const int esz = dtype == TG_F32 ? 4 : 2;
+    const bool any_out = batch > 0 && M > 0 && N > 0;
+    if (any_out && C == nullptr) return TG_ERR_INVALID_ARG;
+    if (any_out && K > 0 && (A == nullptr || B == nullptr)) return TG_ERR_INVALID_ARG;
+    if (reinterpret_cast<uintptr_t>(A) % esz || reinterpret_cast<uintptr_t>(B) % esz ||
+        reinterpret_cast<uintptr_t>(C) % 4)
+        return TG_ERR_INVALID_ARG;
+    if (!any_out) return TG_OK;
+    // distinct batch entries of C must not overlap each other
+    if (batch > 1 && sC < (M - 1) * ldc + N) return TG_ERR_INVALID_ARG;
+    if (K > 0) {
+        const Range rc = span(C, batch, M, N, ldc, sC, 4);
+        if (overlaps(rc, span(A, batch, M, K, lda, sA, esz)) || overlaps(rc, span(B, batch, K, N, ldb, sB, esz)))
+            return TG_ERR_INVALID_ARG;
+    }
+    return TG_OK;
+}
+
+// Per-thread offsets inside a block are 32-bit: the byte offset of any element
+// of an A or B tile from the tile's first row, and the element offset of any C
+// element from the block's first row, must stay below 2^31.
+bool offsets_fit(const tg_plan_info &p, int64_t K, int64_t lda, int64_t ldb, int64_t ldc, int esz) {
+    const int64_t lim = (int64_t(1) << 31) - 1;
+    return ((int64_t)p.block_m * lda + K) * esz < lim && ((int64_t)p.block_k * ldb + p.block_n) * esz < lim &&
+           (int64_t)p.block_m * ldc + p.block_n < lim;
+}
+
+template <class C, int DEPTH, int SWZ>
+tg_status launch_one(const GemmParams &gp, int64_t grid, hipStream_t stream) {
+    if (grid > 0x7fffffffLL) return TG_ERR_UNSUPPORTED;
+    hipLaunchKernelGGL((gemm_kernel<C, DEPTH, SWZ>), dim3((unsigned)grid), dim3(C::THREADS), 0, stream, gp);
+    return hipGetLastError() == hipSuccess ? TG_OK : TG_ERR_LAUNCH;
+}
+
+template <class C>
+tg_status launch_variants(const GemmParams &gp, const tg_plan_info &p, hipStream_t s) {
+    if (p.pipeline_depth == 2 && p.swizzle == SWZ_XOR) return launch_one<C, 2, SWZ_XOR>(gp, p.grid, s);
+    if (p.pipeline_depth == 1 && p.swizzle == SWZ_XOR) return launch_one<C, 1, SWZ_XOR>(gp, p.grid, s);
+    if (p.pipeline_depth == 2 && p.swizzle == SWZ_NONE) return launch_one<C, 2, SWZ_NONE>(gp, p.grid, s);
+    if (p.pipeline_depth == 1 && p.swizzle == SWZ_NONE) return launch_one<C, 1, SWZ_NONE>(gp, p.grid, s);
+    return TG_ERR_UNSUPPORTED;
+}
+
+template <int DT>
+tg_status launch_dtype(const GemmParams &gp, const tg_plan_info &p, hipStream_t s) {
+    switch (p.config) {
+        case TG_CFG_256x256: return launch_variants<Cfg256<DT>>(gp, p, s);
+        case TG_CFG_128x128: return launch_variants<Cfg128<DT>>(gp, p, s);
+        case TG_CFG_64x64: return launch_variants<Cfg64<DT>>(gp, p, s);
+        default: return TG_ERR_UNSUPPORTED;
+    }
+}
+
+tg_status run(int64_t batch, int64_t M, int64_t N, int64_t K, tg_dtype dtype,
+              const void *A, int64_t lda, int64_t sA, const void *B, int64_t ldb, int64_t sB,
+              float *C, int64_t ldc, int64_t sC, float alpha, float beta, void *stream,
+              const tg_options *opt) {
+    tg_status st = validate(batch, M, N, K, dtype, A, lda, sA, B, ldb, sB, C, ldc, sC);
+    if (st != TG_OK) return st;
+    Plan plan;
+    st = make_plan(batch, M, N, K, dtype, opt, plan);
+    if (st != TG_OK) return st;
+    if (batch == 0 || M == 0 || N == 0) return TG_OK;
+    if (!offsets_fit(plan.info, K, lda, ldb, ldc, dtype == TG_F32 ? 4 : 2)) return TG_ERR_UNSUPPORTED;
+    st = current_device_ok();
+    if (st != TG_OK) return st;
+
+    GemmParams gp;
+    gp.A = static_cast<const char *>(A);
+    gp.B = static_cast<const char *>(B);
+    gp.C = C;
+    gp.M = M;
+    gp.N = N;
+    gp.K = K;
+    gp.lda = lda;
+    gp.ldb = ldb;
+    gp.ldc = ldc;
+    gp.sA = sA;
+    gp.sB = sB;
+    gp.sC = sC;
+    gp.tiles_m = plan.info.tiles_m;
+    gp.tiles_n = plan.info.tiles_n;
+    gp.batch = batch;
+    gp.alpha = alpha;
+    gp.beta = beta;
+    gp.block_order = plan.info.block_order;
+    gp.group_m = 8;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    switch (dtype) {
+        case TG_BF16: return launch_dtype<DT_BF16>(gp, plan.info, s);
+        case TG_F16: return launch_dtype<DT_F16>(gp, plan.info, s);
+        case TG_F32:
+            if (plan.info.config != TG_CFG_F32_64x64) return TG_ERR_UNSUPPORTED;
+            return launch_variants<CfgF32>(gp, plan.info, s);
+    }
+    return TG_ERR_INVALID_ARG;
+}
+
+}  // namespace
+
+extern "C" {
+
+tg_status tile_gemm_ex(int64_t batch, int64_t M, int64_t N, int64_t K, tg_dtype dtype,
+                       const void *A, int64_t lda, int64_t strideA,
+                       const void *B, int64_t ldb, int64_t strideB,
+                       float *C, int64_t ldc, int64_t strideC,
+                       float alpha, float beta, void *stream, const tg_options *opt) {
+    try {
+        return run(batch, M, N, K, dtype, A, lda, strideA, B, ldb, strideB, C, ldc, strideC, alpha, beta,
+                   stream, opt);
+    } catch (...) {
+        return TG_ERR_INTERNAL;
+    }
+}
+
+tg_status tile_gemm_strided_batched(int64_t batch, int64_t M, int64_t N, int64_t K, tg_dtype dtype,
+                                    const void *A, int64_t lda, int64_t strideA,
+                                    const void *B, int64_t ldb, int64_t strideB,
+                                    float *C, int64_t ldc, int64_t strideC,
+                                    float alpha, float beta, void *stream) {
+    return tile_gemm_ex(batch, M, N, K, dtype, A, lda, strideA, B, ldb, strideB, C, ldc, strideC, alpha, beta,
+                        stream, nullptr);
+}
+
+tg_status tile_gemm(int64_t M, int64_t N, int64_t K, tg_dtype dtype,
+                    const void *A, int64_t lda, const void *B, int64_t ldb,
+                    float *C, int64_t ldc, float alpha, float beta, void *stream) {
+    return tile_gemm_ex(1, M, N, K, dtype, A, lda, 0, B, ldb, 0, C, ldc, 0, alpha, beta, stream, nullptr);
+}
+
+tg_status tile_gemm_plan(int64_t batch, int64_t M, int64_t N, int64_t K, tg_dtype dtype,
+                         const tg_options *opt, tg_plan_info *out) {
+    if (!out) return TG_ERR_INVALID_ARG;
+    try {
+        Plan p;
+        tg_status st = make_plan(batch, M, N, K, dtype, opt, p);
+        if (st == TG_OK) *out = p.info;
+        return st;
+    } catch (...) {
+        return TG_ERR_INTERNAL;
+    }
+}
+
+const char *tile_gemm_status_string(tg_status s) {
+    switch (s) {
+        case TG_OK: return "TG_OK";
+        case TG_ERR_INVALID_ARG: return "TG_ERR_INVALID_ARG: extents, strides, pointers, dtype or overlap rejected";
+        case TG_ERR_UNSUPPORTED: return "TG_ERR_UNSUPPORTED: no gfx950 device visible, or option not available";
+        case TG_ERR_LAUNCH: return "TG_ERR_LAUNCH: the HIP runtime refused the kernel launch";
+        case TG_ERR_INTERNAL: return "TG_ERR_INTERNAL: unexpected failure inside the library";
+    }
+    return "unknown tg_status";
+}
+
+int tile_gemm_abi_version(void) { return TILE_GEMM_ABI_VERSION; }
+
+}  // extern "C"
