@@ -38,6 +38,9 @@ def parse():
     ap.add_argument("--pipeline-depth", type=int, default=0)
     ap.add_argument("--swizzle", type=int, default=0)
     ap.add_argument("--block-order", type=int, default=0)
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="after timing, run a plain device copy of this many MiB (3 times) so HBM "
+                         "byte counters can be scaled against a kernel of known traffic")
     return ap.parse_args()
 
 
@@ -123,10 +126,23 @@ def main():
     gbs = bytes_alg / (ms_step * 1e-3) / 1e9
     # Each step is exactly one launch of the GEMM kernel, so the event time per
     # step is the kernel's average launch duration (plus launch gaps).
+    # HBM traffic per launch from the committed FETCH_SIZE / WRITE_SIZE summary
+    # of this workload, only while it was taken on the current kernel sources.
+    from tile_scheduled_dense_amd.rocprof_summary import traffic_for
+    traffic = traffic_for(p.name)
     roofline = {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak, "unit": "TFLOP/s",
-                "frac": round(tflops / peak, 4), "traffic": None,
+                "frac": round(tflops / peak, 4), "traffic": None if traffic is None else int(traffic),
                 "algorithmic_flops_per_launch": p.flops, "avg_launch_us": round(ms_step * 1e3, 2),
                 "algorithmic_bytes_per_launch": bytes_alg, "achieved_GBps": round(gbs, 1)}
+
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"# copy calibration: 3 x {args.copy_calibration_mib} MiB read + written", file=sys.stderr)
 
     cpu = None
     if not args.no_cpu_baseline:

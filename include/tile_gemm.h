@@ -85,7 +85,7 @@ typedef enum {
     TG_CFG_AUTO = 0,
     TG_CFG_256x256 = 1,     /* 16-bit inputs: 256x256 block tile, 8 waves        */
     TG_CFG_128x128 = 2,     /* 16-bit inputs: 128x128 block tile, 4 waves        */
-    TG_CFG_64x64 = 3,       /* 16-bit inputs: 64x64 block tile, 4 waves          */
+    TG_CFG_64x64 = 3,       /* 16-bit inputs: 64x64 block tile, 2 waves          */
     TG_CFG_F32_64x64 = 4    /* fp32 inputs: 64x64 block tile, 4 waves            */
 } tg_config;
 
@@ -131,28 +131,32 @@ tg_status tile_gemm_plan(int64_t batch, int64_t M, int64_t N, int64_t K, tg_dtyp
  * "Tensor Layout" page (TileLayout, Forward mapping, SwizzleLayout and
  * ComposeLayout sections): a logical index is flattened row-major, split over
  * the shard iters, each component scaled by its stride onto its axis, the
- * offset added, and every replica combination added; a swizzle, if present,
- * then permutes the coordinate on the memory axis m:
+ * offset added, and every replica combination added; swizzles, if present,
+ * then permute the coordinate on the memory axis m, applied in order:
  *     addr(m) = f(m >> M) * 2^M + (m mod 2^M),  f(x) = x ^ ((x & ((2^B-1) << S)) >> S).
  */
 #define TG_LAYOUT_MAX_ITERS 12
 #define TG_LAYOUT_MAX_RANK 6
+#define TG_LAYOUT_MAX_SWIZZLES 2
 
 typedef enum { TG_AXIS_M = 0, TG_AXIS_LANE = 1, TG_AXIS_WAVE = 2, TG_AXIS_PID = 3,
                TG_AXIS_TLANE = 4, TG_AXIS_TCOL = 5, TG_AXIS_COUNT = 6 } tg_axis;
 
 typedef struct { int64_t extent; int64_t stride; int32_t axis; int32_t pad_; } tg_iter;
 
+typedef struct { int32_t m, b, s; } tg_swizzle;    /* SwizzleLayout(M, B, S), S >= B */
+
 typedef struct {
     int32_t rank;                             /* logical rank                      */
     int32_t n_shard;                          /* D iters                           */
     int32_t n_replica;                        /* R iters                           */
-    int32_t swizzle;                          /* 0: none; 1: (M, B, S) below on m   */
+    int32_t n_swizzle;                        /* swizzles composed after the tile  */
     int64_t shape[TG_LAYOUT_MAX_RANK];        /* logical shape                     */
     tg_iter shard[TG_LAYOUT_MAX_ITERS];
     tg_iter replica[TG_LAYOUT_MAX_ITERS];
     int64_t offset[TG_AXIS_COUNT];            /* O, one integer per axis           */
-    int32_t swz_m, swz_b, swz_s, pad_;
+    tg_swizzle swizzle[TG_LAYOUT_MAX_SWIZZLES];
+    int32_t pad_;
 } tg_layout;
 
 /*

@@ -52,6 +52,16 @@ def test_tensor_memory_case_study():
         assert coord[TLANE] == int(tlane) and coord[TCOL] == int(tcol)
 
 
+def test_two_swizzles_compose_in_order():
+    # Swizzle(3,3,3) then Swizzle(3,2,6) on a (64, 64) 16-bit tile: chunk j//8 is
+    # XORed with row bits 0..2 and then with row bits 3..4
+    L = tg.make_layout((64, 64), [(64, 64, M), (64, 1, M)], swizzle=[(3, 3, 3), (3, 2, 6)])
+    for i in range(64):
+        for j in range(0, 64, 5):
+            (coord,) = tg.tg_layout_eval(L, (i, j))
+            assert coord[M] == 64 * i + 8 * ((j // 8) ^ (i % 8) ^ ((i // 8) % 4)) + j % 8
+
+
 def test_swizzle_worked_example():
     L = tg.make_layout((8, 64), [(8, 64, M), (64, 1, M)], swizzle=(3, 3, 3))
     for i, addr, bank, bank0 in rows("tirx_swizzle_worked_example.txt"):
@@ -103,27 +113,42 @@ def test_kernel_lds_placement_matches_layout(cfg, dt, swz):
         assert seen == set(range(rows_ * bk))                    # a bijection onto the tile
 
 
-def bank_quads(elem_offsets, esz):
-    """16-byte accesses -> set of 4-bank groups under 32 banks x 4 bytes."""
-    return [((off * esz) // 16) % 8 for off in elem_offsets]
+# Two LDS bank models for 16-byte accesses:
+#  * the layout page's: 32 banks x 4 bytes, one 128-byte line per cycle, so the
+#    8 lanes served together must use 8 distinct 16-byte bank groups;
+#  * gfx950's 128-bit reads: 64 banks x 4 bytes, 16 lanes per cycle, so 16
+#    consecutive lanes must use 16 distinct groups of a 256-byte line.
+MODELS = {"32x4B/8 lanes": (8, 8), "64x4B/16 lanes": (16, 16)}
+
+
+def conflict_free(byte_offsets, lanes_per_cycle, groups):
+    for g in range(0, len(byte_offsets), lanes_per_cycle):
+        units = [(b // 16) % groups for b in byte_offsets[g:g + lanes_per_cycle]]
+        if len(set(units)) != len(units):
+            return False
+    return True
 
 
 @pytest.mark.parametrize("cfg,dt", CONFIGS[:3])
-def test_fragment_reads_conflict_free_under_swizzle(cfg, dt):
-    # 32x32x16 MFMA: lane l reads row (l % 32), chunk 2s + l // 32; eight lanes
-    # share one 128-byte access wave, so their 16-byte units must differ mod 128 B.
+@pytest.mark.parametrize("model", sorted(MODELS))
+def test_fragment_reads_conflict_free_under_swizzle(cfg, dt, model):
+    # 32x32x16 MFMA: lane l reads row (l % 32), chunk 2s + l // 32 of the A (or
+    # transposed B) tile, for rows starting at any multiple of 32.
+    lanes_per_cycle, groups = MODELS[model]
     bm, bn, bk, _ = dims(cfg, dt)
     for swz, expect_free in [(tg.SWZ_XOR, True), (tg.SWZ_NONE, False)]:
-        for s in range(4):
-            for g in range(8):
-                lanes = range(8 * g, 8 * g + 8)
-                offs = [tg.tile_gemm_lds_offset(cfg, swz, 0, l % 32, 8 * (2 * s + l // 32)) for l in lanes]
-                quads = bank_quads(offs, 2)
-                assert (len(set(quads)) == 8) == expect_free, (swz, s, g, quads)
+        for base in range(0, bm, 32):
+            for s in range(4):
+                offs = [2 * tg.tile_gemm_lds_offset(cfg, swz, 0, base + l % 32, 8 * (2 * s + l // 32))
+                        for l in range(64)]
+                assert conflict_free(offs, lanes_per_cycle, groups) == expect_free, (swz, base, s)
 
 
 @pytest.mark.parametrize("cfg,dt", CONFIGS[:3])
-def test_a_copy_writes_conflict_free(cfg, dt):
+@pytest.mark.parametrize("model", sorted(MODELS))
+def test_a_copy_writes_conflict_free(cfg, dt, model):
+    # 128-bit LDS writes are served 8 lanes (128 bytes) per cycle in both models
+    groups = MODELS[model][1]
     L = tg.tile_gemm_describe_layout(cfg, 0, tg.LAYOUT_COPY_A)
     bm, bn, bk, waves = dims(cfg, dt)
     owner = {}
@@ -136,8 +161,21 @@ def test_a_copy_writes_conflict_free(cfg, dt):
         if lane % 8:
             continue
         group = [owner[(w, lane + d, q)] for d in range(8)]
-        offs = [tg.tile_gemm_lds_offset(cfg, tg.SWZ_XOR, 0, rr, 8 * cc) for rr, cc in group]
-        assert len(set(bank_quads(offs, 2))) == 8
+        offs = [2 * tg.tile_gemm_lds_offset(cfg, tg.SWZ_XOR, 0, rr, 8 * cc) for rr, cc in group]
+        assert conflict_free(offs, 8, groups)
+
+
+@pytest.mark.parametrize("cfg,dt", CONFIGS[:3])
+@pytest.mark.parametrize("model", sorted(MODELS))
+def test_b_copy_writes_conflict_free(cfg, dt, model):
+    # loader lanes 8g..8g+7 take the squares kb = 0..7 of one column block nb and
+    # write, for each column c of it, chunk kb of transposed-tile row nb*8 + c
+    groups = MODELS[model][1]
+    bm, bn, bk, waves = dims(cfg, dt)
+    for nb in range(bn // 8):
+        for c in range(8):
+            offs = [2 * tg.tile_gemm_lds_offset(cfg, tg.SWZ_XOR, 1, nb * 8 + c, 8 * kb) for kb in range(8)]
+            assert conflict_free(offs, 8, groups)
 
 
 @pytest.mark.parametrize("cfg,dt", CONFIGS)

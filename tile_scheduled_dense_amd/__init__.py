@@ -34,6 +34,7 @@ AXIS_M, AXIS_LANE, AXIS_WAVE, AXIS_PID, AXIS_TLANE, AXIS_TCOL = range(6)
 AXIS_COUNT = 6
 LAYOUT_MAX_ITERS = 12
 LAYOUT_MAX_RANK = 6
+LAYOUT_MAX_SWIZZLES = 2
 
 # every symbol include/tile_gemm.h declares
 EXPORTED = ["tile_gemm", "tile_gemm_strided_batched", "tile_gemm_ex", "tile_gemm_plan",
@@ -69,12 +70,16 @@ class Iter(ctypes.Structure):
                 ("pad_", ctypes.c_int32)]
 
 
+class Swizzle(ctypes.Structure):
+    _fields_ = [("m", ctypes.c_int32), ("b", ctypes.c_int32), ("s", ctypes.c_int32)]
+
+
 class Layout(ctypes.Structure):
     _fields_ = [("rank", ctypes.c_int32), ("n_shard", ctypes.c_int32), ("n_replica", ctypes.c_int32),
-                ("swizzle", ctypes.c_int32), ("shape", ctypes.c_int64 * LAYOUT_MAX_RANK),
+                ("n_swizzle", ctypes.c_int32), ("shape", ctypes.c_int64 * LAYOUT_MAX_RANK),
                 ("shard", Iter * LAYOUT_MAX_ITERS), ("replica", Iter * LAYOUT_MAX_ITERS),
-                ("offset", ctypes.c_int64 * AXIS_COUNT), ("swz_m", ctypes.c_int32), ("swz_b", ctypes.c_int32),
-                ("swz_s", ctypes.c_int32), ("pad_", ctypes.c_int32)]
+                ("offset", ctypes.c_int64 * AXIS_COUNT), ("swizzle", Swizzle * LAYOUT_MAX_SWIZZLES),
+                ("pad_", ctypes.c_int32)]
 
 
 _lib_handle = None
@@ -195,7 +200,8 @@ def tile_gemm_plan(batch, M, N, K, dtype, config=0, pipeline_depth=0, swizzle=0,
 
 
 def make_layout(shape, shard, replica=(), offset=None, swizzle=None) -> Layout:
-    """Build a tg_layout: shard/replica are (extent, stride, axis) triples."""
+    """Build a tg_layout: shard/replica are (extent, stride, axis) triples; swizzle is
+    one (M, B, S) triple or a list of them, applied in order."""
     L = Layout()
     L.rank = len(shape)
     for d, e in enumerate(shape):
@@ -209,8 +215,10 @@ def make_layout(shape, shard, replica=(), offset=None, swizzle=None) -> Layout:
     for a, v in (offset or {}).items():
         L.offset[a] = v
     if swizzle is not None:
-        L.swizzle = 1
-        L.swz_m, L.swz_b, L.swz_s = swizzle
+        chain = [swizzle] if isinstance(swizzle[0], int) else list(swizzle)
+        L.n_swizzle = len(chain)
+        for z, (m, b, sh) in enumerate(chain):
+            L.swizzle[z] = Swizzle(m, b, sh)
     return L
 
 

@@ -192,8 +192,13 @@ __device__ __forceinline__ void mfma_chunk(const u32x4 &a, const u32x4 &b, f32x4
     // four 16x16x4 fp32 MFMAs; element e of both chunks is the same k.
 #pragma unroll
     for (int e = 0; e < 4; ++e)
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__builtin_bit_cast(float, a[e]),
-                                                   __builtin_bit_cast(float, b[e]), acc, 0, 0, 0);
+    {
+        // copy the element out first: a bit_cast of a vector-element lvalue
+        // would read element 0
+        const uint32_t ae = a[e], be = b[e];
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__builtin_bit_cast(float, ae), __builtin_bit_cast(float, be),
+                                                   acc, 0, 0, 0);
+    }
 }
 
 // ---- one workgroup tile ----------------------------------------------------------

@@ -39,7 +39,11 @@ bool layout_valid(const tg_layout *L) {
         const tg_iter &it = L->replica[t];
         if (it.extent < 1 || it.axis < 0 || it.axis >= TG_AXIS_COUNT) return false;
     }
-    if (L->swizzle && (L->swz_m < 0 || L->swz_b < 0 || L->swz_s < L->swz_b)) return false;
+    if (L->n_swizzle < 0 || L->n_swizzle > TG_LAYOUT_MAX_SWIZZLES) return false;
+    for (int z = 0; z < L->n_swizzle; ++z) {
+        const tg_swizzle &w = L->swizzle[z];
+        if (w.m < 0 || w.b < 0 || w.s < w.b || w.m + w.s + w.b > 62) return false;
+    }
     return size == dsize;   // a shape is admitted when its size equals the shard's
 }
 
@@ -52,10 +56,10 @@ void describe_lds(tg_layout *L, int rows, int swz) {
     L->shard[0] = {rows, C::BK, TG_AXIS_M, 0};
     L->shard[1] = {C::BK, 1, TG_AXIS_M, 0};
     if (swz == SWZ_XOR) {
-        L->swizzle = 1;
-        L->swz_m = C::ELEM == 2 ? 3 : 2;
-        L->swz_b = 3;
-        L->swz_s = 3;
+        const int32_t m = C::ELEM == 2 ? 3 : 2;
+        L->n_swizzle = 2;
+        L->swizzle[0] = {m, 3, 3};   // row bits 0..2 into the chunk index
+        L->swizzle[1] = {m, 2, 6};   // row bits 3..4 into the chunk index
     }
 }
 
@@ -166,7 +170,8 @@ int64_t tg_layout_eval(const tg_layout *L, const int64_t *x, int64_t *out, int64
             coord[it.axis] += (rr % it.extent) * it.stride;
             rr /= it.extent;
         }
-        if (L->swizzle) coord[TG_AXIS_M] = swizzle_apply(coord[TG_AXIS_M], L->swz_m, L->swz_b, L->swz_s);
+        for (int z = 0; z < L->n_swizzle; ++z)
+            coord[TG_AXIS_M] = swizzle_apply(coord[TG_AXIS_M], L->swizzle[z].m, L->swizzle[z].b, L->swizzle[z].s);
         if (out) std::memcpy(out + r * TG_AXIS_COUNT, coord, sizeof coord);
     }
     return count;

@@ -74,12 +74,22 @@ enum Swz : int { SWZ_NONE = 1, SWZ_XOR = 2 };
 // LDS placement of one operand tile (rows x BK, k contiguous).
 //
 // The tile layout S[(rows, BK):(BK@m, 1@m)] gives the row-major element
-// address m = row*BK + k; the swizzle of the TIRx page then permutes it:
-//     addr(m) = f(m >> M) * 2^M + (m mod 2^M),   f(x) = x ^ ((x & (7 << 3)) >> 3)
-// with M = log2(elements per 16 bytes) (3 for 16-bit, 2 for fp32), B = 3 and
-// S = 3.  With 8 chunks per row, f XORs the row's low three bits into the
-// chunk index: a per-row bijection of 16-byte units (the Swizzle_b128 flavour
-// of the OCANNL Stage paragraph), so each 16-byte fragment stays contiguous.
+// address m = row*BK + k, which two swizzles of the TIRx page then permute,
+//     addr(m) = f(m >> M) * 2^M + (m mod 2^M),  f(x) = x ^ ((x & ((2^B-1) << S)) >> S),
+// first (B, S) = (3, 3), then (B, S) = (2, 6), with M = log2(elements per 16
+// bytes) (3 for 16-bit, 2 for fp32).  With 8 chunks per 128-byte row this
+// XORs  (row & 7) ^ ((row >> 3) & 3)  into the chunk index: a per-row bijection
+// of 16-byte units (the Swizzle_b128 flavour of the OCANNL Stage paragraph),
+// so every 16-byte fragment stays contiguous.
+//
+// Why two: the page's single Swizzle(M, 3, 3) makes any 8 consecutive rows hit
+// 8 distinct 16-byte bank groups of a 128-byte line (32 banks x 4 bytes), which
+// is what a 128-bit LDS write needs on gfx950 (8 lanes per cycle).  A 128-bit
+// LDS read is served 16 lanes per cycle from 64 banks (a 256-byte line, two
+// tile rows), so 16 consecutive rows at one chunk index must also be distinct
+// among the rows of equal parity; the second term makes them so.  The mask uses
+// row bits 0..4 only, so for every fragment read and copy it is a function of
+// the lane alone (row offsets of 32 leave it unchanged).
 // ---------------------------------------------------------------------------
 TG_HD int64_t swizzle_apply(int64_t m, int M, int B, int S) {
     int64_t x = m >> M;
@@ -87,19 +97,21 @@ TG_HD int64_t swizzle_apply(int64_t m, int M, int B, int S) {
     return (f << M) + (m & ((int64_t(1) << M) - 1));
 }
 
+TG_HD int swizzle_row_mask(int row) { return (row & 7) ^ ((row >> 3) & 3); }
+
 template <class C>
 TG_HD int lds_elem(int row, int k, int swz) {
     int m = row * C::BK + k;
     if (swz == SWZ_NONE) return m;
     constexpr int M = C::ELEM == 2 ? 3 : 2;
-    return (int)swizzle_apply(m, M, 3, 3);
+    return (int)swizzle_apply(swizzle_apply(m, M, 3, 3), M, 2, 6);
 }
 
 // Byte offset of 16-byte chunk `chunk` of tile row `row` (the unit every
 // LDS write and fragment read moves).
 template <class C>
 TG_HD int lds_chunk_byte(int row, int chunk, int swz) {
-    int c = swz == SWZ_NONE ? chunk : (chunk ^ (row & 7));
+    int c = swz == SWZ_NONE ? chunk : (chunk ^ swizzle_row_mask(row));
     return (row * C::CPR + c) * 16;
 }
 

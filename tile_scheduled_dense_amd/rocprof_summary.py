@@ -1,0 +1,147 @@
+"""Summaries of rocprofv3 CSV output for the GEMM kernel, and the traffic figure
+bench.py reports.
+
+  python -m tile_scheduled_dense_amd.rocprof_summary trace  <kernel_stats.csv> <out.txt> <command...>
+  python -m tile_scheduled_dense_amd.rocprof_summary counters <fetch_dir> <write_dir> <copy_mib> <out.txt> <command...>
+
+`counters` reads two --pmc runs (FETCH_SIZE, then WRITE_SIZE, KiB per
+dispatch) of a command that also ran a plain device copy of `copy_mib` MiB
+(bench.py --copy-calibration-mib).  Each counter is scaled by what it reads for
+that copy, whose true traffic is known (copy_mib read and copy_mib written).
+The summary records a hash of the kernel sources; bench.py reports the traffic
+only while the sources still match.
+"""
+from __future__ import annotations
+
+import csv
+import glob
+import hashlib
+import os
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+GEMM_KERNEL_TAG = "gemm_kernel"
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for path in sorted(glob.glob(os.path.join(PKG, "csrc", "*"))):
+        with open(path, "rb") as f:
+            h.update(os.path.basename(path).encode())
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def _rows(path):
+    with open(path) as f:
+        return list(csv.DictReader(f))
+
+
+def _counter_file(d):
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise FileNotFoundError(f"no counter_collection.csv under {d}")
+    return files[0]
+
+
+def per_kernel(path, counter):
+    """{kernel name: [values per dispatch]} for one counter."""
+    out = {}
+    for r in _rows(path):
+        if r["Counter_Name"] == counter:
+            out.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return out
+
+
+def _pick(d, tag):
+    for k, v in d.items():
+        if tag in k:
+            return k, v
+    raise KeyError(tag)
+
+
+def summarize_counters(fetch_dir, write_dir, copy_mib):
+    fetch = per_kernel(_counter_file(fetch_dir), "FETCH_SIZE")
+    write = per_kernel(_counter_file(write_dir), "WRITE_SIZE")
+    name, fk = _pick(fetch, GEMM_KERNEL_TAG)
+    _, wk = _pick(write, GEMM_KERNEL_TAG)
+    _, fc = _pick(fetch, "copyBuffer")
+    _, wc = _pick(write, "copyBuffer")
+    copy_kib = copy_mib * 1024.0
+    f_factor = (sum(fc) / len(fc)) / copy_kib
+    w_factor = (sum(wc) / len(wc)) / copy_kib
+    fetch_kib = sum(fk) / len(fk)
+    write_kib = sum(wk) / len(wk)
+    return {
+        "kernel": name,
+        "dispatches_fetch": len(fk), "dispatches_write": len(wk),
+        "fetch_kib_per_dispatch": fetch_kib, "write_kib_per_dispatch": write_kib,
+        "copy_mib": copy_mib, "copy_fetch_factor": f_factor, "copy_write_factor": w_factor,
+        "hbm_read_bytes_per_launch": fetch_kib / f_factor * 1024.0,
+        "hbm_write_bytes_per_launch": write_kib / w_factor * 1024.0,
+        "traffic_bytes_per_launch": (fetch_kib / f_factor + write_kib / w_factor) * 1024.0,
+        "kernel_source_sha256": kernel_source_hash(),
+    }
+
+
+def write_kv(path, title, command, kv):
+    with open(path, "w") as f:
+        f.write(f"# {title}\n# command: {command}\n")
+        for k, v in kv.items():
+            f.write(f"{k}: {v}\n")
+
+
+def read_kv(path):
+    out = {}
+    with open(path) as f:
+        for line in f:
+            if line.startswith("#") or ":" not in line:
+                continue
+            k, v = line.split(":", 1)
+            out[k.strip()] = v.strip()
+    return out
+
+
+def traffic_for(workload: str):
+    """Bytes per launch from profiles/traffic_<workload>.txt if it matches the sources, else None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    kv = read_kv(path)
+    if kv.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    return float(kv["traffic_bytes_per_launch"])
+
+
+def summarize_trace(stats_csv):
+    rows = _rows(stats_csv)
+    out = {}
+    for r in rows:
+        out[r["Name"]] = {"calls": int(r["Calls"]), "average_ns": float(r["AverageNs"]),
+                          "min_ns": float(r["MinNs"]), "max_ns": float(r["MaxNs"]),
+                          "percentage": float(r["Percentage"])}
+    return out
+
+
+def main(argv):
+    mode = argv[1]
+    if mode == "trace":
+        stats, out, cmd = argv[2], argv[3], " ".join(argv[4:])
+        kv = {}
+        for name, d in summarize_trace(stats).items():
+            short = name if len(name) < 120 else name[:117] + "..."
+            kv[short] = (f"calls={d['calls']} average_us={d['average_ns'] / 1e3:.2f} "
+                         f"min_us={d['min_ns'] / 1e3:.2f} max_us={d['max_ns'] / 1e3:.2f} pct={d['percentage']:.2f}")
+        kv["kernel_source_sha256"] = kernel_source_hash()
+        write_kv(out, "rocprofv3 --kernel-trace --stats summary", cmd, kv)
+    elif mode == "counters":
+        fetch_dir, write_dir, copy_mib, out, cmd = argv[2], argv[3], int(argv[4]), argv[5], " ".join(argv[6:])
+        write_kv(out, "rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE, scaled by a plain copy of known size", cmd,
+                 summarize_counters(fetch_dir, write_dir, copy_mib))
+    else:
+        raise SystemExit(__doc__)
+
+
+if __name__ == "__main__":
+    main(sys.argv)
