@@ -92,14 +92,14 @@ def test_options_validation():
     ((1, 67, 45, 53, "f32"), dict(config=tg.TG_CFG_F32_64x64, tiles_m=2, tiles_n=1, interior_blocks=0,
                                   fringe_blocks=2, k_tiles=2, k_tail=21)),
     ((1, 8192, 8192, 8192, "bf16"), dict(config=tg.TG_CFG_256x256, tiles_m=32, tiles_n=32, grid=1024,
-                                         interior_blocks=1024, fringe_blocks=0, k_tiles=128, k_tail=0,
-                                         lds_bytes=131072)),
+                                         interior_blocks=1024, fringe_blocks=0, k_tiles=256, k_tail=0,
+                                         lds_bytes=4 * 32768, pipeline_depth=4)),
     ((1, 8191, 8193, 8190, "bf16"), dict(config=tg.TG_CFG_256x256, tiles_m=32, tiles_n=33, grid=1056,
-                                         interior_blocks=31 * 32, fringe_blocks=1056 - 992, k_tiles=128,
-                                         k_tail=62)),
+                                         interior_blocks=31 * 32, fringe_blocks=1056 - 992, k_tiles=256,
+                                         k_tail=30)),
     ((512, 257, 129, 1000, "f16"), dict(tiles_m=5, tiles_n=3, interior_blocks=8, fringe_blocks=7,
-                                        grid=15 * 512, k_tiles=16, k_tail=40)),
-    ((1, 512, 512, 131072, "bf16"), dict(k_tiles=2048, k_tail=0, fringe_blocks=0)),
+                                        grid=15 * 512, k_tiles=32, k_tail=8, lds_bytes=4 * 8192)),
+    ((1, 512, 512, 131072, "bf16"), dict(k_tiles=4096, k_tail=0, fringe_blocks=0)),
 ])
 def test_plan_block_classes(args, expect):
     kw = {}
@@ -111,11 +111,18 @@ def test_plan_block_classes(args, expect):
 
 
 def test_plan_depth_changes_lds_only():
-    a = tg.tile_gemm_plan(1, 1000, 1000, 1000, "bf16", config=tg.TG_CFG_128x128, pipeline_depth=1)
-    b = tg.tile_gemm_plan(1, 1000, 1000, 1000, "bf16", config=tg.TG_CFG_128x128, pipeline_depth=2)
-    assert b["lds_bytes"] == 2 * a["lds_bytes"] == 2 * (128 * 64 * 2 * 2)
-    assert {k: v for k, v in a.items() if k not in ("lds_bytes", "pipeline_depth")} == \
-           {k: v for k, v in b.items() if k not in ("lds_bytes", "pipeline_depth")}
+    plans = {d: tg.tile_gemm_plan(1, 1000, 1000, 1000, "bf16", config=tg.TG_CFG_128x128, pipeline_depth=d)
+             for d in (1, 2, 4)}
+    stage = 128 * 32 * 2 * 2
+    for d, info in plans.items():
+        assert info["lds_bytes"] == d * stage
+        assert {k: v for k, v in info.items() if k not in ("lds_bytes", "pipeline_depth")} == \
+               {k: v for k, v in plans[1].items() if k not in ("lds_bytes", "pipeline_depth")}
+    with pytest.raises(tg.TileGemmError):
+        tg.tile_gemm_plan(1, 64, 64, 64, "bf16", pipeline_depth=3)
+    with pytest.raises(tg.TileGemmError):
+        tg.tile_gemm_plan(1, 64, 64, 64, "bf16", pipeline_depth=2, swizzle=tg.SWZ_NONE)
+    assert tg.tile_gemm_plan(1, 64, 64, 64, "f32")["pipeline_depth"] == 2
 
 
 def test_lds_budget():

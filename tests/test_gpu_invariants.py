@@ -65,9 +65,9 @@ def padded(p, Mp, Np, Kp):
     return q
 
 
-@pytest.mark.parametrize("cfg,dt,tile", [(tg.TG_CFG_256x256, "bf16", (256, 256, 64)),
-                                         (tg.TG_CFG_128x128, "f16", (128, 128, 64)),
-                                         (tg.TG_CFG_64x64, "bf16", (64, 64, 64)),
+@pytest.mark.parametrize("cfg,dt,tile", [(tg.TG_CFG_256x256, "bf16", (256, 256, 32)),
+                                         (tg.TG_CFG_128x128, "f16", (128, 128, 32)),
+                                         (tg.TG_CFG_64x64, "bf16", (64, 64, 32)),
                                          (0, "f32", (64, 64, 32))])
 @pytest.mark.parametrize("shape", [(300, 333, 130), (67, 45, 53), (257, 129, 1000)], ids=str)
 def test_ragged_equals_cropped_padded(cfg, dt, tile, shape):
@@ -86,8 +86,10 @@ def test_ragged_equals_cropped_padded(cfg, dt, tile, shape):
 def test_depth_swizzle_order_are_bitwise_invisible(cfg, dt):
     p = workloads.custom(dt, 531, 389, 333, lda_pad=1, ldb_pad=2, alpha=0.75, beta=-1.25, seed=3)
     ref = run(p, config=cfg)
-    for opts in [dict(pipeline_depth=1), dict(swizzle=tg.SWZ_NONE), dict(block_order=1),
-                 dict(pipeline_depth=1, swizzle=tg.SWZ_NONE, block_order=1)]:
+    variants = [dict(pipeline_depth=1), dict(pipeline_depth=2), dict(swizzle=tg.SWZ_NONE), dict(block_order=1)]
+    if dt == "f32":
+        variants.append(dict(pipeline_depth=1, swizzle=tg.SWZ_NONE, block_order=1))
+    for opts in variants:
         got = run(p, config=cfg, **opts)
         assert np.array_equal(bits(got), bits(ref)), opts
 

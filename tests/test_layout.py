@@ -90,6 +90,7 @@ def test_admission_and_invalid():
 
 CONFIGS = [(tg.TG_CFG_256x256, "bf16"), (tg.TG_CFG_128x128, "bf16"), (tg.TG_CFG_64x64, "bf16"),
            (tg.TG_CFG_F32_64x64, "f32")]
+RING = CONFIGS[:3]          # bf16/fp16 configurations: the direct-copy K ring
 
 
 def dims(cfg, dt):
@@ -100,82 +101,90 @@ def dims(cfg, dt):
 @pytest.mark.parametrize("cfg,dt", CONFIGS)
 @pytest.mark.parametrize("swz", [tg.SWZ_NONE, tg.SWZ_XOR])
 def test_kernel_lds_placement_matches_layout(cfg, dt, swz):
-    bm, bn, bk, _ = dims(cfg, dt)
-    for operand, kind, rows_ in [(0, tg.LAYOUT_LDS_A, bm), (1, tg.LAYOUT_LDS_B, bn)]:
+    # the address the kernel computes (same inline function as the device code)
+    # equals the TileLayout + swizzle description, and is a bijection onto the tile
+    for operand, kind in [(0, tg.LAYOUT_LDS_A), (1, tg.LAYOUT_LDS_B)]:
         L = tg.tile_gemm_describe_layout(cfg, swz, kind)
+        rows_, cols_ = L.shape[0], L.shape[1]
         seen = set()
         for r in range(rows_):
-            for k in range(bk):
-                (coord,) = tg.tg_layout_eval(L, (r, k))
-                off = tg.tile_gemm_lds_offset(cfg, swz, operand, r, k)
-                assert off == coord[M], (operand, r, k)
+            for c in range(cols_):
+                (coord,) = tg.tg_layout_eval(L, (r, c))
+                off = tg.tile_gemm_lds_offset(cfg, swz, operand, r, c)
+                assert off == coord[M], (operand, r, c)
                 seen.add(off)
-        assert seen == set(range(rows_ * bk))                    # a bijection onto the tile
+        assert seen == set(range(rows_ * cols_))
 
 
-# Two LDS bank models for 16-byte accesses:
-#  * the layout page's: 32 banks x 4 bytes, one 128-byte line per cycle, so the
-#    8 lanes served together must use 8 distinct 16-byte bank groups;
-#  * gfx950's 128-bit reads: 64 banks x 4 bytes, 16 lanes per cycle, so 16
-#    consecutive lanes must use 16 distinct groups of a 256-byte line.
-MODELS = {"32x4B/8 lanes": (8, 8), "64x4B/16 lanes": (16, 16)}
+# gfx950 LDS, measured: 64 banks x 4 bytes; a 128-bit read serves 16 lanes per
+# cycle, a 64-bit read 32 lanes, a 128-bit write 8 lanes.
+def banks_distinct(byte_offsets, width):
+    banks = []
+    for b in byte_offsets:
+        banks += [((b + 4 * w) // 4) % 64 for w in range(width // 4)]
+    return len(set(banks)) == len(banks)
 
 
-def conflict_free(byte_offsets, lanes_per_cycle, groups):
-    for g in range(0, len(byte_offsets), lanes_per_cycle):
-        units = [(b // 16) % groups for b in byte_offsets[g:g + lanes_per_cycle]]
-        if len(set(units)) != len(units):
-            return False
-    return True
+def a_fragment_bytes(cfg, swz, base, s):
+    # 32x32x16 MFMA A operand: lane l holds row base + l % 32, k = 16 s + 8 (l // 32) .. + 7
+    return [2 * tg.tile_gemm_lds_offset(cfg, swz, 0, base + l % 32, 16 * s + 8 * (l // 32)) for l in range(64)]
 
 
-@pytest.mark.parametrize("cfg,dt", CONFIGS[:3])
-@pytest.mark.parametrize("model", sorted(MODELS))
-def test_fragment_reads_conflict_free_under_swizzle(cfg, dt, model):
-    # 32x32x16 MFMA: lane l reads row (l % 32), chunk 2s + l // 32 of the A (or
-    # transposed B) tile, for rows starting at any multiple of 32.
-    lanes_per_cycle, groups = MODELS[model]
+def b_transpose_bytes(cfg, swz, wcol, j, s, half):
+    # ds_read_b64_tr_b16 for the B operand: lane L = 16 g + i supplies row
+    # k = 16 s + 8 (g // 2) + i // 4 (+4 for the second read), columns
+    # n = wcol + 32 j + 16 (g % 2) + 4 (i % 4) .. + 3
+    out = []
+    for L in range(64):
+        g, i = L // 16, L % 16
+        k = 16 * s + 8 * (g // 2) + i // 4 + 4 * half
+        n = wcol + 32 * j + 16 * (g % 2) + 4 * (i % 4)
+        out.append(2 * tg.tile_gemm_lds_offset(cfg, swz, 1, k, n))
+    return out
+
+
+@pytest.mark.parametrize("cfg,dt", RING)
+def test_ring_a_fragment_reads_conflict_free(cfg, dt):
     bm, bn, bk, _ = dims(cfg, dt)
-    for swz, expect_free in [(tg.SWZ_XOR, True), (tg.SWZ_NONE, False)]:
+    for swz, expect in [(tg.SWZ_XOR, True), (tg.SWZ_NONE, False)]:
         for base in range(0, bm, 32):
-            for s in range(4):
-                offs = [2 * tg.tile_gemm_lds_offset(cfg, swz, 0, base + l % 32, 8 * (2 * s + l // 32))
-                        for l in range(64)]
-                assert conflict_free(offs, lanes_per_cycle, groups) == expect_free, (swz, base, s)
+            for s in range(bk // 16):
+                offs = a_fragment_bytes(cfg, swz, base, s)
+                free = all(banks_distinct(offs[g:g + 16], 16) for g in range(0, 64, 16))
+                assert free == expect, (swz, base, s)
 
 
-@pytest.mark.parametrize("cfg,dt", CONFIGS[:3])
-@pytest.mark.parametrize("model", sorted(MODELS))
-def test_a_copy_writes_conflict_free(cfg, dt, model):
-    # 128-bit LDS writes are served 8 lanes (128 bytes) per cycle in both models
-    groups = MODELS[model][1]
+@pytest.mark.parametrize("cfg,dt", RING)
+def test_ring_b_transpose_reads_conflict_free(cfg, dt):
+    bm, bn, bk, waves = dims(cfg, dt)
+    for swz, expect in [(tg.SWZ_XOR, True), (tg.SWZ_NONE, False)]:
+        for wcol in range(0, bn, 32):
+            for s in range(bk // 16):
+                for half in (0, 1):
+                    offs = b_transpose_bytes(cfg, swz, wcol, 0, s, half)
+                    # each 64-bit read returns 4 consecutive n of one k row
+                    assert all(o % 8 == 0 for o in offs)
+                    free = all(banks_distinct(offs[g:g + 32], 8) for g in (0, 32))
+                    assert free == expect, (swz, wcol, s, half)
+
+
+@pytest.mark.parametrize("cfg,dt", RING)
+def test_ring_copy_ownership(cfg, dt):
+    # every physical 16-byte chunk of the A tile is filled by exactly one
+    # (copy instruction, wave, lane); a copy instruction fills 1 KiB, lane l
+    # writing bytes 16 l .. 16 l + 15 of it
+    bm, bn, bk, waves = dims(cfg, dt)
     L = tg.tile_gemm_describe_layout(cfg, 0, tg.LAYOUT_COPY_A)
-    bm, bn, bk, waves = dims(cfg, dt)
-    owner = {}
+    owners = {}
     for r in range(bm):
-        for ch in range(8):
-            (coord,) = tg.tg_layout_eval(L, (r, ch))
-            owner[(coord[WAVE], coord[LANE], coord[M])] = (r, ch)
-    assert len(owner) == bm * 8                                   # each chunk copied by one thread slot
-    for (w, lane, q), (r, ch) in owner.items():
-        if lane % 8:
-            continue
-        group = [owner[(w, lane + d, q)] for d in range(8)]
-        offs = [2 * tg.tile_gemm_lds_offset(cfg, tg.SWZ_XOR, 0, rr, 8 * cc) for rr, cc in group]
-        assert conflict_free(offs, 8, groups)
-
-
-@pytest.mark.parametrize("cfg,dt", CONFIGS[:3])
-@pytest.mark.parametrize("model", sorted(MODELS))
-def test_b_copy_writes_conflict_free(cfg, dt, model):
-    # loader lanes 8g..8g+7 take the squares kb = 0..7 of one column block nb and
-    # write, for each column c of it, chunk kb of transposed-tile row nb*8 + c
-    groups = MODELS[model][1]
-    bm, bn, bk, waves = dims(cfg, dt)
-    for nb in range(bn // 8):
-        for c in range(8):
-            offs = [2 * tg.tile_gemm_lds_offset(cfg, tg.SWZ_XOR, 1, nb * 8 + c, 8 * kb) for kb in range(8)]
-            assert conflict_free(offs, 8, groups)
+        for p in range(bk * 2 // 16):
+            (coord,) = tg.tg_layout_eval(L, (r, p))
+            key = (coord[M], coord[WAVE], coord[LANE])
+            assert key not in owners
+            owners[key] = (r, p)
+            byte = (r * bk * 2) + 16 * p
+            assert byte == (coord[M] * waves + coord[WAVE]) * 1024 + 16 * coord[LANE]
+    assert len(owners) == bm * bk * 2 // 16
 
 
 @pytest.mark.parametrize("cfg,dt", CONFIGS)

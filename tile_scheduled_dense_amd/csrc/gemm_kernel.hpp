@@ -201,6 +201,47 @@ __device__ __forceinline__ void mfma_chunk(const u32x4 &a, const u32x4 &b, f32x4
     }
 }
 
+// ---- fused alpha/beta store-back -----------------------------------------------
+// C = fma(alpha, acc, beta * C0), or alpha * acc when beta == 0 (C0 not read);
+// masks (fringe blocks only) sit here, on the accumulator transfer.  For each
+// MFMA tile the C0 values are all loaded before any store, so the loads are in
+// flight together instead of each waiting behind the previous store.
+template <class C, bool FRINGE, class Acc>
+__device__ __forceinline__ void store_tile_epilogue(const GemmParams &p, Acc (&acc)[C::TM][C::TN], int64_t b,
+                                                    int64_t m0, int64_t n0, int wave, int lane) {
+    float *Cblk = p.C + b * p.sC + m0 * p.ldc + n0;
+    const int ldc = (int)p.ldc;
+    const float alpha = p.alpha, beta = p.beta;
+    const int64_t M = p.M, N = p.N;
+#pragma unroll
+    for (int i = 0; i < C::TM; ++i) {
+#pragma unroll
+        for (int j = 0; j < C::TN; ++j) {
+            int off[C::ACC_PER_MFMA];
+            bool ok[C::ACC_PER_MFMA];
+#pragma unroll
+            for (int v = 0; v < C::ACC_PER_MFMA; ++v) {
+                int row, col;
+                acc_coord<C>(wave, lane, (i * C::TN + j) * C::ACC_PER_MFMA + v, row, col);
+                off[v] = row * ldc + col;
+                ok[v] = !FRINGE || (m0 + row < M && n0 + col < N);
+            }
+            if (beta != 0.0f) {
+                float c0[C::ACC_PER_MFMA];
+#pragma unroll
+                for (int v = 0; v < C::ACC_PER_MFMA; ++v) c0[v] = ok[v] ? Cblk[off[v]] : 0.0f;
+#pragma unroll
+                for (int v = 0; v < C::ACC_PER_MFMA; ++v)
+                    if (ok[v]) Cblk[off[v]] = __builtin_fmaf(alpha, acc[i][j][v], beta * c0[v]);
+            } else {
+#pragma unroll
+                for (int v = 0; v < C::ACC_PER_MFMA; ++v)
+                    if (ok[v]) Cblk[off[v]] = alpha * acc[i][j][v];
+            }
+        }
+    }
+}
+
 // ---- one workgroup tile ----------------------------------------------------------
 template <class C, int DEPTH, int SWZ, bool FRINGE>
 __device__ __forceinline__ void gemm_tile(const GemmParams &p, char *smem, int64_t b, int64_t tm, int64_t tn) {
@@ -216,7 +257,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams &p, char *smem, int64
 
     const int64_t M = p.M, N = p.N, K = p.K;
     const int64_t m0 = tm * C::BM, n0 = tn * C::BN;
-    const int lda = (int)p.lda, ldb = (int)p.ldb, ldc = (int)p.ldc;
+    const int lda = (int)p.lda, ldb = (int)p.ldb;
     const char *Ablk = p.A + (b * p.sA + m0 * p.lda) * E;   // A[b][m0][0]
     const char *Bblk = p.B + (b * p.sB + n0) * E;           // B[b][0][n0]
     const int64_t nk = (K + C::BK - 1) / C::BK;
@@ -352,23 +393,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams &p, char *smem, int64
     }
 
     // -- epilogue: fused alpha/beta store-back, masks only here
-    float *Cblk = p.C + b * p.sC + m0 * p.ldc + n0;
-    const float alpha = p.alpha, beta = p.beta;
-#pragma unroll
-    for (int i = 0; i < C::TM; ++i) {
-#pragma unroll
-        for (int j = 0; j < C::TN; ++j) {
-#pragma unroll
-            for (int v = 0; v < C::ACC_PER_MFMA; ++v) {
-                int row, col;
-                acc_coord<C>(wave, lane, (i * C::TN + j) * C::ACC_PER_MFMA + v, row, col);
-                if (FRINGE && !(m0 + row < M && n0 + col < N)) continue;
-                float *dst = Cblk + (row * ldc + col);
-                const float a = acc[i][j][v];
-                *dst = beta != 0.0f ? __builtin_fmaf(alpha, a, beta * *dst) : alpha * a;
-            }
-        }
-    }
+    store_tile_epilogue<C, FRINGE>(p, acc, b, m0, n0, wave, lane);
 }
 
 template <class C, int DEPTH, int SWZ>

@@ -116,11 +116,69 @@ tg_status describe(int swz, int kind, tg_layout *out) {
     return TG_ERR_INVALID_ARG;
 }
 
+// The 16-bit ring family: A [BM][32] under Swizzle(3, 2, 4); B [32][BN] under
+// Swizzle(5, B, S) on 64-byte units; copies own physical 16-byte chunks.
+template <class C>
+void describe_ring_lds(tg_layout *L, int operand, int swz) {
+    const int rows = operand == 0 ? C::BM : C::BK;
+    const int cols = operand == 0 ? C::BK : C::BN;
+    L->rank = 2;
+    L->shape[0] = rows;
+    L->shape[1] = cols;
+    L->n_shard = 2;
+    L->shard[0] = {rows, cols, TG_AXIS_M, 0};
+    L->shard[1] = {cols, 1, TG_AXIS_M, 0};
+    if (swz != SWZ_XOR) return;
+    L->n_swizzle = 1;
+    if (operand == 0) {
+        L->swizzle[0] = {3, 2, 4};                          // chunk ^= (row >> 2) & 3
+    } else if (C::B_UNITS >= 4) {
+        L->swizzle[0] = {5, 2, C::B_UNITS == 8 ? 3 : 2};    // 64-byte unit ^= k & 3
+    } else {
+        L->swizzle[0] = {5, 1, 2};                          // 64-byte unit ^= (k >> 1) & 1
+    }
+}
+
+template <class C>
+void describe_ring_copy_a(tg_layout *L) {
+    // physical chunk q = row*4 + p = (d*WAVES + wave)*64 + lane
+    L->rank = 2;
+    L->shape[0] = C::BM;
+    L->shape[1] = C::A_ROW_BYTES / 16;
+    L->n_shard = 3;
+    L->shard[0] = {C::A_DMA, 1, TG_AXIS_M, 0};
+    L->shard[1] = {C::WAVES, 1, TG_AXIS_WAVE, 0};
+    L->shard[2] = {64, 1, TG_AXIS_LANE, 0};
+}
+
+template <class C>
+tg_status describe_ring(int swz, int kind, tg_layout *out) {
+    switch (kind) {
+        case TG_LAYOUT_LDS_A: describe_ring_lds<C>(out, 0, swz); return TG_OK;
+        case TG_LAYOUT_LDS_B: describe_ring_lds<C>(out, 1, swz); return TG_OK;
+        case TG_LAYOUT_ACC: describe_acc<C>(out); return TG_OK;
+        case TG_LAYOUT_COPY_A: describe_ring_copy_a<C>(out); return TG_OK;
+    }
+    return TG_ERR_INVALID_ARG;
+}
+
+// Element offset within one pipeline copy of element (i, j) of an operand
+// tile as stored: fp32 family A (m, k), B (n, k); ring family A (m, k), B (k, n).
 template <class C>
 int64_t lds_offset(int swz, int operand, int64_t row, int64_t k) {
     const int rows = operand == 0 ? C::BM : C::BN;
     if (row < 0 || row >= rows || k < 0 || k >= C::BK) return -1;
     return lds_chunk_byte<C>((int)row, (int)(k / C::CHUNK), swz) / C::ELEM + k % C::CHUNK;
+}
+
+template <class C>
+int64_t ring_lds_offset(int swz, int operand, int64_t i, int64_t j) {
+    if (operand == 0) {
+        if (i < 0 || i >= C::BM || j < 0 || j >= C::BK) return -1;
+        return ring_a_byte<C>((int)i, (int)(j / 8), swz) / 2 + j % 8;
+    }
+    if (i < 0 || i >= C::BK || j < 0 || j >= C::BN) return -1;
+    return ring_b_byte<C>((int)i, (int)j, swz) / 2;
 }
 
 template <class C>
@@ -183,9 +241,9 @@ tg_status tile_gemm_describe_layout(int config, int swizzle, int kind, tg_layout
     if (swizzle != SWZ_NONE && swizzle != SWZ_XOR) return TG_ERR_INVALID_ARG;
     std::memset(out, 0, sizeof *out);
     switch (config) {
-        case TG_CFG_256x256: return describe<Cfg256<DT_BF16>>(swizzle, kind, out);
-        case TG_CFG_128x128: return describe<Cfg128<DT_BF16>>(swizzle, kind, out);
-        case TG_CFG_64x64: return describe<Cfg64<DT_BF16>>(swizzle, kind, out);
+        case TG_CFG_256x256: return describe_ring<Ring256<DT_BF16>>(swizzle, kind, out);
+        case TG_CFG_128x128: return describe_ring<Ring128<DT_BF16>>(swizzle, kind, out);
+        case TG_CFG_64x64: return describe_ring<Ring64<DT_BF16>>(swizzle, kind, out);
         case TG_CFG_F32_64x64: return describe<CfgF32>(swizzle, kind, out);
     }
     return TG_ERR_INVALID_ARG;
@@ -195,9 +253,9 @@ int64_t tile_gemm_lds_offset(int config, int swizzle, int operand, int64_t row, 
     if (swizzle == 0) swizzle = SWZ_XOR;
     if ((swizzle != SWZ_NONE && swizzle != SWZ_XOR) || (operand != 0 && operand != 1)) return -1;
     switch (config) {
-        case TG_CFG_256x256: return lds_offset<Cfg256<DT_BF16>>(swizzle, operand, row, k);
-        case TG_CFG_128x128: return lds_offset<Cfg128<DT_BF16>>(swizzle, operand, row, k);
-        case TG_CFG_64x64: return lds_offset<Cfg64<DT_BF16>>(swizzle, operand, row, k);
+        case TG_CFG_256x256: return ring_lds_offset<Ring256<DT_BF16>>(swizzle, operand, row, k);
+        case TG_CFG_128x128: return ring_lds_offset<Ring128<DT_BF16>>(swizzle, operand, row, k);
+        case TG_CFG_64x64: return ring_lds_offset<Ring64<DT_BF16>>(swizzle, operand, row, k);
         case TG_CFG_F32_64x64: return lds_offset<CfgF32>(swizzle, operand, row, k);
     }
     return -1;
@@ -205,9 +263,9 @@ int64_t tile_gemm_lds_offset(int config, int swizzle, int operand, int64_t row, 
 
 int tile_gemm_acc_coord(int config, int wave, int lane, int slot, int64_t *row, int64_t *col) {
     switch (config) {
-        case TG_CFG_256x256: return acc_coord_checked<Cfg256<DT_BF16>>(wave, lane, slot, row, col);
-        case TG_CFG_128x128: return acc_coord_checked<Cfg128<DT_BF16>>(wave, lane, slot, row, col);
-        case TG_CFG_64x64: return acc_coord_checked<Cfg64<DT_BF16>>(wave, lane, slot, row, col);
+        case TG_CFG_256x256: return acc_coord_checked<Ring256<DT_BF16>>(wave, lane, slot, row, col);
+        case TG_CFG_128x128: return acc_coord_checked<Ring128<DT_BF16>>(wave, lane, slot, row, col);
+        case TG_CFG_64x64: return acc_coord_checked<Ring64<DT_BF16>>(wave, lane, slot, row, col);
         case TG_CFG_F32_64x64: return acc_coord_checked<CfgF32>(wave, lane, slot, row, col);
     }
     return -1;

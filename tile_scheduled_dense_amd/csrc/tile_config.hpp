@@ -62,10 +62,8 @@ struct TileCfg {
     static_assert(B_UNITS % LOADERS == 0 && B_PER_THREAD >= 1, "B copy split");
 };
 
-// The shipped configurations (ids match tg_config in tile_gemm.h).
-template <int DT> using Cfg256 = TileCfg<DT, 256, 256, 2, 4>;  // 8 waves, wave tile 128 x 64
-template <int DT> using Cfg128 = TileCfg<DT, 128, 128, 2, 2>;  // 4 waves, wave tile 64 x 64
-template <int DT> using Cfg64 = TileCfg<DT, 64, 64, 1, 2>;     // 2 waves, wave tile 64 x 32
+// The fp32 configuration (id TG_CFG_F32_64x64 in tile_gemm.h); the 16-bit
+// configurations are the RingCfg family below.
 using CfgF32 = TileCfg<DT_F32, 64, 64, 2, 2>;                  // 4 waves, wave tile 32 x 32 (16x16 MFMA)
 
 enum Swz : int { SWZ_NONE = 1, SWZ_XOR = 2 };
@@ -113,6 +111,105 @@ template <class C>
 TG_HD int lds_chunk_byte(int row, int chunk, int swz) {
     int c = swz == SWZ_NONE ? chunk : (chunk ^ swizzle_row_mask(row));
     return (row * C::CPR + c) * 16;
+}
+
+// ---------------------------------------------------------------------------
+// The 16-bit kernel family: a K ring of STAGES LDS copies filled by direct
+// global -> LDS copies (no staging registers), BK = 32.
+//
+//  * A tile [BM][32] (64-byte rows, k contiguous) under Swizzle(3, 2, 4): the
+//    16-byte chunk index of row r is XORed with (r >> 2) & 3.  A 128-bit
+//    fragment read serves 16 lanes = 16 consecutive rows per cycle; four rows
+//    share a 256-byte bank line, and rows r, r+4, r+8, r+12 land on distinct
+//    chunks, so the 16 reads cover 16 distinct bank groups.
+//  * B tile [32][BN] (k rows, n contiguous) under Swizzle(5, B, S) on 64-byte
+//    units (32 elements): the unit index w of row k is XORed with k & 3 when a
+//    row has >= 4 units, with (k >> 1) & 1 when it has 2.  B is read with the
+//    transposing ds_read_b64_tr_b16: 32 lanes per cycle read 4 consecutive k
+//    rows x 64 bytes, which the XOR spreads over the four 64-byte quarters of
+//    the bank line.
+//  * Copies: each DMA instruction fills 1 KiB of LDS, lane l writing bytes
+//    16l..16l+15; the swizzle is realised by choosing each lane's source.
+// ---------------------------------------------------------------------------
+template <int DT_, int BM_, int BN_, int WAVES_M_, int WAVES_N_>
+struct RingCfg {
+    static constexpr int DT = DT_;
+    static constexpr int ELEM = 2;
+    static constexpr int BM = BM_, BN = BN_, BK = 32;
+    static constexpr int CHUNK = 8;                          // elements per 16 bytes
+    static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
+    static constexpr int WAVES = WAVES_M_ * WAVES_N_;
+    static constexpr int THREADS = 64 * WAVES;
+    static constexpr int MT = 32, ACC_PER_MFMA = 16;
+    static constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
+    static constexpr int TM = WTM / MT, TN = WTN / MT;
+    static constexpr int KSTEPS = BK / 16;                   // 32x32x16 MFMAs per K tile
+    static constexpr int A_ROW_BYTES = BK * ELEM;            // 64
+    static constexpr int B_ROW_BYTES = BN * ELEM;
+    static constexpr int B_UNITS = B_ROW_BYTES / 64;         // 64-byte units per B row
+    static constexpr int A_TILE_BYTES = BM * A_ROW_BYTES;
+    static constexpr int B_TILE_BYTES = BK * B_ROW_BYTES;
+    static constexpr int STAGE_BYTES = A_TILE_BYTES + B_TILE_BYTES;
+    static constexpr int A_DMA = A_TILE_BYTES / 1024 / WAVES;   // 1 KiB copies per wave per tile
+    static constexpr int B_DMA = B_TILE_BYTES / 1024 / WAVES;
+    static constexpr int COPIES = A_DMA + B_DMA;
+    // acc_coord() below is shared with TileCfg
+    static constexpr int LANE_GROUPS = 2;
+
+    static_assert(BM % (WAVES_M * MT) == 0 && BN % (WAVES_N * MT) == 0, "wave tiling");
+    static_assert(A_TILE_BYTES % (1024 * WAVES) == 0 && A_DMA >= 1, "A copy split");
+    static_assert(B_TILE_BYTES % (1024 * WAVES) == 0 && B_DMA >= 1, "B copy split");
+    static_assert(B_UNITS == 2 || B_UNITS == 4 || B_UNITS == 8, "B row of 2, 4 or 8 units");
+};
+
+template <int DT> using Ring256 = RingCfg<DT, 256, 256, 2, 4>;   // 8 waves, wave tile 128 x 64
+template <int DT> using Ring128 = RingCfg<DT, 128, 128, 2, 2>;   // 4 waves, wave tile 64 x 64
+template <int DT> using Ring64 = RingCfg<DT, 64, 64, 1, 2>;      // 2 waves, wave tile 64 x 32
+
+// A tile: byte offset of logical chunk c (0..3) of row r.
+template <class C>
+TG_HD int ring_a_byte(int r, int c, int swz) {
+    const int p = swz == SWZ_NONE ? c : (c ^ ((r >> 2) & 3));
+    return r * C::A_ROW_BYTES + 16 * p;
+}
+
+// B tile: the XOR applied to the 64-byte unit index of k row k.
+template <class C>
+TG_HD int ring_b_mask(int k, int swz) {
+    if (swz == SWZ_NONE) return 0;
+    return C::B_UNITS >= 4 ? (k & 3) : ((k >> 1) & 1);
+}
+
+// B tile: byte offset of element (k, n).
+template <class C>
+TG_HD int ring_b_byte(int k, int n, int swz) {
+    const int w = n / 32, in_unit = (n % 32) * 2;
+    return k * C::B_ROW_BYTES + 64 * (w ^ ring_b_mask<C>(k, swz)) + in_unit;
+}
+
+// Which LDS bytes DMA copy d (0 <= d < A_DMA or B_DMA) of wave w fills:
+// 1 KiB block J = d * WAVES + w of the operand's region.
+template <class C>
+TG_HD int ring_block(int d, int wave) { return d * C::WAVES + wave; }
+
+// The A element (row, first k of the chunk) lane l of block J must fetch.
+template <class C>
+TG_HD void ring_a_source(int J, int lane, int swz, int &row, int &k) {
+    const int byte = J * 1024 + 16 * lane;
+    row = byte / C::A_ROW_BYTES;
+    const int p = (byte % C::A_ROW_BYTES) / 16;
+    const int c = swz == SWZ_NONE ? p : (p ^ ((row >> 2) & 3));
+    k = 8 * c;
+}
+
+// The B element (k, first n of the chunk) lane l of block J must fetch.
+template <class C>
+TG_HD void ring_b_source(int J, int lane, int swz, int &k, int &n) {
+    const int byte = J * 1024 + 16 * lane;
+    k = byte / C::B_ROW_BYTES;
+    const int b = byte % C::B_ROW_BYTES;
+    const int w = (b / 64) ^ ring_b_mask<C>(k, swz);
+    n = 32 * w + (b % 64) / 2;
 }
 
 // ---------------------------------------------------------------------------

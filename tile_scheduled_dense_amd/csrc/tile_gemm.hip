@@ -8,7 +8,7 @@
 #include <mutex>
 #include <new>
 
-#include "gemm_kernel.hpp"
+#include "gemm_ring.hpp"
 #include "tile_gemm.h"
 
 using namespace tg;
@@ -52,26 +52,16 @@ tg_status current_device_ok() {
 }
 
 struct CfgDims {
-    int bm, bn, bk, waves;
+    int bm, bn, bk, waves, stage_bytes;
 };
 
 CfgDims cfg_dims(int config) {
     switch (config) {
-        case TG_CFG_256x256: return {Cfg256<DT_BF16>::BM, Cfg256<DT_BF16>::BN, Cfg256<DT_BF16>::BK, Cfg256<DT_BF16>::WAVES};
-        case TG_CFG_128x128: return {Cfg128<DT_BF16>::BM, Cfg128<DT_BF16>::BN, Cfg128<DT_BF16>::BK, Cfg128<DT_BF16>::WAVES};
-        case TG_CFG_64x64: return {Cfg64<DT_BF16>::BM, Cfg64<DT_BF16>::BN, Cfg64<DT_BF16>::BK, Cfg64<DT_BF16>::WAVES};
-        case TG_CFG_F32_64x64: return {CfgF32::BM, CfgF32::BN, CfgF32::BK, CfgF32::WAVES};
-        default: return {0, 0, 0, 0};
-    }
-}
-
-int stage_bytes(int config) {
-    switch (config) {
-        case TG_CFG_256x256: return Cfg256<DT_BF16>::STAGE_BYTES;
-        case TG_CFG_128x128: return Cfg128<DT_BF16>::STAGE_BYTES;
-        case TG_CFG_64x64: return Cfg64<DT_BF16>::STAGE_BYTES;
-        case TG_CFG_F32_64x64: return CfgF32::STAGE_BYTES;
-        default: return 0;
+        case TG_CFG_256x256: return {Ring256<DT_BF16>::BM, Ring256<DT_BF16>::BN, Ring256<DT_BF16>::BK, Ring256<DT_BF16>::WAVES, Ring256<DT_BF16>::STAGE_BYTES};
+        case TG_CFG_128x128: return {Ring128<DT_BF16>::BM, Ring128<DT_BF16>::BN, Ring128<DT_BF16>::BK, Ring128<DT_BF16>::WAVES, Ring128<DT_BF16>::STAGE_BYTES};
+        case TG_CFG_64x64: return {Ring64<DT_BF16>::BM, Ring64<DT_BF16>::BN, Ring64<DT_BF16>::BK, Ring64<DT_BF16>::WAVES, Ring64<DT_BF16>::STAGE_BYTES};
+        case TG_CFG_F32_64x64: return {CfgF32::BM, CfgF32::BN, CfgF32::BK, CfgF32::WAVES, CfgF32::STAGE_BYTES};
+        default: return {0, 0, 0, 0, 0};
     }
 }
 
@@ -104,10 +94,13 @@ tg_status make_plan(int64_t batch, int64_t M, int64_t N, int64_t K, tg_dtype dty
     int config = o.config ? o.config : choose_config(batch, M, N, dtype);
     if (config < TG_CFG_256x256 || config > TG_CFG_F32_64x64) return TG_ERR_INVALID_ARG;
     if ((dtype == TG_F32) != (config == TG_CFG_F32_64x64)) return TG_ERR_UNSUPPORTED;
-    const int depth = o.pipeline_depth ? o.pipeline_depth : 2;
-    if (depth != 1 && depth != 2) return TG_ERR_UNSUPPORTED;
+    // pipeline depth = LDS copies of the K tile (window = depth - 1)
+    const bool f32 = config == TG_CFG_F32_64x64;
+    const int depth = o.pipeline_depth ? o.pipeline_depth : (f32 ? 2 : 4);
+    if (f32 ? (depth != 1 && depth != 2) : (depth != 1 && depth != 2 && depth != 4)) return TG_ERR_UNSUPPORTED;
     const int swz = o.swizzle ? o.swizzle : SWZ_XOR;
     if (swz != SWZ_NONE && swz != SWZ_XOR) return TG_ERR_UNSUPPORTED;
+    if (!f32 && swz == SWZ_NONE && depth != 4) return TG_ERR_UNSUPPORTED;   // ablation built at depth 4 only
     const int order = o.block_order;
     if (order != 0 && order != 1) return TG_ERR_UNSUPPORTED;
 
@@ -131,7 +124,7 @@ tg_status make_plan(int64_t batch, int64_t M, int64_t N, int64_t K, tg_dtype dty
     p.fringe_blocks = p.tiles_m * p.tiles_n - p.interior_blocks;
     p.k_tiles = cdiv(K, d.bk);
     p.k_tail = K % d.bk;
-    p.lds_bytes = depth * stage_bytes(config);
+    p.lds_bytes = depth * d.stage_bytes;
     return TG_OK;
 }
 
@@ -199,12 +192,33 @@ tg_status launch_variants(const GemmParams &gp, const tg_plan_info &p, hipStream
     return TG_ERR_UNSUPPORTED;
 }
 
+template <class C, int STAGES, int SWZ>
+tg_status launch_ring_one(const GemmParams &gp, int64_t grid, hipStream_t stream) {
+    if (grid > 0x7fffffffLL) return TG_ERR_UNSUPPORTED;
+    hipLaunchKernelGGL((gemm_ring_kernel<C, STAGES, SWZ>), dim3((unsigned)grid), dim3(C::THREADS), 0, stream, gp);
+    return hipGetLastError() == hipSuccess ? TG_OK : TG_ERR_LAUNCH;
+}
+
+template <class C>
+tg_status launch_ring(const GemmParams &gp, const tg_plan_info &p, hipStream_t s) {
+    if (p.swizzle == SWZ_XOR) {
+        switch (p.pipeline_depth) {
+            case 4: return launch_ring_one<C, 4, SWZ_XOR>(gp, p.grid, s);
+            case 2: return launch_ring_one<C, 2, SWZ_XOR>(gp, p.grid, s);
+            case 1: return launch_ring_one<C, 1, SWZ_XOR>(gp, p.grid, s);
+        }
+    } else if (p.pipeline_depth == 4) {
+        return launch_ring_one<C, 4, SWZ_NONE>(gp, p.grid, s);
+    }
+    return TG_ERR_UNSUPPORTED;
+}
+
 template <int DT>
 tg_status launch_dtype(const GemmParams &gp, const tg_plan_info &p, hipStream_t s) {
     switch (p.config) {
-        case TG_CFG_256x256: return launch_variants<Cfg256<DT>>(gp, p, s);
-        case TG_CFG_128x128: return launch_variants<Cfg128<DT>>(gp, p, s);
-        case TG_CFG_64x64: return launch_variants<Cfg64<DT>>(gp, p, s);
+        case TG_CFG_256x256: return launch_ring<Ring256<DT>>(gp, p, s);
+        case TG_CFG_128x128: return launch_ring<Ring128<DT>>(gp, p, s);
+        case TG_CFG_64x64: return launch_ring<Ring64<DT>>(gp, p, s);
         default: return TG_ERR_UNSUPPORTED;
     }
 }
