@@ -172,7 +172,7 @@ def test_ring_b_transpose_reads_conflict_free(cfg, dt):
 def test_ring_copy_ownership(cfg, dt):
     # every physical 16-byte chunk of the A tile is filled by exactly one
     # (copy instruction, wave, lane); a copy instruction fills 1 KiB, lane l
-    # writing bytes 16 l .. 16 l + 15 of it
+    # writing bytes 16 l .. 16 l + 15 of it, and one wave's copies are adjacent
     bm, bn, bk, waves = dims(cfg, dt)
     L = tg.tile_gemm_describe_layout(cfg, 0, tg.LAYOUT_COPY_A)
     owners = {}
@@ -183,7 +183,9 @@ def test_ring_copy_ownership(cfg, dt):
             assert key not in owners
             owners[key] = (r, p)
             byte = (r * bk * 2) + 16 * p
-            assert byte == (coord[M] * waves + coord[WAVE]) * 1024 + 16 * coord[LANE]
+            per_wave = bm * bk * 2 // 1024 // waves
+            assert 0 <= coord[M] < per_wave
+            assert byte == (coord[WAVE] * per_wave + coord[M]) * 1024 + 16 * coord[LANE]
     assert len(owners) == bm * bk * 2 // 16
 
 

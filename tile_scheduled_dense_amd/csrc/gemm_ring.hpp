@@ -35,6 +35,9 @@
 
 namespace tg {
 
+// The two K-loop schedules (template argument of gemm_ring_kernel).
+enum { SCHED_RING = 0, SCHED_SWPIPE = 1 };
+
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 #define TG_LDS_PTR(p) ((__attribute__((address_space(3))) void *)(p))
@@ -77,193 +80,428 @@ __device__ __forceinline__ i32x4 rsrc_words(const char *base, int64_t nbytes) {
     return i32x4{lo, hi, n, 0x00020000};
 }
 
-__device__ __forceinline__ void copy_to_lds(i32x4 rs, uint32_t lds_addr, int voff) {
+__device__ __forceinline__ uint64_t uniform_u64(uint64_t a) {
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    return ((uint64_t)hi << 32) | lo;
+}
+
+// rsrc_words for a base already known to be uniform (no lane reads needed).
+__device__ __forceinline__ i32x4 rsrc_words_u(uint64_t base, int64_t nbytes) {
+    const int n = nbytes > 0x7fffffffLL ? 0x7fffffff : (int)nbytes;
+    return i32x4{(int)(uint32_t)base, (int)((uint32_t)(base >> 32) & 0xffffu), n, 0x00020000};
+}
+
+// G (1, 2 or 4) adjacent 1-KiB buffer-to-LDS copies under one m0 value.
+// Copy g lands at LDS address lds_addr + 1024 g (+ 16 per lane); the
+// instruction's immediate offset 1024 g also moves the global address, so the
+// caller passes voff[g] already reduced by 1024 g relative to the resource base
+// (and the resource's base lowered to keep every voff non-negative).  Writing
+// m0 while an earlier copy of the wave is still being issued holds the wave
+// back, so one m0 write per group instead of one per copy roughly doubles the
+// copy rate a wave can sustain.
+template <int G>
+__device__ __forceinline__ void copy_group_to_lds(i32x4 rs, uint32_t lds_addr, const int (&voff)[G]) {
+    static_assert(G == 1 || G == 2 || G == 4, "1, 2 or 4 copies per group");
+    // both operands are uniform by construction; say so for the SGPR constraints
+    lds_addr = __builtin_amdgcn_readfirstlane(lds_addr);
+    rs = i32x4{__builtin_amdgcn_readfirstlane(rs.x), __builtin_amdgcn_readfirstlane(rs.y),
+               __builtin_amdgcn_readfirstlane(rs.z), __builtin_amdgcn_readfirstlane(rs.w)};
     int saved_m0;
-    asm volatile(
-        "s_mov_b32 %0, m0\n\t"
-        "s_mov_b32 m0, %1\n\t"
-        "s_nop 4\n\t"
-        "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
-        "s_mov_b32 m0, %0"
-        : "=&s"(saved_m0)
-        : "s"(lds_addr), "v"(voff), "s"(rs)
-        : "memory");
+    if constexpr (G == 1) {
+        asm volatile(
+            "s_mov_b32 %0, m0\n\t"
+            "s_mov_b32 m0, %1\n\t"
+            "s_nop 0\n\t"
+            "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+            "s_mov_b32 m0, %0"
+            : "=&s"(saved_m0)
+            : "s"(lds_addr), "v"(voff[0]), "s"(rs)
+            : "memory");
+    } else if constexpr (G == 2) {
+        asm volatile(
+            "s_mov_b32 %0, m0\n\t"
+            "s_mov_b32 m0, %1\n\t"
+            "s_nop 0\n\t"
+            "buffer_load_dwordx4 %2, %4, 0 offen lds\n\t"
+            "buffer_load_dwordx4 %3, %4, 0 offen offset:1024 lds\n\t"
+            "s_mov_b32 m0, %0"
+            : "=&s"(saved_m0)
+            : "s"(lds_addr), "v"(voff[0]), "v"(voff[1]), "s"(rs)
+            : "memory");
+    } else {
+        asm volatile(
+            "s_mov_b32 %0, m0\n\t"
+            "s_mov_b32 m0, %1\n\t"
+            "s_nop 0\n\t"
+            "buffer_load_dwordx4 %2, %6, 0 offen lds\n\t"
+            "buffer_load_dwordx4 %3, %6, 0 offen offset:1024 lds\n\t"
+            "buffer_load_dwordx4 %4, %6, 0 offen offset:2048 lds\n\t"
+            "buffer_load_dwordx4 %5, %6, 0 offen offset:3072 lds\n\t"
+            "s_mov_b32 m0, %0"
+            : "=&s"(saved_m0)
+            : "s"(lds_addr), "v"(voff[0]), "v"(voff[1]), "v"(voff[2]), "v"(voff[3]), "s"(rs)
+            : "memory");
+    }
 }
 
 __device__ __forceinline__ uint32_t lds_address(const char *p) {
     return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)TG_LDS_PTR(p));
 }
 
+// One workgroup's tile of the 16-bit family: copy sources, the copies, the
+// register-path last tile, fragment reads and the MFMAs, shared by the two
+// schedules below.
 template <class C, int STAGES, int SWZ, bool FRINGE>
-__device__ __forceinline__ void ring_tile(const GemmParams &p, char *smem, int64_t b, int64_t tm, int64_t tn) {
-    using Acc = f32x16;
-    constexpr int E = 2;
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int64_t M = p.M, N = p.N, K = p.K;
-    const int64_t m0 = tm * C::BM, n0 = tn * C::BN;
-    const int lda = (int)p.lda, ldb = (int)p.ldb;
-    const char *Ablk = p.A + (b * p.sA + m0 * p.lda) * E;   // A[b][m0][0]
-    const char *Bblk = p.B + (b * p.sB + n0) * E;           // B[b][0][n0]
-    // bytes from the block bases to one past the last valid element
-    const int64_t a_valid = ((M - m0 - 1) * p.lda + K) * E;
-    const int64_t b_valid = ((K - 1) * p.ldb + (N - n0)) * E;
-    const int64_t nk = (K + C::BK - 1) / C::BK;
-    const int64_t ndma = nk > 0 ? nk - 1 : 0;             // tiles copied straight to LDS
-
-    Acc acc[C::TM][C::TN];
-#pragma unroll
-    for (int i = 0; i < C::TM; ++i)
-#pragma unroll
-        for (int j = 0; j < C::TN; ++j) acc[i][j] = Acc{};
-
-    // This lane's sources: A (row, k) and B (k, n) of each of its copies.
-    int a_row[C::A_DMA], a_k[C::A_DMA], a_off[C::A_DMA];
-    int b_k[C::B_DMA], b_n[C::B_DMA], b_off[C::B_DMA];
-#pragma unroll
-    for (int d = 0; d < C::A_DMA; ++d) {
-        ring_a_source<C>(ring_block<C>(d, wave), lane, SWZ, a_row[d], a_k[d]);
-        a_off[d] = (FRINGE && m0 + a_row[d] >= M) ? kOutOfRange : (a_row[d] * lda + a_k[d]) * E;
-    }
-#pragma unroll
-    for (int d = 0; d < C::B_DMA; ++d) {
-        ring_b_source<C>(ring_block<C>(d, wave), lane, SWZ, b_k[d], b_n[d]);
-        b_off[d] = (FRINGE && n0 + b_n[d] >= N) ? kOutOfRange : (b_k[d] * ldb + b_n[d]) * E;
-    }
-
-    // -- direct copy of K tile kt into LDS copy `stage`
-    auto dma = [&](int64_t kt, int stage) {
-        const int64_t k0 = kt * C::BK;
-        const i32x4 ra = rsrc_words(Ablk + k0 * E, a_valid - k0 * E);
-        const i32x4 rb = rsrc_words(Bblk + k0 * p.ldb * E, b_valid - k0 * p.ldb * E);
-        char *sA = smem + stage * C::STAGE_BYTES;
-        char *sB = sA + C::A_TILE_BYTES;
-#pragma unroll
-        for (int d = 0; d < C::A_DMA; ++d) copy_to_lds(ra, lds_address(sA + ring_block<C>(d, wave) * 1024), a_off[d]);
-#pragma unroll
-        for (int d = 0; d < C::B_DMA; ++d) copy_to_lds(rb, lds_address(sB + ring_block<C>(d, wave) * 1024), b_off[d]);
-    };
-
-    // -- the last K tile through registers, element-exact zero fill
+struct RingBlock {
+    static constexpr int E = 2;
+    const GemmParams &p;
+    char *smem;
+    int lane, wave;
+    int64_t b, m0, n0, nk, ndma;
+    int lda, ldb;
+    const char *Ablk, *Bblk;
+    int64_t a_valid, b_valid;
+    int a_row[C::A_DMA], a_k[C::A_DMA], a_off[C::A_DMA], a_voff[C::A_DMA];
+    int b_k[C::B_DMA], b_n[C::B_DMA], b_off[C::B_DMA], b_voff[C::B_DMA];
+    // a group's resource base sits this far below the tile's first byte
+    static constexpr int A_SHIFT = (C::A_DMA - 1) * 1024, B_SHIFT = (C::B_DMA - 1) * 1024;
+    uint64_t a_base, b_base;    // Ablk, Bblk as workgroup-uniform integers
+    uint32_t lds0;              // LDS address of smem
+    int64_t b_step;             // bytes of B per K tile
     u32x4 tail[C::COPIES];
-    auto tail_load = [&]() {
+    f32x16 acc[C::TM][C::TN];
+
+    __device__ __forceinline__ RingBlock(const GemmParams &p_, char *smem_, int64_t b_, int64_t tm, int64_t tn)
+        : p(p_), smem(smem_), b(b_) {
+        lane = threadIdx.x & 63;
+        wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // the same in every lane of a wave
+        m0 = tm * C::BM;
+        n0 = tn * C::BN;
+        lda = (int)p.lda;
+        ldb = (int)p.ldb;
+        Ablk = p.A + (b * p.sA + m0 * p.lda) * E;   // A[b][m0][0]
+        Bblk = p.B + (b * p.sB + n0) * E;           // B[b][0][n0]
+        // bytes from the block bases to one past the last valid element
+        a_valid = ((p.M - m0 - 1) * p.lda + p.K) * E;
+        b_valid = ((p.K - 1) * p.ldb + (p.N - n0)) * E;
+        nk = (p.K + C::BK - 1) / C::BK;
+        ndma = nk > 0 ? nk - 1 : 0;                 // tiles copied straight to LDS
+        a_base = uniform_u64((uint64_t)Ablk);
+        b_base = uniform_u64((uint64_t)Bblk);
+        lds0 = lds_address(smem);
+        b_step = (int64_t)C::BK * p.ldb * E;
+#pragma unroll
+        for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+            for (int j = 0; j < C::TN; ++j) acc[i][j] = f32x16{};
+#pragma unroll
+        for (int d = 0; d < C::A_DMA; ++d) {
+            ring_a_source<C>(ring_block<C>(d, wave, C::A_DMA), lane, SWZ, a_row[d], a_k[d]);
+            a_off[d] = (FRINGE && m0 + a_row[d] >= p.M) ? kOutOfRange : (a_row[d] * lda + a_k[d]) * E;
+            a_voff[d] = a_off[d] + A_SHIFT - 1024 * d;
+        }
+#pragma unroll
+        for (int d = 0; d < C::B_DMA; ++d) {
+            ring_b_source<C>(ring_block<C>(d, wave, C::B_DMA), lane, SWZ, b_k[d], b_n[d]);
+            b_off[d] = (FRINGE && n0 + b_n[d] >= p.N) ? kOutOfRange : (b_k[d] * ldb + b_n[d]) * E;
+            b_voff[d] = b_off[d] + B_SHIFT - 1024 * d;
+        }
+    }
+
+    // this wave's copies of one operand (0 = A, 1 = B) of K tile kt into LDS copy `stage`
+    __device__ __forceinline__ void dma_operand(int64_t kt, int stage, int operand) {
+        const uint32_t sA = lds0 + stage * C::STAGE_BYTES;
+        if (operand == 0) {
+            const int64_t adv = kt * (C::BK * E);
+            copy_group_to_lds<C::A_DMA>(rsrc_words_u(a_base + adv - A_SHIFT, a_valid - adv + A_SHIFT),
+                                        sA + ring_block<C>(0, wave, C::A_DMA) * 1024, a_voff);
+        } else {
+            const int64_t adv = kt * b_step;
+            copy_group_to_lds<C::B_DMA>(rsrc_words_u(b_base + adv - B_SHIFT, b_valid - adv + B_SHIFT),
+                                        sA + C::A_TILE_BYTES + ring_block<C>(0, wave, C::B_DMA) * 1024, b_voff);
+        }
+    }
+
+    // direct copy of K tile kt into LDS copy `stage`
+    __device__ __forceinline__ void dma(int64_t kt, int stage) {
+        dma_operand(kt, stage, 0);
+        dma_operand(kt, stage, 1);
+    }
+
+    // the last K tile through registers, element-exact zero fill
+    __device__ __forceinline__ void tail_load() {
         const int64_t k0 = (nk - 1) * C::BK;
         const rsrc_t ra = make_rsrc_n(Ablk + k0 * E, a_valid - k0 * E);
         const rsrc_t rb = make_rsrc_n(Bblk + k0 * p.ldb * E, b_valid - k0 * p.ldb * E);
 #pragma unroll
         for (int d = 0; d < C::A_DMA; ++d) {
-            const int64_t left = K - (k0 + a_k[d]);
-            const bool row_ok = m0 + a_row[d] < M;
+            const int64_t left = p.K - (k0 + a_k[d]);
+            const bool row_ok = m0 + a_row[d] < p.M;
             const int n = !row_ok || left <= 0 ? 0 : (left >= C::CHUNK ? C::CHUNK : (int)left);
             tail[d] = bload16_n<E>(ra, (a_row[d] * lda + a_k[d]) * E, 0, n);
         }
 #pragma unroll
         for (int d = 0; d < C::B_DMA; ++d) {
-            const int64_t cols = N - (n0 + b_n[d]);
-            const bool k_ok = k0 + b_k[d] < K;
+            const int64_t cols = p.N - (n0 + b_n[d]);
+            const bool k_ok = k0 + b_k[d] < p.K;
             const int n = !k_ok || cols <= 0 ? 0 : (cols >= C::CHUNK ? C::CHUNK : (int)cols);
             tail[C::A_DMA + d] = bload16_n<E>(rb, (b_k[d] * ldb + b_n[d]) * E, 0, n);
         }
-    };
-    auto tail_store = [&](int stage) {
+    }
+    __device__ __forceinline__ void tail_store(int stage) {
         char *sA = smem + stage * C::STAGE_BYTES;
         char *sB = sA + C::A_TILE_BYTES;
 #pragma unroll
-        for (int d = 0; d < C::A_DMA; ++d) *(u32x4 *)(sA + ring_block<C>(d, wave) * 1024 + 16 * lane) = tail[d];
+        for (int d = 0; d < C::A_DMA; ++d)
+            *(u32x4 *)(sA + ring_block<C>(d, wave, C::A_DMA) * 1024 + 16 * lane) = tail[d];
 #pragma unroll
         for (int d = 0; d < C::B_DMA; ++d)
-            *(u32x4 *)(sB + ring_block<C>(d, wave) * 1024 + 16 * lane) = tail[C::A_DMA + d];
-    };
+            *(u32x4 *)(sB + ring_block<C>(d, wave, C::B_DMA) * 1024 + 16 * lane) = tail[C::A_DMA + d];
+    }
 
-    // -- MFMA over LDS copy `stage`
-    const int wrow = (wave / C::WAVES_N) * C::WTM;
-    const int wcol = (wave % C::WAVES_N) * C::WTN;
-    const int grp = lane / 16, gi = lane % 16;
-    auto compute = [&](int stage) {
+    // Wait until this wave's share of tile t is in LDS (its copies, or for
+    // the last tile its register stores), `ahead` = tiles issued after t at
+    // most (the lookahead still in flight).
+    template <int AHEAD>
+    __device__ __forceinline__ void land_tile(int64_t t, int stage) {
+        if (t < ndma) {
+            const int64_t later = ndma - 1 - t;
+            if (AHEAD >= 3 && later >= 3) wait_vmcnt<3 * C::COPIES>();
+            else if (AHEAD >= 2 && later >= 2) wait_vmcnt<2 * C::COPIES>();
+            else if (AHEAD >= 1 && later >= 1) wait_vmcnt<C::COPIES>();
+            else wait_vmcnt<0>();
+        } else {
+            wait_vmcnt<0>();
+            tail_store(stage);
+        }
+        wait_lds();
+    }
+
+    // fragments of K step s of LDS copy `stage`
+    __device__ __forceinline__ void read_frags(int stage, int s, u32x4 (&af)[C::TM], u32x4 (&bfr)[C::TN]) const {
         const char *sA = smem + stage * C::STAGE_BYTES;
         const char *sB = sA + C::A_TILE_BYTES;
+        const int wrow = (wave / C::WAVES_N) * C::WTM;
+        const int wcol = (wave % C::WAVES_N) * C::WTN;
+        const int grp = lane / 16, gi = lane % 16;
+#pragma unroll
+        for (int i = 0; i < C::TM; ++i)
+            af[i] = *(const u32x4 *)(sA + ring_a_byte<C>(wrow + i * C::MT + lane % 32, 2 * s + lane / 32, SWZ));
+#pragma unroll
+        for (int j = 0; j < C::TN; ++j) {
+            const int k = 16 * s + 8 * (grp / 2) + gi / 4;
+            const int n = wcol + j * C::MT + 16 * (grp % 2) + 4 * (gi % 4);
+            const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) v4i16 *)(sB + ring_b_byte<C>(k, n, SWZ)));
+            const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) v4i16 *)(sB + ring_b_byte<C>(k + 4, n, SWZ)));
+            const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+            bfr[j] = u32x4{l2.x, l2.y, h2.x, h2.y};
+        }
+    }
+
+    // Fragment piece r of K tile `stage` (r < READS): A pieces first
+    // (s, i), then B half-reads (s, j, half); B pieces fill one half of a
+    // u32x4 each.
+    static constexpr int READS = C::KSTEPS * (C::TM + 2 * C::TN);
+    __device__ __forceinline__ void read_piece(int stage, int r, u32x4 (&af)[C::KSTEPS][C::TM],
+                                               u32x4 (&bfr)[C::KSTEPS][C::TN]) const {
+        const char *sA = smem + stage * C::STAGE_BYTES;
+        const char *sB = sA + C::A_TILE_BYTES;
+        const int wrow = (wave / C::WAVES_N) * C::WTM;
+        const int wcol = (wave % C::WAVES_N) * C::WTN;
+        constexpr int NA = C::KSTEPS * C::TM;
+        if (r < NA) {
+            const int s = r / C::TM, i = r % C::TM;
+            af[s][i] = *(const u32x4 *)(sA + ring_a_byte<C>(wrow + i * C::MT + lane % 32, 2 * s + lane / 32, SWZ));
+        } else {
+            const int q = r - NA;
+            const int s = q / (2 * C::TN), j = (q / 2) % C::TN, half = q % 2;
+            const int grp = lane / 16, gi = lane % 16;
+            const int k = 16 * s + 8 * (grp / 2) + gi / 4 + 4 * half;
+            const int n = wcol + j * C::MT + 16 * (grp % 2) + 4 * (gi % 4);
+            const v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) v4i16 *)(sB + ring_b_byte<C>(k, n, SWZ)));
+            const u32x2 w2 = __builtin_bit_cast(u32x2, v);
+            if (half == 0) {
+                bfr[s][j].x = w2.x;
+                bfr[s][j].y = w2.y;
+            } else {
+                bfr[s][j].z = w2.x;
+                bfr[s][j].w = w2.y;
+            }
+        }
+    }
+
+    __device__ __forceinline__ void mfmas(const u32x4 (&af)[C::TM], const u32x4 (&bfr)[C::TN]) {
+#pragma unroll
+        for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+            for (int j = 0; j < C::TN; ++j) mfma_chunk<C::DT>(af[i], bfr[j], acc[i][j]);
+    }
+
+    __device__ __forceinline__ void compute(int stage) {
 #pragma unroll
         for (int s = 0; s < C::KSTEPS; ++s) {
             u32x4 af[C::TM], bfr[C::TN];
-#pragma unroll
-            for (int i = 0; i < C::TM; ++i)
-                af[i] = *(const u32x4 *)(sA + ring_a_byte<C>(wrow + i * C::MT + lane % 32, 2 * s + lane / 32, SWZ));
-#pragma unroll
-            for (int j = 0; j < C::TN; ++j) {
-                const int k = 16 * s + 8 * (grp / 2) + gi / 4;
-                const int n = wcol + j * C::MT + 16 * (grp % 2) + 4 * (gi % 4);
-                const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (__attribute__((address_space(3))) v4i16 *)(sB + ring_b_byte<C>(k, n, SWZ)));
-                const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (__attribute__((address_space(3))) v4i16 *)(sB + ring_b_byte<C>(k + 4, n, SWZ)));
-                const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
-                bfr[j] = u32x4{l2.x, l2.y, h2.x, h2.y};
-            }
-#pragma unroll
-            for (int i = 0; i < C::TM; ++i)
-#pragma unroll
-                for (int j = 0; j < C::TN; ++j) mfma_chunk<C::DT>(af[i], bfr[j], acc[i][j]);
+            read_frags(stage, s, af, bfr);
+            mfmas(af, bfr);
         }
-    };
+    }
+};
 
+// SCHED_RING (all waves in step): iteration kt waits for tile kt, one
+// barrier (tile kt visible, copy of tile kt-1 released), issues tile
+// kt + STAGES - 1, multiplies tile kt.  STAGES == 1 is the unpipelined form.
+template <class C, int STAGES, int SWZ, bool FRINGE>
+__device__ __forceinline__ void ring_tile(const GemmParams &p, char *smem, int64_t b, int64_t tm, int64_t tn) {
+    RingBlock<C, STAGES, SWZ, FRINGE> blk(p, smem, b, tm, tn);
+    const int64_t nk = blk.nk, ndma = blk.ndma;
     if (nk > 0) {
-        tail_load();
+        blk.tail_load();
         if (STAGES == 1) {
             for (int64_t kt = 0; kt < nk; ++kt) {
                 if (kt > 0) {
                     wait_lds();
                     block_barrier();        // every wave is done reading the single copy
                 }
-                if (kt < ndma) {
-                    dma(kt, 0);
-                    wait_vmcnt<0>();
-                } else {
-                    wait_vmcnt<0>();
-                    tail_store(0);
-                }
-                wait_lds();
+                if (kt < ndma) blk.dma(kt, 0);
+                blk.template land_tile<0>(kt, 0);
                 block_barrier();            // tile kt is in LDS for every wave
-                compute(0);
+                blk.compute(0);
             }
         } else {
 #pragma unroll
             for (int t = 0; t < STAGES - 1; ++t)
-                if (t < ndma) dma(t, t);
+                if (t < ndma) blk.dma(t, t);
+            int cur = 0, nxt = STAGES - 1;   // LDS copies of tile kt and of tile kt + STAGES - 1
             for (int64_t kt = 0; kt < nk; ++kt) {
-                const int stage = (int)(kt % STAGES);
-                if (kt < ndma) {
-                    // copies issued after tile kt: tiles kt+1 .. min(kt+STAGES-2, ndma-1)
-                    const int64_t later = ndma - 1 - kt;
-                    if (STAGES >= 4 && later >= 2) wait_vmcnt<2 * C::COPIES>();
-                    else if (STAGES >= 3 && later >= 1) wait_vmcnt<C::COPIES>();
-                    else wait_vmcnt<0>();
-                } else {
-                    wait_vmcnt<0>();
-                    tail_store(stage);
-                }
-                wait_lds();
+                blk.template land_tile<STAGES - 2>(kt, cur);
                 block_barrier();            // tile kt visible; copy of tile kt-1 released
                 const int64_t t = kt + STAGES - 1;
-                if (t < ndma) dma(t, (int)(t % STAGES));
-                compute(stage);
+                if (t < ndma) blk.dma(t, nxt);
+                blk.compute(cur);
+                cur = cur + 1 == STAGES ? 0 : cur + 1;
+                nxt = nxt + 1 == STAGES ? 0 : nxt + 1;
             }
         }
     }
-
-    // -- epilogue: fused alpha/beta store-back, masks only here
-    store_tile_epilogue<C, FRINGE>(p, acc, b, m0, n0, wave, lane);
+    store_tile_epilogue<C, FRINGE>(p, blk.acc, b, blk.m0, blk.n0, blk.wave, blk.lane);
 }
 
-template <class C, int STAGES, int SWZ>
+// SCHED_SWPIPE (software pipeline, one wave per SIMD, large wave tiles): the
+// fragments of a whole K tile live in registers, double-buffered.  Iteration
+// t: land tile t + 1 (this wave's copies of it) and wait for tile t's
+// fragments; one barrier (tile t + 1 is visible to every wave and nobody reads
+// tile t's LDS copy any more); then the MFMAs of tile t, with the fragment
+// reads of tile t + 1 and the copies of tile t + STAGES (into tile t's LDS
+// copy) placed between them, so the matrix core is fed while LDS and the
+// texture unit work.  Copies run STAGES - 1 tiles ahead of the tile being
+// landed.
+template <class C, int STAGES, int SWZ, bool FRINGE>
+struct SwPipe {
+    using Blk = RingBlock<C, STAGES, SWZ, FRINGE>;
+    static constexpr int NMFMA = C::KSTEPS * C::TM * C::TN;
+    static constexpr int READS = Blk::READS;
+    static_assert(READS <= NMFMA, "one fragment read per MFMA at most");
+    static_assert(NMFMA % 4 == 0, "copy groups after a quarter and three quarters of the MFMAs");
+
+    // One iteration: multiply tile t from (fa, fb) while reading tile t + 1
+    // into (na, nb).  STEADY: tile t + 1 exists and tile t + STAGES is copied
+    // (no conditions inside the MFMA stream); otherwise both are checked.
+    template <bool STEADY>
+    __device__ __forceinline__ static void iter(Blk &blk, int64_t t, int cur, int nxt_read,
+                                                u32x4 (&fa)[C::KSTEPS][C::TM], u32x4 (&fb)[C::KSTEPS][C::TN],
+                                                u32x4 (&na)[C::KSTEPS][C::TM], u32x4 (&nb)[C::KSTEPS][C::TN]) {
+        const int64_t nk = blk.nk, ndma = blk.ndma;
+        const bool more = STEADY || t + 1 < nk;
+        if (more) blk.template land_tile<STAGES - 2>(t + 1, nxt_read);
+        wait_lds();
+        __builtin_amdgcn_sched_barrier(0);
+        block_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        const int64_t tc = t + STAGES;          // copy into tile t's LDS copy
+        if (STEADY) {
+#pragma unroll
+            for (int q = 0; q < NMFMA; ++q) {
+                const int s = q / (C::TM * C::TN), i = (q / C::TN) % C::TM, j = q % C::TN;
+                mfma_chunk<C::DT>(fa[s][i], fb[s][j], blk.acc[i][j]);
+                if (q < READS) blk.read_piece(nxt_read, q, na, nb);
+                if (q == NMFMA / 4 - 1 || q == 3 * NMFMA / 4 - 1) blk.dma_operand(tc, cur, q < NMFMA / 2 ? 0 : 1);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        } else {
+            if (more) {
+#pragma unroll
+                for (int r = 0; r < READS; ++r) blk.read_piece(nxt_read, r, na, nb);
+            }
+            if (tc < ndma) blk.dma(tc, cur);
+#pragma unroll
+            for (int q = 0; q < NMFMA; ++q) {
+                const int s = q / (C::TM * C::TN), i = (q / C::TN) % C::TM, j = q % C::TN;
+                mfma_chunk<C::DT>(fa[s][i], fb[s][j], blk.acc[i][j]);
+            }
+        }
+    }
+};
+
+template <class C, int STAGES, int SWZ, bool FRINGE>
+__device__ __forceinline__ void ring_tile_swpipe(const GemmParams &p, char *smem, int64_t b, int64_t tm, int64_t tn) {
+    static_assert(STAGES >= 2, "software pipeline needs at least two LDS copies");
+    using SP = SwPipe<C, STAGES, SWZ, FRINGE>;
+    RingBlock<C, STAGES, SWZ, FRINGE> blk(p, smem, b, tm, tn);
+    const int64_t nk = blk.nk, ndma = blk.ndma;
+    if (nk > 0) {
+        blk.tail_load();
+#pragma unroll
+        for (int t = 0; t < STAGES; ++t)
+            if (t < ndma) blk.dma(t, t);
+        // tile 0: land, publish, read its fragments
+        blk.template land_tile<STAGES - 1>(0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        block_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        u32x4 a0[C::KSTEPS][C::TM], b0[C::KSTEPS][C::TN], a1[C::KSTEPS][C::TM], b1[C::KSTEPS][C::TN];
+#pragma unroll
+        for (int r = 0; r < SP::READS; ++r) blk.read_piece(0, r, a0, b0);
+        int cur = 0;
+        int64_t t = 0;
+        auto adv = [](int x) { return x + 1 == STAGES ? 0 : x + 1; };
+        // steady state, two tiles per trip (the fragment buffers swap roles)
+        for (; t + STAGES + 1 < ndma; t += 2) {
+            const int c1 = adv(cur), c2 = adv(c1);
+            SP::template iter<true>(blk, t, cur, c1, a0, b0, a1, b1);
+            SP::template iter<true>(blk, t + 1, c1, c2, a1, b1, a0, b0);
+            cur = c2;
+        }
+        // drain
+        for (; t + 1 < nk; t += 2) {
+            const int c1 = adv(cur), c2 = adv(c1);
+            SP::template iter<false>(blk, t, cur, c1, a0, b0, a1, b1);
+            SP::template iter<false>(blk, t + 1, c1, c2, a1, b1, a0, b0);
+            cur = c2;
+        }
+        if (t < nk) SP::template iter<false>(blk, t, cur, adv(cur), a0, b0, a1, b1);
+    }
+    store_tile_epilogue<C, FRINGE>(p, blk.acc, b, blk.m0, blk.n0, blk.wave, blk.lane);
+}
+
+template <class C, int STAGES, int SWZ, int SCHED>
 __global__ __launch_bounds__(C::THREADS, 1) void gemm_ring_kernel(GemmParams p) {
-    static_assert(STAGES >= 1 && STAGES <= 4, "1 to 4 LDS copies");
+    static_assert(STAGES >= 1 && STAGES <= 5, "1 to 5 LDS copies");
+    static_assert(SCHED == SCHED_RING || SCHED == SCHED_SWPIPE, "schedule");
     __shared__ __attribute__((aligned(1024))) char smem[STAGES * C::STAGE_BYTES];
     int64_t b, tm, tn;
     block_coords(p, b, tm, tn);
     const bool interior = (tm + 1) * C::BM <= p.M && (tn + 1) * C::BN <= p.N;
-    if (interior) ring_tile<C, STAGES, SWZ, false>(p, smem, b, tm, tn);
-    else ring_tile<C, STAGES, SWZ, true>(p, smem, b, tm, tn);
+    if constexpr (SCHED == SCHED_SWPIPE) {
+        if (interior) ring_tile_swpipe<C, STAGES, SWZ, false>(p, smem, b, tm, tn);
+        else ring_tile_swpipe<C, STAGES, SWZ, true>(p, smem, b, tm, tn);
+    } else {
+        if (interior) ring_tile<C, STAGES, SWZ, false>(p, smem, b, tm, tn);
+        else ring_tile<C, STAGES, SWZ, true>(p, smem, b, tm, tn);
+    }
 }
 
 }  // namespace tg

@@ -141,13 +141,13 @@ void describe_ring_lds(tg_layout *L, int operand, int swz) {
 
 template <class C>
 void describe_ring_copy_a(tg_layout *L) {
-    // physical chunk q = row*4 + p = (d*WAVES + wave)*64 + lane
+    // physical chunk q = row*4 + p = (wave*A_DMA + d)*64 + lane
     L->rank = 2;
     L->shape[0] = C::BM;
     L->shape[1] = C::A_ROW_BYTES / 16;
     L->n_shard = 3;
-    L->shard[0] = {C::A_DMA, 1, TG_AXIS_M, 0};
-    L->shard[1] = {C::WAVES, 1, TG_AXIS_WAVE, 0};
+    L->shard[0] = {C::WAVES, 1, TG_AXIS_WAVE, 0};
+    L->shard[1] = {C::A_DMA, 1, TG_AXIS_M, 0};
     L->shard[2] = {64, 1, TG_AXIS_LANE, 0};
 }
 

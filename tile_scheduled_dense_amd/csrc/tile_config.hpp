@@ -160,9 +160,10 @@ struct RingCfg {
     static_assert(A_TILE_BYTES % (1024 * WAVES) == 0 && A_DMA >= 1, "A copy split");
     static_assert(B_TILE_BYTES % (1024 * WAVES) == 0 && B_DMA >= 1, "B copy split");
     static_assert(B_UNITS == 2 || B_UNITS == 4 || B_UNITS == 8, "B row of 2, 4 or 8 units");
+    static_assert(A_DMA <= 4 && B_DMA <= 4, "a wave's copies of one operand span at most 4 KiB");
 };
 
-template <int DT> using Ring256 = RingCfg<DT, 256, 256, 2, 4>;   // 8 waves, wave tile 128 x 64
+template <int DT> using Ring256 = RingCfg<DT, 256, 256, 2, 2>;   // 4 waves, wave tile 128 x 128
 template <int DT> using Ring128 = RingCfg<DT, 128, 128, 2, 2>;   // 4 waves, wave tile 64 x 64
 template <int DT> using Ring64 = RingCfg<DT, 64, 64, 1, 2>;      // 2 waves, wave tile 64 x 32
 
@@ -187,10 +188,12 @@ TG_HD int ring_b_byte(int k, int n, int swz) {
     return k * C::B_ROW_BYTES + 64 * (w ^ ring_b_mask<C>(k, swz)) + in_unit;
 }
 
-// Which LDS bytes DMA copy d (0 <= d < A_DMA or B_DMA) of wave w fills:
-// 1 KiB block J = d * WAVES + w of the operand's region.
+// Which LDS bytes copy d (0 <= d < per_wave, per_wave = A_DMA or B_DMA) of
+// wave w fills: 1 KiB block J = w * per_wave + d of the operand's region.  A
+// wave's copies of one operand are adjacent, so they can share one LDS base
+// address and differ only by an immediate offset.
 template <class C>
-TG_HD int ring_block(int d, int wave) { return d * C::WAVES + wave; }
+TG_HD int ring_block(int d, int wave, int per_wave) { return wave * per_wave + d; }
 
 // The A element (row, first k of the chunk) lane l of block J must fetch.
 template <class C>

@@ -170,8 +170,10 @@ tg_status validate(int64_t batch, int64_t M, int64_t N, int64_t K, tg_dtype dtyp
 // Per-thread offsets inside a block are 32-bit: the byte offset of any element
 // of an A or B tile from the tile's first row, and the element offset of any C
 // element from the block's first row, must stay below 2^31.
+// Per-lane byte offsets within a block are 32-bit; the 16-bit kernel adds up
+// to 3 KiB to them (a copy group's resource base sits below the tile).
 bool offsets_fit(const tg_plan_info &p, int64_t K, int64_t lda, int64_t ldb, int64_t ldc, int esz) {
-    const int64_t lim = (int64_t(1) << 31) - 1;
+    const int64_t lim = (int64_t(1) << 31) - 1 - 4096;
     return ((int64_t)p.block_m * lda + K) * esz < lim && ((int64_t)p.block_k * ldb + p.block_n) * esz < lim &&
            (int64_t)p.block_m * ldc + p.block_n < lim;
 }
@@ -192,23 +194,26 @@ tg_status launch_variants(const GemmParams &gp, const tg_plan_info &p, hipStream
     return TG_ERR_UNSUPPORTED;
 }
 
-template <class C, int STAGES, int SWZ>
+template <class C, int STAGES, int SWZ, int SCHED>
 tg_status launch_ring_one(const GemmParams &gp, int64_t grid, hipStream_t stream) {
     if (grid > 0x7fffffffLL) return TG_ERR_UNSUPPORTED;
-    hipLaunchKernelGGL((gemm_ring_kernel<C, STAGES, SWZ>), dim3((unsigned)grid), dim3(C::THREADS), 0, stream, gp);
+    hipLaunchKernelGGL((gemm_ring_kernel<C, STAGES, SWZ, SCHED>), dim3((unsigned)grid), dim3(C::THREADS), 0, stream, gp);
     return hipGetLastError() == hipSuccess ? TG_OK : TG_ERR_LAUNCH;
 }
 
-template <class C>
+// SWPIPE: the 256 x 256 tile (one wave per SIMD, a whole K tile of fragments
+// in registers) whenever it has two or more LDS copies; RING otherwise.
+template <class C, bool SWPIPE>
 tg_status launch_ring(const GemmParams &gp, const tg_plan_info &p, hipStream_t s) {
+    constexpr int SCHED = SWPIPE ? SCHED_SWPIPE : SCHED_RING;
     if (p.swizzle == SWZ_XOR) {
         switch (p.pipeline_depth) {
-            case 4: return launch_ring_one<C, 4, SWZ_XOR>(gp, p.grid, s);
-            case 2: return launch_ring_one<C, 2, SWZ_XOR>(gp, p.grid, s);
-            case 1: return launch_ring_one<C, 1, SWZ_XOR>(gp, p.grid, s);
+            case 4: return launch_ring_one<C, 4, SWZ_XOR, SCHED>(gp, p.grid, s);
+            case 2: return launch_ring_one<C, 2, SWZ_XOR, SCHED>(gp, p.grid, s);
+            case 1: return launch_ring_one<C, 1, SWZ_XOR, SCHED_RING>(gp, p.grid, s);
         }
     } else if (p.pipeline_depth == 4) {
-        return launch_ring_one<C, 4, SWZ_NONE>(gp, p.grid, s);
+        return launch_ring_one<C, 4, SWZ_NONE, SCHED>(gp, p.grid, s);
     }
     return TG_ERR_UNSUPPORTED;
 }
@@ -216,9 +221,9 @@ tg_status launch_ring(const GemmParams &gp, const tg_plan_info &p, hipStream_t s
 template <int DT>
 tg_status launch_dtype(const GemmParams &gp, const tg_plan_info &p, hipStream_t s) {
     switch (p.config) {
-        case TG_CFG_256x256: return launch_ring<Ring256<DT>>(gp, p, s);
-        case TG_CFG_128x128: return launch_ring<Ring128<DT>>(gp, p, s);
-        case TG_CFG_64x64: return launch_ring<Ring64<DT>>(gp, p, s);
+        case TG_CFG_256x256: return launch_ring<Ring256<DT>, true>(gp, p, s);
+        case TG_CFG_128x128: return launch_ring<Ring128<DT>, false>(gp, p, s);
+        case TG_CFG_64x64: return launch_ring<Ring64<DT>, false>(gp, p, s);
         default: return TG_ERR_UNSUPPORTED;
     }
 }
