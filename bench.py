@@ -38,6 +38,8 @@ def parse():
     ap.add_argument("--pipeline-depth", type=int, default=0)
     ap.add_argument("--swizzle", type=int, default=0)
     ap.add_argument("--block-order", type=int, default=0)
+    ap.add_argument("--split-k", type=int, default=0,
+                    help="K slices (0 = automatic with the workspace the library asks for, 1 = off)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after timing, run a plain device copy of this many MiB (3 times) so HBM "
                          "byte counters can be scaled against a kernel of known traffic")
@@ -97,7 +99,11 @@ def main():
     C = to_dev(p.C0.copy()) if p.beta != 0 else torch.zeros(p.sizeC(), dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
     opts = dict(config=args.config, pipeline_depth=args.pipeline_depth, swizzle=args.swizzle,
-                block_order=args.block_order)
+                block_order=args.block_order, split_k=args.split_k)
+    # split-K workspace: allocated once, outside the timed region, as a caller would
+    ws_bytes = tg.tile_gemm_workspace_size(p.batch, p.M, p.N, p.K, p.dtype, **opts)
+    if ws_bytes:
+        opts["workspace"] = torch.empty(ws_bytes // 4, dtype=torch.float32, device="cuda")
     plan = tg.tile_gemm_plan(p.batch, p.M, p.N, p.K, p.dtype, **opts)
 
     def step():
@@ -124,16 +130,26 @@ def main():
     peak = PEAK_TFLOPS[p.dtype]
     bytes_alg = p.compulsory_bytes()
     gbs = bytes_alg / (ms_step * 1e-3) / 1e9
-    # Each step is exactly one launch of the GEMM kernel, so the event time per
-    # step is the kernel's average launch duration (plus launch gaps).
+    # Each step is one call: one launch of the GEMM kernel, or with split-K the
+    # partial-product launch and its combine; the event time per step is the
+    # whole call (plus launch gaps), so a split call is charged for both passes.
     # HBM traffic per launch from the committed FETCH_SIZE / WRITE_SIZE summary
     # of this workload, only while it was taken on the current kernel sources.
     from tile_scheduled_dense_amd.rocprof_summary import traffic_for
     traffic = traffic_for(p.name)
-    roofline = {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak, "unit": "TFLOP/s",
-                "frac": round(tflops / peak, 4), "traffic": None if traffic is None else int(traffic),
-                "algorithmic_flops_per_launch": p.flops, "avg_launch_us": round(ms_step * 1e3, 2),
-                "algorithmic_bytes_per_launch": bytes_alg, "achieved_GBps": round(gbs, 1)}
+    # The binding roof: MFMA when the workload's intensity (algorithmic flops
+    # per compulsory byte) is above the ridge peak / HBM bandwidth, else HBM.
+    hbm_bound = p.flops / bytes_alg < peak * 1e12 / (PEAK_HBM_GBS * 1e9)
+    if hbm_bound:
+        roofline = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                    "frac": round(gbs / PEAK_HBM_GBS, 4)}
+    else:
+        roofline = {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak, "unit": "TFLOP/s",
+                    "frac": round(tflops / peak, 4)}
+    roofline.update({"traffic": None if traffic is None else int(traffic),
+                     "algorithmic_flops_per_launch": p.flops, "algorithmic_bytes_per_launch": bytes_alg,
+                     "avg_launch_us": round(ms_step * 1e3, 2), "achieved_TFLOPs": round(tflops, 2),
+                     "mfma_frac": round(tflops / peak, 4), "achieved_GBps": round(gbs, 1)})
 
     if args.copy_calibration_mib:
         n = args.copy_calibration_mib * (1 << 20) // 4
@@ -157,7 +173,8 @@ def main():
                    "lda": p.lda, "ldb": p.ldb, "ldc": p.ldc, "alpha": p.alpha, "beta": p.beta,
                    "inputs": f"{p.dist} seed {p.seed}", "accumulate": "fp32", "output": "fp32",
                    "tile": f"{plan['block_m']}x{plan['block_n']}x{plan['block_k']}",
-                   "pipeline_depth": plan["pipeline_depth"], "grid": plan["grid"]},
+                   "pipeline_depth": plan["pipeline_depth"], "split_k": plan["split_k"],
+                   "grid": plan["grid"]},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "device": {"name": props.name, "arch": getattr(props, "gcnArchName", ""),

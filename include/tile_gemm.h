@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define TILE_GEMM_ABI_VERSION 1
+#define TILE_GEMM_ABI_VERSION 2
 
 typedef enum { TG_F32 = 0, TG_BF16 = 1, TG_F16 = 2 } tg_dtype;
 
@@ -83,18 +83,51 @@ tg_status tile_gemm_strided_batched(int64_t batch, int64_t M, int64_t N, int64_t
 /* Schedule knobs, for tests and measurements; zero-initialise for defaults. */
 typedef enum {
     TG_CFG_AUTO = 0,
-    TG_CFG_256x256 = 1,     /* 16-bit inputs: 256x256 block tile, 8 waves        */
+    TG_CFG_256x256 = 1,     /* 16-bit inputs: 256x256 block tile, 4 waves        */
     TG_CFG_128x128 = 2,     /* 16-bit inputs: 128x128 block tile, 4 waves        */
     TG_CFG_64x64 = 3,       /* 16-bit inputs: 64x64 block tile, 2 waves          */
     TG_CFG_F32_64x64 = 4    /* fp32 inputs: 64x64 block tile, 4 waves            */
 } tg_config;
 
+/*
+ * Options.  struct_size is sizeof(tg_options) of the caller's header; it must
+ * cover at least the first five fields (20 bytes, the version-1 layout), and
+ * fields past it read as zero.
+ *
+ * pipeline_depth is the number of LDS copies of the K tile (the window is one
+ * less): 16-bit inputs take 1, 2 or 4 (default 4), fp32 inputs 1 or 2 (default
+ * 2).  Depth 1 is the unpipelined form.
+ *
+ * Split-K (16-bit inputs): the deterministic two-pass split reduction of the
+ * OCANNL "Module Ir.Schedule" page (paragraph of that name).  The K range is
+ * cut into S slices of a multiple of block_k elements (the last one shorter);
+ * each slice's product goes, unscaled, to its own fp32 M x N partial in
+ * `workspace` (slice s of problem b at float offset (s * batch + b) * M * N),
+ * written whole by the first kernel (no zeroing pass); a second kernel then
+ * adds the S partials of every element in a fixed balanced-tree order and
+ * applies the epilogue, fma(alpha, sum, beta * C0) or alpha * sum.  The result
+ * is bitwise reproducible for a given (config, S) but, as that paragraph
+ * notes, not bitwise equal to the unsplit sum (the k sum is regrouped).
+ *   split_k == 0: automatic -- split only when the plan has too few output
+ *                 tiles to fill the GPU, K is deep, and `workspace` holds the
+ *                 partials (tile_gemm_workspace_size says how many bytes);
+ *   split_k == 1: never split;
+ *   split_k >= 2: at most split_k slices (fewer when K is short); the call
+ *                 fails with TG_ERR_INVALID_ARG if the workspace is too small.
+ * The workspace is caller-owned device memory, 16-byte aligned, that must not
+ * overlap A, B or C; its contents on entry do not matter and are undefined
+ * afterwards.  Calls that share one workspace must be ordered (e.g. on one
+ * stream).
+ */
 typedef struct {
-    int struct_size;     /* sizeof(tg_options); a smaller value is rejected         */
+    int struct_size;
     int config;          /* tg_config; TG_CFG_AUTO picks by dtype and shape           */
-    int pipeline_depth;  /* 0 = default (2); 1 = unpipelined; 2 = window-2 pipeline  */
+    int pipeline_depth;  /* 0 = default (see above)                                   */
     int swizzle;         /* 0 = default (XOR); 1 = none (row-major tile); 2 = XOR   */
     int block_order;     /* 0 = default (XCD-grouped); 1 = plain row-major          */
+    int split_k;         /* 0 = automatic, 1 = off, S >= 2 = at most S K slices      */
+    void *workspace;     /* device memory for split-K partials, or NULL             */
+    int64_t workspace_bytes;
 } tg_options;
 
 /* tile_gemm_strided_batched with explicit schedule knobs (opt may be NULL).
@@ -121,10 +154,19 @@ typedef struct {
     int64_t k_tiles;              /* ceil(K / block_k)                             */
     int64_t k_tail;               /* K mod block_k (0: no peeled tail tile)        */
     int lds_bytes;                /* LDS per workgroup, all pipeline copies        */
+    int split_k;                  /* K slices S (1: no split)                      */
+    int64_t k_slice;              /* K elements per slice (the last may be shorter)*/
+    int64_t workspace_bytes;      /* workspace the call uses: S * batch * M * N * 4 */
 } tg_plan_info;
 
 tg_status tile_gemm_plan(int64_t batch, int64_t M, int64_t N, int64_t K, tg_dtype dtype,
                          const tg_options *opt, tg_plan_info *out);
+
+/* Workspace bytes a call with these arguments would use if the workspace were
+ * large enough (0 when it would not split K).  With split_k == 0 this is the
+ * size the automatic choice wants; pass that much to let it split. */
+tg_status tile_gemm_workspace_size(int64_t batch, int64_t M, int64_t N, int64_t K, tg_dtype dtype,
+                                   const tg_options *opt, int64_t *bytes);
 
 /*
  * Tile layouts in the TileLayout / SwizzleLayout model of the Apache TVM TIRx

@@ -28,7 +28,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert tg.abi_version() == 1
+    assert tg.abi_version() == 2
     for s in range(5):
         assert tg.STATUS_NAMES[s] in tg.status_string(s)
 
@@ -75,10 +75,18 @@ def test_no_gpu_is_unsupported():
 
 
 def test_options_validation():
-    opt = tg.Options(ctypes.sizeof(tg.Options) - 4, 0, 0, 0, 0)
     info = tg.PlanInfo()
     lib = tg._lib()
+    # shorter than the version-1 layout: rejected
+    opt = tg.Options(tg.OPTIONS_V1_SIZE - 4, 0, 0, 0, 0)
     assert lib.tile_gemm_plan(1, 8, 8, 8, tg.TG_BF16, ctypes.byref(opt), ctypes.byref(info)) == tg.TG_ERR_INVALID_ARG
+    # a version-1 sized struct: the split-K fields beyond it are not read
+    opt = tg.Options(tg.OPTIONS_V1_SIZE, 0, 0, 0, 0, 4, None, 0)
+    assert lib.tile_gemm_plan(1, 64, 64, 8192, tg.TG_BF16, ctypes.byref(opt), ctypes.byref(info)) == tg.TG_OK
+    assert info.split_k == 1
+    opt.struct_size = ctypes.sizeof(tg.Options)
+    assert lib.tile_gemm_plan(1, 64, 64, 8192, tg.TG_BF16, ctypes.byref(opt), ctypes.byref(info)) == tg.TG_OK
+    assert info.split_k == 4
     with pytest.raises(tg.TileGemmError):
         tg.tile_gemm_plan(1, 8, 8, 8, "bf16", pipeline_depth=3)
     with pytest.raises(tg.TileGemmError):
@@ -123,6 +131,37 @@ def test_plan_depth_changes_lds_only():
     with pytest.raises(tg.TileGemmError):
         tg.tile_gemm_plan(1, 64, 64, 64, "bf16", pipeline_depth=2, swizzle=tg.SWZ_NONE)
     assert tg.tile_gemm_plan(1, 64, 64, 64, "f32")["pipeline_depth"] == 2
+
+
+def test_split_k_plans():
+    # forced: at most S slices of a multiple of block_k, the last one shorter
+    info = tg.tile_gemm_plan(1, 512, 512, 131072, "bf16", config=tg.TG_CFG_128x128, split_k=16)
+    assert (info["split_k"], info["k_slice"], info["grid"]) == (16, 8192, 16 * 16)
+    assert info["workspace_bytes"] == 16 * 512 * 512 * 4
+    info = tg.tile_gemm_plan(3, 100, 70, 1000, "f16", config=tg.TG_CFG_64x64, split_k=3)
+    assert (info["split_k"], info["k_slice"]) == (3, 352)
+    assert info["grid"] == 2 * 2 * 3 * 3 and info["workspace_bytes"] == 3 * 3 * 100 * 70 * 4
+    info = tg.tile_gemm_plan(1, 64, 64, 40, "bf16", config=tg.TG_CFG_64x64, split_k=8)
+    assert (info["split_k"], info["k_slice"]) == (2, 32)       # K = 40 has two K tiles
+    assert tg.tile_gemm_plan(1, 64, 64, 32, "bf16", split_k=8)["split_k"] == 1
+    assert tg.tile_gemm_plan(1, 64, 64, 0, "bf16", split_k=8)["split_k"] == 1
+    assert tg.tile_gemm_plan(1, 64, 64, 8192, "bf16", split_k=1000)["split_k"] == 64
+    # automatic: only for too few tiles, deep K, and with the workspace it asks for
+    assert tg.tile_gemm_workspace_size(1, 8192, 8192, 8192, "bf16") == 0
+    need = tg.tile_gemm_workspace_size(1, 512, 512, 131072, "bf16")
+    assert need > 0
+    assert tg.tile_gemm_plan(1, 512, 512, 131072, "bf16")["split_k"] == 1
+    assert tg.tile_gemm_plan(1, 512, 512, 131072, "bf16", workspace=FAKE, workspace_bytes=need)["split_k"] > 1
+    assert tg.tile_gemm_workspace_size(1, 512, 512, 131072, "bf16", split_k=1) == 0
+    with pytest.raises(tg.TileGemmError):
+        tg.tile_gemm_plan(1, 64, 64, 8192, "f32", split_k=4)
+    with pytest.raises(tg.TileGemmError):
+        tg.tile_gemm_plan(1, 64, 64, 8192, "bf16", split_k=-2)
+    # a forced split with no workspace is rejected before any device work
+    st = tg.tile_gemm_status("tile_gemm_ex", 1, 64, 64, 8192, tg.TG_BF16, FAKE, 8192, 0, FAKE * 64, 64, 0,
+                             FAKE * 4096, 64, 0, 1.0, 0.0, 0,
+                             ctypes.byref(tg.Options(ctypes.sizeof(tg.Options), 0, 0, 0, 0, 4, None, 0)))
+    assert st in (tg.TG_ERR_INVALID_ARG, tg.TG_ERR_UNSUPPORTED)
 
 
 def test_lds_budget():

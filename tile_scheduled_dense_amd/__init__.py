@@ -38,7 +38,7 @@ LAYOUT_MAX_SWIZZLES = 2
 
 # every symbol include/tile_gemm.h declares
 EXPORTED = ["tile_gemm", "tile_gemm_strided_batched", "tile_gemm_ex", "tile_gemm_plan",
-            "tg_layout_eval", "tile_gemm_describe_layout", "tile_gemm_lds_offset",
+            "tile_gemm_workspace_size", "tg_layout_eval", "tile_gemm_describe_layout", "tile_gemm_lds_offset",
             "tile_gemm_acc_coord", "tile_gemm_status_string", "tile_gemm_abi_version"]
 
 
@@ -50,7 +50,12 @@ class TileGemmError(RuntimeError):
 
 class Options(ctypes.Structure):
     _fields_ = [("struct_size", ctypes.c_int), ("config", ctypes.c_int), ("pipeline_depth", ctypes.c_int),
-                ("swizzle", ctypes.c_int), ("block_order", ctypes.c_int)]
+                ("swizzle", ctypes.c_int), ("block_order", ctypes.c_int), ("split_k", ctypes.c_int),
+                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_int64)]
+
+
+# size of the options struct in ABI version 1 (the first five ints)
+OPTIONS_V1_SIZE = 5 * ctypes.sizeof(ctypes.c_int)
 
 
 class PlanInfo(ctypes.Structure):
@@ -59,7 +64,8 @@ class PlanInfo(ctypes.Structure):
                 ("pipeline_depth", ctypes.c_int), ("swizzle", ctypes.c_int), ("block_order", ctypes.c_int),
                 ("tiles_m", ctypes.c_int64), ("tiles_n", ctypes.c_int64), ("grid", ctypes.c_int64),
                 ("interior_blocks", ctypes.c_int64), ("fringe_blocks", ctypes.c_int64),
-                ("k_tiles", ctypes.c_int64), ("k_tail", ctypes.c_int64), ("lds_bytes", ctypes.c_int)]
+                ("k_tiles", ctypes.c_int64), ("k_tail", ctypes.c_int64), ("lds_bytes", ctypes.c_int),
+                ("split_k", ctypes.c_int), ("k_slice", ctypes.c_int64), ("workspace_bytes", ctypes.c_int64)]
 
     def as_dict(self):
         return {f: getattr(self, f) for f, _ in self._fields_}
@@ -108,6 +114,8 @@ def _lib():
     lib.tile_gemm_ex.restype = ci
     lib.tile_gemm_plan.argtypes = [i64, i64, i64, i64, ci, ctypes.POINTER(Options), ctypes.POINTER(PlanInfo)]
     lib.tile_gemm_plan.restype = ci
+    lib.tile_gemm_workspace_size.argtypes = [i64, i64, i64, i64, ci, ctypes.POINTER(Options), ctypes.POINTER(i64)]
+    lib.tile_gemm_workspace_size.restype = ci
     lib.tg_layout_eval.argtypes = [ctypes.POINTER(Layout), ctypes.POINTER(i64), ctypes.POINTER(i64), i64]
     lib.tg_layout_eval.restype = i64
     lib.tile_gemm_describe_layout.argtypes = [ci, ci, ci, ctypes.POINTER(Layout)]
@@ -148,8 +156,13 @@ def _dtype(d) -> int:
     return DTYPES[d] if isinstance(d, str) else int(d)
 
 
-def _options(config=0, pipeline_depth=0, swizzle=0, block_order=0) -> Options:
-    return Options(ctypes.sizeof(Options), int(config), int(pipeline_depth), int(swizzle), int(block_order))
+def _options(config=0, pipeline_depth=0, swizzle=0, block_order=0, split_k=0, workspace=None,
+             workspace_bytes=None) -> Options:
+    ws = _addr(workspace)
+    if workspace_bytes is None:
+        workspace_bytes = workspace.numel() * workspace.element_size() if hasattr(workspace, "numel") else 0
+    return Options(ctypes.sizeof(Options), int(config), int(pipeline_depth), int(swizzle), int(block_order),
+                   int(split_k), ws, int(workspace_bytes))
 
 
 def _check(status: int, where: str):
@@ -179,8 +192,10 @@ def tile_gemm_strided_batched(batch, M, N, K, dtype, A, lda, strideA, B, ldb, st
 
 def tile_gemm_ex(batch, M, N, K, dtype, A, lda, strideA, B, ldb, strideB, C, ldc, strideC,
                  alpha=1.0, beta=0.0, stream=None, config=0, pipeline_depth=0, swizzle=0,
-                 block_order=0) -> None:
-    opt = _options(config, pipeline_depth, swizzle, block_order)
+                 block_order=0, split_k=0, workspace=None, workspace_bytes=None) -> None:
+    """`workspace`: a device tensor or address for split-K partials (its byte
+    size is taken from the tensor unless `workspace_bytes` is given)."""
+    opt = _options(config, pipeline_depth, swizzle, block_order, split_k, workspace, workspace_bytes)
     _check(_lib().tile_gemm_ex(batch, M, N, K, _dtype(dtype), _addr(A), lda, strideA, _addr(B), ldb, strideB,
                                _addr(C), ldc, strideC, alpha, beta, _stream(stream), ctypes.byref(opt)),
            "tile_gemm_ex")
@@ -191,12 +206,23 @@ def tile_gemm_status(fn: str, *args) -> int:
     return int(getattr(_lib(), fn)(*args))
 
 
-def tile_gemm_plan(batch, M, N, K, dtype, config=0, pipeline_depth=0, swizzle=0, block_order=0) -> dict:
+def tile_gemm_plan(batch, M, N, K, dtype, config=0, pipeline_depth=0, swizzle=0, block_order=0,
+                   split_k=0, workspace=None, workspace_bytes=None) -> dict:
     info = PlanInfo()
-    opt = _options(config, pipeline_depth, swizzle, block_order)
+    opt = _options(config, pipeline_depth, swizzle, block_order, split_k, workspace, workspace_bytes)
     _check(_lib().tile_gemm_plan(batch, M, N, K, _dtype(dtype), ctypes.byref(opt), ctypes.byref(info)),
            "tile_gemm_plan")
     return info.as_dict()
+
+
+def tile_gemm_workspace_size(batch, M, N, K, dtype, config=0, pipeline_depth=0, swizzle=0, block_order=0,
+                             split_k=0) -> int:
+    """Bytes of split-K workspace a call with these arguments would use (0: it does not split)."""
+    n = ctypes.c_int64(0)
+    opt = _options(config, pipeline_depth, swizzle, block_order, split_k)
+    _check(_lib().tile_gemm_workspace_size(batch, M, N, K, _dtype(dtype), ctypes.byref(opt), ctypes.byref(n)),
+           "tile_gemm_workspace_size")
+    return int(n.value)
 
 
 def make_layout(shape, shard, replica=(), offset=None, swizzle=None) -> Layout:

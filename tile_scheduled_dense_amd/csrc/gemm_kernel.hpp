@@ -66,6 +66,13 @@ struct GemmParams {
     float alpha, beta;
     int block_order;             // 0: XCD-grouped, 1: plain
     int group_m;                 // tile rows per group in the grouped order
+    // split-K: `batch` above counts (slice, problem) pairs, problem fastest;
+    // slice s of problem b multiplies k in [s * k_slice, min(K, (s+1) * k_slice))
+    // into the fp32 partial W + (s * problems + b) * M * N (row stride N).
+    int splits;                  // 1: no split
+    int64_t problems;            // batch of the call
+    int64_t k_slice;
+    float *W;
 };
 
 template <class C>

@@ -494,13 +494,31 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_ring_kernel(GemmParams p) 
     __shared__ __attribute__((aligned(1024))) char smem[STAGES * C::STAGE_BYTES];
     int64_t b, tm, tn;
     block_coords(p, b, tm, tn);
+    // This block's problem with its batch offsets folded into the pointers;
+    // for a split-K pass, its K slice, written unscaled to its fp32 partial.
+    GemmParams q = p;
+    if (p.splits > 1) {
+        const int64_t s = b / p.problems, pb = b - s * p.problems;
+        const int64_t k0 = s * p.k_slice;
+        q.A = p.A + (pb * p.sA + k0) * 2;
+        q.B = p.B + (pb * p.sB + k0 * p.ldb) * 2;
+        q.K = p.K - k0 < p.k_slice ? p.K - k0 : p.k_slice;
+        q.C = p.W + b * p.M * p.N;
+        q.ldc = p.N;
+        q.alpha = 1.0f;
+        q.beta = 0.0f;
+    } else {
+        q.A = p.A + b * p.sA * 2;
+        q.B = p.B + b * p.sB * 2;
+        q.C = p.C + b * p.sC;
+    }
     const bool interior = (tm + 1) * C::BM <= p.M && (tn + 1) * C::BN <= p.N;
     if constexpr (SCHED == SCHED_SWPIPE) {
-        if (interior) ring_tile_swpipe<C, STAGES, SWZ, false>(p, smem, b, tm, tn);
-        else ring_tile_swpipe<C, STAGES, SWZ, true>(p, smem, b, tm, tn);
+        if (interior) ring_tile_swpipe<C, STAGES, SWZ, false>(q, smem, 0, tm, tn);
+        else ring_tile_swpipe<C, STAGES, SWZ, true>(q, smem, 0, tm, tn);
     } else {
-        if (interior) ring_tile<C, STAGES, SWZ, false>(p, smem, b, tm, tn);
-        else ring_tile<C, STAGES, SWZ, true>(p, smem, b, tm, tn);
+        if (interior) ring_tile<C, STAGES, SWZ, false>(q, smem, 0, tm, tn);
+        else ring_tile<C, STAGES, SWZ, true>(q, smem, 0, tm, tn);
     }
 }
 

@@ -9,6 +9,7 @@
 #include <new>
 
 #include "gemm_ring.hpp"
+#include "splitk.hpp"
 #include "tile_gemm.h"
 
 using namespace tg;
@@ -78,8 +79,25 @@ int choose_config(int64_t batch, int64_t M, int64_t N, tg_dtype dtype) {
     return TG_CFG_64x64;
 }
 
+// Size of tg_options in ABI version 1 (five ints, before the split-K fields).
+constexpr int kOptionsV1Size = 5 * (int)sizeof(int);
+constexpr int64_t kMaxSplits = 64;
+
+// Automatic split count: split only when the output tiles cannot fill the
+// GPU's 256 CUs, doubling while the blocks still fit in one round and each
+// slice keeps at least 1024 of K.
+int64_t auto_splits(int64_t tiles, int64_t K) {
+    if (tiles >= 128) return 1;
+    int64_t s = 1;
+    while (2 * s <= kMaxSplits && tiles * 2 * s <= 256 && K / (2 * s) >= 1024) s *= 2;
+    return s;
+}
+
 struct Plan {
     tg_plan_info info;
+    int64_t wanted_workspace = 0;      // bytes the split it would like needs
+    void *workspace = nullptr;         // set when the call splits
+    int64_t workspace_given = 0;
 };
 
 tg_status make_plan(int64_t batch, int64_t M, int64_t N, int64_t K, tg_dtype dtype,
@@ -88,10 +106,36 @@ tg_status make_plan(int64_t batch, int64_t M, int64_t N, int64_t K, tg_dtype dty
     if (dtype != TG_F32 && dtype != TG_BF16 && dtype != TG_F16) return TG_ERR_INVALID_ARG;
     tg_options o{};
     if (opt) {
-        if (opt->struct_size < (int)sizeof(tg_options)) return TG_ERR_INVALID_ARG;
-        o = *opt;
+        // the caller's struct may predate the split-K fields: read what it has
+        if (opt->struct_size < kOptionsV1Size) return TG_ERR_INVALID_ARG;
+        std::memcpy(&o, opt, opt->struct_size < (int)sizeof o ? (size_t)opt->struct_size : sizeof o);
     }
-    int config = o.config ? o.config : choose_config(batch, M, N, dtype);
+    // Split-K (16-bit): a forced count applies to the chosen config; the
+    // automatic choice looks at the largest tile (fewest re-reads of A and
+    // B) and splits only when that has too few tiles and K is deep, and only
+    // if the caller's workspace holds the partials -- otherwise the plain plan.
+    if (o.split_k < 0) return TG_ERR_INVALID_ARG;
+    const bool sixteen = dtype != TG_F32;
+    const bool some = K > 0 && M > 0 && N > 0 && batch > 0;
+    int64_t want = 1, wanted_bytes = 0;
+    int config = o.config;
+    if (sixteen && some && o.split_k == 0) {
+        const int cfg = o.config ? o.config : TG_CFG_256x256;
+        if (cfg >= TG_CFG_256x256 && cfg <= TG_CFG_64x64) {
+            const CfgDims dd = cfg_dims(cfg);
+            const int64_t s_auto = auto_splits(cdiv(M, dd.bm) * cdiv(N, dd.bn) * batch, K);
+            const int64_t slice = cdiv(cdiv(K, s_auto), dd.bk) * dd.bk;
+            const int64_t s_eff = cdiv(K, slice);
+            wanted_bytes = s_eff > 1 ? s_eff * batch * M * N * 4 : 0;
+            if (s_eff > 1 && o.workspace && o.workspace_bytes >= wanted_bytes) {
+                want = s_auto;
+                config = cfg;
+            }
+        }
+    } else if (sixteen && some && o.split_k >= 2) {
+        want = o.split_k < kMaxSplits ? o.split_k : kMaxSplits;
+    }
+    if (!config) config = choose_config(batch, M, N, dtype);
     if (config < TG_CFG_256x256 || config > TG_CFG_F32_64x64) return TG_ERR_INVALID_ARG;
     if ((dtype == TG_F32) != (config == TG_CFG_F32_64x64)) return TG_ERR_UNSUPPORTED;
     // pipeline depth = LDS copies of the K tile (window = depth - 1)
@@ -125,6 +169,19 @@ tg_status make_plan(int64_t batch, int64_t M, int64_t N, int64_t K, tg_dtype dty
     p.k_tiles = cdiv(K, d.bk);
     p.k_tail = K % d.bk;
     p.lds_bytes = depth * d.stage_bytes;
+
+    // split-K
+    if (f32 && o.split_k >= 2) return TG_ERR_UNSUPPORTED;
+    const int64_t k_slice = K > 0 ? cdiv(cdiv(K, want), d.bk) * d.bk : 0;
+    const int64_t splits = K > 0 ? cdiv(K, k_slice) : 1;
+    const int64_t bytes = splits > 1 ? splits * batch * M * N * 4 : 0;
+    out.wanted_workspace = o.split_k == 0 ? wanted_bytes : bytes;
+    p.split_k = (int)splits;
+    p.k_slice = splits > 1 ? k_slice : K;
+    p.workspace_bytes = bytes;
+    if (splits > 1) p.grid *= splits;
+    out.workspace = splits > 1 ? o.workspace : nullptr;
+    out.workspace_given = o.workspace_bytes;
     return TG_OK;
 }
 
@@ -169,9 +226,9 @@ tg_status validate(int64_t batch, int64_t M, int64_t N, int64_t K, tg_dtype dtyp
 
 // Per-thread offsets inside a block are 32-bit: the byte offset of any element
 // of an A or B tile from the tile's first row, and the element offset of any C
-// element from the block's first row, must stay below 2^31.
-// Per-lane byte offsets within a block are 32-bit; the 16-bit kernel adds up
-// to 3 KiB to them (a copy group's resource base sits below the tile).
+// element from the block's first row, must stay below 2^31, with 4 KiB to
+// spare (the 16-bit kernel adds up to 3 KiB: a copy group's resource base sits
+// below the tile).
 bool offsets_fit(const tg_plan_info &p, int64_t K, int64_t lda, int64_t ldb, int64_t ldc, int esz) {
     const int64_t lim = (int64_t(1) << 31) - 1 - 4096;
     return ((int64_t)p.block_m * lda + K) * esz < lim && ((int64_t)p.block_k * ldb + p.block_n) * esz < lim &&
@@ -218,6 +275,27 @@ tg_status launch_ring(const GemmParams &gp, const tg_plan_info &p, hipStream_t s
     return TG_ERR_UNSUPPORTED;
 }
 
+template <int P>
+tg_status launch_combine_p(const float *W, float *C, int64_t M, int64_t N, int64_t ldc, int64_t sC,
+                           int64_t problems, int S, float alpha, float beta, hipStream_t stream) {
+    const int64_t total = problems * M * N;
+    const int64_t blocks = cdiv(total, 256) < 8192 ? cdiv(total, 256) : 8192;
+    hipLaunchKernelGGL((splitk_combine_kernel<P>), dim3((unsigned)blocks), dim3(256), 0, stream, W, C, M, N, ldc,
+                       sC, problems, S, alpha, beta);
+    return hipGetLastError() == hipSuccess ? TG_OK : TG_ERR_LAUNCH;
+}
+
+tg_status launch_combine(const float *W, float *C, int64_t M, int64_t N, int64_t ldc, int64_t sC,
+                         int64_t problems, int S, float alpha, float beta, hipStream_t stream) {
+    if (S <= 2) return launch_combine_p<2>(W, C, M, N, ldc, sC, problems, S, alpha, beta, stream);
+    if (S <= 4) return launch_combine_p<4>(W, C, M, N, ldc, sC, problems, S, alpha, beta, stream);
+    if (S <= 8) return launch_combine_p<8>(W, C, M, N, ldc, sC, problems, S, alpha, beta, stream);
+    if (S <= 16) return launch_combine_p<16>(W, C, M, N, ldc, sC, problems, S, alpha, beta, stream);
+    if (S <= 32) return launch_combine_p<32>(W, C, M, N, ldc, sC, problems, S, alpha, beta, stream);
+    if (S <= 64) return launch_combine_p<64>(W, C, M, N, ldc, sC, problems, S, alpha, beta, stream);
+    return TG_ERR_INTERNAL;
+}
+
 template <int DT>
 tg_status launch_dtype(const GemmParams &gp, const tg_plan_info &p, hipStream_t s) {
     switch (p.config) {
@@ -239,6 +317,20 @@ tg_status run(int64_t batch, int64_t M, int64_t N, int64_t K, tg_dtype dtype,
     if (st != TG_OK) return st;
     if (batch == 0 || M == 0 || N == 0) return TG_OK;
     if (!offsets_fit(plan.info, K, lda, ldb, ldc, dtype == TG_F32 ? 4 : 2)) return TG_ERR_UNSUPPORTED;
+    const bool split = plan.info.split_k > 1;
+    if (split) {
+        // a forced split needs the workspace; an automatic one only happens with it
+        if (!plan.workspace || plan.workspace_given < plan.info.workspace_bytes ||
+            reinterpret_cast<uintptr_t>(plan.workspace) % 16)
+            return TG_ERR_INVALID_ARG;
+        const int esz = dtype == TG_F32 ? 4 : 2;
+        const Range rw{reinterpret_cast<uintptr_t>(plan.workspace),
+                       reinterpret_cast<uintptr_t>(plan.workspace) + (uintptr_t)plan.info.workspace_bytes};
+        if (overlaps(rw, span(A, batch, M, K, lda, sA, esz)) || overlaps(rw, span(B, batch, K, N, ldb, sB, esz)) ||
+            overlaps(rw, span(C, batch, M, N, ldc, sC, 4)))
+            return TG_ERR_INVALID_ARG;
+        if (!offsets_fit(plan.info, plan.info.k_slice, lda, ldb, N, esz)) return TG_ERR_UNSUPPORTED;
+    }
     st = current_device_ok();
     if (st != TG_OK) return st;
 
@@ -262,15 +354,22 @@ tg_status run(int64_t batch, int64_t M, int64_t N, int64_t K, tg_dtype dtype,
     gp.beta = beta;
     gp.block_order = plan.info.block_order;
     gp.group_m = 8;
+    gp.splits = plan.info.split_k;
+    gp.problems = batch;
+    gp.k_slice = plan.info.k_slice;
+    gp.W = static_cast<float *>(plan.workspace);
+    if (split) gp.batch = batch * plan.info.split_k;   // (slice, problem) pairs
     hipStream_t s = static_cast<hipStream_t>(stream);
     switch (dtype) {
-        case TG_BF16: return launch_dtype<DT_BF16>(gp, plan.info, s);
-        case TG_F16: return launch_dtype<DT_F16>(gp, plan.info, s);
+        case TG_BF16: st = launch_dtype<DT_BF16>(gp, plan.info, s); break;
+        case TG_F16: st = launch_dtype<DT_F16>(gp, plan.info, s); break;
         case TG_F32:
             if (plan.info.config != TG_CFG_F32_64x64) return TG_ERR_UNSUPPORTED;
             return launch_variants<CfgF32>(gp, plan.info, s);
+        default: return TG_ERR_INVALID_ARG;
     }
-    return TG_ERR_INVALID_ARG;
+    if (st != TG_OK || !split) return st;
+    return launch_combine(gp.W, C, M, N, ldc, sC, batch, plan.info.split_k, alpha, beta, s);
 }
 
 }  // namespace
@@ -312,6 +411,19 @@ tg_status tile_gemm_plan(int64_t batch, int64_t M, int64_t N, int64_t K, tg_dtyp
         Plan p;
         tg_status st = make_plan(batch, M, N, K, dtype, opt, p);
         if (st == TG_OK) *out = p.info;
+        return st;
+    } catch (...) {
+        return TG_ERR_INTERNAL;
+    }
+}
+
+tg_status tile_gemm_workspace_size(int64_t batch, int64_t M, int64_t N, int64_t K, tg_dtype dtype,
+                                   const tg_options *opt, int64_t *bytes) {
+    if (!bytes) return TG_ERR_INVALID_ARG;
+    try {
+        Plan p;
+        tg_status st = make_plan(batch, M, N, K, dtype, opt, p);
+        if (st == TG_OK) *bytes = p.wanted_workspace;
         return st;
     } catch (...) {
         return TG_ERR_INTERNAL;

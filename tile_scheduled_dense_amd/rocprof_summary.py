@@ -3,6 +3,7 @@ bench.py reports.
 
   python -m tile_scheduled_dense_amd.rocprof_summary trace  <kernel_stats.csv> <out.txt> <command...>
   python -m tile_scheduled_dense_amd.rocprof_summary counters <fetch_dir> <write_dir> <copy_mib> <out.txt> <command...>
+  python -m tile_scheduled_dense_amd.rocprof_summary sq <sq_dir> <trace_kernel_stats.csv> <out.txt> <command...>
 
 `counters` reads two --pmc runs (FETCH_SIZE, then WRITE_SIZE, KiB per
 dispatch) of a command that also ran a plain device copy of `copy_mib` MiB
@@ -10,6 +11,10 @@ dispatch) of a command that also ran a plain device copy of `copy_mib` MiB
 that copy, whose true traffic is known (copy_mib read and copy_mib written).
 The summary records a hash of the kernel sources; bench.py reports the traffic
 only while the sources still match.
+
+`sq` averages the SQ/GRBM counters of one --pmc run over the GEMM dispatches
+and derives the shader clock (GRBM_GUI_ACTIVE counts cycles on each of the 8
+XCDs) and the fraction of SIMD cycles the matrix cores were busy.
 """
 from __future__ import annotations
 
@@ -21,7 +26,7 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-GEMM_KERNEL_TAG = "gemm_kernel"
+GEMM_KERNEL_TAG = "tg::gemm"     # gemm_kernel (fp32) and gemm_ring_kernel (16-bit)
 
 
 def kernel_source_hash() -> str:
@@ -114,6 +119,28 @@ def traffic_for(workload: str):
     return float(kv["traffic_bytes_per_launch"])
 
 
+def summarize_sq(sq_dir, stats_csv):
+    rows = _rows(_counter_file(sq_dir))
+    vals = {}
+    for r in rows:
+        if GEMM_KERNEL_TAG in r["Kernel_Name"]:
+            vals.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    out = {k: sum(v) / len(v) for k, v in sorted(vals.items())}
+    _, d = _pick(summarize_trace(stats_csv), GEMM_KERNEL_TAG)
+    dur_ns = d["average_ns"]
+    out["kernel_duration_ns (from the kernel trace)"] = dur_ns
+    if "GRBM_GUI_ACTIVE" in out:
+        cycles = out["GRBM_GUI_ACTIVE"] / 8.0
+        out["derived_clock_GHz (GRBM_GUI_ACTIVE / 8 XCDs / duration)"] = round(cycles / dur_ns, 3)
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in out:
+            out["derived_mfma_busy_fraction (MFMA busy / (1024 SIMDs x cycles))"] = round(
+                out["SQ_VALU_MFMA_BUSY_CYCLES"] / (1024.0 * cycles), 3)
+    if "SQ_LDS_BANK_CONFLICT" in out and out.get("SQ_LDS_IDX_ACTIVE"):
+        out["derived_lds_conflict_fraction"] = round(out["SQ_LDS_BANK_CONFLICT"] / out["SQ_LDS_IDX_ACTIVE"], 4)
+    out["kernel_source_sha256"] = kernel_source_hash()
+    return out
+
+
 def summarize_trace(stats_csv):
     rows = _rows(stats_csv)
     out = {}
@@ -139,6 +166,10 @@ def main(argv):
         fetch_dir, write_dir, copy_mib, out, cmd = argv[2], argv[3], int(argv[4]), argv[5], " ".join(argv[6:])
         write_kv(out, "rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE, scaled by a plain copy of known size", cmd,
                  summarize_counters(fetch_dir, write_dir, copy_mib))
+    elif mode == "sq":
+        sq_dir, stats, out, cmd = argv[2], argv[3], argv[4], " ".join(argv[5:])
+        write_kv(out, "rocprofv3 --pmc SQ counters of the GEMM kernel, averaged over dispatches", cmd,
+                 summarize_sq(sq_dir, stats))
     else:
         raise SystemExit(__doc__)
 
