@@ -70,12 +70,18 @@ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Default choice: the largest tile that still gives the chip (256 CUs) at
 // least about one workgroup per CU; fp32 has one configuration.
+// The largest tile that still gives about one workgroup per CU (240 of 256)
+// and pads the output by at most a quarter more than the next smaller tile
+// (a 257 x 129 problem pads to 512 x 256 in 256-wide tiles, 384 x 256 in
+// 128-wide ones: a third more).
 int choose_config(int64_t batch, int64_t M, int64_t N, tg_dtype dtype) {
     if (dtype == TG_F32) return TG_CFG_F32_64x64;
     const int64_t big = cdiv(M, 256) * cdiv(N, 256) * batch;
-    if (big >= 240) return TG_CFG_256x256;
     const int64_t mid = cdiv(M, 128) * cdiv(N, 128) * batch;
+    const int64_t area_big = big * 256 * 256, area_mid = mid * 128 * 128;
+    if (big >= 240 && 4 * area_big <= 5 * area_mid) return TG_CFG_256x256;
     if (mid >= 240) return TG_CFG_128x128;
+    if (big >= 240) return TG_CFG_256x256;
     return TG_CFG_64x64;
 }
 
