@@ -196,7 +196,17 @@ __device__ __forceinline__ void mfma_chunk(const u32x4 &a, const u32x4 &b, f32x1
 
 template <int DT>
 __device__ __forceinline__ void mfma_chunk(const u32x4 &a, const u32x4 &b, f32x4 &acc) {
-    // four 16x16x4 fp32 MFMAs; element e of both chunks is the same k.
+    if constexpr (DT == DT_BF16) {
+        // one 16x16x32 MFMA: the chunks hold 8 consecutive k of one row / column
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                       __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
+        return;
+    } else if constexpr (DT == DT_F16) {
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                      __builtin_bit_cast(f16x8, b), acc, 0, 0, 0);
+        return;
+    }
+    // fp32: four 16x16x4 MFMAs; element e of both chunks is the same k.
 #pragma unroll
     for (int e = 0; e < 4; ++e)
     {
@@ -213,8 +223,9 @@ __device__ __forceinline__ void mfma_chunk(const u32x4 &a, const u32x4 &b, f32x4
 // masks (fringe blocks only) sit here, on the accumulator transfer.  For each
 // MFMA tile the C0 values are all loaded before any store, so the loads are in
 // flight together instead of each waiting behind the previous store.
-template <class C, bool FRINGE, class Acc>
-__device__ __forceinline__ void store_tile_epilogue(const GemmParams &p, Acc (&acc)[C::TM][C::TN], int64_t b,
+// `acc(i, j, v)` is value v of MFMA tile (i, j) of this lane.
+template <class C, bool FRINGE, class AccFn>
+__device__ __forceinline__ void store_tile_epilogue(const GemmParams &p, const AccFn &acc, int64_t b,
                                                     int64_t m0, int64_t n0, int wave, int lane) {
     float *Cblk = p.C + b * p.sC + m0 * p.ldc + n0;
     const int ldc = (int)p.ldc;
@@ -239,11 +250,11 @@ __device__ __forceinline__ void store_tile_epilogue(const GemmParams &p, Acc (&a
                 for (int v = 0; v < C::ACC_PER_MFMA; ++v) c0[v] = ok[v] ? Cblk[off[v]] : 0.0f;
 #pragma unroll
                 for (int v = 0; v < C::ACC_PER_MFMA; ++v)
-                    if (ok[v]) Cblk[off[v]] = __builtin_fmaf(alpha, acc[i][j][v], beta * c0[v]);
+                    if (ok[v]) Cblk[off[v]] = __builtin_fmaf(alpha, acc(i, j, v), beta * c0[v]);
             } else {
 #pragma unroll
                 for (int v = 0; v < C::ACC_PER_MFMA; ++v)
-                    if (ok[v]) Cblk[off[v]] = alpha * acc[i][j][v];
+                    if (ok[v]) Cblk[off[v]] = alpha * acc(i, j, v);
             }
         }
     }
@@ -400,7 +411,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams &p, char *smem, int64
     }
 
     // -- epilogue: fused alpha/beta store-back, masks only here
-    store_tile_epilogue<C, FRINGE>(p, acc, b, m0, n0, wave, lane);
+    store_tile_epilogue<C, FRINGE>(p, [&](int i, int j, int v) { return acc[i][j][v]; }, b, m0, n0, wave, lane);
 }
 
 template <class C, int DEPTH, int SWZ>

@@ -36,7 +36,7 @@
 namespace tg {
 
 // The two K-loop schedules (template argument of gemm_ring_kernel).
-enum { SCHED_RING = 0, SCHED_SWPIPE = 1 };
+enum { SCHED_RING = 0, SCHED_SWPIPE = 1, SCHED_PINGPONG = 2 };
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -67,7 +67,7 @@ constexpr int kOutOfRange = (int)0x80000000u;   // >= every resource size: reads
 // vmcnt(0) wait in front of every later LDS read (which would empty the ring
 // each iteration); the ring's own waits cover it.  The s_nop covers the
 // SGPR-written-by-VALU and M0 hazards before the memory instruction; M0 is
-// restored afterwards.
+// declared clobbered, so the compiler sets it again wherever it needs it.
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 // The same 128-bit resource as make_rsrc_n, as four scalar words: base (48
@@ -100,6 +100,11 @@ __device__ __forceinline__ i32x4 rsrc_words_u(uint64_t base, int64_t nbytes) {
 // m0 while an earlier copy of the wave is still being issued holds the wave
 // back, so one m0 write per group instead of one per copy roughly doubles the
 // copy rate a wave can sustain.
+// M0 is named in the clobber list, which clang flags as a reserved register
+// (-Winline-asm); the kernels use M0 nowhere else (a test scans the built code
+// object for any other M0 access), so the compiler has no value in it to lose.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
 template <int G>
 __device__ __forceinline__ void copy_group_to_lds(i32x4 rs, uint32_t lds_addr, const int (&voff)[G]) {
     static_assert(G == 1 || G == 2 || G == 4, "1, 2 or 4 copies per group");
@@ -107,50 +112,62 @@ __device__ __forceinline__ void copy_group_to_lds(i32x4 rs, uint32_t lds_addr, c
     lds_addr = __builtin_amdgcn_readfirstlane(lds_addr);
     rs = i32x4{__builtin_amdgcn_readfirstlane(rs.x), __builtin_amdgcn_readfirstlane(rs.y),
                __builtin_amdgcn_readfirstlane(rs.z), __builtin_amdgcn_readfirstlane(rs.w)};
-    int saved_m0;
     if constexpr (G == 1) {
         asm volatile(
-            "s_mov_b32 %0, m0\n\t"
-            "s_mov_b32 m0, %1\n\t"
+            "s_mov_b32 m0, %0\n\t"
             "s_nop 0\n\t"
-            "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
-            "s_mov_b32 m0, %0"
-            : "=&s"(saved_m0)
+            "buffer_load_dwordx4 %1, %2, 0 offen lds"
+            :
             : "s"(lds_addr), "v"(voff[0]), "s"(rs)
-            : "memory");
+            : "memory", "m0");
     } else if constexpr (G == 2) {
         asm volatile(
-            "s_mov_b32 %0, m0\n\t"
-            "s_mov_b32 m0, %1\n\t"
+            "s_mov_b32 m0, %0\n\t"
             "s_nop 0\n\t"
-            "buffer_load_dwordx4 %2, %4, 0 offen lds\n\t"
-            "buffer_load_dwordx4 %3, %4, 0 offen offset:1024 lds\n\t"
-            "s_mov_b32 m0, %0"
-            : "=&s"(saved_m0)
+            "buffer_load_dwordx4 %1, %3, 0 offen lds\n\t"
+            "buffer_load_dwordx4 %2, %3, 0 offen offset:1024 lds"
+            :
             : "s"(lds_addr), "v"(voff[0]), "v"(voff[1]), "s"(rs)
-            : "memory");
+            : "memory", "m0");
     } else {
         asm volatile(
-            "s_mov_b32 %0, m0\n\t"
-            "s_mov_b32 m0, %1\n\t"
+            "s_mov_b32 m0, %0\n\t"
             "s_nop 0\n\t"
-            "buffer_load_dwordx4 %2, %6, 0 offen lds\n\t"
-            "buffer_load_dwordx4 %3, %6, 0 offen offset:1024 lds\n\t"
-            "buffer_load_dwordx4 %4, %6, 0 offen offset:2048 lds\n\t"
-            "buffer_load_dwordx4 %5, %6, 0 offen offset:3072 lds\n\t"
-            "s_mov_b32 m0, %0"
-            : "=&s"(saved_m0)
+            "buffer_load_dwordx4 %1, %5, 0 offen lds\n\t"
+            "buffer_load_dwordx4 %2, %5, 0 offen offset:1024 lds\n\t"
+            "buffer_load_dwordx4 %3, %5, 0 offen offset:2048 lds\n\t"
+            "buffer_load_dwordx4 %4, %5, 0 offen offset:3072 lds"
+            :
             : "s"(lds_addr), "v"(voff[0]), "v"(voff[1]), "v"(voff[2]), "v"(voff[3]), "s"(rs)
-            : "memory");
+            : "memory", "m0");
     }
 }
+#pragma clang diagnostic pop
 
 __device__ __forceinline__ uint32_t lds_address(const char *p) {
     return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)TG_LDS_PTR(p));
 }
 
+// The accumulators of one wave's TM x TN MFMA tiles: an f32x16 per 32x32
+// tile, an f32x4 per 16x16 tile.
+template <class C>
+struct AccTiles {
+    typename AccT<C>::type r[C::TM][C::TN];
+    __device__ __forceinline__ void zero() {
+#pragma unroll
+        for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+            for (int j = 0; j < C::TN; ++j) r[i][j] = typename AccT<C>::type{};
+    }
+    __device__ __forceinline__ void mma(int i, int j, const u32x4 &a, const u32x4 &b) {
+        mfma_chunk<C::DT>(a, b, r[i][j]);
+    }
+    // value v (0 <= v < ACC_PER_MFMA) of MFMA tile (i, j)
+    __device__ __forceinline__ float get(int i, int j, int v) const { return r[i][j][v]; }
+};
+
 // One workgroup's tile of the 16-bit family: copy sources, the copies, the
-// register-path last tile, fragment reads and the MFMAs, shared by the two
+// register-path last tile, fragment reads and the MFMAs, shared by the
 // schedules below.
 template <class C, int STAGES, int SWZ, bool FRINGE>
 struct RingBlock {
@@ -170,7 +187,7 @@ struct RingBlock {
     uint32_t lds0;              // LDS address of smem
     int64_t b_step;             // bytes of B per K tile
     u32x4 tail[C::COPIES];
-    f32x16 acc[C::TM][C::TN];
+    AccTiles<C> acc;
 
     __device__ __forceinline__ RingBlock(const GemmParams &p_, char *smem_, int64_t b_, int64_t tm, int64_t tn)
         : p(p_), smem(smem_), b(b_) {
@@ -191,10 +208,7 @@ struct RingBlock {
         b_base = uniform_u64((uint64_t)Bblk);
         lds0 = lds_address(smem);
         b_step = (int64_t)C::BK * p.ldb * E;
-#pragma unroll
-        for (int i = 0; i < C::TM; ++i)
-#pragma unroll
-            for (int j = 0; j < C::TN; ++j) acc[i][j] = f32x16{};
+        acc.zero();
 #pragma unroll
         for (int d = 0; d < C::A_DMA; ++d) {
             ring_a_source<C>(ring_block<C>(d, wave, C::A_DMA), lane, SWZ, a_row[d], a_k[d]);
@@ -212,13 +226,16 @@ struct RingBlock {
     // this wave's copies of one operand (0 = A, 1 = B) of K tile kt into LDS copy `stage`
     __device__ __forceinline__ void dma_operand(int64_t kt, int stage, int operand) {
         const uint32_t sA = lds0 + stage * C::STAGE_BYTES;
+        // An interior block's copied tiles lie wholly inside A and B, so its
+        // resources need no size limit beyond the 31-bit offsets; a fringe
+        // block's limit ends at the last valid element (past it reads as 0).
         if (operand == 0) {
             const int64_t adv = kt * (C::BK * E);
-            copy_group_to_lds<C::A_DMA>(rsrc_words_u(a_base + adv - A_SHIFT, a_valid - adv + A_SHIFT),
+            copy_group_to_lds<C::A_DMA>(rsrc_words_u(a_base + adv - A_SHIFT, FRINGE ? a_valid - adv + A_SHIFT : 0x7fffffff),
                                         sA + ring_block<C>(0, wave, C::A_DMA) * 1024, a_voff);
         } else {
             const int64_t adv = kt * b_step;
-            copy_group_to_lds<C::B_DMA>(rsrc_words_u(b_base + adv - B_SHIFT, b_valid - adv + B_SHIFT),
+            copy_group_to_lds<C::B_DMA>(rsrc_words_u(b_base + adv - B_SHIFT, FRINGE ? b_valid - adv + B_SHIFT : 0x7fffffff),
                                         sA + C::A_TILE_BYTES + ring_block<C>(0, wave, C::B_DMA) * 1024, b_voff);
         }
     }
@@ -284,20 +301,38 @@ struct RingBlock {
         const char *sB = sA + C::A_TILE_BYTES;
         const int wrow = (wave / C::WAVES_N) * C::WTM;
         const int wcol = (wave % C::WAVES_N) * C::WTN;
-        const int grp = lane / 16, gi = lane % 16;
 #pragma unroll
         for (int i = 0; i < C::TM; ++i)
-            af[i] = *(const u32x4 *)(sA + ring_a_byte<C>(wrow + i * C::MT + lane % 32, 2 * s + lane / 32, SWZ));
+            af[i] = *(const u32x4 *)(sA + ring_a_byte<C>(a_frag_row(wrow, i), a_frag_chunk(s), SWZ));
 #pragma unroll
         for (int j = 0; j < C::TN; ++j) {
-            const int k = 16 * s + 8 * (grp / 2) + gi / 4;
-            const int n = wcol + j * C::MT + 16 * (grp % 2) + 4 * (gi % 4);
+            int k, n;
+            b_frag_src(wcol, j, s, 0, k, n);
             const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                 (__attribute__((address_space(3))) v4i16 *)(sB + ring_b_byte<C>(k, n, SWZ)));
             const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                 (__attribute__((address_space(3))) v4i16 *)(sB + ring_b_byte<C>(k + 4, n, SWZ)));
             const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
             bfr[j] = u32x4{l2.x, l2.y, h2.x, h2.y};
+        }
+    }
+
+    // MFMA operand fragments.  A: lane l holds 8 consecutive k (one 16-byte
+    // chunk) of row l % MT of MFMA row tile i; the LANE_GROUPS groups of MT
+    // lanes take consecutive chunks.  B (transposing read): lane L = 16 g + i
+    // of a 16-lane group supplies the address of 4 consecutive n of one k row
+    // and receives 4 consecutive k of column i; (k, n) below is that row and
+    // first column for the first of the two reads (the second is 4 rows on).
+    __device__ __forceinline__ int a_frag_row(int wrow, int i) const { return wrow + i * C::MT + lane % C::MT; }
+    __device__ __forceinline__ int a_frag_chunk(int s) const { return C::LANE_GROUPS * s + lane / C::MT; }
+    __device__ __forceinline__ void b_frag_src(int wcol, int j, int s, int half, int &k, int &n) const {
+        const int grp = lane / 16, gi = lane % 16;
+        if (C::MT == 32) {
+            k = 16 * s + 8 * (grp / 2) + gi / 4 + 4 * half;
+            n = wcol + j * 32 + 16 * (grp % 2) + 4 * (gi % 4);
+        } else {
+            k = 32 * s + 8 * grp + gi / 4 + 4 * half;
+            n = wcol + j * 16 + 4 * (gi % 4);
         }
     }
 
@@ -314,13 +349,12 @@ struct RingBlock {
         constexpr int NA = C::KSTEPS * C::TM;
         if (r < NA) {
             const int s = r / C::TM, i = r % C::TM;
-            af[s][i] = *(const u32x4 *)(sA + ring_a_byte<C>(wrow + i * C::MT + lane % 32, 2 * s + lane / 32, SWZ));
+            af[s][i] = *(const u32x4 *)(sA + ring_a_byte<C>(a_frag_row(wrow, i), a_frag_chunk(s), SWZ));
         } else {
             const int q = r - NA;
             const int s = q / (2 * C::TN), j = (q / 2) % C::TN, half = q % 2;
-            const int grp = lane / 16, gi = lane % 16;
-            const int k = 16 * s + 8 * (grp / 2) + gi / 4 + 4 * half;
-            const int n = wcol + j * C::MT + 16 * (grp % 2) + 4 * (gi % 4);
+            int k, n;
+            b_frag_src(wcol, j, s, half, k, n);
             const v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                 (__attribute__((address_space(3))) v4i16 *)(sB + ring_b_byte<C>(k, n, SWZ)));
             const u32x2 w2 = __builtin_bit_cast(u32x2, v);
@@ -338,7 +372,7 @@ struct RingBlock {
 #pragma unroll
         for (int i = 0; i < C::TM; ++i)
 #pragma unroll
-            for (int j = 0; j < C::TN; ++j) mfma_chunk<C::DT>(af[i], bfr[j], acc[i][j]);
+            for (int j = 0; j < C::TN; ++j) acc.mma(i, j, af[i], bfr[j]);
     }
 
     __device__ __forceinline__ void compute(int stage) {
@@ -387,7 +421,8 @@ __device__ __forceinline__ void ring_tile(const GemmParams &p, char *smem, int64
             }
         }
     }
-    store_tile_epilogue<C, FRINGE>(p, blk.acc, b, blk.m0, blk.n0, blk.wave, blk.lane);
+    store_tile_epilogue<C, FRINGE>(p, [&](int i, int j, int v) { return blk.acc.get(i, j, v); }, b, blk.m0, blk.n0,
+                                   blk.wave, blk.lane);
 }
 
 // SCHED_SWPIPE (software pipeline, one wave per SIMD, large wave tiles): the
@@ -416,7 +451,13 @@ struct SwPipe {
                                                 u32x4 (&na)[C::KSTEPS][C::TM], u32x4 (&nb)[C::KSTEPS][C::TN]) {
         const int64_t nk = blk.nk, ndma = blk.ndma;
         const bool more = STEADY || t + 1 < nk;
-        if (more) blk.template land_tile<STAGES - 2>(t + 1, nxt_read);
+        if (STEADY) {
+            // tile t + 1 is a copied tile with STAGES - 2 copied tiles issued after it
+            wait_vmcnt<(STAGES - 2) * C::COPIES>();
+            wait_lds();
+        } else if (more) {
+            blk.template land_tile<STAGES - 2>(t + 1, nxt_read);
+        }
         wait_lds();
         __builtin_amdgcn_sched_barrier(0);
         block_barrier();
@@ -426,7 +467,7 @@ struct SwPipe {
 #pragma unroll
             for (int q = 0; q < NMFMA; ++q) {
                 const int s = q / (C::TM * C::TN), i = (q / C::TN) % C::TM, j = q % C::TN;
-                mfma_chunk<C::DT>(fa[s][i], fb[s][j], blk.acc[i][j]);
+                blk.acc.mma(i, j, fa[s][i], fb[s][j]);
                 if (q < READS) blk.read_piece(nxt_read, q, na, nb);
                 if (q == NMFMA / 4 - 1 || q == 3 * NMFMA / 4 - 1) blk.dma_operand(tc, cur, q < NMFMA / 2 ? 0 : 1);
                 __builtin_amdgcn_sched_barrier(0);
@@ -440,7 +481,7 @@ struct SwPipe {
 #pragma unroll
             for (int q = 0; q < NMFMA; ++q) {
                 const int s = q / (C::TM * C::TN), i = (q / C::TN) % C::TM, j = q % C::TN;
-                mfma_chunk<C::DT>(fa[s][i], fb[s][j], blk.acc[i][j]);
+                blk.acc.mma(i, j, fa[s][i], fb[s][j]);
             }
         }
     }
@@ -453,7 +494,7 @@ __device__ __forceinline__ void ring_tile_swpipe(const GemmParams &p, char *smem
     RingBlock<C, STAGES, SWZ, FRINGE> blk(p, smem, b, tm, tn);
     const int64_t nk = blk.nk, ndma = blk.ndma;
     if (nk > 0) {
-        blk.tail_load();
+        if (ndma == 0) blk.tail_load();             // tile 0 is the last tile: landed just below
 #pragma unroll
         for (int t = 0; t < STAGES; ++t)
             if (t < ndma) blk.dma(t, t);
@@ -475,7 +516,13 @@ __device__ __forceinline__ void ring_tile_swpipe(const GemmParams &p, char *smem
             SP::template iter<true>(blk, t + 1, c1, c2, a1, b1, a0, b0);
             cur = c2;
         }
-        // drain
+        // drain.  The last K tile (landed in the drain whenever there are copied
+        // tiles: the steady state lands tiles below ndma only) has its register
+        // loads issued here, not in the prologue, so their registers are not
+        // held through the steady state; they are younger than some copies,
+        // which only makes the vmcnt waits of those copies conservative (loads
+        // complete in issue order).
+        if (ndma > 0) blk.tail_load();
         for (; t + 1 < nk; t += 2) {
             const int c1 = adv(cur), c2 = adv(c1);
             SP::template iter<false>(blk, t, cur, c1, a0, b0, a1, b1);
@@ -484,13 +531,81 @@ __device__ __forceinline__ void ring_tile_swpipe(const GemmParams &p, char *smem
         }
         if (t < nk) SP::template iter<false>(blk, t, cur, adv(cur), a0, b0, a1, b1);
     }
-    store_tile_epilogue<C, FRINGE>(p, blk.acc, b, blk.m0, blk.n0, blk.wave, blk.lane);
+    store_tile_epilogue<C, FRINGE>(p, [&](int i, int j, int v) { return blk.acc.get(i, j, v); }, b, blk.m0, blk.n0,
+                                   blk.wave, blk.lane);
+}
+
+// SCHED_PINGPONG (two waves per SIMD, 8 waves): waves 0-3 form group 0 and
+// waves 4-7 group 1, one wave of each per SIMD.  Each wave alternates a memory
+// phase (read the fragments of its next K tile from LDS into registers, issue
+// its share of the copies of tile t + STAGES - 1, wait for its share of tile
+// t + 1) and a compute phase (the MFMAs of the tile whose fragments it holds).
+// Group 1 runs one phase behind group 0, so on every SIMD one wave multiplies
+// while the other moves data, and the matrix core is fed across the LDS and
+// copy traffic.  Every phase ends in one workgroup barrier (2 per K tile):
+//   barrier 2t+1 closes group 0's memory phase of tile t (group 1 is then in
+//   its compute phase of tile t - 1), barrier 2t+2 closes group 0's compute
+//   phase of tile t and group 1's memory phase of tile t.
+// Tile t is read after barrier 2t (group 0) or 2t + 1 (group 1); every wave
+// lands its share of tile t before barrier 2t - 1 or 2t, so it is visible.
+// The copy of tile t + STAGES - 1 reuses tile t - 1's LDS copy, whose last
+// reader (group 1) finished before barrier 2t.
+template <class C, int STAGES, int SWZ, bool FRINGE>
+__device__ __forceinline__ void ring_tile_pingpong(const GemmParams &p, char *smem, int64_t b, int64_t tm, int64_t tn) {
+    static_assert(C::WAVES == 8, "two groups of four waves, one wave of each per SIMD");
+    static_assert(STAGES >= 2 && STAGES <= 4, "2 to 4 LDS copies");
+    constexpr int D = STAGES - 1;                  // copies run D tiles ahead of the tile being read
+    using Blk = RingBlock<C, STAGES, SWZ, FRINGE>;
+    Blk blk(p, smem, b, tm, tn);
+    const int64_t nk = blk.nk, ndma = blk.ndma;
+    const bool group1 = blk.wave >= 4;             // wave-uniform
+    auto adv = [](int x, int by) { return (x + by) % STAGES; };
+    if (nk > 0) {
+        blk.tail_load();
+#pragma unroll
+        for (int t = 0; t < D; ++t)
+            if (t < ndma) blk.dma(t, t);
+        blk.template land_tile<D - 1>(0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        block_barrier();                            // barrier 0: tile 0 visible
+        if (group1) block_barrier();                // barrier 1: group 1 starts one phase late
+        __builtin_amdgcn_sched_barrier(0);
+        u32x4 fa[C::KSTEPS][C::TM], fb[C::KSTEPS][C::TN];
+        int cur = 0;                                // LDS copy holding tile t
+        for (int64_t t = 0; t < nk; ++t) {
+            // memory phase of tile t
+#pragma unroll
+            for (int r = 0; r < Blk::READS; ++r) blk.read_piece(cur, r, fa, fb);
+            if (t + D < ndma) blk.dma(t + D, adv(cur, D));
+            if (t + 1 < nk) blk.template land_tile<D - 1>(t + 1, adv(cur, 1));
+            wait_lds();
+            __builtin_amdgcn_sched_barrier(0);
+            block_barrier();
+            __builtin_amdgcn_sched_barrier(0);
+            // compute phase of tile t
+            __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+            for (int s = 0; s < C::KSTEPS; ++s)
+#pragma unroll
+                for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+                    for (int j = 0; j < C::TN; ++j) blk.acc.mma(i, j, fa[s][i], fb[s][j]);
+            __builtin_amdgcn_s_setprio(0);
+            __builtin_amdgcn_sched_barrier(0);
+            block_barrier();
+            __builtin_amdgcn_sched_barrier(0);
+            cur = adv(cur, 1);
+        }
+        if (!group1) block_barrier();               // group 0's count matches group 1's late start
+    }
+    store_tile_epilogue<C, FRINGE>(p, [&](int i, int j, int v) { return blk.acc.get(i, j, v); }, b, blk.m0, blk.n0,
+                                   blk.wave, blk.lane);
 }
 
 template <class C, int STAGES, int SWZ, int SCHED>
 __global__ __launch_bounds__(C::THREADS, 1) void gemm_ring_kernel(GemmParams p) {
     static_assert(STAGES >= 1 && STAGES <= 5, "1 to 5 LDS copies");
-    static_assert(SCHED == SCHED_RING || SCHED == SCHED_SWPIPE, "schedule");
+    static_assert(SCHED == SCHED_RING || SCHED == SCHED_SWPIPE || SCHED == SCHED_PINGPONG, "schedule");
     __shared__ __attribute__((aligned(1024))) char smem[STAGES * C::STAGE_BYTES];
     int64_t b, tm, tn;
     block_coords(p, b, tm, tn);
@@ -513,7 +628,10 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_ring_kernel(GemmParams p) 
         q.C = p.C + b * p.sC;
     }
     const bool interior = (tm + 1) * C::BM <= p.M && (tn + 1) * C::BN <= p.N;
-    if constexpr (SCHED == SCHED_SWPIPE) {
+    if constexpr (SCHED == SCHED_PINGPONG) {
+        if (interior) ring_tile_pingpong<C, STAGES, SWZ, false>(q, smem, 0, tm, tn);
+        else ring_tile_pingpong<C, STAGES, SWZ, true>(q, smem, 0, tm, tn);
+    } else if constexpr (SCHED == SCHED_SWPIPE) {
         if (interior) ring_tile_swpipe<C, STAGES, SWZ, false>(q, smem, 0, tm, tn);
         else ring_tile_swpipe<C, STAGES, SWZ, true>(q, smem, 0, tm, tn);
     } else {

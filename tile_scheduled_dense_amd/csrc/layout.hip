@@ -131,9 +131,14 @@ void describe_ring_lds(tg_layout *L, int operand, int swz) {
     if (swz != SWZ_XOR) return;
     L->n_swizzle = 1;
     if (operand == 0) {
-        L->swizzle[0] = {3, 2, 4};                          // chunk ^= (row >> 2) & 3
+        if (C::MT == 32) L->swizzle[0] = {3, 2, 4};         // chunk ^= (row >> 2) & 3
+        else L->swizzle[0] = {3, 2, 3};                     // chunk ^= (row >> 1) & 3
     } else if (C::B_UNITS >= 4) {
         L->swizzle[0] = {5, 2, C::B_UNITS == 8 ? 3 : 2};    // 64-byte unit ^= k & 3
+        if (C::B_HALF_SWZ) {                                // 32-byte half ^= (k >> 3) & 1
+            L->n_swizzle = 2;
+            L->swizzle[1] = {4, 1, C::B_UNITS == 8 ? 7 : 6};
+        }
     } else {
         L->swizzle[0] = {5, 1, 2};                          // 64-byte unit ^= (k >> 1) & 1
     }

@@ -117,11 +117,10 @@ TG_HD int lds_chunk_byte(int row, int chunk, int swz) {
 // The 16-bit kernel family: a K ring of STAGES LDS copies filled by direct
 // global -> LDS copies (no staging registers), BK = 32.
 //
-//  * A tile [BM][32] (64-byte rows, k contiguous) under Swizzle(3, 2, 4): the
-//    16-byte chunk index of row r is XORed with (r >> 2) & 3.  A 128-bit
-//    fragment read serves 16 lanes = 16 consecutive rows per cycle; four rows
-//    share a 256-byte bank line, and rows r, r+4, r+8, r+12 land on distinct
-//    chunks, so the 16 reads cover 16 distinct bank groups.
+//  * A tile [BM][32] (64-byte rows, k contiguous) under Swizzle(3, 2, 4) (the
+//    16-byte chunk index of row r XORed with (r >> 2) & 3) for 32x32x16 MFMAs,
+//    Swizzle(3, 2, 3) ((r >> 1) & 3) for 16x16x32: the choice that measured
+//    conflict-free for that MFMA's fragment reads (ring_a_mask).
 //  * B tile [32][BN] (k rows, n contiguous) under Swizzle(5, B, S) on 64-byte
 //    units (32 elements): the unit index w of row k is XORed with k & 3 when a
 //    row has >= 4 units, with (k >> 1) & 1 when it has 2.  B is read with the
@@ -130,8 +129,13 @@ TG_HD int lds_chunk_byte(int row, int chunk, int swz) {
 //    the bank line.
 //  * Copies: each DMA instruction fills 1 KiB of LDS, lane l writing bytes
 //    16l..16l+15; the swizzle is realised by choosing each lane's source.
+//  * MFMA shape MT_: 32 (32x32x16, two K steps per tile) or 16 (16x16x32, one
+//    K step per tile).  With 16x16x32 the four 16-lane groups of a B read take
+//    k rows 8g.. of the same 16 columns, so groups 0 and 1 (read in one cycle)
+//    touch rows k and k + 8; a second swizzle term XORs the 32-byte half of
+//    each 64-byte unit with (k >> 3) & 1 to keep them on distinct banks.
 // ---------------------------------------------------------------------------
-template <int DT_, int BM_, int BN_, int WAVES_M_, int WAVES_N_>
+template <int DT_, int BM_, int BN_, int WAVES_M_, int WAVES_N_, int MT_ = 32>
 struct RingCfg {
     static constexpr int DT = DT_;
     static constexpr int ELEM = 2;
@@ -140,10 +144,11 @@ struct RingCfg {
     static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
     static constexpr int WAVES = WAVES_M_ * WAVES_N_;
     static constexpr int THREADS = 64 * WAVES;
-    static constexpr int MT = 32, ACC_PER_MFMA = 16;
+    static constexpr int MT = MT_, ACC_PER_MFMA = MT_ * MT_ / 64;
+    static constexpr int MK = 512 / MT_;                     // k per MFMA: 16 (32x32) or 32 (16x16)
     static constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
     static constexpr int TM = WTM / MT, TN = WTN / MT;
-    static constexpr int KSTEPS = BK / 16;                   // 32x32x16 MFMAs per K tile
+    static constexpr int KSTEPS = BK / MK;                   // MFMA K steps per K tile
     static constexpr int A_ROW_BYTES = BK * ELEM;            // 64
     static constexpr int B_ROW_BYTES = BN * ELEM;
     static constexpr int B_UNITS = B_ROW_BYTES / 64;         // 64-byte units per B row
@@ -154,24 +159,39 @@ struct RingCfg {
     static constexpr int B_DMA = B_TILE_BYTES / 1024 / WAVES;
     static constexpr int COPIES = A_DMA + B_DMA;
     // acc_coord() below is shared with TileCfg
-    static constexpr int LANE_GROUPS = 2;
+    static constexpr int LANE_GROUPS = 64 / MT_;             // lanes sharing a row: 2 or 4
+    static constexpr bool B_HALF_SWZ = MT_ == 16;            // (k >> 3) & 1 into the 32-byte half
 
     static_assert(BM % (WAVES_M * MT) == 0 && BN % (WAVES_N * MT) == 0, "wave tiling");
     static_assert(A_TILE_BYTES % (1024 * WAVES) == 0 && A_DMA >= 1, "A copy split");
     static_assert(B_TILE_BYTES % (1024 * WAVES) == 0 && B_DMA >= 1, "B copy split");
     static_assert(B_UNITS == 2 || B_UNITS == 4 || B_UNITS == 8, "B row of 2, 4 or 8 units");
     static_assert(A_DMA <= 4 && B_DMA <= 4, "a wave's copies of one operand span at most 4 KiB");
+    static_assert(MT_ == 32 || (MT_ == 16 && B_UNITS >= 4), "16x16x32 needs B rows of 4 or 8 units");
 };
 
 template <int DT> using Ring256 = RingCfg<DT, 256, 256, 2, 2>;   // 4 waves, wave tile 128 x 128
+template <int DT> using Ring256x8 = RingCfg<DT, 256, 256, 2, 4>; // 8 waves, wave tile 128 x 64
+template <int DT> using Ring256m16 = RingCfg<DT, 256, 256, 2, 2, 16>;   // 4 waves, 16x16x32 MFMA
 template <int DT> using Ring128 = RingCfg<DT, 128, 128, 2, 2>;   // 4 waves, wave tile 64 x 64
 template <int DT> using Ring64 = RingCfg<DT, 64, 64, 1, 2>;      // 2 waves, wave tile 64 x 32
+
+// A tile: the XOR applied to the 16-byte chunk index of row r.  Which row
+// bits make the fragment reads conflict-free depends on the MFMA lane pattern
+// and was measured on gfx950 (SQ_LDS_BANK_CONFLICT of ds_read_b128 over every
+// candidate): (r >> 2) & 3 for the 32x32x16 pattern (lane l: row l % 32,
+// chunk l / 32), (r >> 1) & 3 for the 16x16x32 pattern (row l % 16, chunk
+// l / 16); the other choice costs one extra cycle in two.
+template <class C>
+TG_HD int ring_a_mask(int r, int swz) {
+    if (swz == SWZ_NONE) return 0;
+    return C::MT == 32 ? ((r >> 2) & 3) : ((r >> 1) & 3);
+}
 
 // A tile: byte offset of logical chunk c (0..3) of row r.
 template <class C>
 TG_HD int ring_a_byte(int r, int c, int swz) {
-    const int p = swz == SWZ_NONE ? c : (c ^ ((r >> 2) & 3));
-    return r * C::A_ROW_BYTES + 16 * p;
+    return r * C::A_ROW_BYTES + 16 * (c ^ ring_a_mask<C>(r, swz));
 }
 
 // B tile: the XOR applied to the 64-byte unit index of k row k.
@@ -181,11 +201,17 @@ TG_HD int ring_b_mask(int k, int swz) {
     return C::B_UNITS >= 4 ? (k & 3) : ((k >> 1) & 1);
 }
 
+// B tile: the XOR applied to the 32-byte half of a 64-byte unit of k row k.
+template <class C>
+TG_HD int ring_b_half_mask(int k, int swz) {
+    return (C::B_HALF_SWZ && swz != SWZ_NONE) ? ((k >> 3) & 1) : 0;
+}
+
 // B tile: byte offset of element (k, n).
 template <class C>
 TG_HD int ring_b_byte(int k, int n, int swz) {
-    const int w = n / 32, in_unit = (n % 32) * 2;
-    return k * C::B_ROW_BYTES + 64 * (w ^ ring_b_mask<C>(k, swz)) + in_unit;
+    const int w = n / 32, half = ((n % 32) / 16) ^ ring_b_half_mask<C>(k, swz), in_half = (n % 16) * 2;
+    return k * C::B_ROW_BYTES + 64 * (w ^ ring_b_mask<C>(k, swz)) + 32 * half + in_half;
 }
 
 // Which LDS bytes copy d (0 <= d < per_wave, per_wave = A_DMA or B_DMA) of
@@ -201,8 +227,7 @@ TG_HD void ring_a_source(int J, int lane, int swz, int &row, int &k) {
     const int byte = J * 1024 + 16 * lane;
     row = byte / C::A_ROW_BYTES;
     const int p = (byte % C::A_ROW_BYTES) / 16;
-    const int c = swz == SWZ_NONE ? p : (p ^ ((row >> 2) & 3));
-    k = 8 * c;
+    k = 8 * (p ^ ring_a_mask<C>(row, swz));
 }
 
 // The B element (k, first n of the chunk) lane l of block J must fetch.
@@ -212,7 +237,8 @@ TG_HD void ring_b_source(int J, int lane, int swz, int &k, int &n) {
     k = byte / C::B_ROW_BYTES;
     const int b = byte % C::B_ROW_BYTES;
     const int w = (b / 64) ^ ring_b_mask<C>(k, swz);
-    n = 32 * w + (b % 64) / 2;
+    const int half = ((b % 64) / 32) ^ ring_b_half_mask<C>(k, swz);
+    n = 32 * w + 16 * half + (b % 32) / 2;
 }
 
 // ---------------------------------------------------------------------------
