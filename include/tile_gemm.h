@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define TILE_GEMM_ABI_VERSION 2
+#define TILE_GEMM_ABI_VERSION 3
 
 typedef enum { TG_F32 = 0, TG_BF16 = 1, TG_F16 = 2 } tg_dtype;
 
@@ -83,7 +83,7 @@ tg_status tile_gemm_strided_batched(int64_t batch, int64_t M, int64_t N, int64_t
 /* Schedule knobs, for tests and measurements; zero-initialise for defaults. */
 typedef enum {
     TG_CFG_AUTO = 0,
-    TG_CFG_256x256 = 1,     /* 16-bit inputs: 256x256 block tile, 4 waves        */
+    TG_CFG_256x256 = 1,     /* 16-bit inputs: 256x256 block tile, 4 waves, 16x16x32 MFMA */
     TG_CFG_128x128 = 2,     /* 16-bit inputs: 128x128 block tile, 4 waves        */
     TG_CFG_64x64 = 3,       /* 16-bit inputs: 64x64 block tile, 2 waves          */
     TG_CFG_F32_64x64 = 4    /* fp32 inputs: 64x64 block tile, 4 waves            */
@@ -157,6 +157,9 @@ typedef struct {
     int split_k;                  /* K slices S (1: no split)                      */
     int64_t k_slice;              /* K elements per slice (the last may be shorter)*/
     int64_t workspace_bytes;      /* workspace the call uses: S * batch * M * N * 4 */
+    int mfma_m, mfma_n, mfma_k;   /* MFMA instruction shape: 32x32x16, 16x16x32 or 16x16x4 */
+    int pad0_;
+    int64_t strip_blocks;         /* thin fringe-strip blocks per problem (in grid) */
 } tg_plan_info;
 
 tg_status tile_gemm_plan(int64_t batch, int64_t M, int64_t N, int64_t K, tg_dtype dtype,
@@ -220,6 +223,11 @@ int64_t tg_layout_eval(const tg_layout *L, const int64_t *x, int64_t *out, int64
  *                          of the thread and the load slot m that copies it. */
 typedef enum { TG_LAYOUT_LDS_A = 0, TG_LAYOUT_LDS_B = 1, TG_LAYOUT_ACC = 2,
                TG_LAYOUT_COPY_A = 3 } tg_layout_kind;
+
+/* The introspection calls below take a tg_config, or one of these ids for the
+ * thin fringe-strip blocks of TG_CFG_256x256 (256 x 64 for an N tail of at
+ * most 64 columns, 64 x 256 for an M tail of at most 64 rows). */
+enum { TG_LAYOUT_CFG_STRIP_N = 101, TG_LAYOUT_CFG_STRIP_M = 102 };
 
 tg_status tile_gemm_describe_layout(int config, int swizzle, int kind, tg_layout *out);
 

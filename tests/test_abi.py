@@ -28,7 +28,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert tg.abi_version() == 2
+    assert tg.abi_version() == 3
     for s in range(5):
         assert tg.STATUS_NAMES[s] in tg.status_string(s)
 
@@ -98,15 +98,18 @@ def test_options_validation():
 # Block classes of the five measured problems (pad-to-tile + partition).
 @pytest.mark.parametrize("args,expect", [
     ((1, 67, 45, 53, "f32"), dict(config=tg.TG_CFG_F32_64x64, tiles_m=2, tiles_n=1, interior_blocks=0,
-                                  fringe_blocks=2, k_tiles=2, k_tail=21)),
+                                  fringe_blocks=2, k_tiles=2, k_tail=21, mfma_m=16, mfma_k=4)),
     ((1, 8192, 8192, 8192, "bf16"), dict(config=tg.TG_CFG_256x256, tiles_m=32, tiles_n=32, grid=1024,
                                          interior_blocks=1024, fringe_blocks=0, k_tiles=256, k_tail=0,
-                                         lds_bytes=4 * 32768, pipeline_depth=4)),
-    ((1, 8191, 8193, 8190, "bf16"), dict(config=tg.TG_CFG_256x256, tiles_m=32, tiles_n=33, grid=1056,
-                                         interior_blocks=31 * 32, fringe_blocks=1056 - 992, k_tiles=256,
-                                         k_tail=30)),
+                                         lds_bytes=4 * 32768, pipeline_depth=4, strip_blocks=0,
+                                         mfma_m=16, mfma_n=16, mfma_k=32)),
+    # N = 32 * 256 + 1: the one-column tail goes to 32 strip blocks of 256 x 64
+    ((1, 8191, 8193, 8190, "bf16"), dict(config=tg.TG_CFG_256x256, tiles_m=32, tiles_n=32, grid=1024 + 32,
+                                         interior_blocks=31 * 32, fringe_blocks=32, strip_blocks=32,
+                                         k_tiles=256, k_tail=30)),
     ((512, 257, 129, 1000, "f16"), dict(tiles_m=5, tiles_n=3, interior_blocks=8, fringe_blocks=7,
-                                        grid=15 * 512, k_tiles=32, k_tail=8, lds_bytes=4 * 8192)),
+                                        grid=15 * 512, k_tiles=32, k_tail=8, lds_bytes=4 * 8192,
+                                        mfma_m=32, mfma_k=16, strip_blocks=0)),
     ((1, 512, 512, 131072, "bf16"), dict(k_tiles=4096, k_tail=0, fringe_blocks=0)),
 ])
 def test_plan_block_classes(args, expect):
@@ -169,3 +172,21 @@ def test_lds_budget():
     for cfg, dt in [(1, "bf16"), (2, "bf16"), (3, "bf16"), (4, "f32")]:
         info = tg.tile_gemm_plan(1, 4096, 4096, 4096, dt, config=cfg)
         assert info["lds_bytes"] <= 160 * 1024
+
+
+@pytest.mark.parametrize("M,N,strips", [
+    (1000, 1000, dict(tiles_m=4, tiles_n=4, strip_blocks=0)),        # tails of 232: whole tiles
+    (1000, 1025, dict(tiles_m=4, tiles_n=4, strip_blocks=4)),        # N tail of 1: one strip per tile row
+    (1025, 1000, dict(tiles_m=4, tiles_n=4, strip_blocks=4)),        # M tail of 1: one strip per tile column
+    (1025, 1025, dict(tiles_m=4, tiles_n=4, strip_blocks=4 + 5)),    # both, the corner in the M strip
+    (1088, 1088, dict(tiles_m=4, tiles_n=4, strip_blocks=9)),        # tails of exactly 64
+    (1089, 1089, dict(tiles_m=5, tiles_n=5, strip_blocks=0)),        # tails of 65: whole tiles
+    (300, 200, dict(tiles_m=2, tiles_n=1, strip_blocks=0)),          # N < 256: no main grid to strip
+])
+def test_plan_thin_strips(M, N, strips):
+    info = tg.tile_gemm_plan(3, M, N, 512, "bf16", config=tg.TG_CFG_256x256)
+    for k, v in strips.items():
+        assert info[k] == v, (k, info)
+    assert info["grid"] == 3 * (info["tiles_m"] * info["tiles_n"] + info["strip_blocks"])
+    # other configurations have no strips
+    assert tg.tile_gemm_plan(1, M, N, 512, "bf16", config=tg.TG_CFG_128x128)["strip_blocks"] == 0

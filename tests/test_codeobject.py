@@ -4,7 +4,7 @@ The buffer-to-LDS copies are inline assembly that sets M0 (the LDS base of a
 copy group) and declares it clobbered instead of saving and restoring it; that
 is only sound while the compiler itself keeps nothing in M0.  This scans the
 disassembly for every M0 access and requires each to be one of the copy
-groups: `s_mov_b32 m0, sN`, `s_nop 0`, then the group's `buffer_load_dwordx4
+groups: `s_mov_b32 m0, <scalar register>`, `s_nop 0`, then the group's `buffer_load_dwordx4
 ... lds` instructions, and every such load to follow an M0 write of its group.
 """
 import os
@@ -40,7 +40,7 @@ def test_m0_only_in_copy_groups(tmp_path):
     for i, l in enumerate(lines):
         op = l.split()[0] if l.split() else ""
         if re.search(r"\bm0\b", l):
-            assert re.fullmatch(r"s_mov_b32 m0, s\d+", l), f"unexpected M0 access: {l}"
+            assert re.fullmatch(r"s_mov_b32 m0, (s\d+|vcc_lo|vcc_hi)", l), f"unexpected M0 access: {l}"
             assert lines[i + 1] == "s_nop 0", f"M0 write not followed by s_nop 0: {lines[i + 1]}"
             assert lines[i + 2].startswith("buffer_load_dwordx4") and lines[i + 2].endswith(" lds"), lines[i + 2]
             m0_set = True

@@ -27,6 +27,8 @@ STATUS_NAMES = {0: "TG_OK", 1: "TG_ERR_INVALID_ARG", 2: "TG_ERR_UNSUPPORTED", 3:
                 4: "TG_ERR_INTERNAL"}
 
 TG_CFG_AUTO, TG_CFG_256x256, TG_CFG_128x128, TG_CFG_64x64, TG_CFG_F32_64x64 = range(5)
+# layout-introspection ids of the thin fringe-strip blocks of TG_CFG_256x256
+LAYOUT_CFG_STRIP_N, LAYOUT_CFG_STRIP_M = 101, 102
 SWZ_DEFAULT, SWZ_NONE, SWZ_XOR = 0, 1, 2
 
 LAYOUT_LDS_A, LAYOUT_LDS_B, LAYOUT_ACC, LAYOUT_COPY_A = range(4)
@@ -65,7 +67,9 @@ class PlanInfo(ctypes.Structure):
                 ("tiles_m", ctypes.c_int64), ("tiles_n", ctypes.c_int64), ("grid", ctypes.c_int64),
                 ("interior_blocks", ctypes.c_int64), ("fringe_blocks", ctypes.c_int64),
                 ("k_tiles", ctypes.c_int64), ("k_tail", ctypes.c_int64), ("lds_bytes", ctypes.c_int),
-                ("split_k", ctypes.c_int), ("k_slice", ctypes.c_int64), ("workspace_bytes", ctypes.c_int64)]
+                ("split_k", ctypes.c_int), ("k_slice", ctypes.c_int64), ("workspace_bytes", ctypes.c_int64),
+                ("mfma_m", ctypes.c_int), ("mfma_n", ctypes.c_int), ("mfma_k", ctypes.c_int), ("pad0_", ctypes.c_int),
+                ("strip_blocks", ctypes.c_int64)]
 
     def as_dict(self):
         return {f: getattr(self, f) for f, _ in self._fields_}

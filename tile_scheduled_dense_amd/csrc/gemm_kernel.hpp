@@ -73,6 +73,13 @@ struct GemmParams {
     int64_t problems;            // batch of the call
     int64_t k_slice;
     float *W;
+    // Thin fringe strips (16-bit 256 x 256 configuration): the first
+    // tiles_m * tiles_n * batch workgroups run the main tiles, the rest, per
+    // batch entry, strip_n blocks of 256 x 64 (tile rows 0.., columns from
+    // n_main) and then strip_m blocks of 64 x 256 (rows from m_main, tile
+    // columns 0..).  tiles_m / tiles_n then count the main tiles only.
+    int64_t strip_n, strip_m;
+    int64_t n_main, m_main;
 };
 
 template <class C>

@@ -36,7 +36,7 @@
 namespace tg {
 
 // The two K-loop schedules (template argument of gemm_ring_kernel).
-enum { SCHED_RING = 0, SCHED_SWPIPE = 1, SCHED_PINGPONG = 2 };
+enum { SCHED_RING = 0, SCHED_SWPIPE = 1 };
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -150,8 +150,19 @@ __device__ __forceinline__ uint32_t lds_address(const char *p) {
 
 // The accumulators of one wave's TM x TN MFMA tiles: an f32x16 per 32x32
 // tile, an f32x4 per 16x16 tile.
+//
+// 16x16x32 MFMAs are issued as inline assembly with the accumulator tied to
+// AGPRs: through the builtin, the register allocator keeps a third of the 64
+// four-register accumulators in VGPRs and copies them into AGPRs and back
+// around their MFMAs every K tile.  The compiler does not see these as
+// MFMAs, so the two hazards that involve them are handled here: the first
+// K tile's MFMAs take a zero accumulator input (mma<true>, no VALU write of
+// an accumulator ever precedes an MFMA), and settle() pads the last MFMA's
+// results with wait states before anything else reads them.  Dependent MFMAs
+// on one accumulator are a whole K tile apart.
 template <class C>
 struct AccTiles {
+    static constexpr bool ASM = C::MT == 16 && C::DT != DT_F32;
     typename AccT<C>::type r[C::TM][C::TN];
     __device__ __forceinline__ void zero() {
 #pragma unroll
@@ -159,8 +170,30 @@ struct AccTiles {
 #pragma unroll
             for (int j = 0; j < C::TN; ++j) r[i][j] = typename AccT<C>::type{};
     }
+    // r[i][j] += a . b, or r[i][j] = a . b for the first K step (FIRST)
+    template <bool FIRST>
     __device__ __forceinline__ void mma(int i, int j, const u32x4 &a, const u32x4 &b) {
-        mfma_chunk<C::DT>(a, b, r[i][j]);
+        if constexpr (ASM) {
+            if constexpr (C::DT == DT_BF16) {
+                if (FIRST) asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=a"(r[i][j]) : "v"(a), "v"(b));
+                else asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(r[i][j]) : "v"(a), "v"(b));
+            } else {
+                if (FIRST) asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, 0" : "=a"(r[i][j]) : "v"(a), "v"(b));
+                else asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+a"(r[i][j]) : "v"(a), "v"(b));
+            }
+        } else {
+            mfma_chunk<C::DT>(a, b, r[i][j]);
+        }
+    }
+    // after the last MFMA: 32 wait states (an XDL result needs at most 19
+    // before a VALU or memory instruction reads it), fenced so the scheduler
+    // moves nothing across
+    __device__ __forceinline__ void settle() {
+        if constexpr (ASM) {
+            __builtin_amdgcn_sched_barrier(0);
+            asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+            __builtin_amdgcn_sched_barrier(0);
+        }
     }
     // value v (0 <= v < ACC_PER_MFMA) of MFMA tile (i, j)
     __device__ __forceinline__ float get(int i, int j, int v) const { return r[i][j][v]; }
@@ -368,19 +401,23 @@ struct RingBlock {
         }
     }
 
+    template <bool FIRST>
     __device__ __forceinline__ void mfmas(const u32x4 (&af)[C::TM], const u32x4 (&bfr)[C::TN]) {
 #pragma unroll
         for (int i = 0; i < C::TM; ++i)
 #pragma unroll
-            for (int j = 0; j < C::TN; ++j) acc.mma(i, j, af[i], bfr[j]);
+            for (int j = 0; j < C::TN; ++j) acc.template mma<FIRST>(i, j, af[i], bfr[j]);
     }
 
+    // the MFMAs of LDS copy `stage`; FIRST: the block's first K tile
+    template <bool FIRST>
     __device__ __forceinline__ void compute(int stage) {
 #pragma unroll
         for (int s = 0; s < C::KSTEPS; ++s) {
             u32x4 af[C::TM], bfr[C::TN];
             read_frags(stage, s, af, bfr);
-            mfmas(af, bfr);
+            if (FIRST && s == 0) mfmas<true>(af, bfr);
+            else mfmas<false>(af, bfr);
         }
     }
 };
@@ -403,7 +440,8 @@ __device__ __forceinline__ void ring_tile(const GemmParams &p, char *smem, int64
                 if (kt < ndma) blk.dma(kt, 0);
                 blk.template land_tile<0>(kt, 0);
                 block_barrier();            // tile kt is in LDS for every wave
-                blk.compute(0);
+                if (kt == 0) blk.template compute<true>(0);
+                else blk.template compute<false>(0);
             }
         } else {
 #pragma unroll
@@ -415,11 +453,13 @@ __device__ __forceinline__ void ring_tile(const GemmParams &p, char *smem, int64
                 block_barrier();            // tile kt visible; copy of tile kt-1 released
                 const int64_t t = kt + STAGES - 1;
                 if (t < ndma) blk.dma(t, nxt);
-                blk.compute(cur);
+                if (kt == 0) blk.template compute<true>(cur);
+                else blk.template compute<false>(cur);
                 cur = cur + 1 == STAGES ? 0 : cur + 1;
                 nxt = nxt + 1 == STAGES ? 0 : nxt + 1;
             }
         }
+        blk.acc.settle();
     }
     store_tile_epilogue<C, FRINGE>(p, [&](int i, int j, int v) { return blk.acc.get(i, j, v); }, b, blk.m0, blk.n0,
                                    blk.wave, blk.lane);
@@ -445,7 +485,7 @@ struct SwPipe {
     // One iteration: multiply tile t from (fa, fb) while reading tile t + 1
     // into (na, nb).  STEADY: tile t + 1 exists and tile t + STAGES is copied
     // (no conditions inside the MFMA stream); otherwise both are checked.
-    template <bool STEADY>
+    template <bool STEADY, bool FIRST = false>
     __device__ __forceinline__ static void iter(Blk &blk, int64_t t, int cur, int nxt_read,
                                                 u32x4 (&fa)[C::KSTEPS][C::TM], u32x4 (&fb)[C::KSTEPS][C::TN],
                                                 u32x4 (&na)[C::KSTEPS][C::TM], u32x4 (&nb)[C::KSTEPS][C::TN]) {
@@ -467,7 +507,8 @@ struct SwPipe {
 #pragma unroll
             for (int q = 0; q < NMFMA; ++q) {
                 const int s = q / (C::TM * C::TN), i = (q / C::TN) % C::TM, j = q % C::TN;
-                blk.acc.mma(i, j, fa[s][i], fb[s][j]);
+                if (FIRST && s == 0) blk.acc.template mma<true>(i, j, fa[s][i], fb[s][j]);
+                else blk.acc.template mma<false>(i, j, fa[s][i], fb[s][j]);
                 if (q < READS) blk.read_piece(nxt_read, q, na, nb);
                 if (q == NMFMA / 4 - 1 || q == 3 * NMFMA / 4 - 1) blk.dma_operand(tc, cur, q < NMFMA / 2 ? 0 : 1);
                 __builtin_amdgcn_sched_barrier(0);
@@ -481,7 +522,8 @@ struct SwPipe {
 #pragma unroll
             for (int q = 0; q < NMFMA; ++q) {
                 const int s = q / (C::TM * C::TN), i = (q / C::TN) % C::TM, j = q % C::TN;
-                blk.acc.mma(i, j, fa[s][i], fb[s][j]);
+                if (FIRST && s == 0) blk.acc.template mma<true>(i, j, fa[s][i], fb[s][j]);
+                else blk.acc.template mma<false>(i, j, fa[s][i], fb[s][j]);
             }
         }
     }
@@ -494,7 +536,10 @@ __device__ __forceinline__ void ring_tile_swpipe(const GemmParams &p, char *smem
     RingBlock<C, STAGES, SWZ, FRINGE> blk(p, smem, b, tm, tn);
     const int64_t nk = blk.nk, ndma = blk.ndma;
     if (nk > 0) {
-        if (ndma == 0) blk.tail_load();             // tile 0 is the last tile: landed just below
+        // With at most STAGES copied tiles the last tile is landed by the
+        // prologue or the first iteration: load it first, before any copy.
+        const bool early_tail = ndma <= STAGES;
+        if (early_tail) blk.tail_load();
 #pragma unroll
         for (int t = 0; t < STAGES; ++t)
             if (t < ndma) blk.dma(t, t);
@@ -506,111 +551,44 @@ __device__ __forceinline__ void ring_tile_swpipe(const GemmParams &p, char *smem
         u32x4 a0[C::KSTEPS][C::TM], b0[C::KSTEPS][C::TN], a1[C::KSTEPS][C::TM], b1[C::KSTEPS][C::TN];
 #pragma unroll
         for (int r = 0; r < SP::READS; ++r) blk.read_piece(0, r, a0, b0);
-        int cur = 0;
-        int64_t t = 0;
         auto adv = [](int x) { return x + 1 == STAGES ? 0 : x + 1; };
+        // tile 0, whose MFMAs start the accumulators; an iteration t is steady
+        // when tile t + STAGES is copied (t + STAGES < ndma)
+        if (STAGES < ndma) SP::template iter<true, true>(blk, 0, 0, 1, a0, b0, a1, b1);
+        else SP::template iter<false, true>(blk, 0, 0, adv(0), a0, b0, a1, b1);
+        int cur = adv(0);
+        int64_t t = 1;
         // steady state, two tiles per trip (the fragment buffers swap roles)
-        for (; t + STAGES + 1 < ndma; t += 2) {
+        for (; t + 1 + STAGES < ndma; t += 2) {
             const int c1 = adv(cur), c2 = adv(c1);
-            SP::template iter<true>(blk, t, cur, c1, a0, b0, a1, b1);
-            SP::template iter<true>(blk, t + 1, c1, c2, a1, b1, a0, b0);
+            SP::template iter<true>(blk, t, cur, c1, a1, b1, a0, b0);
+            SP::template iter<true>(blk, t + 1, c1, c2, a0, b0, a1, b1);
             cur = c2;
         }
-        // drain.  The last K tile (landed in the drain whenever there are copied
-        // tiles: the steady state lands tiles below ndma only) has its register
-        // loads issued here, not in the prologue, so their registers are not
-        // held through the steady state; they are younger than some copies,
-        // which only makes the vmcnt waits of those copies conservative (loads
-        // complete in issue order).
-        if (ndma > 0) blk.tail_load();
+        // drain.  With more than STAGES copied tiles the last K tile is landed
+        // here (a steady iteration t lands tile t + 1 < ndma), so its register
+        // loads are issued here rather than in the prologue and their
+        // registers are not held through the steady state; they are younger
+        // than some copies, which only makes the vmcnt waits of those copies
+        // conservative (loads complete in issue order).
+        if (!early_tail) blk.tail_load();
         for (; t + 1 < nk; t += 2) {
             const int c1 = adv(cur), c2 = adv(c1);
-            SP::template iter<false>(blk, t, cur, c1, a0, b0, a1, b1);
-            SP::template iter<false>(blk, t + 1, c1, c2, a1, b1, a0, b0);
+            SP::template iter<false>(blk, t, cur, c1, a1, b1, a0, b0);
+            SP::template iter<false>(blk, t + 1, c1, c2, a0, b0, a1, b1);
             cur = c2;
         }
-        if (t < nk) SP::template iter<false>(blk, t, cur, adv(cur), a0, b0, a1, b1);
+        if (t < nk) SP::template iter<false>(blk, t, cur, adv(cur), a1, b1, a0, b0);
+        blk.acc.settle();
     }
     store_tile_epilogue<C, FRINGE>(p, [&](int i, int j, int v) { return blk.acc.get(i, j, v); }, b, blk.m0, blk.n0,
                                    blk.wave, blk.lane);
 }
 
-// SCHED_PINGPONG (two waves per SIMD, 8 waves): waves 0-3 form group 0 and
-// waves 4-7 group 1, one wave of each per SIMD.  Each wave alternates a memory
-// phase (read the fragments of its next K tile from LDS into registers, issue
-// its share of the copies of tile t + STAGES - 1, wait for its share of tile
-// t + 1) and a compute phase (the MFMAs of the tile whose fragments it holds).
-// Group 1 runs one phase behind group 0, so on every SIMD one wave multiplies
-// while the other moves data, and the matrix core is fed across the LDS and
-// copy traffic.  Every phase ends in one workgroup barrier (2 per K tile):
-//   barrier 2t+1 closes group 0's memory phase of tile t (group 1 is then in
-//   its compute phase of tile t - 1), barrier 2t+2 closes group 0's compute
-//   phase of tile t and group 1's memory phase of tile t.
-// Tile t is read after barrier 2t (group 0) or 2t + 1 (group 1); every wave
-// lands its share of tile t before barrier 2t - 1 or 2t, so it is visible.
-// The copy of tile t + STAGES - 1 reuses tile t - 1's LDS copy, whose last
-// reader (group 1) finished before barrier 2t.
-template <class C, int STAGES, int SWZ, bool FRINGE>
-__device__ __forceinline__ void ring_tile_pingpong(const GemmParams &p, char *smem, int64_t b, int64_t tm, int64_t tn) {
-    static_assert(C::WAVES == 8, "two groups of four waves, one wave of each per SIMD");
-    static_assert(STAGES >= 2 && STAGES <= 4, "2 to 4 LDS copies");
-    constexpr int D = STAGES - 1;                  // copies run D tiles ahead of the tile being read
-    using Blk = RingBlock<C, STAGES, SWZ, FRINGE>;
-    Blk blk(p, smem, b, tm, tn);
-    const int64_t nk = blk.nk, ndma = blk.ndma;
-    const bool group1 = blk.wave >= 4;             // wave-uniform
-    auto adv = [](int x, int by) { return (x + by) % STAGES; };
-    if (nk > 0) {
-        blk.tail_load();
-#pragma unroll
-        for (int t = 0; t < D; ++t)
-            if (t < ndma) blk.dma(t, t);
-        blk.template land_tile<D - 1>(0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-        block_barrier();                            // barrier 0: tile 0 visible
-        if (group1) block_barrier();                // barrier 1: group 1 starts one phase late
-        __builtin_amdgcn_sched_barrier(0);
-        u32x4 fa[C::KSTEPS][C::TM], fb[C::KSTEPS][C::TN];
-        int cur = 0;                                // LDS copy holding tile t
-        for (int64_t t = 0; t < nk; ++t) {
-            // memory phase of tile t
-#pragma unroll
-            for (int r = 0; r < Blk::READS; ++r) blk.read_piece(cur, r, fa, fb);
-            if (t + D < ndma) blk.dma(t + D, adv(cur, D));
-            if (t + 1 < nk) blk.template land_tile<D - 1>(t + 1, adv(cur, 1));
-            wait_lds();
-            __builtin_amdgcn_sched_barrier(0);
-            block_barrier();
-            __builtin_amdgcn_sched_barrier(0);
-            // compute phase of tile t
-            __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-            for (int s = 0; s < C::KSTEPS; ++s)
-#pragma unroll
-                for (int i = 0; i < C::TM; ++i)
-#pragma unroll
-                    for (int j = 0; j < C::TN; ++j) blk.acc.mma(i, j, fa[s][i], fb[s][j]);
-            __builtin_amdgcn_s_setprio(0);
-            __builtin_amdgcn_sched_barrier(0);
-            block_barrier();
-            __builtin_amdgcn_sched_barrier(0);
-            cur = adv(cur, 1);
-        }
-        if (!group1) block_barrier();               // group 0's count matches group 1's late start
-    }
-    store_tile_epilogue<C, FRINGE>(p, [&](int i, int j, int v) { return blk.acc.get(i, j, v); }, b, blk.m0, blk.n0,
-                                   blk.wave, blk.lane);
-}
-
-template <class C, int STAGES, int SWZ, int SCHED>
-__global__ __launch_bounds__(C::THREADS, 1) void gemm_ring_kernel(GemmParams p) {
-    static_assert(STAGES >= 1 && STAGES <= 5, "1 to 5 LDS copies");
-    static_assert(SCHED == SCHED_RING || SCHED == SCHED_SWPIPE || SCHED == SCHED_PINGPONG, "schedule");
-    __shared__ __attribute__((aligned(1024))) char smem[STAGES * C::STAGE_BYTES];
-    int64_t b, tm, tn;
-    block_coords(p, b, tm, tn);
-    // This block's problem with its batch offsets folded into the pointers;
-    // for a split-K pass, its K slice, written unscaled to its fp32 partial.
+// The problem of grid batch entry b with its batch offsets folded into the
+// pointers; for a split-K pass, its K slice, written unscaled to its fp32
+// partial.
+__device__ __forceinline__ GemmParams entry_params(const GemmParams &p, int64_t b) {
     GemmParams q = p;
     if (p.splits > 1) {
         const int64_t s = b / p.problems, pb = b - s * p.problems;
@@ -627,17 +605,43 @@ __global__ __launch_bounds__(C::THREADS, 1) void gemm_ring_kernel(GemmParams p) 
         q.B = p.B + b * p.sB * 2;
         q.C = p.C + b * p.sC;
     }
-    const bool interior = (tm + 1) * C::BM <= p.M && (tn + 1) * C::BN <= p.N;
-    if constexpr (SCHED == SCHED_PINGPONG) {
-        if (interior) ring_tile_pingpong<C, STAGES, SWZ, false>(q, smem, 0, tm, tn);
-        else ring_tile_pingpong<C, STAGES, SWZ, true>(q, smem, 0, tm, tn);
-    } else if constexpr (SCHED == SCHED_SWPIPE) {
-        if (interior) ring_tile_swpipe<C, STAGES, SWZ, false>(q, smem, 0, tm, tn);
-        else ring_tile_swpipe<C, STAGES, SWZ, true>(q, smem, 0, tm, tn);
-    } else {
-        if (interior) ring_tile<C, STAGES, SWZ, false>(q, smem, 0, tm, tn);
-        else ring_tile<C, STAGES, SWZ, true>(q, smem, 0, tm, tn);
+    return q;
+}
+
+template <class C, int STAGES, int SWZ, int SCHED, bool FRINGE>
+__device__ __forceinline__ void run_tile(const GemmParams &q, char *smem, int64_t tm, int64_t tn) {
+    if constexpr (SCHED == SCHED_SWPIPE) ring_tile_swpipe<C, STAGES, SWZ, FRINGE>(q, smem, 0, tm, tn);
+    else ring_tile<C, STAGES, SWZ, FRINGE>(q, smem, 0, tm, tn);
+}
+
+template <class C, int STAGES, int SWZ, int SCHED>
+__global__ __launch_bounds__(C::THREADS, 1) void gemm_ring_kernel(GemmParams p) {
+    static_assert(STAGES >= 1 && STAGES <= 5, "1 to 5 LDS copies");
+    static_assert(SCHED == SCHED_RING || SCHED == SCHED_SWPIPE, "schedule");
+    __shared__ __attribute__((aligned(1024))) char smem[STAGES * C::STAGE_BYTES];
+    if constexpr (std::is_same<C, Ring256<C::DT>>::value) {
+        // thin fringe strips (Partition: a narrow block for a narrow remainder)
+        using SN = Strip256xN<C::DT>;
+        using SM = StripMx256<C::DT>;
+        static_assert(SN::THREADS == C::THREADS && SM::THREADS == C::THREADS, "one workgroup size");
+        static_assert(SN::STAGE_BYTES <= C::STAGE_BYTES && SM::STAGE_BYTES <= C::STAGE_BYTES, "LDS");
+        const int64_t main_blocks = p.tiles_m * p.tiles_n * p.batch;
+        if ((int64_t)blockIdx.x >= main_blocks) {
+            const int64_t per = p.strip_n + p.strip_m;
+            const int64_t s = (int64_t)blockIdx.x - main_blocks;
+            const int64_t b = s / per, r = s - b * per;
+            const GemmParams q = entry_params(p, b);
+            if (r < p.strip_n) run_tile<SN, STAGES, SWZ, SCHED, true>(q, smem, r, p.n_main / SN::BN);
+            else run_tile<SM, STAGES, SWZ, SCHED, true>(q, smem, p.m_main / SM::BM, r - p.strip_n);
+            return;
+        }
     }
+    int64_t b, tm, tn;
+    block_coords(p, b, tm, tn);
+    const GemmParams q = entry_params(p, b);
+    const bool interior = (tm + 1) * C::BM <= p.M && (tn + 1) * C::BN <= p.N;
+    if (interior) run_tile<C, STAGES, SWZ, SCHED, false>(q, smem, tm, tn);
+    else run_tile<C, STAGES, SWZ, SCHED, true>(q, smem, tm, tn);
 }
 
 }  // namespace tg

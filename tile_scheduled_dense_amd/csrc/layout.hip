@@ -139,8 +139,12 @@ void describe_ring_lds(tg_layout *L, int operand, int swz) {
             L->n_swizzle = 2;
             L->swizzle[1] = {4, 1, C::B_UNITS == 8 ? 7 : 6};
         }
-    } else {
+    } else if (!C::B_HALF_SWZ) {
         L->swizzle[0] = {5, 1, 2};                          // 64-byte unit ^= (k >> 1) & 1
+    } else {
+        L->swizzle[0] = {5, 1, 4};                          // 64-byte unit ^= (k >> 3) & 1
+        L->n_swizzle = 2;
+        L->swizzle[1] = {4, 1, 3};                          // 32-byte half ^= (k >> 1) & 1
     }
 }
 
@@ -247,6 +251,8 @@ tg_status tile_gemm_describe_layout(int config, int swizzle, int kind, tg_layout
     std::memset(out, 0, sizeof *out);
     switch (config) {
         case TG_CFG_256x256: return describe_ring<Ring256<DT_BF16>>(swizzle, kind, out);
+        case TG_LAYOUT_CFG_STRIP_N: return describe_ring<Strip256xN<DT_BF16>>(swizzle, kind, out);
+        case TG_LAYOUT_CFG_STRIP_M: return describe_ring<StripMx256<DT_BF16>>(swizzle, kind, out);
         case TG_CFG_128x128: return describe_ring<Ring128<DT_BF16>>(swizzle, kind, out);
         case TG_CFG_64x64: return describe_ring<Ring64<DT_BF16>>(swizzle, kind, out);
         case TG_CFG_F32_64x64: return describe<CfgF32>(swizzle, kind, out);
@@ -259,6 +265,8 @@ int64_t tile_gemm_lds_offset(int config, int swizzle, int operand, int64_t row, 
     if ((swizzle != SWZ_NONE && swizzle != SWZ_XOR) || (operand != 0 && operand != 1)) return -1;
     switch (config) {
         case TG_CFG_256x256: return ring_lds_offset<Ring256<DT_BF16>>(swizzle, operand, row, k);
+        case TG_LAYOUT_CFG_STRIP_N: return ring_lds_offset<Strip256xN<DT_BF16>>(swizzle, operand, row, k);
+        case TG_LAYOUT_CFG_STRIP_M: return ring_lds_offset<StripMx256<DT_BF16>>(swizzle, operand, row, k);
         case TG_CFG_128x128: return ring_lds_offset<Ring128<DT_BF16>>(swizzle, operand, row, k);
         case TG_CFG_64x64: return ring_lds_offset<Ring64<DT_BF16>>(swizzle, operand, row, k);
         case TG_CFG_F32_64x64: return lds_offset<CfgF32>(swizzle, operand, row, k);
@@ -269,6 +277,8 @@ int64_t tile_gemm_lds_offset(int config, int swizzle, int operand, int64_t row, 
 int tile_gemm_acc_coord(int config, int wave, int lane, int slot, int64_t *row, int64_t *col) {
     switch (config) {
         case TG_CFG_256x256: return acc_coord_checked<Ring256<DT_BF16>>(wave, lane, slot, row, col);
+        case TG_LAYOUT_CFG_STRIP_N: return acc_coord_checked<Strip256xN<DT_BF16>>(wave, lane, slot, row, col);
+        case TG_LAYOUT_CFG_STRIP_M: return acc_coord_checked<StripMx256<DT_BF16>>(wave, lane, slot, row, col);
         case TG_CFG_128x128: return acc_coord_checked<Ring128<DT_BF16>>(wave, lane, slot, row, col);
         case TG_CFG_64x64: return acc_coord_checked<Ring64<DT_BF16>>(wave, lane, slot, row, col);
         case TG_CFG_F32_64x64: return acc_coord_checked<CfgF32>(wave, lane, slot, row, col);

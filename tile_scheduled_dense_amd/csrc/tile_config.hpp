@@ -167,12 +167,16 @@ struct RingCfg {
     static_assert(B_TILE_BYTES % (1024 * WAVES) == 0 && B_DMA >= 1, "B copy split");
     static_assert(B_UNITS == 2 || B_UNITS == 4 || B_UNITS == 8, "B row of 2, 4 or 8 units");
     static_assert(A_DMA <= 4 && B_DMA <= 4, "a wave's copies of one operand span at most 4 KiB");
-    static_assert(MT_ == 32 || (MT_ == 16 && B_UNITS >= 4), "16x16x32 needs B rows of 4 or 8 units");
+
 };
 
-template <int DT> using Ring256 = RingCfg<DT, 256, 256, 2, 2>;   // 4 waves, wave tile 128 x 128
-template <int DT> using Ring256x8 = RingCfg<DT, 256, 256, 2, 4>; // 8 waves, wave tile 128 x 64
-template <int DT> using Ring256m16 = RingCfg<DT, 256, 256, 2, 2, 16>;   // 4 waves, 16x16x32 MFMA
+template <int DT> using Ring256 = RingCfg<DT, 256, 256, 2, 2, 16>;      // 4 waves, wave tile 128 x 128, 16x16x32
+template <int DT> using Ring256m32 = RingCfg<DT, 256, 256, 2, 2, 32>;   // the same with 32x32x16 MFMAs
+// Thin fringe strips of the 256 x 256 configuration (4 waves, wave tile 64 x 64):
+// a 256 x 64 block for a ragged N tail of at most 64 columns, a 64 x 256 block
+// for a ragged M tail of at most 64 rows.
+template <int DT> using Strip256xN = RingCfg<DT, 256, 64, 4, 1, 16>;
+template <int DT> using StripMx256 = RingCfg<DT, 64, 256, 1, 4, 16>;
 template <int DT> using Ring128 = RingCfg<DT, 128, 128, 2, 2>;   // 4 waves, wave tile 64 x 64
 template <int DT> using Ring64 = RingCfg<DT, 64, 64, 1, 2>;      // 2 waves, wave tile 64 x 32
 
@@ -195,16 +199,25 @@ TG_HD int ring_a_byte(int r, int c, int swz) {
 }
 
 // B tile: the XOR applied to the 64-byte unit index of k row k.
+//  * rows of 4 or 8 units: k & 3;
+//  * rows of 2 units (128 bytes, two rows per 256-byte bank line): (k >> 1) & 1
+//    for 32x32x16; (k >> 3) & 1 for 16x16x32, whose reads pair rows k and
+//    k + 8 (the half swizzle below then takes (k >> 1) & 1).
 template <class C>
 TG_HD int ring_b_mask(int k, int swz) {
     if (swz == SWZ_NONE) return 0;
-    return C::B_UNITS >= 4 ? (k & 3) : ((k >> 1) & 1);
+    if (C::B_UNITS >= 4) return k & 3;
+    return C::MT == 32 ? ((k >> 1) & 1) : ((k >> 3) & 1);
 }
 
-// B tile: the XOR applied to the 32-byte half of a 64-byte unit of k row k.
+// B tile: the XOR applied to the 32-byte half of a 64-byte unit of k row k
+// (16x16x32 only): with the unit XOR, the 16-column segments of the eight rows
+// one B read pairs (k0..k0+3 and k0+8..k0+11) land on eight distinct 32-byte
+// quarters of a bank line.
 template <class C>
 TG_HD int ring_b_half_mask(int k, int swz) {
-    return (C::B_HALF_SWZ && swz != SWZ_NONE) ? ((k >> 3) & 1) : 0;
+    if (!C::B_HALF_SWZ || swz == SWZ_NONE) return 0;
+    return C::B_UNITS >= 4 ? ((k >> 3) & 1) : ((k >> 1) & 1);
 }
 
 // B tile: byte offset of element (k, n).

@@ -53,16 +53,21 @@ tg_status current_device_ok() {
 }
 
 struct CfgDims {
-    int bm, bn, bk, waves, stage_bytes;
+    int bm, bn, bk, waves, stage_bytes, mfma_m, mfma_k;
 };
+
+template <class C>
+CfgDims dims_of(int mfma_k) {
+    return {C::BM, C::BN, C::BK, C::WAVES, C::STAGE_BYTES, C::MT, mfma_k};
+}
 
 CfgDims cfg_dims(int config) {
     switch (config) {
-        case TG_CFG_256x256: return {Ring256<DT_BF16>::BM, Ring256<DT_BF16>::BN, Ring256<DT_BF16>::BK, Ring256<DT_BF16>::WAVES, Ring256<DT_BF16>::STAGE_BYTES};
-        case TG_CFG_128x128: return {Ring128<DT_BF16>::BM, Ring128<DT_BF16>::BN, Ring128<DT_BF16>::BK, Ring128<DT_BF16>::WAVES, Ring128<DT_BF16>::STAGE_BYTES};
-        case TG_CFG_64x64: return {Ring64<DT_BF16>::BM, Ring64<DT_BF16>::BN, Ring64<DT_BF16>::BK, Ring64<DT_BF16>::WAVES, Ring64<DT_BF16>::STAGE_BYTES};
-        case TG_CFG_F32_64x64: return {CfgF32::BM, CfgF32::BN, CfgF32::BK, CfgF32::WAVES, CfgF32::STAGE_BYTES};
-        default: return {0, 0, 0, 0, 0};
+        case TG_CFG_256x256: return dims_of<Ring256<DT_BF16>>(Ring256<DT_BF16>::MK);
+        case TG_CFG_128x128: return dims_of<Ring128<DT_BF16>>(Ring128<DT_BF16>::MK);
+        case TG_CFG_64x64: return dims_of<Ring64<DT_BF16>>(Ring64<DT_BF16>::MK);
+        case TG_CFG_F32_64x64: return dims_of<CfgF32>(4);
+        default: return {0, 0, 0, 0, 0, 0, 0};
     }
 }
 
@@ -101,6 +106,7 @@ int64_t auto_splits(int64_t tiles, int64_t K) {
 
 struct Plan {
     tg_plan_info info;
+    int64_t strip_n = 0, strip_m = 0;  // strip blocks per problem (256 x 64, 64 x 256)
     int64_t wanted_workspace = 0;      // bytes the split it would like needs
     void *workspace = nullptr;         // set when the call splits
     int64_t workspace_given = 0;
@@ -168,10 +174,30 @@ tg_status make_plan(int64_t batch, int64_t M, int64_t N, int64_t K, tg_dtype dty
     p.block_order = order;
     p.tiles_m = cdiv(M, d.bm);
     p.tiles_n = cdiv(N, d.bn);
-    p.grid = p.tiles_m * p.tiles_n * batch;
-    const int64_t full_m = M / d.bm, full_n = N / d.bn;
+    // Partition of a thin remainder: with the 256 x 256 tile, an N tail of at
+    // most 64 columns goes to 256 x 64 strip blocks (one per tile row) and an
+    // M tail of at most 64 rows to 64 x 256 strip blocks (one per tile column,
+    // plus the corner), instead of a column or row of mostly empty tiles.
+    int64_t strip_n = 0, strip_m = 0;
+    if (config == TG_CFG_256x256 && M >= 256 && N >= 256) {
+        const bool thin_n = N % 256 != 0 && N % 256 <= 64;
+        const bool thin_m = M % 256 != 0 && M % 256 <= 64;
+        if (thin_n) p.tiles_n = N / 256;
+        if (thin_m) p.tiles_m = M / 256;
+        strip_n = thin_n ? p.tiles_m : 0;
+        strip_m = thin_m ? p.tiles_n + (thin_n ? 1 : 0) : 0;
+    }
+    out.strip_n = strip_n;
+    out.strip_m = strip_m;
+    p.strip_blocks = strip_n + strip_m;
+    p.grid = (p.tiles_m * p.tiles_n + p.strip_blocks) * batch;
+    const int64_t full_m = M / d.bm < p.tiles_m ? M / d.bm : p.tiles_m;
+    const int64_t full_n = N / d.bn < p.tiles_n ? N / d.bn : p.tiles_n;
     p.interior_blocks = full_m * full_n;
     p.fringe_blocks = p.tiles_m * p.tiles_n - p.interior_blocks;
+    p.mfma_m = d.mfma_m;
+    p.mfma_n = d.mfma_m;
+    p.mfma_k = d.mfma_k;
     p.k_tiles = cdiv(K, d.bk);
     p.k_tail = K % d.bk;
     p.lds_bytes = depth * d.stage_bytes;
@@ -364,6 +390,10 @@ tg_status run(int64_t batch, int64_t M, int64_t N, int64_t K, tg_dtype dtype,
     gp.problems = batch;
     gp.k_slice = plan.info.k_slice;
     gp.W = static_cast<float *>(plan.workspace);
+    gp.strip_n = plan.strip_n;
+    gp.strip_m = plan.strip_m;
+    gp.n_main = plan.info.tiles_n * plan.info.block_n;
+    gp.m_main = plan.info.tiles_m * plan.info.block_m;
     if (split) gp.batch = batch * plan.info.split_k;   // (slice, problem) pairs
     hipStream_t s = static_cast<hipStream_t>(stream);
     switch (dtype) {
