@@ -227,9 +227,11 @@ __device__ __forceinline__ void mfma_chunk(const u32x4 &a, const u32x4 &b, f32x4
 
 // ---- fused alpha/beta store-back -----------------------------------------------
 // C = fma(alpha, acc, beta * C0), or alpha * acc when beta == 0 (C0 not read);
-// masks (fringe blocks only) sit here, on the accumulator transfer.  For each
-// MFMA tile the C0 values are all loaded before any store, so the loads are in
-// flight together instead of each waiting behind the previous store.
+// masks (fringe blocks only) sit here, on the accumulator transfer.
+// C0 and C are the same array, so the compiler may not move a C0 load above
+// an earlier store; the MFMA tiles are therefore taken in chunks of 64 values
+// per lane whose C0 loads are all issued before any of the chunk's stores:
+// one memory round trip per chunk instead of one per MFMA tile.
 // `acc(i, j, v)` is value v of MFMA tile (i, j) of this lane.
 template <class C, bool FRINGE, class AccFn>
 __device__ __forceinline__ void store_tile_epilogue(const GemmParams &p, const AccFn &acc, int64_t b,
@@ -238,31 +240,44 @@ __device__ __forceinline__ void store_tile_epilogue(const GemmParams &p, const A
     const int ldc = (int)p.ldc;
     const float alpha = p.alpha, beta = p.beta;
     const int64_t M = p.M, N = p.N;
+    constexpr int V = C::ACC_PER_MFMA;
+    constexpr int TILES = C::TM * C::TN;
+    constexpr int CH = 64 / V < TILES ? 64 / V : TILES;       // MFMA tiles per chunk
+    static_assert(TILES % CH == 0, "whole chunks");
 #pragma unroll
-    for (int i = 0; i < C::TM; ++i) {
+    for (int c0t = 0; c0t < TILES; c0t += CH) {
+        int off[CH][V];
+        bool ok[CH][V];
 #pragma unroll
-        for (int j = 0; j < C::TN; ++j) {
-            int off[C::ACC_PER_MFMA];
-            bool ok[C::ACC_PER_MFMA];
+        for (int t = 0; t < CH; ++t)
 #pragma unroll
-            for (int v = 0; v < C::ACC_PER_MFMA; ++v) {
+            for (int v = 0; v < V; ++v) {
                 int row, col;
-                acc_coord<C>(wave, lane, (i * C::TN + j) * C::ACC_PER_MFMA + v, row, col);
-                off[v] = row * ldc + col;
-                ok[v] = !FRINGE || (m0 + row < M && n0 + col < N);
+                acc_coord<C>(wave, lane, (c0t + t) * V + v, row, col);
+                off[t][v] = row * ldc + col;
+                ok[t][v] = !FRINGE || (m0 + row < M && n0 + col < N);
             }
-            if (beta != 0.0f) {
-                float c0[C::ACC_PER_MFMA];
+        if (beta != 0.0f) {
+            float cv[CH][V];
 #pragma unroll
-                for (int v = 0; v < C::ACC_PER_MFMA; ++v) c0[v] = ok[v] ? Cblk[off[v]] : 0.0f;
+            for (int t = 0; t < CH; ++t)
 #pragma unroll
-                for (int v = 0; v < C::ACC_PER_MFMA; ++v)
-                    if (ok[v]) Cblk[off[v]] = __builtin_fmaf(alpha, acc(i, j, v), beta * c0[v]);
-            } else {
+                for (int v = 0; v < V; ++v) cv[t][v] = ok[t][v] ? Cblk[off[t][v]] : 0.0f;
 #pragma unroll
-                for (int v = 0; v < C::ACC_PER_MFMA; ++v)
-                    if (ok[v]) Cblk[off[v]] = alpha * acc(i, j, v);
-            }
+            for (int t = 0; t < CH; ++t)
+#pragma unroll
+                for (int v = 0; v < V; ++v) {
+                    const int i = (c0t + t) / C::TN, j = (c0t + t) % C::TN;
+                    if (ok[t][v]) Cblk[off[t][v]] = __builtin_fmaf(alpha, acc(i, j, v), beta * cv[t][v]);
+                }
+        } else {
+#pragma unroll
+            for (int t = 0; t < CH; ++t)
+#pragma unroll
+                for (int v = 0; v < V; ++v) {
+                    const int i = (c0t + t) / C::TN, j = (c0t + t) % C::TN;
+                    if (ok[t][v]) Cblk[off[t][v]] = alpha * acc(i, j, v);
+                }
         }
     }
 }
