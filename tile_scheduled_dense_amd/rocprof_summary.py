@@ -2,6 +2,7 @@
 bench.py reports.
 
   python -m tile_scheduled_dense_amd.rocprof_summary trace  <kernel_stats.csv> <out.txt> <command...>
+  python -m tile_scheduled_dense_amd.rocprof_summary timed  <kernel_stats.csv> <kernel_trace.csv> <K> <out.txt> <command...>
   python -m tile_scheduled_dense_amd.rocprof_summary counters <fetch_dir> <write_dir> <copy_mib> <out.txt> <command...>
   python -m tile_scheduled_dense_amd.rocprof_summary sq <sq_dir> <trace_kernel_stats.csv> <out.txt> <command...>
 
@@ -11,6 +12,10 @@ dispatch) of a command that also ran a plain device copy of `copy_mib` MiB
 that copy, whose true traffic is known (copy_mib read and copy_mib written).
 The summary records a hash of the kernel sources; bench.py reports the traffic
 only while the sources still match.
+
+`timed` is `trace` plus the mean duration of the last K dispatches of the GEMM
+kernel (the K timed steps of a bench.py run, after its warm-up), the figure to
+set beside bench.py's own HIP-event time per launch.
 
 `sq` averages the SQ/GRBM counters of one --pmc run over the GEMM dispatches
 and derives the shader clock (GRBM_GUI_ACTIVE counts cycles on each of the 8
@@ -151,9 +156,28 @@ def summarize_trace(stats_csv):
     return out
 
 
+def timed_average_ns(trace_csv, k):
+    """Mean duration of the last k dispatches of the GEMM kernel (in dispatch order)."""
+    rows = [r for r in _rows(trace_csv) if GEMM_KERNEL_TAG in r["Kernel_Name"]]
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    last = rows[-k:]
+    return sum(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in last) / len(last), len(rows)
+
+
 def main(argv):
     mode = argv[1]
-    if mode == "trace":
+    if mode == "timed":
+        stats, trace, k, out, cmd = argv[2], argv[3], int(argv[4]), argv[5], " ".join(argv[6:])
+        kv = {}
+        for name, d in summarize_trace(stats).items():
+            short = name if len(name) < 120 else name[:117] + "..."
+            kv[short] = (f"calls={d['calls']} average_us={d['average_ns'] / 1e3:.2f} "
+                         f"min_us={d['min_ns'] / 1e3:.2f} max_us={d['max_ns'] / 1e3:.2f} pct={d['percentage']:.2f}")
+        avg, n = timed_average_ns(trace, k)
+        kv[f"gemm_timed_average_us (last {k} of {n} GEMM dispatches)"] = f"{avg / 1e3:.2f}"
+        kv["kernel_source_sha256"] = kernel_source_hash()
+        write_kv(out, "rocprofv3 --kernel-trace --stats summary", cmd, kv)
+    elif mode == "trace":
         stats, out, cmd = argv[2], argv[3], " ".join(argv[4:])
         kv = {}
         for name, d in summarize_trace(stats).items():
