@@ -219,8 +219,22 @@ struct RingBlock {
     uint64_t a_base, b_base;    // Ablk, Bblk as workgroup-uniform integers
     uint32_t lds0;              // LDS address of smem
     int64_t b_step;             // bytes of B per K tile
+    i32x4 rsa, rsb;             // interior blocks: resources of the next K tile to copy
+    uint32_t a_rd[C::KSTEPS];           // LDS address of this lane's A fragment of row tile 0, copy 0
+    uint32_t b_rd[C::KSTEPS][C::TN];    // ... of its B fragment (first read) of column tile j, copy 0
     u32x4 tail[C::COPIES];
     AccTiles<C> acc;
+
+    // LDS: the STAGES copies of the B tile, then the STAGES copies of the A
+    // tile, so a fragment read of a known copy is a fixed base register plus an
+    // offset that fits the 16-bit immediate of a DS instruction.  B goes first:
+    // its reads need one base register per MFMA column tile (the swizzle XOR
+    // depends on it), A's a single one, which then absorbs the region offset.
+    static constexpr int A_REGION = STAGES * C::B_TILE_BYTES;
+    static constexpr int a_tile(int stage) { return A_REGION + stage * C::A_TILE_BYTES; }
+    static constexpr int b_tile(int stage) { return stage * C::B_TILE_BYTES; }
+    static_assert((STAGES - 1) * C::A_TILE_BYTES + C::A_TILE_BYTES <= 65536 &&
+                  (STAGES - 1) * C::B_TILE_BYTES + 4 * C::B_ROW_BYTES < 65536, "DS immediate offsets");
 
     __device__ __forceinline__ RingBlock(const GemmParams &p_, char *smem_, int64_t b_, int64_t tm, int64_t tn)
         : p(p_), smem(smem_), b(b_) {
@@ -241,6 +255,28 @@ struct RingBlock {
         b_base = uniform_u64((uint64_t)Bblk);
         lds0 = lds_address(smem);
         b_step = (int64_t)C::BK * p.ldb * E;
+        rsa = rsrc_words_u(a_base - A_SHIFT, 0x7fffffff);
+        rsb = rsrc_words_u(b_base - B_SHIFT, 0x7fffffff);
+        // Fragment read addresses: every read is one of these plus a constant
+        // (the LDS copy, the row / column tile, the second half of a B read).
+        // The empty asm keeps the compiler from splitting a base back into a
+        // constant part, which would not fit the 16-bit DS offset.
+        {
+            const int wrow = (wave / C::WAVES_N) * C::WTM;
+            const int wcol = (wave % C::WAVES_N) * C::WTN;
+#pragma unroll
+            for (int s = 0; s < C::KSTEPS; ++s) {
+                a_rd[s] = lds0 + a_tile(0) + ring_a_byte<C>(a_frag_row(wrow, 0), a_frag_chunk(s), SWZ);
+                asm("" : "+v"(a_rd[s]));
+#pragma unroll
+                for (int j = 0; j < C::TN; ++j) {
+                    int k, n;
+                    b_frag_src(wcol, j, s, 0, k, n);
+                    b_rd[s][j] = lds0 + b_tile(0) + ring_b_byte<C>(k, n, SWZ);
+                    asm("" : "+v"(b_rd[s][j]));
+                }
+            }
+        }
         acc.zero();
 #pragma unroll
         for (int d = 0; d < C::A_DMA; ++d) {
@@ -256,20 +292,38 @@ struct RingBlock {
         }
     }
 
-    // this wave's copies of one operand (0 = A, 1 = B) of K tile kt into LDS copy `stage`
+    // 64-bit add to the base address held in the first two resource words
+    __device__ __forceinline__ static void advance(i32x4 &rs, uint64_t bytes) {
+        const uint64_t a = (((uint64_t)(uint32_t)rs.y << 32) | (uint32_t)rs.x) + bytes;
+        rs.x = (int)(uint32_t)a;
+        rs.y = (int)(uint32_t)(a >> 32);
+    }
+
+    // this wave's copies of one operand (0 = A, 1 = B) of K tile kt into LDS copy `stage`.
+    // Every schedule copies the K tiles in increasing order, each once.
     __device__ __forceinline__ void dma_operand(int64_t kt, int stage, int operand) {
-        const uint32_t sA = lds0 + stage * C::STAGE_BYTES;
         // An interior block's copied tiles lie wholly inside A and B, so its
-        // resources need no size limit beyond the 31-bit offsets; a fringe
-        // block's limit ends at the last valid element (past it reads as 0).
+        // resources need no size limit beyond the 31-bit offsets and are
+        // advanced by one K tile per copy; a fringe block's limit ends at the
+        // last valid element (past it reads as 0).
         if (operand == 0) {
-            const int64_t adv = kt * (C::BK * E);
-            copy_group_to_lds<C::A_DMA>(rsrc_words_u(a_base + adv - A_SHIFT, FRINGE ? a_valid - adv + A_SHIFT : 0x7fffffff),
-                                        sA + ring_block<C>(0, wave, C::A_DMA) * 1024, a_voff);
+            const uint32_t dst = lds0 + a_tile(stage) + ring_block<C>(0, wave, C::A_DMA) * 1024;
+            if (FRINGE) {
+                const int64_t adv = kt * (C::BK * E);
+                copy_group_to_lds<C::A_DMA>(rsrc_words_u(a_base + adv - A_SHIFT, a_valid - adv + A_SHIFT), dst, a_voff);
+            } else {
+                copy_group_to_lds<C::A_DMA>(rsa, dst, a_voff);
+                advance(rsa, C::BK * E);
+            }
         } else {
-            const int64_t adv = kt * b_step;
-            copy_group_to_lds<C::B_DMA>(rsrc_words_u(b_base + adv - B_SHIFT, FRINGE ? b_valid - adv + B_SHIFT : 0x7fffffff),
-                                        sA + C::A_TILE_BYTES + ring_block<C>(0, wave, C::B_DMA) * 1024, b_voff);
+            const uint32_t dst = lds0 + b_tile(stage) + ring_block<C>(0, wave, C::B_DMA) * 1024;
+            if (FRINGE) {
+                const int64_t adv = kt * b_step;
+                copy_group_to_lds<C::B_DMA>(rsrc_words_u(b_base + adv - B_SHIFT, b_valid - adv + B_SHIFT), dst, b_voff);
+            } else {
+                copy_group_to_lds<C::B_DMA>(rsb, dst, b_voff);
+                advance(rsb, (uint64_t)b_step);
+            }
         }
     }
 
@@ -300,8 +354,8 @@ struct RingBlock {
         }
     }
     __device__ __forceinline__ void tail_store(int stage) {
-        char *sA = smem + stage * C::STAGE_BYTES;
-        char *sB = sA + C::A_TILE_BYTES;
+        char *sA = smem + a_tile(stage);
+        char *sB = smem + b_tile(stage);
 #pragma unroll
         for (int d = 0; d < C::A_DMA; ++d)
             *(u32x4 *)(sA + ring_block<C>(d, wave, C::A_DMA) * 1024 + 16 * lane) = tail[d];
@@ -328,24 +382,27 @@ struct RingBlock {
         wait_lds();
     }
 
+    // A fragment of row tile i, K step s, from LDS copy `stage`: row tile i
+    // lies i * MT rows on (the swizzle XOR is the same for it), so its address
+    // is a_rd[s] plus a constant
+    __device__ __forceinline__ u32x4 read_a(int stage, int s, int i) const {
+        const uint32_t addr = a_rd[s] + stage * C::A_TILE_BYTES + i * C::MT * C::A_ROW_BYTES;
+        return *(const __attribute__((address_space(3))) u32x4 *)(uintptr_t)addr;
+    }
+    // one of the two transposing B reads (half: 4 k rows on, the same XOR)
+    __device__ __forceinline__ u32x2 read_b(int stage, int s, int j, int half) const {
+        const uint32_t addr = b_rd[s][j] + stage * C::B_TILE_BYTES + half * 4 * C::B_ROW_BYTES;
+        const v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16 *)(uintptr_t)addr);
+        return __builtin_bit_cast(u32x2, v);
+    }
+
     // fragments of K step s of LDS copy `stage`
     __device__ __forceinline__ void read_frags(int stage, int s, u32x4 (&af)[C::TM], u32x4 (&bfr)[C::TN]) const {
-        const char *sA = smem + stage * C::STAGE_BYTES;
-        const char *sB = sA + C::A_TILE_BYTES;
-        const int wrow = (wave / C::WAVES_N) * C::WTM;
-        const int wcol = (wave % C::WAVES_N) * C::WTN;
 #pragma unroll
-        for (int i = 0; i < C::TM; ++i)
-            af[i] = *(const u32x4 *)(sA + ring_a_byte<C>(a_frag_row(wrow, i), a_frag_chunk(s), SWZ));
+        for (int i = 0; i < C::TM; ++i) af[i] = read_a(stage, s, i);
 #pragma unroll
         for (int j = 0; j < C::TN; ++j) {
-            int k, n;
-            b_frag_src(wcol, j, s, 0, k, n);
-            const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) v4i16 *)(sB + ring_b_byte<C>(k, n, SWZ)));
-            const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) v4i16 *)(sB + ring_b_byte<C>(k + 4, n, SWZ)));
-            const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+            const u32x2 l2 = read_b(stage, s, j, 0), h2 = read_b(stage, s, j, 1);
             bfr[j] = u32x4{l2.x, l2.y, h2.x, h2.y};
         }
     }
@@ -375,22 +432,14 @@ struct RingBlock {
     static constexpr int READS = C::KSTEPS * (C::TM + 2 * C::TN);
     __device__ __forceinline__ void read_piece(int stage, int r, u32x4 (&af)[C::KSTEPS][C::TM],
                                                u32x4 (&bfr)[C::KSTEPS][C::TN]) const {
-        const char *sA = smem + stage * C::STAGE_BYTES;
-        const char *sB = sA + C::A_TILE_BYTES;
-        const int wrow = (wave / C::WAVES_N) * C::WTM;
-        const int wcol = (wave % C::WAVES_N) * C::WTN;
         constexpr int NA = C::KSTEPS * C::TM;
         if (r < NA) {
             const int s = r / C::TM, i = r % C::TM;
-            af[s][i] = *(const u32x4 *)(sA + ring_a_byte<C>(a_frag_row(wrow, i), a_frag_chunk(s), SWZ));
+            af[s][i] = read_a(stage, s, i);
         } else {
             const int q = r - NA;
             const int s = q / (2 * C::TN), j = (q / 2) % C::TN, half = q % 2;
-            int k, n;
-            b_frag_src(wcol, j, s, half, k, n);
-            const v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) v4i16 *)(sB + ring_b_byte<C>(k, n, SWZ)));
-            const u32x2 w2 = __builtin_bit_cast(u32x2, v);
+            const u32x2 w2 = read_b(stage, s, j, half);
             if (half == 0) {
                 bfr[s][j].x = w2.x;
                 bfr[s][j].y = w2.y;
@@ -556,15 +605,18 @@ __device__ __forceinline__ void ring_tile_swpipe(const GemmParams &p, char *smem
         // when tile t + STAGES is copied (t + STAGES < ndma)
         if (STAGES < ndma) SP::template iter<true, true>(blk, 0, 0, 1, a0, b0, a1, b1);
         else SP::template iter<false, true>(blk, 0, 0, adv(0), a0, b0, a1, b1);
-        int cur = adv(0);
         int64_t t = 1;
-        // steady state, two tiles per trip (the fragment buffers swap roles)
-        for (; t + 1 + STAGES < ndma; t += 2) {
-            const int c1 = adv(cur), c2 = adv(c1);
-            SP::template iter<true>(blk, t, cur, c1, a1, b1, a0, b0);
-            SP::template iter<true>(blk, t + 1, c1, c2, a0, b0, a1, b1);
-            cur = c2;
+        // steady state, four tiles per trip: tile t sits in LDS copy t % STAGES
+        // (STAGES is 2 or 4) and the fragment buffers swap roles every tile, so
+        // every copy index below is a constant
+        static_assert(4 % STAGES == 0, "four tiles per trip cycle the LDS copies");
+        for (; t + 3 + STAGES < ndma; t += 4) {
+            SP::template iter<true>(blk, t, 1 % STAGES, 2 % STAGES, a1, b1, a0, b0);
+            SP::template iter<true>(blk, t + 1, 2 % STAGES, 3 % STAGES, a0, b0, a1, b1);
+            SP::template iter<true>(blk, t + 2, 3 % STAGES, 4 % STAGES, a1, b1, a0, b0);
+            SP::template iter<true>(blk, t + 3, 4 % STAGES, 5 % STAGES, a0, b0, a1, b1);
         }
+        int cur = (int)(t % STAGES);
         // drain.  With more than STAGES copied tiles the last K tile is landed
         // here (a steady iteration t lands tile t + 1 < ndma), so its register
         // loads are issued here rather than in the prologue and their
