@@ -667,7 +667,7 @@ __device__ __forceinline__ void run_tile(const GemmParams &q, char *smem, int64_
 }
 
 template <class C, int STAGES, int SWZ, int SCHED>
-__global__ __launch_bounds__(C::THREADS, 1) void gemm_ring_kernel(GemmParams p) {
+__global__ __launch_bounds__(C::THREADS, C::OCCUPANCY) void gemm_ring_kernel(GemmParams p) {
     static_assert(STAGES >= 1 && STAGES <= 5, "1 to 5 LDS copies");
     static_assert(SCHED == SCHED_RING || SCHED == SCHED_SWPIPE, "schedule");
     __shared__ __attribute__((aligned(1024))) char smem[STAGES * C::STAGE_BYTES];
