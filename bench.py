@@ -41,6 +41,8 @@ def parse():
     ap.add_argument("--block-order", type=int, default=0)
     ap.add_argument("--split-k", type=int, default=0,
                     help="K slices (0 = automatic with the workspace the library asks for, 1 = off)")
+    ap.add_argument("--pack-a", type=int, default=0,
+                    help="repack misaligned A rows into the workspace (0 = automatic, 1 = never, 2 = always)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after timing, run a plain device copy of this many MiB (3 times) so HBM "
                          "byte counters can be scaled against a kernel of known traffic")
@@ -100,8 +102,9 @@ def main():
     C = to_dev(p.C0.copy()) if p.beta != 0 else torch.zeros(p.sizeC(), dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
     opts = dict(config=args.config, pipeline_depth=args.pipeline_depth, swizzle=args.swizzle,
-                block_order=args.block_order, split_k=args.split_k)
-    # split-K workspace: allocated once, outside the timed region, as a caller would
+                block_order=args.block_order, split_k=args.split_k, pack_a=args.pack_a, plan_lda=p.lda)
+    # workspace (split-K partials or the aligned copy of A): allocated once, outside
+    # the timed region, as a caller would
     ws_bytes = tg.tile_gemm_workspace_size(p.batch, p.M, p.N, p.K, p.dtype, **opts)
     if ws_bytes:
         opts["workspace"] = torch.empty(ws_bytes // 4, dtype=torch.float32, device="cuda")
@@ -175,6 +178,7 @@ def main():
                    "inputs": f"{p.dist} seed {p.seed}", "accumulate": "fp32", "output": "fp32",
                    "tile": f"{plan['block_m']}x{plan['block_n']}x{plan['block_k']}",
                    "pipeline_depth": plan["pipeline_depth"], "split_k": plan["split_k"],
+                   "pack_a": plan["pack_a"],
                    "grid": plan["grid"]},
         "roofline": roofline,
         "cpu_baseline": cpu,

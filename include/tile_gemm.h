@@ -114,6 +114,21 @@ typedef enum {
  *   split_k == 1: never split;
  *   split_k >= 2: at most split_k slices (fewer when K is short); the call
  *                 fails with TG_ERR_INVALID_ARG if the workspace is too small.
+ * Repack of A (16-bit inputs, TG_CFG_256x256, no split): when A's rows do not
+ * start on 16-byte boundaries (lda not a multiple of 8, or A itself not
+ * 16-byte aligned), every 16-byte copy of an A tile straddles cache lines.  A
+ * first kernel then copies A into `workspace` with rows of roundup(K, 8)
+ * elements (batch entries packed, zero past K), and the GEMM reads that copy;
+ * the values and the MFMA sequence are unchanged, so the result is bitwise the
+ * unpacked one.
+ *   pack_a == 0: automatic -- repack when the rows are misaligned, the plan
+ *                has at least 8 tile columns (each A panel is read by that many
+ *                workgroups), and `workspace` holds the copy;
+ *   pack_a == 1: never;  pack_a == 2: always (TG_ERR_INVALID_ARG without the
+ *                workspace; TG_ERR_UNSUPPORTED for another configuration).
+ * plan_lda is the lda that tile_gemm_plan and tile_gemm_workspace_size assume
+ * (0: a multiple of 8); tile_gemm_ex uses its own lda and A.
+ *
  * The workspace is caller-owned device memory, 16-byte aligned, that must not
  * overlap A, B or C; its contents on entry do not matter and are undefined
  * afterwards.  Calls that share one workspace must be ordered (e.g. on one
@@ -126,8 +141,11 @@ typedef struct {
     int swizzle;         /* 0 = default (XOR); 1 = none (row-major tile); 2 = XOR   */
     int block_order;     /* 0 = default (XCD-grouped); 1 = plain row-major          */
     int split_k;         /* 0 = automatic, 1 = off, S >= 2 = at most S K slices      */
-    void *workspace;     /* device memory for split-K partials, or NULL             */
+    void *workspace;     /* device memory for split-K partials or the A copy, or NULL */
     int64_t workspace_bytes;
+    int pack_a;          /* 0 = automatic, 1 = never, 2 = always (see above)        */
+    int pad0_;
+    int64_t plan_lda;    /* lda assumed by the plan queries (0: a multiple of 8)    */
 } tg_options;
 
 /* tile_gemm_strided_batched with explicit schedule knobs (opt may be NULL).
@@ -156,9 +174,9 @@ typedef struct {
     int lds_bytes;                /* LDS per workgroup, all pipeline copies        */
     int split_k;                  /* K slices S (1: no split)                      */
     int64_t k_slice;              /* K elements per slice (the last may be shorter)*/
-    int64_t workspace_bytes;      /* workspace the call uses: S * batch * M * N * 4 */
+    int64_t workspace_bytes;      /* workspace the call uses: S * batch * M * N * 4, or the A copy */
     int mfma_m, mfma_n, mfma_k;   /* MFMA instruction shape: 32x32x16, 16x16x32 or 16x16x4 */
-    int pad0_;
+    int pack_a;                   /* 1: A is first copied to aligned rows in the workspace */
     int64_t strip_blocks;         /* thin fringe-strip blocks per problem (in grid) */
 } tg_plan_info;
 

@@ -190,3 +190,32 @@ def test_plan_thin_strips(M, N, strips):
     assert info["grid"] == 3 * (info["tiles_m"] * info["tiles_n"] + info["strip_blocks"])
     # other configurations have no strips
     assert tg.tile_gemm_plan(1, M, N, 512, "bf16", config=tg.TG_CFG_128x128)["strip_blocks"] == 0
+
+
+def test_plan_pack_a():
+    big = dict(workspace=1 << 40, workspace_bytes=1 << 40)
+    args = (1, 8191, 8193, 8190, "bf16")
+    ldp_bytes = -(-8191 * 8192 * 2 // 256) * 256
+    # misaligned rows, many tile columns, workspace: repack
+    p = tg.tile_gemm_plan(*args, plan_lda=8193, **big)
+    assert p["pack_a"] == 1 and p["workspace_bytes"] == ldp_bytes and p["split_k"] == 1
+    assert tg.tile_gemm_workspace_size(*args, plan_lda=8193) == ldp_bytes
+    # aligned rows (lda a multiple of 8, or unknown): no repack, no workspace wanted
+    assert tg.tile_gemm_plan(*args, plan_lda=8192, **big)["pack_a"] == 0
+    assert tg.tile_gemm_workspace_size(*args, plan_lda=8192) == 0
+    assert tg.tile_gemm_workspace_size(*args) == 0
+    # too small a workspace: the plain plan, but the size it wants is reported
+    p = tg.tile_gemm_plan(*args, plan_lda=8193, workspace=1 << 20, workspace_bytes=ldp_bytes - 256)
+    assert p["pack_a"] == 0
+    # never, and few tile columns (each A panel read by few workgroups)
+    assert tg.tile_gemm_plan(*args, plan_lda=8193, pack_a=1, **big)["pack_a"] == 0
+    assert tg.tile_gemm_plan(1, 8191, 1000, 8190, "bf16", plan_lda=8193, **big)["pack_a"] == 0
+    # forced: only for the 16-bit 256 x 256 configuration without a split
+    assert tg.tile_gemm_plan(1, 100, 100, 100, "bf16", config=tg.TG_CFG_256x256, pack_a=2)["pack_a"] == 1
+    for kw in (dict(config=tg.TG_CFG_128x128), dict(config=tg.TG_CFG_256x256, split_k=4)):
+        with pytest.raises(tg.TileGemmError):
+            tg.tile_gemm_plan(1, 512, 512, 4096, "bf16", pack_a=2, **kw)
+    with pytest.raises(tg.TileGemmError):
+        tg.tile_gemm_plan(1, 64, 64, 64, "f32", pack_a=2)
+    with pytest.raises(tg.TileGemmError):
+        tg.tile_gemm_plan(*args, pack_a=3)

@@ -9,6 +9,7 @@
 #include <new>
 
 #include "gemm_ring.hpp"
+#include "pack.hpp"
 #include "splitk.hpp"
 #include "tile_gemm.h"
 
@@ -107,13 +108,18 @@ int64_t auto_splits(int64_t tiles, int64_t K) {
 struct Plan {
     tg_plan_info info;
     int64_t strip_n = 0, strip_m = 0;  // strip blocks per problem (256 x 64, 64 x 256)
-    int64_t wanted_workspace = 0;      // bytes the split it would like needs
-    void *workspace = nullptr;         // set when the call splits
+    int64_t wanted_workspace = 0;      // bytes the split or the A copy it would like needs
+    void *workspace = nullptr;         // set when the call splits or repacks A
     int64_t workspace_given = 0;
+    int64_t lda_packed = 0;            // row stride of the A copy (elements)
 };
 
+inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+
+// lda: the call's (or, for the plan queries, the assumed) leading dimension of
+// A; a_aligned: A itself starts on a 16-byte boundary.
 tg_status make_plan(int64_t batch, int64_t M, int64_t N, int64_t K, tg_dtype dtype,
-                    const tg_options *opt, Plan &out) {
+                    const tg_options *opt, int64_t lda, bool a_aligned, Plan &out) {
     if (batch < 0 || M < 0 || N < 0 || K < 0) return TG_ERR_INVALID_ARG;
     if (dtype != TG_F32 && dtype != TG_BF16 && dtype != TG_F16) return TG_ERR_INVALID_ARG;
     tg_options o{};
@@ -214,6 +220,26 @@ tg_status make_plan(int64_t batch, int64_t M, int64_t N, int64_t K, tg_dtype dty
     if (splits > 1) p.grid *= splits;
     out.workspace = splits > 1 ? o.workspace : nullptr;
     out.workspace_given = o.workspace_bytes;
+
+    // Repack of A (see tile_gemm.h): rows not on 16-byte boundaries, a plan
+    // whose A panels are each read by many workgroups, no split.
+    if (o.pack_a < 0 || o.pack_a > 2) return TG_ERR_INVALID_ARG;
+    if (o.pack_a == 2 && (!sixteen || config != TG_CFG_256x256 || splits > 1)) return TG_ERR_UNSUPPORTED;
+    if (sixteen && some && config == TG_CFG_256x256 && splits == 1 && o.pack_a != 1) {
+        const int64_t ldp = round_up(K, 8);
+        const int64_t bytes_a = round_up(batch * M * ldp * 2, 256);
+        const bool misaligned = lda % 8 != 0 || !a_aligned;
+        const bool worth = misaligned && p.tiles_n >= 8;
+        if (o.pack_a == 2 || worth) {
+            out.wanted_workspace = out.wanted_workspace > bytes_a ? out.wanted_workspace : bytes_a;
+            if (o.pack_a == 2 || (o.workspace && o.workspace_bytes >= bytes_a)) {
+                p.pack_a = 1;
+                p.workspace_bytes = bytes_a;
+                out.lda_packed = ldp;
+                out.workspace = o.workspace;
+            }
+        }
+    }
     return TG_OK;
 }
 
@@ -345,13 +371,14 @@ tg_status run(int64_t batch, int64_t M, int64_t N, int64_t K, tg_dtype dtype,
     tg_status st = validate(batch, M, N, K, dtype, A, lda, sA, B, ldb, sB, C, ldc, sC);
     if (st != TG_OK) return st;
     Plan plan;
-    st = make_plan(batch, M, N, K, dtype, opt, plan);
+    st = make_plan(batch, M, N, K, dtype, opt, lda, reinterpret_cast<uintptr_t>(A) % 16 == 0, plan);
     if (st != TG_OK) return st;
     if (batch == 0 || M == 0 || N == 0) return TG_OK;
     if (!offsets_fit(plan.info, K, lda, ldb, ldc, dtype == TG_F32 ? 4 : 2)) return TG_ERR_UNSUPPORTED;
     const bool split = plan.info.split_k > 1;
-    if (split) {
-        // a forced split needs the workspace; an automatic one only happens with it
+    const bool pack = plan.info.pack_a != 0;
+    if (split || pack) {
+        // a forced split or repack needs the workspace; an automatic one only happens with it
         if (!plan.workspace || plan.workspace_given < plan.info.workspace_bytes ||
             reinterpret_cast<uintptr_t>(plan.workspace) % 16)
             return TG_ERR_INVALID_ARG;
@@ -361,7 +388,9 @@ tg_status run(int64_t batch, int64_t M, int64_t N, int64_t K, tg_dtype dtype,
         if (overlaps(rw, span(A, batch, M, K, lda, sA, esz)) || overlaps(rw, span(B, batch, K, N, ldb, sB, esz)) ||
             overlaps(rw, span(C, batch, M, N, ldc, sC, 4)))
             return TG_ERR_INVALID_ARG;
-        if (!offsets_fit(plan.info, plan.info.k_slice, lda, ldb, N, esz)) return TG_ERR_UNSUPPORTED;
+        if (split && !offsets_fit(plan.info, plan.info.k_slice, lda, ldb, N, esz)) return TG_ERR_UNSUPPORTED;
+        if (pack && (!offsets_fit(plan.info, K, plan.lda_packed, ldb, ldc, esz) || batch * M > 0x7fffffffLL))
+            return TG_ERR_UNSUPPORTED;
     }
     st = current_device_ok();
     if (st != TG_OK) return st;
@@ -396,6 +425,17 @@ tg_status run(int64_t batch, int64_t M, int64_t N, int64_t K, tg_dtype dtype,
     gp.m_main = plan.info.tiles_m * plan.info.block_m;
     if (split) gp.batch = batch * plan.info.split_k;   // (slice, problem) pairs
     hipStream_t s = static_cast<hipStream_t>(stream);
+    if (pack) {
+        // A -> aligned rows of lda_packed elements in the workspace, then the GEMM on that copy
+        hipLaunchKernelGGL(pack_rows_kernel, dim3((unsigned)(batch * M)), dim3(256), 0, s,
+                           static_cast<const char *>(A), lda, sA, static_cast<char *>(plan.workspace),
+                           plan.lda_packed, M, K);
+        if (hipGetLastError() != hipSuccess) return TG_ERR_LAUNCH;
+        gp.A = static_cast<const char *>(plan.workspace);
+        gp.lda = plan.lda_packed;
+        gp.sA = M * plan.lda_packed;
+        gp.W = nullptr;
+    }
     switch (dtype) {
         case TG_BF16: st = launch_dtype<DT_BF16>(gp, plan.info, s); break;
         case TG_F16: st = launch_dtype<DT_F16>(gp, plan.info, s); break;
@@ -445,7 +485,8 @@ tg_status tile_gemm_plan(int64_t batch, int64_t M, int64_t N, int64_t K, tg_dtyp
     if (!out) return TG_ERR_INVALID_ARG;
     try {
         Plan p;
-        tg_status st = make_plan(batch, M, N, K, dtype, opt, p);
+        tg_status st = make_plan(batch, M, N, K, dtype, opt, opt && opt->struct_size >= (int)sizeof(tg_options) &&
+                                 opt->plan_lda > 0 ? opt->plan_lda : 8, true, p);
         if (st == TG_OK) *out = p.info;
         return st;
     } catch (...) {
@@ -458,7 +499,8 @@ tg_status tile_gemm_workspace_size(int64_t batch, int64_t M, int64_t N, int64_t 
     if (!bytes) return TG_ERR_INVALID_ARG;
     try {
         Plan p;
-        tg_status st = make_plan(batch, M, N, K, dtype, opt, p);
+        tg_status st = make_plan(batch, M, N, K, dtype, opt, opt && opt->struct_size >= (int)sizeof(tg_options) &&
+                                 opt->plan_lda > 0 ? opt->plan_lda : 8, true, p);
         if (st == TG_OK) *bytes = p.wanted_workspace;
         return st;
     } catch (...) {
