@@ -181,7 +181,10 @@ def test_lds_budget():
     (1025, 1025, dict(tiles_m=4, tiles_n=4, strip_blocks=4 + 5)),    # both, the corner in the M strip
     (1088, 1088, dict(tiles_m=4, tiles_n=4, strip_blocks=9)),        # tails of exactly 64
     (1089, 1089, dict(tiles_m=5, tiles_n=5, strip_blocks=0)),        # tails of 65: whole tiles
-    (300, 200, dict(tiles_m=2, tiles_n=1, strip_blocks=0)),          # N < 256: no main grid to strip
+    (300, 200, dict(tiles_m=1, tiles_n=1, strip_blocks=1)),          # M tail of 44 beside one tile, N < 256
+    (257, 129, dict(tiles_m=1, tiles_n=1, strip_blocks=1)),          # M strip beside a 256-row tile, N < 256
+    (129, 257, dict(tiles_m=1, tiles_n=1, strip_blocks=1)),          # N strip beside a 256-column tile
+    (200, 200, dict(tiles_m=1, tiles_n=1, strip_blocks=0)),          # no main tile to put a strip beside
 ])
 def test_plan_thin_strips(M, N, strips):
     info = tg.tile_gemm_plan(3, M, N, 512, "bf16", config=tg.TG_CFG_256x256)

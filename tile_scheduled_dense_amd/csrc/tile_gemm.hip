@@ -159,7 +159,12 @@ tg_status make_plan(int64_t batch, int64_t M, int64_t N, int64_t K, tg_dtype dty
     // pipeline depth = LDS copies of the K tile (window = depth - 1)
     const bool f32 = config == TG_CFG_F32_64x64;
     const int depth = o.pipeline_depth ? o.pipeline_depth : (f32 ? 2 : 4);
-    if (f32 ? (depth != 1 && depth != 2) : (depth != 1 && depth != 2 && depth != 4)) return TG_ERR_UNSUPPORTED;
+    // depth 5 (a window of 4 tiles) for the smaller 16-bit tiles, whose two
+    // workgroups per CU still fit 160 KiB of LDS; the 256 x 256 tile's software
+    // pipeline cycles its copies four at a time
+    const bool depth_ok = f32 ? (depth == 1 || depth == 2)
+                              : (depth == 1 || depth == 2 || depth == 4 || (depth == 5 && config != TG_CFG_256x256));
+    if (!depth_ok) return TG_ERR_UNSUPPORTED;
     const int swz = o.swizzle ? o.swizzle : SWZ_XOR;
     if (swz != SWZ_NONE && swz != SWZ_XOR) return TG_ERR_UNSUPPORTED;
     if (!f32 && swz == SWZ_NONE && depth != 4) return TG_ERR_UNSUPPORTED;   // ablation built at depth 4 only
@@ -185,9 +190,10 @@ tg_status make_plan(int64_t batch, int64_t M, int64_t N, int64_t K, tg_dtype dty
     // M tail of at most 64 rows to 64 x 256 strip blocks (one per tile column,
     // plus the corner), instead of a column or row of mostly empty tiles.
     int64_t strip_n = 0, strip_m = 0;
-    if (config == TG_CFG_256x256 && M >= 256 && N >= 256) {
-        const bool thin_n = N % 256 != 0 && N % 256 <= 64;
-        const bool thin_m = M % 256 != 0 && M % 256 <= 64;
+    if (config == TG_CFG_256x256) {
+        // a strip needs a main tile beside it: N >= 256 for an N strip, M >= 256 for an M strip
+        const bool thin_n = N >= 256 && N % 256 != 0 && N % 256 <= 64;
+        const bool thin_m = M >= 256 && M % 256 != 0 && M % 256 <= 64;
         if (thin_n) p.tiles_n = N / 256;
         if (thin_m) p.tiles_m = M / 256;
         strip_n = thin_n ? p.tiles_m : 0;
@@ -323,6 +329,9 @@ tg_status launch_ring(const GemmParams &gp, const tg_plan_info &p, hipStream_t s
     constexpr int SCHED = SWPIPE ? SCHED_SWPIPE : SCHED_RING;
     if (p.swizzle == SWZ_XOR) {
         switch (p.pipeline_depth) {
+            case 5:
+                if constexpr (!SWPIPE) return launch_ring_one<C, 5, SWZ_XOR, SCHED>(gp, p.grid, s);
+                return TG_ERR_UNSUPPORTED;
             case 4: return launch_ring_one<C, 4, SWZ_XOR, SCHED>(gp, p.grid, s);
             case 2: return launch_ring_one<C, 2, SWZ_XOR, SCHED>(gp, p.grid, s);
             case 1: return launch_ring_one<C, 1, SWZ_XOR, SCHED_RING>(gp, p.grid, s);
