@@ -43,6 +43,8 @@ def parse():
                     help="K slices (0 = automatic with the workspace the library asks for, 1 = off)")
     ap.add_argument("--pack-a", type=int, default=0,
                     help="repack misaligned A rows into the workspace (0 = automatic, 1 = never, 2 = always)")
+    ap.add_argument("--tail-gemm", type=int, default=0,
+                    help="thin N/M remainder as a GEMM of its own (0, 1 = strips in the grid, 2 = always)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after timing, run a plain device copy of this many MiB (3 times) so HBM "
                          "byte counters can be scaled against a kernel of known traffic")
@@ -102,8 +104,9 @@ def main():
     C = to_dev(p.C0.copy()) if p.beta != 0 else torch.zeros(p.sizeC(), dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
     opts = dict(config=args.config, pipeline_depth=args.pipeline_depth, swizzle=args.swizzle,
-                block_order=args.block_order, split_k=args.split_k, pack_a=args.pack_a, plan_lda=p.lda)
-    # workspace (split-K partials or the aligned copy of A): allocated once, outside
+                block_order=args.block_order, split_k=args.split_k, pack_a=args.pack_a, plan_lda=p.lda,
+                tail_gemm=args.tail_gemm)
+    # workspace (split-K partials, the aligned copy of A, remainder partials): allocated once, outside
     # the timed region, as a caller would
     ws_bytes = tg.tile_gemm_workspace_size(p.batch, p.M, p.N, p.K, p.dtype, **opts)
     if ws_bytes:
@@ -178,7 +181,8 @@ def main():
                    "inputs": f"{p.dist} seed {p.seed}", "accumulate": "fp32", "output": "fp32",
                    "tile": f"{plan['block_m']}x{plan['block_n']}x{plan['block_k']}",
                    "pipeline_depth": plan["pipeline_depth"], "split_k": plan["split_k"],
-                   "pack_a": plan["pack_a"],
+                   "pack_a": plan["pack_a"], "strip_blocks": plan["strip_blocks"],
+                   "tail_n_splits": plan["tail_n_splits"], "tail_m_splits": plan["tail_m_splits"],
                    "grid": plan["grid"]},
         "roofline": roofline,
         "cpu_baseline": cpu,

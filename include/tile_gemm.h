@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define TILE_GEMM_ABI_VERSION 3
+#define TILE_GEMM_ABI_VERSION 4
 
 typedef enum { TG_F32 = 0, TG_BF16 = 1, TG_F16 = 2 } tg_dtype;
 
@@ -128,6 +128,19 @@ typedef enum {
  *                workspace; TG_ERR_UNSUPPORTED for another configuration).
  * plan_lda is the lda that tile_gemm_plan and tile_gemm_workspace_size assume
  * (0: a multiple of 8); tile_gemm_ex uses its own lda and A.
+ * Thin remainders (TG_CFG_256x256): an N tail of at most 64 columns (N >= 256)
+ * and an M tail of at most 64 rows (M >= 256) are fringe partitions of their
+ * own (OCANNL "Module Ir.Schedule": index-set splitting of a block loop at
+ * its last full tile, the Partition of a padded loop).  By default they run
+ * as narrow strip blocks in the main grid.  On request the remainder is
+ * computed instead by a second GEMM on TG_CFG_64x64: C[:, n0:N] from
+ * A . B[:, n0:N] over all M rows for the N tail, C[m0:M, 0:n1] from
+ * A[m0:M, :] . B[:, 0:n1] for the M tail (n1 = N, or n0 when the N tail has
+ * its own GEMM), split along K as above when the workspace also holds its
+ * partials (after the A copy, N tail first).  The value is the same
+ * contraction; the tail's k sum may be regrouped by its split.
+ *   tail_gemm == 0 or 1: strips in the grid;
+ *   tail_gemm == 2: the remainder GEMMs whenever there is a thin remainder.
  *
  * The workspace is caller-owned device memory, 16-byte aligned, that must not
  * overlap A, B or C; its contents on entry do not matter and are undefined
@@ -146,6 +159,8 @@ typedef struct {
     int pack_a;          /* 0 = automatic, 1 = never, 2 = always (see above)        */
     int pad0_;
     int64_t plan_lda;    /* lda assumed by the plan queries (0: a multiple of 8)    */
+    int tail_gemm;       /* 0, 1 = strips; 2 = thin remainders as GEMMs (see above)  */
+    int pad1_;
 } tg_options;
 
 /* tile_gemm_strided_batched with explicit schedule knobs (opt may be NULL).
@@ -174,10 +189,13 @@ typedef struct {
     int lds_bytes;                /* LDS per workgroup, all pipeline copies        */
     int split_k;                  /* K slices S (1: no split)                      */
     int64_t k_slice;              /* K elements per slice (the last may be shorter)*/
-    int64_t workspace_bytes;      /* workspace the call uses: S * batch * M * N * 4, or the A copy */
+    int64_t workspace_bytes;      /* workspace the call uses: S * batch * M * N * 4, or the A copy
+                                     plus the remainder GEMMs' partials                  */
     int mfma_m, mfma_n, mfma_k;   /* MFMA instruction shape: 32x32x16, 16x16x32 or 16x16x4 */
     int pack_a;                   /* 1: A is first copied to aligned rows in the workspace */
     int64_t strip_blocks;         /* thin fringe-strip blocks per problem (in grid) */
+    int tail_n_splits;            /* 0: no N-remainder GEMM; S >= 1: one, with S K slices */
+    int tail_m_splits;            /* the same for the M remainder                  */
 } tg_plan_info;
 
 tg_status tile_gemm_plan(int64_t batch, int64_t M, int64_t N, int64_t K, tg_dtype dtype,

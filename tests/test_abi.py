@@ -28,7 +28,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert tg.abi_version() == 3
+    assert tg.abi_version() == 4
     for s in range(5):
         assert tg.STATUS_NAMES[s] in tg.status_string(s)
 
@@ -106,7 +106,7 @@ def test_options_validation():
     # N = 32 * 256 + 1: the one-column tail goes to 32 strip blocks of 256 x 64
     ((1, 8191, 8193, 8190, "bf16"), dict(config=tg.TG_CFG_256x256, tiles_m=32, tiles_n=32, grid=1024 + 32,
                                          interior_blocks=31 * 32, fringe_blocks=32, strip_blocks=32,
-                                         k_tiles=256, k_tail=30)),
+                                         tail_n_splits=0, tail_m_splits=0, k_tiles=256, k_tail=30)),
     ((512, 257, 129, 1000, "f16"), dict(tiles_m=5, tiles_n=3, interior_blocks=8, fringe_blocks=7,
                                         grid=15 * 512, k_tiles=32, k_tail=8, lds_bytes=4 * 8192,
                                         mfma_m=32, mfma_k=16, strip_blocks=0)),
@@ -196,19 +196,21 @@ def test_plan_thin_strips(M, N, strips):
 
 
 def test_plan_pack_a():
-    big = dict(workspace=1 << 40, workspace_bytes=1 << 40)
+    # the remainder column of this shape is kept in the grid here (tail_gemm=1): the
+    # A copy alone; test_plan_tail_gemm covers the two together
+    big = dict(workspace=1 << 40, workspace_bytes=1 << 40, tail_gemm=1)
     args = (1, 8191, 8193, 8190, "bf16")
     ldp_bytes = -(-8191 * 8192 * 2 // 256) * 256
     # misaligned rows, many tile columns, workspace: repack
     p = tg.tile_gemm_plan(*args, plan_lda=8193, **big)
     assert p["pack_a"] == 1 and p["workspace_bytes"] == ldp_bytes and p["split_k"] == 1
-    assert tg.tile_gemm_workspace_size(*args, plan_lda=8193) == ldp_bytes
+    assert tg.tile_gemm_workspace_size(*args, plan_lda=8193, tail_gemm=1) == ldp_bytes
     # aligned rows (lda a multiple of 8, or unknown): no repack, no workspace wanted
     assert tg.tile_gemm_plan(*args, plan_lda=8192, **big)["pack_a"] == 0
-    assert tg.tile_gemm_workspace_size(*args, plan_lda=8192) == 0
-    assert tg.tile_gemm_workspace_size(*args) == 0
+    assert tg.tile_gemm_workspace_size(*args, plan_lda=8192, tail_gemm=1) == 0
+    assert tg.tile_gemm_workspace_size(*args, tail_gemm=1) == 0
     # too small a workspace: the plain plan, but the size it wants is reported
-    p = tg.tile_gemm_plan(*args, plan_lda=8193, workspace=1 << 20, workspace_bytes=ldp_bytes - 256)
+    p = tg.tile_gemm_plan(*args, plan_lda=8193, workspace=1 << 20, workspace_bytes=ldp_bytes - 256, tail_gemm=1)
     assert p["pack_a"] == 0
     # never, and few tile columns (each A panel read by few workgroups)
     assert tg.tile_gemm_plan(*args, plan_lda=8193, pack_a=1, **big)["pack_a"] == 0
@@ -222,3 +224,39 @@ def test_plan_pack_a():
         tg.tile_gemm_plan(1, 64, 64, 64, "f32", pack_a=2)
     with pytest.raises(tg.TileGemmError):
         tg.tile_gemm_plan(*args, pack_a=3)
+
+
+def test_plan_tail_gemm():
+    """A thin remainder as a GEMM of its own, on request (tail_gemm=2)."""
+    args = (1, 8191, 8193, 8190, "bf16")
+    big = dict(workspace=1 << 40, workspace_bytes=1 << 40)
+    tail_bytes = 8 * 8191 * 1 * 4 + 32            # 8 K slices of an 8191 x 1 partial, rounded to 256
+    # by default (0) and never (1): 32 strip blocks after the 1024 main tiles, no workspace
+    for t in (0, 1):
+        p = tg.tile_gemm_plan(*args, tail_gemm=t, **big)
+        assert (p["strip_blocks"], p["tail_n_splits"], p["tail_m_splits"], p["grid"]) == (32, 0, 0, 1056)
+        assert tg.tile_gemm_workspace_size(*args, tail_gemm=t) == 0
+    # forced: 8 K slices of the one-column GEMM (about 1024 workgroups of 64 x 64)
+    p = tg.tile_gemm_plan(*args, tail_gemm=2, **big)
+    assert (p["strip_blocks"], p["tail_n_splits"], p["tail_m_splits"], p["grid"]) == (0, 8, 0, 1024)
+    assert p["workspace_bytes"] == tail_bytes
+    assert tg.tile_gemm_workspace_size(*args, tail_gemm=2) == tail_bytes
+    # with the A copy: the copy first, the partials after it
+    ldp_bytes = -(-8191 * 8192 * 2 // 256) * 256
+    p = tg.tile_gemm_plan(*args, plan_lda=8193, tail_gemm=2, **big)
+    assert p["pack_a"] == 1 and p["tail_n_splits"] == 8 and p["workspace_bytes"] == ldp_bytes + tail_bytes
+    assert tg.tile_gemm_workspace_size(*args, plan_lda=8193, tail_gemm=2) == ldp_bytes + tail_bytes
+    # no workspace for the partials: the remainder GEMM is not split
+    p = tg.tile_gemm_plan(*args, tail_gemm=2)
+    assert (p["strip_blocks"], p["tail_n_splits"], p["workspace_bytes"]) == (0, 1, 0)
+    # both remainders, short K (no split), batches
+    p = tg.tile_gemm_plan(2, 300, 257, 100, "bf16", config=tg.TG_CFG_256x256, tail_gemm=2)
+    assert (p["strip_blocks"], p["tail_n_splits"], p["tail_m_splits"], p["grid"]) == (0, 1, 1, 2)
+    # an M remainder (8193 rows), K deep enough for 8 slices of 1024
+    p = tg.tile_gemm_plan(1, 8193, 8192, 8192, "bf16", tail_gemm=2, **big)
+    assert (p["strip_blocks"], p["tail_n_splits"], p["tail_m_splits"]) == (0, 0, 8)
+    # no thin remainder: nothing to do
+    p = tg.tile_gemm_plan(1, 8192, 8192, 8192, "bf16", tail_gemm=2, **big)
+    assert (p["strip_blocks"], p["tail_n_splits"], p["tail_m_splits"]) == (0, 0, 0)
+    with pytest.raises(tg.TileGemmError):
+        tg.tile_gemm_plan(*args, tail_gemm=3)

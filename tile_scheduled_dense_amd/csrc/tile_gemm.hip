@@ -74,17 +74,39 @@ CfgDims cfg_dims(int config) {
 
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Default choice: the largest tile that still gives the chip (256 CUs) at
-// least about one workgroup per CU; fp32 has one configuration.
-// The largest tile that still gives about one workgroup per CU (240 of 256)
-// and pads the output by at most a quarter more than the next smaller tile
-// (a 257 x 129 problem pads to 512 x 256 in 256-wide tiles, 384 x 256 in
-// 128-wide ones: a third more).
+// The 256 x 256 partition of one M x N problem: main tile rows and columns,
+// and the thin-remainder strips beside them (an N tail of at most 64 columns
+// goes to 256 x 64 strip blocks, one per tile row; an M tail of at most 64
+// rows to 64 x 256 strip blocks, one per tile column plus the corner) instead
+// of a column or row of mostly empty tiles.  A strip needs a main tile beside
+// it: N >= 256 for an N strip, M >= 256 for an M strip.
+struct Partition256 {
+    int64_t tiles_m, tiles_n, strip_n, strip_m;
+    int64_t area() const { return (tiles_m * tiles_n * 256 + (strip_n + strip_m) * 64) * 256; }
+};
+
+Partition256 partition256(int64_t M, int64_t N) {
+    const bool thin_n = N >= 256 && N % 256 != 0 && N % 256 <= 64;
+    const bool thin_m = M >= 256 && M % 256 != 0 && M % 256 <= 64;
+    Partition256 q;
+    q.tiles_m = thin_m ? M / 256 : cdiv(M, 256);
+    q.tiles_n = thin_n ? N / 256 : cdiv(N, 256);
+    q.strip_n = thin_n ? q.tiles_m : 0;
+    q.strip_m = thin_m ? q.tiles_n + (thin_n ? 1 : 0) : 0;
+    return q;
+}
+
+// Default choice (fp32 has one configuration): the largest tile that still
+// gives about one workgroup per CU (240 of the 256) and pads the output by at
+// most a quarter more than the next smaller tile.  The 256-wide padding counts
+// its strips: a 257 x 129 problem covers 256 x 256 plus a 64 x 256 strip, 5/6
+// of the 384 x 256 it pads to in 128-wide tiles.
 int choose_config(int64_t batch, int64_t M, int64_t N, tg_dtype dtype) {
     if (dtype == TG_F32) return TG_CFG_F32_64x64;
-    const int64_t big = cdiv(M, 256) * cdiv(N, 256) * batch;
+    const Partition256 q = partition256(M, N);
+    const int64_t big = (q.tiles_m * q.tiles_n + q.strip_n + q.strip_m) * batch;
     const int64_t mid = cdiv(M, 128) * cdiv(N, 128) * batch;
-    const int64_t area_big = big * 256 * 256, area_mid = mid * 128 * 128;
+    const int64_t area_big = q.area() * batch, area_mid = mid * 128 * 128;
     if (big >= 240 && 4 * area_big <= 5 * area_mid) return TG_CFG_256x256;
     if (mid >= 240) return TG_CFG_128x128;
     if (big >= 240) return TG_CFG_256x256;
@@ -105,9 +127,18 @@ int64_t auto_splits(int64_t tiles, int64_t K) {
     return s;
 }
 
+// A thin remainder computed by a GEMM of its own (see tile_gemm.h): its
+// extents, where it starts in C, and its K split and workspace region.
+struct Tail {
+    int64_t splits = 0;                // 0: none
+    int64_t m0 = 0, n0 = 0, rows = 0, cols = 0;
+    int64_t ws_offset = 0, ws_bytes = 0;
+};
+
 struct Plan {
     tg_plan_info info;
     int64_t strip_n = 0, strip_m = 0;  // strip blocks per problem (256 x 64, 64 x 256)
+    Tail tail_n, tail_m;
     int64_t wanted_workspace = 0;      // bytes the split or the A copy it would like needs
     void *workspace = nullptr;         // set when the call splits or repacks A
     int64_t workspace_given = 0;
@@ -185,19 +216,14 @@ tg_status make_plan(int64_t batch, int64_t M, int64_t N, int64_t K, tg_dtype dty
     p.block_order = order;
     p.tiles_m = cdiv(M, d.bm);
     p.tiles_n = cdiv(N, d.bn);
-    // Partition of a thin remainder: with the 256 x 256 tile, an N tail of at
-    // most 64 columns goes to 256 x 64 strip blocks (one per tile row) and an
-    // M tail of at most 64 rows to 64 x 256 strip blocks (one per tile column,
-    // plus the corner), instead of a column or row of mostly empty tiles.
+    // Partition of a thin remainder into strips (partition256)
     int64_t strip_n = 0, strip_m = 0;
     if (config == TG_CFG_256x256) {
-        // a strip needs a main tile beside it: N >= 256 for an N strip, M >= 256 for an M strip
-        const bool thin_n = N >= 256 && N % 256 != 0 && N % 256 <= 64;
-        const bool thin_m = M >= 256 && M % 256 != 0 && M % 256 <= 64;
-        if (thin_n) p.tiles_n = N / 256;
-        if (thin_m) p.tiles_m = M / 256;
-        strip_n = thin_n ? p.tiles_m : 0;
-        strip_m = thin_m ? p.tiles_n + (thin_n ? 1 : 0) : 0;
+        const Partition256 q = partition256(M, N);
+        p.tiles_m = q.tiles_m;
+        p.tiles_n = q.tiles_n;
+        strip_n = q.strip_n;
+        strip_m = q.strip_m;
     }
     out.strip_n = strip_n;
     out.strip_m = strip_m;
@@ -231,17 +257,66 @@ tg_status make_plan(int64_t batch, int64_t M, int64_t N, int64_t K, tg_dtype dty
     // whose A panels are each read by many workgroups, no split.
     if (o.pack_a < 0 || o.pack_a > 2) return TG_ERR_INVALID_ARG;
     if (o.pack_a == 2 && (!sixteen || config != TG_CFG_256x256 || splits > 1)) return TG_ERR_UNSUPPORTED;
+    int64_t used = 0;         // workspace bytes taken so far by the A copy
+    int64_t wanted_pack = 0;  // bytes of the A copy the plan would like
     if (sixteen && some && config == TG_CFG_256x256 && splits == 1 && o.pack_a != 1) {
         const int64_t ldp = round_up(K, 8);
         const int64_t bytes_a = round_up(batch * M * ldp * 2, 256);
         const bool misaligned = lda % 8 != 0 || !a_aligned;
         const bool worth = misaligned && p.tiles_n >= 8;
         if (o.pack_a == 2 || worth) {
+            wanted_pack = bytes_a;
             out.wanted_workspace = out.wanted_workspace > bytes_a ? out.wanted_workspace : bytes_a;
             if (o.pack_a == 2 || (o.workspace && o.workspace_bytes >= bytes_a)) {
                 p.pack_a = 1;
                 p.workspace_bytes = bytes_a;
                 out.lda_packed = ldp;
+                out.workspace = o.workspace;
+                used = bytes_a;
+            }
+        }
+    }
+
+    // Thin remainders as GEMMs of their own (tile_gemm.h), when asked: each
+    // tail is split along K until it has about 1024 workgroups of the 64 x 64
+    // tile (four per CU), slices of at least 512, if the workspace past the A
+    // copy holds the partials.  Not chosen automatically: on 8191 x 8193 x
+    // 8190 the 32 strips that follow the 1024 main tiles cost the grid about
+    // 8 us, the separate GEMM and its combine about 33 us.
+    if (o.tail_gemm < 0 || o.tail_gemm > 2) return TG_ERR_INVALID_ARG;
+    if (some && strip_n + strip_m > 0 && splits == 1) {
+        if (o.tail_gemm == 2) {
+            const int64_t n_main = p.tiles_n * d.bn, m_main = p.tiles_m * d.bm;
+            int64_t wanted_tail = wanted_pack;
+            auto set_tail = [&](Tail &t, int64_t m0, int64_t n0, int64_t rows, int64_t cols) {
+                t.m0 = m0;
+                t.n0 = n0;
+                t.rows = rows;
+                t.cols = cols;
+                const int64_t tiles = cdiv(rows, 64) * cdiv(cols, 64) * batch;
+                int64_t sp = 1;
+                while (2 * sp <= 16 && tiles * 2 * sp <= 1024 && K / (2 * sp) >= 512) sp *= 2;
+                const int64_t bytes = sp > 1 ? round_up(sp * batch * rows * cols * 4, 256) : 0;
+                wanted_tail += bytes;
+                if (sp > 1 && o.workspace && o.workspace_bytes >= used + bytes) {
+                    t.splits = sp;
+                    t.ws_offset = used;
+                    t.ws_bytes = bytes;
+                    used += bytes;
+                } else {
+                    t.splits = 1;
+                }
+            };
+            if (strip_n) set_tail(out.tail_n, 0, n_main, M, N - n_main);
+            if (strip_m) set_tail(out.tail_m, m_main, 0, M - m_main, strip_n ? n_main : N);
+            out.wanted_workspace = out.wanted_workspace > wanted_tail ? out.wanted_workspace : wanted_tail;
+            p.tail_n_splits = (int)out.tail_n.splits;
+            p.tail_m_splits = (int)out.tail_m.splits;
+            out.strip_n = out.strip_m = 0;
+            p.grid -= p.strip_blocks * batch;
+            p.strip_blocks = 0;
+            if (used > 0) {
+                p.workspace_bytes = used;
                 out.workspace = o.workspace;
             }
         }
@@ -386,7 +461,8 @@ tg_status run(int64_t batch, int64_t M, int64_t N, int64_t K, tg_dtype dtype,
     if (!offsets_fit(plan.info, K, lda, ldb, ldc, dtype == TG_F32 ? 4 : 2)) return TG_ERR_UNSUPPORTED;
     const bool split = plan.info.split_k > 1;
     const bool pack = plan.info.pack_a != 0;
-    if (split || pack) {
+    const bool tail_ws = plan.tail_n.ws_bytes > 0 || plan.tail_m.ws_bytes > 0;
+    if (split || pack || tail_ws) {
         // a forced split or repack needs the workspace; an automatic one only happens with it
         if (!plan.workspace || plan.workspace_given < plan.info.workspace_bytes ||
             reinterpret_cast<uintptr_t>(plan.workspace) % 16)
@@ -453,8 +529,24 @@ tg_status run(int64_t batch, int64_t M, int64_t N, int64_t K, tg_dtype dtype,
             return launch_variants<CfgF32>(gp, plan.info, s);
         default: return TG_ERR_INVALID_ARG;
     }
-    if (st != TG_OK || !split) return st;
-    return launch_combine(gp.W, C, M, N, ldc, sC, batch, plan.info.split_k, alpha, beta, s);
+    if (st != TG_OK) return st;
+    if (split) return launch_combine(gp.W, C, M, N, ldc, sC, batch, plan.info.split_k, alpha, beta, s);
+    // the thin remainders' own GEMMs (on the A copy when there is one)
+    for (const Tail *t : {&plan.tail_n, &plan.tail_m}) {
+        if (t->splits == 0) continue;
+        tg_options sub{};
+        sub.struct_size = (int)sizeof sub;
+        sub.config = TG_CFG_64x64;
+        sub.split_k = (int)t->splits;
+        sub.workspace = t->ws_bytes ? static_cast<char *>(plan.workspace) + t->ws_offset : nullptr;
+        sub.workspace_bytes = t->ws_bytes;
+        sub.pack_a = 1;
+        sub.tail_gemm = 1;
+        st = run(batch, t->rows, t->cols, K, dtype, gp.A + t->m0 * gp.lda * 2, gp.lda, gp.sA, gp.B + t->n0 * 2, ldb,
+                 sB, C + t->m0 * ldc + t->n0, ldc, sC, alpha, beta, stream, &sub);
+        if (st != TG_OK) return st;
+    }
+    return TG_OK;
 }
 
 }  // namespace
