@@ -45,6 +45,8 @@ def parse():
                     help="repack misaligned A rows into the workspace (0 = automatic, 1 = never, 2 = always)")
     ap.add_argument("--tail-gemm", type=int, default=0,
                     help="thin N/M remainder as a GEMM of its own (0, 1 = strips in the grid, 2 = always)")
+    ap.add_argument("--persistent", type=int, default=0,
+                    help="persistent workgroups (0, 1 = the plain grid; 2 = persistent where the plan allows)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after timing, run a plain device copy of this many MiB (3 times) so HBM "
                          "byte counters can be scaled against a kernel of known traffic")
@@ -105,7 +107,7 @@ def main():
     stream = torch.cuda.current_stream()
     opts = dict(config=args.config, pipeline_depth=args.pipeline_depth, swizzle=args.swizzle,
                 block_order=args.block_order, split_k=args.split_k, pack_a=args.pack_a, plan_lda=p.lda,
-                tail_gemm=args.tail_gemm)
+                tail_gemm=args.tail_gemm, persistent=args.persistent)
     # workspace (split-K partials, the aligned copy of A, remainder partials): allocated once, outside
     # the timed region, as a caller would
     ws_bytes = tg.tile_gemm_workspace_size(p.batch, p.M, p.N, p.K, p.dtype, **opts)
@@ -183,6 +185,7 @@ def main():
                    "pipeline_depth": plan["pipeline_depth"], "split_k": plan["split_k"],
                    "pack_a": plan["pack_a"], "strip_blocks": plan["strip_blocks"],
                    "tail_n_splits": plan["tail_n_splits"], "tail_m_splits": plan["tail_m_splits"],
+                   "persistent": plan["persistent"],
                    "grid": plan["grid"]},
         "roofline": roofline,
         "cpu_baseline": cpu,

@@ -28,7 +28,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert tg.abi_version() == 4
+    assert tg.abi_version() == 5
     for s in range(5):
         assert tg.STATUS_NAMES[s] in tg.status_string(s)
 
@@ -99,7 +99,7 @@ def test_options_validation():
 @pytest.mark.parametrize("args,expect", [
     ((1, 67, 45, 53, "f32"), dict(config=tg.TG_CFG_F32_64x64, tiles_m=2, tiles_n=1, interior_blocks=0,
                                   fringe_blocks=2, k_tiles=2, k_tail=21, mfma_m=16, mfma_k=4)),
-    ((1, 8192, 8192, 8192, "bf16"), dict(config=tg.TG_CFG_256x256, tiles_m=32, tiles_n=32, grid=1024,
+    ((1, 8192, 8192, 8192, "bf16"), dict(config=tg.TG_CFG_256x256, tiles_m=32, tiles_n=32, grid=1024, persistent=0,
                                          interior_blocks=1024, fringe_blocks=0, k_tiles=256, k_tail=0,
                                          lds_bytes=4 * 32768, pipeline_depth=4, strip_blocks=0,
                                          mfma_m=16, mfma_n=16, mfma_k=32)),
@@ -260,3 +260,31 @@ def test_plan_tail_gemm():
     assert (p["strip_blocks"], p["tail_n_splits"], p["tail_m_splits"]) == (0, 0, 0)
     with pytest.raises(tg.TileGemmError):
         tg.tile_gemm_plan(*args, tail_gemm=3)
+
+
+def test_plan_persistent():
+    """Persistent workgroups, on request: a whole grid of interior 256 x 256 tiles of one problem."""
+    on = dict(persistent=2)
+    p = tg.tile_gemm_plan(1, 8192, 8192, 8192, "bf16", **on)
+    assert (p["persistent"], p["grid"], p["tiles_m"] * p["tiles_n"]) == (1, 256, 1024)
+    p = tg.tile_gemm_plan(1, 6144, 6144, 384, "f16", **on)    # 576 tiles: two or three per workgroup
+    assert (p["persistent"], p["grid"]) == (1, 256)
+    # not by default; and each condition broken in turn
+    for t in (0, 1):
+        assert tg.tile_gemm_plan(1, 8192, 8192, 8192, "bf16", persistent=t)["persistent"] == 0
+    for args, kw in [((1, 8192, 8192, 8160, "bf16"), {}),       # K not a multiple of 128
+                     ((1, 8192, 8192, 128, "bf16"), {}),        # fewer than 8 K tiles
+                     ((1, 8192, 8200, 8192, "bf16"), {}),       # N not a multiple of 256 (strips)
+                     ((1, 8191, 8192, 8192, "bf16"), {}),       # a fringe row
+                     ((2, 4096, 4096, 4096, "bf16"), {}),       # a batch
+                     ((1, 4096, 4096, 4096, "bf16"), {}),       # 256 tiles: one per workgroup
+                     ((1, 8192, 8192, 8192, "bf16"), dict(pipeline_depth=2)),
+                     ((1, 8192, 8192, 8192, "bf16"), dict(block_order=1)),
+                     ((1, 8192, 8192, 8192, "bf16"), dict(config=tg.TG_CFG_128x128)),
+                     ((1, 8192, 8192, 8192, "f32"), {})]:
+        p = tg.tile_gemm_plan(*args, **kw, **on)
+        assert p["persistent"] == 0, (args, kw)
+    big = dict(workspace=1 << 40, workspace_bytes=1 << 40)
+    assert tg.tile_gemm_plan(1, 8192, 8192, 8192, "bf16", plan_lda=8193, **big, **on)["persistent"] == 0   # repack
+    with pytest.raises(tg.TileGemmError):
+        tg.tile_gemm_plan(1, 8192, 8192, 8192, "bf16", persistent=3)

@@ -52,3 +52,71 @@ def test_m0_only_in_copy_groups(tmp_path):
         else:
             m0_set = False
     assert copies > 0
+
+
+# An MFMA written as inline assembly is invisible to the compiler's hazard
+# handling: a VALU or memory instruction that reads its accumulator must come
+# at least 19 wait states after it (the XDL write-to-read distance), which the
+# kernels provide by construction (settle() and reading the accumulators in
+# place).  This scans for any instruction other than an MFMA that names an
+# AGPR written by a 16x16x32 MFMA fewer than 19 wait states earlier (an
+# s_nop N counts N + 1, any other instruction 1), along the text of each
+# function.
+_AREG = re.compile(r"\ba(\d+)\b|\ba\[(\d+):(\d+)\]")
+_XDL_WAIT = 19
+
+
+def _agprs(operands):
+    regs = set()
+    for m in _AREG.finditer(operands):
+        if m.group(1) is not None:
+            regs.add(int(m.group(1)))
+        else:
+            regs.update(range(int(m.group(2)), int(m.group(3)) + 1))
+    return regs
+
+
+def accumulator_hazards(lines):
+    """(instruction, wait states) pairs that read an MFMA result too early."""
+    bad = []
+    pending = []                      # [registers written, wait states since]
+    for l in lines:
+        if not l or l.endswith(":"):
+            if l.endswith(">:"):      # a new function
+                pending = []
+            continue
+        parts = l.split(None, 1)
+        op, rest = parts[0], parts[1] if len(parts) > 1 else ""
+        if op.startswith("v_mfma_f32_16x16x32"):
+            dst = rest.split(",")[0]
+            for p in pending:
+                p[1] += 1
+            pending.append([_agprs(dst), 0])
+            continue
+        used = _agprs(rest)
+        for regs, waited in pending:
+            if used & regs and waited < _XDL_WAIT:
+                bad.append((l, waited))
+        step = int(rest) + 1 if op == "s_nop" else 1
+        for p in pending:
+            p[1] += step
+        pending = [p for p in pending if p[1] < _XDL_WAIT]
+    return bad
+
+
+def test_accumulator_reads_wait_for_mfma(tmp_path):
+    lines = _disassembly(tmp_path)
+    assert any(l.startswith("v_mfma_f32_16x16x32") for l in lines)
+    bad = accumulator_hazards(lines)
+    assert not bad, f"{len(bad)} early reads of MFMA results, e.g. {bad[:3]}"
+
+
+def test_accumulator_hazard_scan_finds_an_early_read():
+    # the pattern the compiler once produced: a copy right behind the MFMA
+    early = ["v_mfma_f32_16x16x32_bf16 a[252:255], v[8:11], v[72:75], a[252:255]", "s_nop 0",
+             "v_accvgpr_read_b32 v60, a252"]
+    assert accumulator_hazards(early) == [("v_accvgpr_read_b32 v60, a252", 1)]
+    settled = early[:1] + ["s_nop 7"] * 4 + early[2:]
+    assert accumulator_hazards(settled) == []
+    other = early[:2] + ["v_accvgpr_read_b32 v60, a12"]           # a different accumulator
+    assert accumulator_hazards(other) == []

@@ -55,7 +55,7 @@ class Options(ctypes.Structure):
                 ("swizzle", ctypes.c_int), ("block_order", ctypes.c_int), ("split_k", ctypes.c_int),
                 ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_int64),
                 ("pack_a", ctypes.c_int), ("pad0_", ctypes.c_int), ("plan_lda", ctypes.c_int64),
-                ("tail_gemm", ctypes.c_int), ("pad1_", ctypes.c_int)]
+                ("tail_gemm", ctypes.c_int), ("persistent", ctypes.c_int)]
 
 
 # size of the options struct in ABI version 1 (the first five ints)
@@ -72,7 +72,7 @@ class PlanInfo(ctypes.Structure):
                 ("split_k", ctypes.c_int), ("k_slice", ctypes.c_int64), ("workspace_bytes", ctypes.c_int64),
                 ("mfma_m", ctypes.c_int), ("mfma_n", ctypes.c_int), ("mfma_k", ctypes.c_int), ("pack_a", ctypes.c_int),
                 ("strip_blocks", ctypes.c_int64), ("tail_n_splits", ctypes.c_int),
-                ("tail_m_splits", ctypes.c_int)]
+                ("tail_m_splits", ctypes.c_int), ("persistent", ctypes.c_int), ("pad_", ctypes.c_int)]
 
     def as_dict(self):
         return {f: getattr(self, f) for f, _ in self._fields_}
@@ -164,12 +164,13 @@ def _dtype(d) -> int:
 
 
 def _options(config=0, pipeline_depth=0, swizzle=0, block_order=0, split_k=0, workspace=None,
-             workspace_bytes=None, pack_a=0, plan_lda=0, tail_gemm=0) -> Options:
+             workspace_bytes=None, pack_a=0, plan_lda=0, tail_gemm=0, persistent=0) -> Options:
     ws = _addr(workspace)
     if workspace_bytes is None:
         workspace_bytes = workspace.numel() * workspace.element_size() if hasattr(workspace, "numel") else 0
     return Options(ctypes.sizeof(Options), int(config), int(pipeline_depth), int(swizzle), int(block_order),
-                   int(split_k), ws, int(workspace_bytes), int(pack_a), 0, int(plan_lda), int(tail_gemm), 0)
+                   int(split_k), ws, int(workspace_bytes), int(pack_a), 0, int(plan_lda), int(tail_gemm),
+                   int(persistent))
 
 
 def _check(status: int, where: str):
@@ -200,12 +201,12 @@ def tile_gemm_strided_batched(batch, M, N, K, dtype, A, lda, strideA, B, ldb, st
 def tile_gemm_ex(batch, M, N, K, dtype, A, lda, strideA, B, ldb, strideB, C, ldc, strideC,
                  alpha=1.0, beta=0.0, stream=None, config=0, pipeline_depth=0, swizzle=0,
                  block_order=0, split_k=0, workspace=None, workspace_bytes=None, pack_a=0,
-                 plan_lda=0, tail_gemm=0) -> None:
+                 plan_lda=0, tail_gemm=0, persistent=0) -> None:
     """`workspace`: a device tensor or address for split-K partials or the
     aligned copy of A (its byte size is taken from the tensor unless
     `workspace_bytes` is given)."""
     opt = _options(config, pipeline_depth, swizzle, block_order, split_k, workspace, workspace_bytes, pack_a,
-                   plan_lda, tail_gemm)
+                   plan_lda, tail_gemm, persistent)
     _check(_lib().tile_gemm_ex(batch, M, N, K, _dtype(dtype), _addr(A), lda, strideA, _addr(B), ldb, strideB,
                                _addr(C), ldc, strideC, alpha, beta, _stream(stream), ctypes.byref(opt)),
            "tile_gemm_ex")
@@ -217,21 +218,23 @@ def tile_gemm_status(fn: str, *args) -> int:
 
 
 def tile_gemm_plan(batch, M, N, K, dtype, config=0, pipeline_depth=0, swizzle=0, block_order=0,
-                   split_k=0, workspace=None, workspace_bytes=None, pack_a=0, plan_lda=0, tail_gemm=0) -> dict:
+                   split_k=0, workspace=None, workspace_bytes=None, pack_a=0, plan_lda=0, tail_gemm=0,
+                   persistent=0) -> dict:
     info = PlanInfo()
     opt = _options(config, pipeline_depth, swizzle, block_order, split_k, workspace, workspace_bytes, pack_a,
-                   plan_lda, tail_gemm)
+                   plan_lda, tail_gemm, persistent)
     _check(_lib().tile_gemm_plan(batch, M, N, K, _dtype(dtype), ctypes.byref(opt), ctypes.byref(info)),
            "tile_gemm_plan")
     return info.as_dict()
 
 
 def tile_gemm_workspace_size(batch, M, N, K, dtype, config=0, pipeline_depth=0, swizzle=0, block_order=0,
-                             split_k=0, pack_a=0, plan_lda=0, tail_gemm=0) -> int:
+                             split_k=0, pack_a=0, plan_lda=0, tail_gemm=0, persistent=0) -> int:
     """Bytes of workspace a call with these arguments would use (split-K partials, the
     aligned copy of A and the remainder GEMMs' partials; 0: none)."""
     n = ctypes.c_int64(0)
-    opt = _options(config, pipeline_depth, swizzle, block_order, split_k, None, None, pack_a, plan_lda, tail_gemm)
+    opt = _options(config, pipeline_depth, swizzle, block_order, split_k, None, None, pack_a, plan_lda, tail_gemm,
+                   persistent)
     _check(_lib().tile_gemm_workspace_size(batch, M, N, K, _dtype(dtype), ctypes.byref(opt), ctypes.byref(n)),
            "tile_gemm_workspace_size")
     return int(n.value)

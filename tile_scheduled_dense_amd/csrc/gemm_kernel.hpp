@@ -88,12 +88,14 @@ struct AccT {
 };
 
 // ---- block order -----------------------------------------------------------
-__device__ __forceinline__ void block_coords(const GemmParams &p, int64_t &b, int64_t &tm, int64_t &tn) {
+// Tile of workgroup id w (blockIdx.x, or a persistent workgroup's w-th
+// virtual id).
+__device__ __forceinline__ void block_coords_of(const GemmParams &p, uint32_t w, int64_t &b, int64_t &tm,
+                                                int64_t &tn) {
     // The grid is below 2^31 workgroups (checked on the host): 32-bit math.
     const uint32_t tiles_m = (uint32_t)p.tiles_m, tiles_n = (uint32_t)p.tiles_n;
     const uint32_t per_batch = tiles_m * tiles_n;
     const uint32_t total = per_batch * (uint32_t)p.batch;
-    const uint32_t w = blockIdx.x;
     uint32_t lid = w;
     if (p.block_order == 0) {
         // Undo the round-robin over 8 XCDs: XCD x = w % 8 gets the x-th
@@ -116,6 +118,10 @@ __device__ __forceinline__ void block_coords(const GemmParams &p, int64_t &b, in
         tm = t / tiles_n;
         tn = t % tiles_n;
     }
+}
+
+__device__ __forceinline__ void block_coords(const GemmParams &p, int64_t &b, int64_t &tm, int64_t &tn) {
+    block_coords_of(p, blockIdx.x, b, tm, tn);
 }
 
 // ---- 16-byte chunk loads -----------------------------------------------------
@@ -233,7 +239,7 @@ __device__ __forceinline__ void mfma_chunk(const u32x4 &a, const u32x4 &b, f32x4
 // per lane whose C0 loads are all issued before any of the chunk's stores:
 // one memory round trip per chunk instead of one per MFMA tile.
 // `acc(i, j, v)` is value v of MFMA tile (i, j) of this lane.
-template <class C, bool FRINGE, class AccFn>
+template <class C, bool FRINGE, class AccFn, int CHUNK_VALUES = 64>
 __device__ __forceinline__ void store_tile_epilogue(const GemmParams &p, const AccFn &acc, int64_t b,
                                                     int64_t m0, int64_t n0, int wave, int lane) {
     float *Cblk = p.C + b * p.sC + m0 * p.ldc + n0;
@@ -242,7 +248,7 @@ __device__ __forceinline__ void store_tile_epilogue(const GemmParams &p, const A
     const int64_t M = p.M, N = p.N;
     constexpr int V = C::ACC_PER_MFMA;
     constexpr int TILES = C::TM * C::TN;
-    constexpr int CH = 64 / V < TILES ? 64 / V : TILES;       // MFMA tiles per chunk
+    constexpr int CH = CHUNK_VALUES / V < TILES ? CHUNK_VALUES / V : TILES;   // MFMA tiles per chunk
     static_assert(TILES % CH == 0, "whole chunks");
 #pragma unroll
     for (int c0t = 0; c0t < TILES; c0t += CH) {

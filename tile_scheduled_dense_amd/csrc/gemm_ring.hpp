@@ -159,10 +159,13 @@ __device__ __forceinline__ uint32_t lds_address(const char *p) {
 // K tile's MFMAs take a zero accumulator input (mma<true>, no VALU write of
 // an accumulator ever precedes an MFMA), and settle() pads the last MFMA's
 // results with wait states before anything else reads them.  Dependent MFMAs
-// on one accumulator are a whole K tile apart.
-template <class C>
+// on one accumulator are a whole K tile apart.  INLINE = false keeps the
+// compiler's builtin (and its hazard handling): the unpipelined depth-1
+// schedule of the 256 x 256 tile spills accumulators, and the spill copies
+// next to an MFMA the compiler cannot see would read its result too early.
+template <class C, bool INLINE = true>
 struct AccTiles {
-    static constexpr bool ASM = C::MT == 16 && C::DT != DT_F32;
+    static constexpr bool ASM = INLINE && C::MT == 16 && C::DT != DT_F32;
     typename AccT<C>::type r[C::TM][C::TN];
     __device__ __forceinline__ void zero() {
 #pragma unroll
@@ -195,8 +198,20 @@ struct AccTiles {
             __builtin_amdgcn_sched_barrier(0);
         }
     }
-    // value v (0 <= v < ACC_PER_MFMA) of MFMA tile (i, j)
-    __device__ __forceinline__ float get(int i, int j, int v) const { return r[i][j][v]; }
+    // value v (0 <= v < ACC_PER_MFMA) of MFMA tile (i, j), after settle().  The
+    // inline-assembly MFMAs' accumulators are read by an inline-assembly
+    // v_accvgpr_read of the AGPR itself: left to the compiler, a value needed
+    // later in a VGPR may be copied out right behind the MFMA that writes it,
+    // before the result is there (the compiler does not know these are MFMAs).
+    __device__ __forceinline__ float get(int i, int j, int v) const {
+        if constexpr (ASM) {
+            float x;
+            asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(x) : "a"(r[i][j][v]));
+            return x;
+        } else {
+            return r[i][j][v];
+        }
+    }
 };
 
 // One workgroup's tile of the 16-bit family: copy sources, the copies, the
@@ -223,7 +238,7 @@ struct RingBlock {
     uint32_t a_rd[C::KSTEPS];           // LDS address of this lane's A fragment of row tile 0, copy 0
     uint32_t b_rd[C::KSTEPS][C::TN];    // ... of its B fragment (first read) of column tile j, copy 0
     u32x4 tail[C::COPIES];
-    AccTiles<C> acc;
+    AccTiles<C, (STAGES > 1)> acc;
 
     // LDS: the STAGES copies of the B tile, then the STAGES copies of the A
     // tile, so a fragment read of a known copy is a fixed base register plus an
@@ -290,6 +305,15 @@ struct RingBlock {
             b_off[d] = (FRINGE && n0 + b_n[d] >= p.N) ? kOutOfRange : (b_k[d] * ldb + b_n[d]) * E;
             b_voff[d] = b_off[d] + B_SHIFT - 1024 * d;
         }
+    }
+
+    // Interior blocks of one problem (batch entry 0): point the copy resources
+    // at K tile 0 of tile (tm, tn), leaving m0 / n0 (the epilogue's) alone.
+    __device__ __forceinline__ void retarget(int64_t tm, int64_t tn) {
+        a_base = uniform_u64((uint64_t)(p.A + tm * C::BM * p.lda * E));
+        b_base = uniform_u64((uint64_t)(p.B + tn * C::BN * E));
+        rsa = rsrc_words_u(a_base - A_SHIFT, 0x7fffffff);
+        rsb = rsrc_words_u(b_base - B_SHIFT, 0x7fffffff);
     }
 
     // 64-bit add to the base address held in the first two resource words
@@ -534,7 +558,9 @@ struct SwPipe {
     // One iteration: multiply tile t from (fa, fb) while reading tile t + 1
     // into (na, nb).  STEADY: tile t + 1 exists and tile t + STAGES is copied
     // (no conditions inside the MFMA stream); otherwise both are checked.
-    template <bool STEADY, bool FIRST = false>
+    // READ = false (steady only): tile t + 1 is landed and published but its
+    // fragments are left for the caller to read.
+    template <bool STEADY, bool FIRST = false, bool READ = true>
     __device__ __forceinline__ static void iter(Blk &blk, int64_t t, int cur, int nxt_read,
                                                 u32x4 (&fa)[C::KSTEPS][C::TM], u32x4 (&fb)[C::KSTEPS][C::TN],
                                                 u32x4 (&na)[C::KSTEPS][C::TM], u32x4 (&nb)[C::KSTEPS][C::TN]) {
@@ -558,7 +584,7 @@ struct SwPipe {
                 const int s = q / (C::TM * C::TN), i = (q / C::TN) % C::TM, j = q % C::TN;
                 if (FIRST && s == 0) blk.acc.template mma<true>(i, j, fa[s][i], fb[s][j]);
                 else blk.acc.template mma<false>(i, j, fa[s][i], fb[s][j]);
-                if (q < READS) blk.read_piece(nxt_read, q, na, nb);
+                if (READ && q < READS) blk.read_piece(nxt_read, q, na, nb);
                 if (q == NMFMA / 4 - 1 || q == 3 * NMFMA / 4 - 1) blk.dma_operand(tc, cur, q < NMFMA / 2 ? 0 : 1);
                 __builtin_amdgcn_sched_barrier(0);
             }
@@ -635,6 +661,85 @@ __device__ __forceinline__ void ring_tile_swpipe(const GemmParams &p, char *smem
     }
     store_tile_epilogue<C, FRINGE>(p, [&](int i, int j, int v) { return blk.acc.get(i, j, v); }, b, blk.m0, blk.n0,
                                    blk.wave, blk.lane);
+}
+
+// Persistent form of the software pipeline for a grid of interior tiles of
+// one problem whose K is a multiple of 4 K tiles (at least 8): workgroup w
+// takes tiles w, w + G, w + 2G, ... (G workgroups, a multiple of the 8 XCDs,
+// so every id keeps its XCD and the XCDs' tile runs are those of the plain
+// grid).  Every K tile is copied straight to LDS (K is whole tiles).  The
+// pipeline does not stop between tiles: the last four iterations of a tile
+// copy the next tile's K tiles 0..3 into LDS copies 0..3 (K tile t of any
+// tile sits in copy t mod 4) and the last one lands and publishes K tile 0,
+// so the next tile starts with its first copies in LDS.  Only its first
+// fragments are read after the epilogue (holding them through it would take
+// the epilogue's registers); no iteration but the last tile's drain leaves
+// the steady form.
+template <class C, int STAGES, int SWZ>
+__device__ __forceinline__ void ring_persistent(const GemmParams &p, char *smem) {
+    static_assert(STAGES == 4, "four LDS copies: a tile's copies sit at t mod 4");
+    using SP = SwPipe<C, STAGES, SWZ, false>;
+    const uint32_t total = (uint32_t)(p.tiles_m * p.tiles_n);
+    uint32_t v = blockIdx.x;
+    int64_t b, tm, tn;
+    block_coords_of(p, v, b, tm, tn);
+    RingBlock<C, STAGES, SWZ, false> blk(p, smem, 0, tm, tn);
+    blk.ndma = blk.nk;
+    const int64_t nk = blk.nk;
+#pragma unroll
+    for (int t = 0; t < STAGES; ++t) blk.dma(t, t);
+    blk.template land_tile<STAGES - 1>(0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    block_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    u32x4 a0[C::KSTEPS][C::TM], b0[C::KSTEPS][C::TN], a1[C::KSTEPS][C::TM], b1[C::KSTEPS][C::TN];
+#pragma unroll
+    for (int r = 0; r < SP::READS; ++r) blk.read_piece(0, r, a0, b0);
+    while (true) {
+        const uint32_t vn = v + gridDim.x;
+        const bool next = vn < total;
+        SP::template iter<true, true>(blk, 0, 0, 1, a0, b0, a1, b1);
+        int64_t t = 1;
+        for (; t + 3 + STAGES < nk; t += 4) {
+            SP::template iter<true>(blk, t, 1, 2, a1, b1, a0, b0);
+            SP::template iter<true>(blk, t + 1, 2, 3, a0, b0, a1, b1);
+            SP::template iter<true>(blk, t + 2, 3, 0, a1, b1, a0, b0);
+            SP::template iter<true>(blk, t + 3, 0, 1, a0, b0, a1, b1);
+        }
+        // t = nk - 7: seven K tiles left, in LDS copies 1, 2, 3, 0, 1, 2, 3.  The
+        // last tile of a workgroup copies its own K tiles 0..3 again (unused), so
+        // every tile ends the same way.
+        int64_t bn, tmn = 0, tnn = 0;
+        if (next) block_coords_of(p, vn, bn, tmn, tnn);
+        else tmn = blk.m0 / C::BM, tnn = blk.n0 / C::BN;
+        SP::template iter<true>(blk, t, 1, 2, a1, b1, a0, b0);           // copies K tile nk - 3
+        SP::template iter<true>(blk, t + 1, 2, 3, a0, b0, a1, b1);       // nk - 2
+        SP::template iter<true>(blk, t + 2, 3, 0, a1, b1, a0, b0);       // nk - 1
+        blk.retarget(tmn, tnn);
+        SP::template iter<true>(blk, t + 3, 0, 1, a0, b0, a1, b1);       // the next tile's 0
+        SP::template iter<true>(blk, t + 4, 1, 2, a1, b1, a0, b0);       // its 1
+        SP::template iter<true>(blk, t + 5, 2, 3, a0, b0, a1, b1);       // its 2
+        SP::template iter<true, false, false>(blk, t + 6, 3, 0, a1, b1, a0, b0);   // its 3; lands its 0
+        blk.acc.settle();
+        store_tile_epilogue<C, false>(p, [&](int i, int j, int v2) { return blk.acc.get(i, j, v2); }, 0, blk.m0,
+                                      blk.n0, blk.wave, blk.lane);
+        if (!next) break;
+        blk.m0 = tmn * C::BM;
+        blk.n0 = tnn * C::BN;
+#pragma unroll
+        for (int r = 0; r < SP::READS; ++r) blk.read_piece(0, r, a0, b0);
+        // the epilogue's accumulator reads before the next tile's first MFMAs overwrite them
+        blk.acc.settle();
+        v = vn;
+    }
+    // the unused copies must land before the workgroup's LDS is released
+    wait_vmcnt<0>();
+}
+
+template <class C, int STAGES, int SWZ>
+__global__ __launch_bounds__(C::THREADS, C::OCCUPANCY) void gemm_ring_persistent_kernel(GemmParams p) {
+    __shared__ __attribute__((aligned(1024))) char smem[STAGES * C::STAGE_BYTES];
+    ring_persistent<C, STAGES, SWZ>(p, smem);
 }
 
 // The problem of grid batch entry b with its batch offsets folded into the

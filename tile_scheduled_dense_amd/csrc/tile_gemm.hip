@@ -284,6 +284,7 @@ tg_status make_plan(int64_t batch, int64_t M, int64_t N, int64_t K, tg_dtype dty
     // 8190 the 32 strips that follow the 1024 main tiles cost the grid about
     // 8 us, the separate GEMM and its combine about 33 us.
     if (o.tail_gemm < 0 || o.tail_gemm > 2) return TG_ERR_INVALID_ARG;
+    if (o.persistent < 0 || o.persistent > 2) return TG_ERR_INVALID_ARG;
     if (some && strip_n + strip_m > 0 && splits == 1) {
         if (o.tail_gemm == 2) {
             const int64_t n_main = p.tiles_n * d.bn, m_main = p.tiles_m * d.bm;
@@ -320,6 +321,17 @@ tg_status make_plan(int64_t batch, int64_t M, int64_t N, int64_t K, tg_dtype dty
                 out.workspace = o.workspace;
             }
         }
+    }
+
+    // Persistent workgroups (tile_gemm.h), on request: a whole grid of
+    // interior tiles of one problem, K in whole groups of four K tiles, at
+    // least two tiles per workgroup.
+    constexpr int64_t kPersistentBlocks = 256;
+    if (sixteen && some && o.persistent == 2 && config == TG_CFG_256x256 && depth == 4 && swz == SWZ_XOR &&
+        order == 0 && batch == 1 && splits == 1 && !p.pack_a && p.strip_blocks == 0 && M % 256 == 0 &&
+        N % 256 == 0 && K % (4 * d.bk) == 0 && K >= 8 * d.bk && p.tiles_m * p.tiles_n >= 2 * kPersistentBlocks) {
+        p.persistent = 1;
+        p.grid = kPersistentBlocks;
     }
     return TG_OK;
 }
@@ -440,6 +452,13 @@ tg_status launch_combine(const float *W, float *C, int64_t M, int64_t N, int64_t
 
 template <int DT>
 tg_status launch_dtype(const GemmParams &gp, const tg_plan_info &p, hipStream_t s) {
+    if (p.persistent) {
+        if (p.config != TG_CFG_256x256 || p.pipeline_depth != 4 || p.swizzle != SWZ_XOR) return TG_ERR_INTERNAL;
+        using C = Ring256<DT>;
+        hipLaunchKernelGGL((gemm_ring_persistent_kernel<C, 4, SWZ_XOR>), dim3((unsigned)p.grid), dim3(C::THREADS), 0,
+                           s, gp);
+        return hipGetLastError() == hipSuccess ? TG_OK : TG_ERR_LAUNCH;
+    }
     switch (p.config) {
         case TG_CFG_256x256: return launch_ring<Ring256<DT>, true>(gp, p, s);
         case TG_CFG_128x128: return launch_ring<Ring128<DT>, false>(gp, p, s);
