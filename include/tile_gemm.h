@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define TILE_GEMM_ABI_VERSION 5
+#define TILE_GEMM_ABI_VERSION 6
 
 typedef enum { TG_F32 = 0, TG_BF16 = 1, TG_F16 = 2 } tg_dtype;
 
@@ -154,6 +154,24 @@ typedef enum {
  * never waits for (8192^3 bf16: 0.797 ms against 0.783 ms).
  *   persistent == 0 or 1: the plain grid;
  *   persistent == 2: persistent workgroups where the conditions hold.
+ * Fused elementwise tail (OCANNL "Module Ir.Schedule", epilogue fusion: the
+ * bias add / activation / residual that follows a reduction, folded into its
+ * store-back): with bias_mode or activation nonzero every output is
+ *     C <- act(alpha * A.B + bias) + beta * C0
+ * computed as y = act(fma(alpha, acc, bias)), then fma(beta, C0, y) (C0 not
+ * read when beta == 0), in fp32.  bias_mode 1: bias[j], one value per column
+ * (N floats per problem); 2: bias[i], one per row (M floats); problem b reads
+ * its vector at bias + b * bias_stride (0 = one vector shared by the batch).
+ * activation 1: ReLU, x < 0 ? 0 : x (NaN passes through); 2: GELU in its erf
+ * form, x * Phi(x) = x/2 * (1 + erf(x / sqrt(2))), with the device's erff.
+ * Without them the epilogue is fma(alpha, acc, beta * C0) as before.  The
+ * bias must be 4-byte aligned, non-NULL exactly when bias_mode != 0, and
+ * must not overlap C (tile_gemm_plan and tile_gemm_workspace_size do not read
+ * it: for them the modes alone shape the plan, and a NULL bias is accepted).  The tail is built for the default pipeline depth and
+ * swizzle (others: TG_ERR_UNSUPPORTED) and, without a split, not for the
+ * 256 x 256 tile (its accumulators fill the registers): the automatic choice
+ * then takes 128 x 128, a forced TG_CFG_256x256 returns TG_ERR_UNSUPPORTED;
+ * with a split the combine pass applies the tail for any configuration.
  *
  * The workspace is caller-owned device memory, 16-byte aligned, that must not
  * overlap A, B or C; its contents on entry do not matter and are undefined
@@ -174,6 +192,10 @@ typedef struct {
     int64_t plan_lda;    /* lda assumed by the plan queries (0: a multiple of 8)    */
     int tail_gemm;       /* 0, 1 = strips; 2 = thin remainders as GEMMs (see above)  */
     int persistent;      /* 0, 1 = plain grid; 2 = persistent where allowed (above) */
+    const float *bias;   /* fused tail bias (see above), NULL when bias_mode == 0    */
+    int64_t bias_stride; /* floats between the bias vectors of batch entries          */
+    int bias_mode;       /* 0 = none, 1 = per column (bias[j]), 2 = per row (bias[i]) */
+    int activation;      /* 0 = none, 1 = ReLU, 2 = GELU (erf form)                  */
 } tg_options;
 
 /* tile_gemm_strided_batched with explicit schedule knobs (opt may be NULL).

@@ -28,11 +28,11 @@ DTYPE_CODES = {"f32": F32, "bf16": BF16, "f16": F16}
 def compile_library(src: str, out: str, verbose: bool = False) -> str:
     """gcc, binary64, no fast-math and no FP contraction."""
     cmd = ["gcc", "-O2", "-fopenmp", "-fno-fast-math", "-ffp-contract=off",
-           "-fPIC", "-shared", "-std=c11", "-Wall", "-o", out + ".tmp", src, "-lm"]
+           "-fPIC", "-shared", "-std=c11", "-Wall", "-o", f"{out}.{os.getpid()}.tmp", src, "-lm"]
     if verbose:
         print(" ".join(cmd))
     subprocess.run(cmd, check=True)
-    os.replace(out + ".tmp", out)
+    os.replace(f"{out}.{os.getpid()}.tmp", out)   # per-process name: parallel test workers may build at once
     return out
 
 
@@ -46,6 +46,15 @@ def _ptr(a):
 
 def _code(dtype):
     return DTYPE_CODES[dtype] if isinstance(dtype, str) else int(dtype)
+
+
+def _f32_or_none(x):
+    if x is None:
+        return None
+    x = np.ascontiguousarray(x)
+    if x.dtype != np.float32:
+        raise TypeError("the bias is float32 storage")
+    return x
 
 
 def _check_storage(x, code):
@@ -73,11 +82,18 @@ class OracleLibrary:
         lib.oracle_decode_f16.argtypes = [ctypes.c_uint16]
         lib.oracle_decode_f16.restype = dbl
         lib.oracle_max_threads.restype = ctypes.c_int
+        lib.oracle_tail.argtypes = [i64, i64, i64, vp, i64, i64, vp, i64, ctypes.c_int, ctypes.c_int,
+                                    vp, i64, i64, dbl]
+        lib.oracle_tail.restype = ctypes.c_int
+        lib.oracle_tail_points.argtypes = [i64, vp, vp, vp, vp, vp, i64, ctypes.c_int, ctypes.c_int,
+                                           vp, i64, i64, dbl]
+        lib.oracle_tail_points.restype = ctypes.c_int
         self.lib = lib
         self.path = path
 
     def gemm(self, M, N, K, dtype, A, lda, B, ldb, C0=None, ldc=None, alpha=1.0, beta=0.0,
-             batch=1, strideA=0, strideB=0, strideC=0, with_absden=False):
+             batch=1, strideA=0, strideB=0, strideC=0, with_absden=False, bias=None, bias_stride=0,
+             bias_mode=0, activation=0):
         """Full result as float64 (batch, M, N); with_absden adds sum_k |a||b|.
 
         A, B: flat numpy storage (uint16 bit patterns for bf16/f16, float32 for
@@ -92,15 +108,26 @@ class OracleLibrary:
             raise TypeError("beta != 0 needs a float32 C0")
         out = np.empty((batch, M, N), dtype=np.float64)
         den = np.empty((batch, M, N), dtype=np.float64) if with_absden else None
+        tail = bias_mode != 0 or activation != 0
+        # with a fused tail the contraction runs with beta = 0 and the tail adds beta * C0
         rc = self.lib.oracle_gemm(batch, M, N, K, code, _ptr(A), lda, strideA, _ptr(B), ldb, strideB,
-                                  _ptr(C0) if beta != 0.0 else None, ldc, strideC,
-                                  float(alpha), float(beta), _ptr(out), max(N, 1), M * N, _ptr(den))
+                                  _ptr(C0) if beta != 0.0 and not tail else None, ldc, strideC,
+                                  float(alpha), 0.0 if tail else float(beta), _ptr(out), max(N, 1), M * N,
+                                  _ptr(den))
         if rc != 0:
             raise ValueError(f"oracle_gemm rejected its arguments (rc={rc})")
+        if tail:
+            bias = _f32_or_none(bias)
+            rc = self.lib.oracle_tail(batch, M, N, _ptr(out), max(N, 1), M * N, _ptr(bias), int(bias_stride),
+                                      int(bias_mode), int(activation), _ptr(C0) if beta != 0.0 else None, ldc,
+                                      strideC, float(beta))
+            if rc != 0:
+                raise ValueError(f"oracle_tail rejected its arguments (rc={rc})")
         return (out, den) if with_absden else out
 
     def gemm_points(self, M, N, K, dtype, A, lda, B, ldb, pts, C0=None, ldc=None, alpha=1.0,
-                    beta=0.0, batch=1, strideA=0, strideB=0, strideC=0):
+                    beta=0.0, batch=1, strideA=0, strideB=0, strideC=0, bias=None, bias_stride=0,
+                    bias_mode=0, activation=0):
         """Values and sum_k |a||b| at sampled outputs pts = int64 (P, 3) of (b, i, j)."""
         code = _code(dtype)
         _check_storage(A, code)
@@ -110,12 +137,20 @@ class OracleLibrary:
         pb, pi, pj = (np.ascontiguousarray(pts[:, c]) for c in range(3))
         out = np.empty(len(pts), dtype=np.float64)
         den = np.empty(len(pts), dtype=np.float64)
+        tail = bias_mode != 0 or activation != 0
         rc = self.lib.oracle_gemm_points(batch, M, N, K, code, _ptr(A), lda, strideA, _ptr(B), ldb,
-                                         strideB, _ptr(C0) if beta != 0.0 else None, ldc, strideC,
-                                         float(alpha), float(beta), len(pts), _ptr(pb), _ptr(pi),
-                                         _ptr(pj), _ptr(out), _ptr(den))
+                                         strideB, _ptr(C0) if beta != 0.0 and not tail else None, ldc, strideC,
+                                         float(alpha), 0.0 if tail else float(beta), len(pts), _ptr(pb),
+                                         _ptr(pi), _ptr(pj), _ptr(out), _ptr(den))
         if rc != 0:
             raise ValueError(f"oracle_gemm_points rejected its arguments (rc={rc})")
+        if tail:
+            bias = _f32_or_none(bias)
+            rc = self.lib.oracle_tail_points(len(pts), _ptr(pb), _ptr(pi), _ptr(pj), _ptr(out), _ptr(bias),
+                                             int(bias_stride), int(bias_mode), int(activation),
+                                             _ptr(C0) if beta != 0.0 else None, ldc, strideC, float(beta))
+            if rc != 0:
+                raise ValueError(f"oracle_tail_points rejected its arguments (rc={rc})")
         return out, den
 
     def decode(self, bits, dtype):

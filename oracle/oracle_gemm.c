@@ -188,6 +188,58 @@ int oracle_gemm_points(int64_t batch, int64_t M, int64_t N, int64_t K, int dtype
     return 0;
 }
 
+/*
+ * Fused elementwise tail (OCANNL "Module Ir.Schedule", epilogue fusion: the
+ * bias add / activation / residual that follows a reduction, folded into its
+ * store-back; it never reorders the reduction).  Applied to a result computed
+ * with beta = 0 (out = alpha * sum), in place and in binary64:
+ *     out <- act(out + bias) + beta * C0
+ * bias_mode 1: one value per column, bias[b * bias_stride + j]; 2: one per
+ * row, bias[b * bias_stride + i]; 0: none.  act 1: ReLU, x < 0 ? 0 : x; 2:
+ * GELU, x * Phi(x) with the standard normal CDF Phi(x) = (1 + erf(x / sqrt 2)) / 2;
+ * 0: none.  C0 (fp32, ldc, sC) is read only when beta != 0.
+ */
+static double oracle_activation(double x, int act) {
+    if (act == 1) return x < 0.0 ? 0.0 : x;
+    if (act == 2) return x * 0.5 * (1.0 + erf(x / sqrt(2.0)));
+    return x;
+}
+
+static double tail_one(double x, int64_t b, int64_t i, int64_t j, const float *bias, int64_t bias_stride,
+                       int bias_mode, int act, const float *C0, int64_t ldc, int64_t sC, double beta) {
+    if (bias_mode == 1) x += (double)bias[b * bias_stride + j];
+    if (bias_mode == 2) x += (double)bias[b * bias_stride + i];
+    double y = oracle_activation(x, act);
+    if (beta != 0.0) y += beta * (double)C0[b * sC + ldc * i + j];
+    return y;
+}
+
+static int bad_tail(int bias_mode, int act, const float *bias, int64_t bias_stride) {
+    return bias_mode < 0 || bias_mode > 2 || act < 0 || act > 2 || (bias_mode != 0 && !bias) || bias_stride < 0;
+}
+
+int oracle_tail(int64_t batch, int64_t M, int64_t N, double *out, int64_t ldo, int64_t sO,
+                const float *bias, int64_t bias_stride, int bias_mode, int act,
+                const float *C0, int64_t ldc, int64_t sC, double beta) {
+    if (bad_tail(bias_mode, act, bias, bias_stride) || batch < 0 || M < 0 || N < 0 || ldo < N) return 1;
+    for (int64_t b = 0; b < batch; ++b)
+        for (int64_t i = 0; i < M; ++i)
+            for (int64_t j = 0; j < N; ++j) {
+                double *o = &out[b * sO + i * ldo + j];
+                *o = tail_one(*o, b, i, j, bias, bias_stride, bias_mode, act, C0, ldc, sC, beta);
+            }
+    return 0;
+}
+
+int oracle_tail_points(int64_t npts, const int64_t *pb, const int64_t *pi, const int64_t *pj, double *out,
+                       const float *bias, int64_t bias_stride, int bias_mode, int act,
+                       const float *C0, int64_t ldc, int64_t sC, double beta) {
+    if (bad_tail(bias_mode, act, bias, bias_stride) || npts < 0) return 1;
+    for (int64_t p = 0; p < npts; ++p)
+        out[p] = tail_one(out[p], pb[p], pi[p], pj[p], bias, bias_stride, bias_mode, act, C0, ldc, sC, beta);
+    return 0;
+}
+
 int oracle_max_threads(void) {
 #ifdef _OPENMP
     extern int omp_get_max_threads(void);

@@ -235,5 +235,81 @@ def pin_batched_and_points(lib):
         assert np.array_equal(d, den[pts[:, 0], pts[:, 1], pts[:, 2]])
 
 
+def pin_fused_tail(lib):
+    """The fused tail act(alpha A.B + bias) + beta C0 against values fixed outside the oracle.
+
+    * GELU is x Phi(x) with Phi the standard normal CDF: at the normal quantiles
+      z(0.975) = 1.959963984540054 and z(0.75) = 0.6744897501960817 (fp32-rounded
+      as the bias stores them) it is z times 0.975 and 0.75 to within Phi's slope
+      times the rounding; GELU(0) = 0; and GELU(x) - GELU(-x) = x, since Phi(x) +
+      Phi(-x) = 1;
+    * ReLU keeps x > 0 and zeroes x < 0, so relu(x) - relu(-x) = x;
+    * the residual is added after the activation: with K = 0, bias -1, ReLU,
+      beta 1 and C0 = 2 every output is 2 (inside the activation it would be 1);
+    * a per-column bias varies along a row, a per-row bias down a column;
+    * K > 0: against numpy's product and scipy's normal CDF (ndtr) on the decoded
+      operands; a strided batch with a bias stride equals its separate problems;
+      sampled points equal the full result bitwise.
+    """
+    from scipy.special import ndtr
+    empty = np.zeros(0, np.float32)
+    # quantiles: K = 0, so the output is act(bias)
+    z = np.array([1.959963984540054, 0.6744897501960817, 0.0, -1.959963984540054, -0.6744897501960817],
+                 dtype=np.float32)
+    got = lib.gemm(1, 5, 0, "f32", empty, 1, empty, 5, bias=z, bias_mode=1, activation=2)[0, 0]
+    zq = z.astype(np.float64)
+    phi = np.array([0.975, 0.75, 0.5, 0.025, 0.25])
+    slack = np.abs(zq) * 0.4 * 1e-7 * np.abs(zq)      # |z| * pdf * |z - z_exact|, pdf < 0.4
+    assert np.all(np.abs(got - zq * phi) <= slack + 1e-15), got
+    assert got[2] == 0.0
+    # odd part of GELU and ReLU
+    x = np.linspace(-6, 6, 97).astype(np.float32)
+    for act in (1, 2):
+        pos = lib.gemm(1, 97, 0, "f32", empty, 1, empty, 97, bias=x, bias_mode=1, activation=act)[0, 0]
+        neg = lib.gemm(1, 97, 0, "f32", empty, 1, empty, 97, bias=-x, bias_mode=1, activation=act)[0, 0]
+        assert np.allclose(pos - neg, x.astype(np.float64), rtol=0, atol=1e-15), act
+    relu = lib.gemm(1, 97, 0, "f32", empty, 1, empty, 97, bias=x, bias_mode=1, activation=1)[0, 0]
+    assert np.array_equal(relu, np.where(x > 0, x, 0).astype(np.float64))
+    # the residual after the activation
+    c0 = np.full(6, 2.0, np.float32)
+    got = lib.gemm(2, 3, 0, "f32", empty, 1, empty, 3, C0=c0, ldc=3, beta=1.0, bias=np.full(3, -1.0, np.float32),
+                   bias_mode=1, activation=1)
+    assert np.array_equal(got, np.full((1, 2, 3), 2.0))
+    # bias orientation
+    col = np.array([1.0, 2.0, 3.0], np.float32)
+    row = np.array([10.0, 20.0], np.float32)
+    assert np.array_equal(lib.gemm(2, 3, 0, "f32", empty, 1, empty, 3, bias=col, bias_mode=1)[0],
+                          np.array([[1.0, 2.0, 3.0], [1.0, 2.0, 3.0]]))
+    assert np.array_equal(lib.gemm(2, 3, 0, "f32", empty, 1, empty, 3, bias=row, bias_mode=2)[0],
+                          np.array([[10.0, 10.0, 10.0], [20.0, 20.0, 20.0]]))
+    # K > 0 against numpy and scipy
+    rng = np.random.default_rng(21)
+    for dt in ("f32", "bf16", "f16"):
+        p = workloads.custom(dt, 21, 19, 37, batch=3, ldc_pad=2, alpha=0.5, beta=-0.75, seed=22)
+        A, B = dense(p, "A"), dense(p, "B")
+        C0 = np.stack([p.C0[b * p.strideC: b * p.strideC + p.M * p.ldc].reshape(p.M, p.ldc)[:, :p.N]
+                       for b in range(p.batch)]).astype(np.float64)
+        for mode, length in ((1, p.N), (2, p.M)):
+            stride = length + 4
+            bias = rng.standard_normal(p.batch * stride).astype(np.float32)
+            for act in (0, 1, 2):
+                got = lib.gemm(p.M, p.N, p.K, dt, p.A, p.lda, p.B, p.ldb, C0=p.C0, ldc=p.ldc, alpha=p.alpha,
+                               beta=p.beta, batch=p.batch, strideA=p.strideA, strideB=p.strideB,
+                               strideC=p.strideC, bias=bias, bias_stride=stride, bias_mode=mode, activation=act)
+                for b in range(p.batch):
+                    bv = bias[b * stride: b * stride + length].astype(np.float64)
+                    y = p.alpha * (A[b] @ B[b]) + (bv[None, :] if mode == 1 else bv[:, None])
+                    y = y if act == 0 else np.maximum(y, 0.0) if act == 1 else y * ndtr(y)
+                    exp = y + p.beta * C0[b]
+                    scale = p.alpha * (np.abs(A[b]) @ np.abs(B[b])) + np.abs(bv).max() + abs(p.beta) * np.abs(C0[b])
+                    assert np.all(np.abs(got[b] - exp) <= 1e-12 * scale), (dt, mode, act, b)
+                pts = workloads.sample_points(p, 60)
+                v, _ = lib.gemm_points(p.M, p.N, p.K, dt, p.A, p.lda, p.B, p.ldb, pts, C0=p.C0, ldc=p.ldc,
+                                       alpha=p.alpha, beta=p.beta, batch=p.batch, strideA=p.strideA,
+                                       strideB=p.strideB, strideC=p.strideC, bias=bias, bias_stride=stride,
+                                       bias_mode=mode, activation=act)
+                assert np.array_equal(v, got[pts[:, 0], pts[:, 1], pts[:, 2]]), (dt, mode, act)
+
+
 ALL_PINS = [pin_decode, pin_identity_permutation, pin_bruteforce_python, pin_numpy_matmul,
-            pin_padding_invariance, pin_closed_forms, pin_batched_and_points]
+            pin_padding_invariance, pin_closed_forms, pin_batched_and_points, pin_fused_tail]

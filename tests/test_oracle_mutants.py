@@ -31,6 +31,17 @@ MUTANTS = {
     "batch_stride_A": [("(size_t)(b * sA)", "(size_t)(b * sB)"), ("(size_t)(pb[p] * sA)", "(size_t)(pb[p] * sB)")],
     "c0_ldc": [("C0[b * sC + i * ldc + j]", "C0[b * sC + i * N + j]"),
                ("C0[pb[p] * sC + pi[p] * ldc + pj[p]]", "C0[pb[p] * sC + pi[p] * N + pj[p]]")],
+    "tail_bias_swapped": [("bias[b * bias_stride + j];\n    if (bias_mode == 2) x += (double)bias[b * bias_stride + i]",
+                           "bias[b * bias_stride + i];\n    if (bias_mode == 2) x += (double)bias[b * bias_stride + j]")],
+    "tail_bias_sign": [("if (bias_mode == 1) x += ", "if (bias_mode == 1) x -= ")],
+    "tail_bias_no_stride": [("bias[b * bias_stride + j]", "bias[j]")],
+    "tail_residual_inside": [("double y = oracle_activation(x, act);\n    if (beta != 0.0) y += beta * (double)C0[b * sC + ldc * i + j];",
+                              "if (beta != 0.0) x += beta * (double)C0[b * sC + ldc * i + j];\n    double y = oracle_activation(x, act);")],
+    "tail_c0_ldc": [("C0[b * sC + ldc * i + j]", "C0[b * sC + (ldc - 1) * i + j]")],
+    "tail_gelu_no_sqrt2": [("erf(x / sqrt(2.0))", "erf(x)")],
+    "tail_gelu_tanh_form": [("x * 0.5 * (1.0 + erf(x / sqrt(2.0)))",
+                             "x * 0.5 * (1.0 + tanh(0.7978845608028654 * (x + 0.044715 * x * x * x)))")],
+    "tail_relu_leaky": [("x < 0.0 ? 0.0 : x", "x < 0.0 ? 0.01 * x : x")],
     "absden_signed": [("t[j] += fabs(a) * fabs(bv);", "t[j] += a * bv;"), ("t += fabs(a) * fabs(bv);", "t += a * bv;")],
 }
 

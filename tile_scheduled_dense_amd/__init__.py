@@ -30,6 +30,8 @@ TG_CFG_AUTO, TG_CFG_256x256, TG_CFG_128x128, TG_CFG_64x64, TG_CFG_F32_64x64 = ra
 # layout-introspection ids of the thin fringe-strip blocks of TG_CFG_256x256
 LAYOUT_CFG_STRIP_N, LAYOUT_CFG_STRIP_M = 101, 102
 SWZ_DEFAULT, SWZ_NONE, SWZ_XOR = 0, 1, 2
+BIAS_NONE, BIAS_PER_COLUMN, BIAS_PER_ROW = 0, 1, 2
+ACT_NONE, ACT_RELU, ACT_GELU = 0, 1, 2
 
 LAYOUT_LDS_A, LAYOUT_LDS_B, LAYOUT_ACC, LAYOUT_COPY_A = range(4)
 AXIS_M, AXIS_LANE, AXIS_WAVE, AXIS_PID, AXIS_TLANE, AXIS_TCOL = range(6)
@@ -55,7 +57,9 @@ class Options(ctypes.Structure):
                 ("swizzle", ctypes.c_int), ("block_order", ctypes.c_int), ("split_k", ctypes.c_int),
                 ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_int64),
                 ("pack_a", ctypes.c_int), ("pad0_", ctypes.c_int), ("plan_lda", ctypes.c_int64),
-                ("tail_gemm", ctypes.c_int), ("persistent", ctypes.c_int)]
+                ("tail_gemm", ctypes.c_int), ("persistent", ctypes.c_int),
+                ("bias", ctypes.c_void_p), ("bias_stride", ctypes.c_int64), ("bias_mode", ctypes.c_int),
+                ("activation", ctypes.c_int)]
 
 
 # size of the options struct in ABI version 1 (the first five ints)
@@ -164,13 +168,14 @@ def _dtype(d) -> int:
 
 
 def _options(config=0, pipeline_depth=0, swizzle=0, block_order=0, split_k=0, workspace=None,
-             workspace_bytes=None, pack_a=0, plan_lda=0, tail_gemm=0, persistent=0) -> Options:
+             workspace_bytes=None, pack_a=0, plan_lda=0, tail_gemm=0, persistent=0, bias=None, bias_stride=0,
+             bias_mode=0, activation=0) -> Options:
     ws = _addr(workspace)
     if workspace_bytes is None:
         workspace_bytes = workspace.numel() * workspace.element_size() if hasattr(workspace, "numel") else 0
     return Options(ctypes.sizeof(Options), int(config), int(pipeline_depth), int(swizzle), int(block_order),
                    int(split_k), ws, int(workspace_bytes), int(pack_a), 0, int(plan_lda), int(tail_gemm),
-                   int(persistent))
+                   int(persistent), _addr(bias), int(bias_stride), int(bias_mode), int(activation))
 
 
 def _check(status: int, where: str):
@@ -201,12 +206,13 @@ def tile_gemm_strided_batched(batch, M, N, K, dtype, A, lda, strideA, B, ldb, st
 def tile_gemm_ex(batch, M, N, K, dtype, A, lda, strideA, B, ldb, strideB, C, ldc, strideC,
                  alpha=1.0, beta=0.0, stream=None, config=0, pipeline_depth=0, swizzle=0,
                  block_order=0, split_k=0, workspace=None, workspace_bytes=None, pack_a=0,
-                 plan_lda=0, tail_gemm=0, persistent=0) -> None:
+                 plan_lda=0, tail_gemm=0, persistent=0, bias=None, bias_stride=0, bias_mode=0,
+                 activation=0) -> None:
     """`workspace`: a device tensor or address for split-K partials or the
     aligned copy of A (its byte size is taken from the tensor unless
     `workspace_bytes` is given)."""
     opt = _options(config, pipeline_depth, swizzle, block_order, split_k, workspace, workspace_bytes, pack_a,
-                   plan_lda, tail_gemm, persistent)
+                   plan_lda, tail_gemm, persistent, bias, bias_stride, bias_mode, activation)
     _check(_lib().tile_gemm_ex(batch, M, N, K, _dtype(dtype), _addr(A), lda, strideA, _addr(B), ldb, strideB,
                                _addr(C), ldc, strideC, alpha, beta, _stream(stream), ctypes.byref(opt)),
            "tile_gemm_ex")
@@ -219,22 +225,23 @@ def tile_gemm_status(fn: str, *args) -> int:
 
 def tile_gemm_plan(batch, M, N, K, dtype, config=0, pipeline_depth=0, swizzle=0, block_order=0,
                    split_k=0, workspace=None, workspace_bytes=None, pack_a=0, plan_lda=0, tail_gemm=0,
-                   persistent=0) -> dict:
+                   persistent=0, bias_mode=0, activation=0) -> dict:
     info = PlanInfo()
     opt = _options(config, pipeline_depth, swizzle, block_order, split_k, workspace, workspace_bytes, pack_a,
-                   plan_lda, tail_gemm, persistent)
+                   plan_lda, tail_gemm, persistent, bias_mode=bias_mode, activation=activation)
     _check(_lib().tile_gemm_plan(batch, M, N, K, _dtype(dtype), ctypes.byref(opt), ctypes.byref(info)),
            "tile_gemm_plan")
     return info.as_dict()
 
 
 def tile_gemm_workspace_size(batch, M, N, K, dtype, config=0, pipeline_depth=0, swizzle=0, block_order=0,
-                             split_k=0, pack_a=0, plan_lda=0, tail_gemm=0, persistent=0) -> int:
+                             split_k=0, pack_a=0, plan_lda=0, tail_gemm=0, persistent=0, bias_mode=0,
+                             activation=0) -> int:
     """Bytes of workspace a call with these arguments would use (split-K partials, the
     aligned copy of A and the remainder GEMMs' partials; 0: none)."""
     n = ctypes.c_int64(0)
     opt = _options(config, pipeline_depth, swizzle, block_order, split_k, None, None, pack_a, plan_lda, tail_gemm,
-                   persistent)
+                   persistent, bias_mode=bias_mode, activation=activation)
     _check(_lib().tile_gemm_workspace_size(batch, M, N, K, _dtype(dtype), ctypes.byref(opt), ctypes.byref(n)),
            "tile_gemm_workspace_size")
     return int(n.value)

@@ -80,7 +80,28 @@ struct GemmParams {
     // columns 0..).  tiles_m / tiles_n then count the main tiles only.
     int64_t strip_n, strip_m;
     int64_t n_main, m_main;
+    // Fused elementwise tail (bias_mode or act nonzero): out = act(alpha * acc
+    // + bias) + beta * C0, the bias one value per column (bias_mode 1) or per
+    // row (2) of each problem, problem b's vector at bias + b * bias_stride.
+    const float *bias;
+    int64_t bias_stride;
+    int bias_mode, act;
 };
+
+// The tail's activation: 1 = ReLU (x < 0 ? 0 : x, so a NaN stays NaN), 2 =
+// GELU in its erf form, x * Phi(x) = x / 2 * (1 + erf(x / sqrt 2)).
+__device__ __forceinline__ float tail_activation(float x, int act) {
+    if (act == 1) return x < 0.0f ? 0.0f : x;
+    if (act == 2) return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f));
+    return x;
+}
+
+// One output of the fused tail: fma(alpha, acc, bias) rounded once, the
+// activation, then beta * C0 added by one more fma (C0 not read when beta is 0).
+__device__ __forceinline__ float tail_value(float acc, float alpha, float bias_v, int act, float beta, float c0) {
+    const float y = tail_activation(__builtin_fmaf(alpha, acc, bias_v), act);
+    return beta != 0.0f ? __builtin_fmaf(beta, c0, y) : y;
+}
 
 template <class C>
 struct AccT {
@@ -239,7 +260,7 @@ __device__ __forceinline__ void mfma_chunk(const u32x4 &a, const u32x4 &b, f32x4
 // per lane whose C0 loads are all issued before any of the chunk's stores:
 // one memory round trip per chunk instead of one per MFMA tile.
 // `acc(i, j, v)` is value v of MFMA tile (i, j) of this lane.
-template <class C, bool FRINGE, class AccFn, int CHUNK_VALUES = 64>
+template <class C, bool FRINGE, class AccFn, int CHUNK_VALUES = 64, bool TAIL = false>
 __device__ __forceinline__ void store_tile_epilogue(const GemmParams &p, const AccFn &acc, int64_t b,
                                                     int64_t m0, int64_t n0, int wave, int lane) {
     float *Cblk = p.C + b * p.sC + m0 * p.ldc + n0;
@@ -263,6 +284,29 @@ __device__ __forceinline__ void store_tile_epilogue(const GemmParams &p, const A
                 off[t][v] = row * ldc + col;
                 ok[t][v] = !FRINGE || (m0 + row < M && n0 + col < N);
             }
+        if constexpr (TAIL) {
+            // fused tail: the chunk's bias values and C0 loads first, then the outputs
+            const float *bias = p.bias + b * p.bias_stride;
+            float bv[CH][V], cv[CH][V];
+#pragma unroll
+            for (int t = 0; t < CH; ++t)
+#pragma unroll
+                for (int v = 0; v < V; ++v) {
+                    int row, col;
+                    acc_coord<C>(wave, lane, (c0t + t) * V + v, row, col);
+                    const int64_t bi = p.bias_mode == 1 ? n0 + col : m0 + row;
+                    bv[t][v] = ok[t][v] && p.bias_mode != 0 ? bias[bi] : 0.0f;
+                    cv[t][v] = ok[t][v] && beta != 0.0f ? Cblk[off[t][v]] : 0.0f;
+                }
+#pragma unroll
+            for (int t = 0; t < CH; ++t)
+#pragma unroll
+                for (int v = 0; v < V; ++v) {
+                    const int i = (c0t + t) / C::TN, j = (c0t + t) % C::TN;
+                    if (ok[t][v]) Cblk[off[t][v]] = tail_value(acc(i, j, v), alpha, bv[t][v], p.act, beta, cv[t][v]);
+                }
+            continue;
+        }
         if (beta != 0.0f) {
             float cv[CH][V];
 #pragma unroll
@@ -289,7 +333,7 @@ __device__ __forceinline__ void store_tile_epilogue(const GemmParams &p, const A
 }
 
 // ---- one workgroup tile ----------------------------------------------------------
-template <class C, int DEPTH, int SWZ, bool FRINGE>
+template <class C, int DEPTH, int SWZ, bool FRINGE, bool TAIL>
 __device__ __forceinline__ void gemm_tile(const GemmParams &p, char *smem, int64_t b, int64_t tm, int64_t tn) {
     using Acc = typename AccT<C>::type;
     constexpr int E = C::ELEM;
@@ -439,17 +483,18 @@ __device__ __forceinline__ void gemm_tile(const GemmParams &p, char *smem, int64
     }
 
     // -- epilogue: fused alpha/beta store-back, masks only here
-    store_tile_epilogue<C, FRINGE>(p, [&](int i, int j, int v) { return acc[i][j][v]; }, b, m0, n0, wave, lane);
+    auto get = [&](int i, int j, int v) { return acc[i][j][v]; };
+    store_tile_epilogue<C, FRINGE, decltype(get), 64, TAIL>(p, get, b, m0, n0, wave, lane);
 }
 
-template <class C, int DEPTH, int SWZ>
+template <class C, int DEPTH, int SWZ, bool TAIL = false>
 __global__ __launch_bounds__(C::THREADS, 1) void gemm_kernel(GemmParams p) {
     __shared__ __attribute__((aligned(16))) char smem[(DEPTH == 2 ? 2 : 1) * C::STAGE_BYTES];
     int64_t b, tm, tn;
     block_coords(p, b, tm, tn);
     const bool interior = (tm + 1) * C::BM <= p.M && (tn + 1) * C::BN <= p.N;
-    if (interior) gemm_tile<C, DEPTH, SWZ, false>(p, smem, b, tm, tn);
-    else gemm_tile<C, DEPTH, SWZ, true>(p, smem, b, tm, tn);
+    if (interior) gemm_tile<C, DEPTH, SWZ, false, TAIL>(p, smem, b, tm, tn);
+    else gemm_tile<C, DEPTH, SWZ, true, TAIL>(p, smem, b, tm, tn);
 }
 
 }  // namespace tg

@@ -498,7 +498,7 @@ struct RingBlock {
 // SCHED_RING (all waves in step): iteration kt waits for tile kt, one
 // barrier (tile kt visible, copy of tile kt-1 released), issues tile
 // kt + STAGES - 1, multiplies tile kt.  STAGES == 1 is the unpipelined form.
-template <class C, int STAGES, int SWZ, bool FRINGE>
+template <class C, int STAGES, int SWZ, bool FRINGE, bool TAIL = false>
 __device__ __forceinline__ void ring_tile(const GemmParams &p, char *smem, int64_t b, int64_t tm, int64_t tn) {
     RingBlock<C, STAGES, SWZ, FRINGE> blk(p, smem, b, tm, tn);
     const int64_t nk = blk.nk, ndma = blk.ndma;
@@ -534,8 +534,8 @@ __device__ __forceinline__ void ring_tile(const GemmParams &p, char *smem, int64
         }
         blk.acc.settle();
     }
-    store_tile_epilogue<C, FRINGE>(p, [&](int i, int j, int v) { return blk.acc.get(i, j, v); }, b, blk.m0, blk.n0,
-                                   blk.wave, blk.lane);
+    auto get = [&](int i, int j, int v) { return blk.acc.get(i, j, v); };
+    store_tile_epilogue<C, FRINGE, decltype(get), TAIL ? 16 : 64, TAIL>(p, get, b, blk.m0, blk.n0, blk.wave, blk.lane);
 }
 
 // SCHED_SWPIPE (software pipeline, one wave per SIMD, large wave tiles): the
@@ -604,7 +604,7 @@ struct SwPipe {
     }
 };
 
-template <class C, int STAGES, int SWZ, bool FRINGE>
+template <class C, int STAGES, int SWZ, bool FRINGE, bool TAIL = false>
 __device__ __forceinline__ void ring_tile_swpipe(const GemmParams &p, char *smem, int64_t b, int64_t tm, int64_t tn) {
     static_assert(STAGES >= 2, "software pipeline needs at least two LDS copies");
     using SP = SwPipe<C, STAGES, SWZ, FRINGE>;
@@ -659,8 +659,8 @@ __device__ __forceinline__ void ring_tile_swpipe(const GemmParams &p, char *smem
         if (t < nk) SP::template iter<false>(blk, t, cur, adv(cur), a1, b1, a0, b0);
         blk.acc.settle();
     }
-    store_tile_epilogue<C, FRINGE>(p, [&](int i, int j, int v) { return blk.acc.get(i, j, v); }, b, blk.m0, blk.n0,
-                                   blk.wave, blk.lane);
+    auto get = [&](int i, int j, int v) { return blk.acc.get(i, j, v); };
+    store_tile_epilogue<C, FRINGE, decltype(get), TAIL ? 16 : 64, TAIL>(p, get, b, blk.m0, blk.n0, blk.wave, blk.lane);
 }
 
 // Persistent form of the software pipeline for a grid of interior tiles of
@@ -675,7 +675,7 @@ __device__ __forceinline__ void ring_tile_swpipe(const GemmParams &p, char *smem
 // fragments are read after the epilogue (holding them through it would take
 // the epilogue's registers); no iteration but the last tile's drain leaves
 // the steady form.
-template <class C, int STAGES, int SWZ>
+template <class C, int STAGES, int SWZ, bool TAIL = false>
 __device__ __forceinline__ void ring_persistent(const GemmParams &p, char *smem) {
     static_assert(STAGES == 4, "four LDS copies: a tile's copies sit at t mod 4");
     using SP = SwPipe<C, STAGES, SWZ, false>;
@@ -721,8 +721,8 @@ __device__ __forceinline__ void ring_persistent(const GemmParams &p, char *smem)
         SP::template iter<true>(blk, t + 5, 2, 3, a0, b0, a1, b1);       // its 2
         SP::template iter<true, false, false>(blk, t + 6, 3, 0, a1, b1, a0, b0);   // its 3; lands its 0
         blk.acc.settle();
-        store_tile_epilogue<C, false>(p, [&](int i, int j, int v2) { return blk.acc.get(i, j, v2); }, 0, blk.m0,
-                                      blk.n0, blk.wave, blk.lane);
+        auto get = [&](int i, int j, int v2) { return blk.acc.get(i, j, v2); };
+        store_tile_epilogue<C, false, decltype(get), TAIL ? 16 : 64, TAIL>(p, get, 0, blk.m0, blk.n0, blk.wave, blk.lane);
         if (!next) break;
         blk.m0 = tmn * C::BM;
         blk.n0 = tnn * C::BN;
@@ -736,10 +736,10 @@ __device__ __forceinline__ void ring_persistent(const GemmParams &p, char *smem)
     wait_vmcnt<0>();
 }
 
-template <class C, int STAGES, int SWZ>
+template <class C, int STAGES, int SWZ, bool TAIL = false>
 __global__ __launch_bounds__(C::THREADS, C::OCCUPANCY) void gemm_ring_persistent_kernel(GemmParams p) {
     __shared__ __attribute__((aligned(1024))) char smem[STAGES * C::STAGE_BYTES];
-    ring_persistent<C, STAGES, SWZ>(p, smem);
+    ring_persistent<C, STAGES, SWZ, TAIL>(p, smem);
 }
 
 // The problem of grid batch entry b with its batch offsets folded into the
@@ -757,6 +757,8 @@ __device__ __forceinline__ GemmParams entry_params(const GemmParams &p, int64_t 
         q.ldc = p.N;
         q.alpha = 1.0f;
         q.beta = 0.0f;
+        q.bias_mode = 0;        // the tail belongs to the combine pass
+        q.act = 0;
     } else {
         q.A = p.A + b * p.sA * 2;
         q.B = p.B + b * p.sB * 2;
@@ -765,13 +767,13 @@ __device__ __forceinline__ GemmParams entry_params(const GemmParams &p, int64_t 
     return q;
 }
 
-template <class C, int STAGES, int SWZ, int SCHED, bool FRINGE>
+template <class C, int STAGES, int SWZ, int SCHED, bool FRINGE, bool TAIL>
 __device__ __forceinline__ void run_tile(const GemmParams &q, char *smem, int64_t tm, int64_t tn) {
-    if constexpr (SCHED == SCHED_SWPIPE) ring_tile_swpipe<C, STAGES, SWZ, FRINGE>(q, smem, 0, tm, tn);
-    else ring_tile<C, STAGES, SWZ, FRINGE>(q, smem, 0, tm, tn);
+    if constexpr (SCHED == SCHED_SWPIPE) ring_tile_swpipe<C, STAGES, SWZ, FRINGE, TAIL>(q, smem, 0, tm, tn);
+    else ring_tile<C, STAGES, SWZ, FRINGE, TAIL>(q, smem, 0, tm, tn);
 }
 
-template <class C, int STAGES, int SWZ, int SCHED>
+template <class C, int STAGES, int SWZ, int SCHED, bool TAIL = false>
 __global__ __launch_bounds__(C::THREADS, C::OCCUPANCY) void gemm_ring_kernel(GemmParams p) {
     static_assert(STAGES >= 1 && STAGES <= 5, "1 to 5 LDS copies");
     static_assert(SCHED == SCHED_RING || SCHED == SCHED_SWPIPE, "schedule");
@@ -788,8 +790,8 @@ __global__ __launch_bounds__(C::THREADS, C::OCCUPANCY) void gemm_ring_kernel(Gem
             const int64_t s = (int64_t)blockIdx.x - main_blocks;
             const int64_t b = s / per, r = s - b * per;
             const GemmParams q = entry_params(p, b);
-            if (r < p.strip_n) run_tile<SN, STAGES, SWZ, SCHED, true>(q, smem, r, p.n_main / SN::BN);
-            else run_tile<SM, STAGES, SWZ, SCHED, true>(q, smem, p.m_main / SM::BM, r - p.strip_n);
+            if (r < p.strip_n) run_tile<SN, STAGES, SWZ, SCHED, true, TAIL>(q, smem, r, p.n_main / SN::BN);
+            else run_tile<SM, STAGES, SWZ, SCHED, true, TAIL>(q, smem, p.m_main / SM::BM, r - p.strip_n);
             return;
         }
     }
@@ -797,8 +799,8 @@ __global__ __launch_bounds__(C::THREADS, C::OCCUPANCY) void gemm_ring_kernel(Gem
     block_coords(p, b, tm, tn);
     const GemmParams q = entry_params(p, b);
     const bool interior = (tm + 1) * C::BM <= p.M && (tn + 1) * C::BN <= p.N;
-    if (interior) run_tile<C, STAGES, SWZ, SCHED, false>(q, smem, tm, tn);
-    else run_tile<C, STAGES, SWZ, SCHED, true>(q, smem, tm, tn);
+    if (interior) run_tile<C, STAGES, SWZ, SCHED, false, TAIL>(q, smem, tm, tn);
+    else run_tile<C, STAGES, SWZ, SCHED, true, TAIL>(q, smem, tm, tn);
 }
 
 }  // namespace tg

@@ -12,6 +12,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "gemm_kernel.hpp"
+
 namespace tg {
 
 // Partial s of element idx (idx = b * M * N + i * N + j over all problems) is
@@ -21,7 +23,9 @@ namespace tg {
 template <int P>
 __global__ __launch_bounds__(256) void splitk_combine_kernel(const float *__restrict__ W, float *__restrict__ C,
                                                              int64_t M, int64_t N, int64_t ldc, int64_t sC,
-                                                             int64_t problems, int S, float alpha, float beta) {
+                                                             int64_t problems, int S, float alpha, float beta,
+                                                             const float *__restrict__ bias, int64_t bias_stride,
+                                                             int bias_mode, int act) {
     const int64_t plane = M * N, total = problems * plane;
     const int64_t step = (int64_t)gridDim.x * blockDim.x;
     for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total; idx += step) {
@@ -36,7 +40,12 @@ __global__ __launch_bounds__(256) void splitk_combine_kernel(const float *__rest
         const int64_t b = idx / plane, r = idx - b * plane;
         const int64_t i = r / N, j = r - i * N;
         float *c = C + b * sC + i * ldc + j;
-        *c = beta != 0.0f ? __builtin_fmaf(alpha, v[0], beta * *c) : alpha * v[0];
+        if (bias_mode != 0 || act != 0) {
+            const float bv = bias_mode == 1 ? bias[b * bias_stride + j] : (bias_mode == 2 ? bias[b * bias_stride + i] : 0.0f);
+            *c = tail_value(v[0], alpha, bv, act, beta, beta != 0.0f ? *c : 0.0f);
+        } else {
+            *c = beta != 0.0f ? __builtin_fmaf(alpha, v[0], beta * *c) : alpha * v[0];
+        }
     }
 }
 

@@ -185,6 +185,22 @@ tg_status make_plan(int64_t batch, int64_t M, int64_t N, int64_t K, tg_dtype dty
         want = o.split_k < kMaxSplits ? o.split_k : kMaxSplits;
     }
     if (!config) config = choose_config(batch, M, N, dtype);
+    // A fused tail in the GEMM's own epilogue (no split) is built for every
+    // configuration but the 256 x 256 tile: there its 256 accumulators per
+    // lane leave no registers for the tail, and the compiler would move
+    // accumulators to scratch right behind the (inline, hazard-unaware) MFMAs.
+    // The automatic choice then takes 128 x 128; a forced 256 x 256 with a
+    // tail needs a split (the combine pass applies the tail).
+    const bool tail_req = o.bias_mode != 0 || o.activation != 0;
+    if (tail_req && config == TG_CFG_256x256) {
+        // the split that takes effect: a K that fits one slice is not split
+        const int64_t bk = cfg_dims(TG_CFG_256x256).bk;
+        const int64_t eff = K > 0 ? cdiv(K, cdiv(cdiv(K, want), bk) * bk) : 1;
+        if (eff == 1) {
+            if (o.config) return TG_ERR_UNSUPPORTED;
+            config = TG_CFG_128x128;
+        }
+    }
     if (config < TG_CFG_256x256 || config > TG_CFG_F32_64x64) return TG_ERR_INVALID_ARG;
     if ((dtype == TG_F32) != (config == TG_CFG_F32_64x64)) return TG_ERR_UNSUPPORTED;
     // pipeline depth = LDS copies of the K tile (window = depth - 1)
@@ -253,6 +269,12 @@ tg_status make_plan(int64_t batch, int64_t M, int64_t N, int64_t K, tg_dtype dty
     out.workspace = splits > 1 ? o.workspace : nullptr;
     out.workspace_given = o.workspace_bytes;
 
+    // the fused tail is built into the default depth and swizzle only (a split
+    // call applies it in the combine pass)
+    if ((o.bias_mode != 0 || o.activation != 0) && splits == 1 &&
+        (depth != (f32 ? 2 : 4) || swz != SWZ_XOR))
+        return TG_ERR_UNSUPPORTED;
+
     // Repack of A (see tile_gemm.h): rows not on 16-byte boundaries, a plan
     // whose A panels are each read by many workgroups, no split.
     if (o.pack_a < 0 || o.pack_a > 2) return TG_ERR_INVALID_ARG;
@@ -285,6 +307,10 @@ tg_status make_plan(int64_t batch, int64_t M, int64_t N, int64_t K, tg_dtype dty
     // 8 us, the separate GEMM and its combine about 33 us.
     if (o.tail_gemm < 0 || o.tail_gemm > 2) return TG_ERR_INVALID_ARG;
     if (o.persistent < 0 || o.persistent > 2) return TG_ERR_INVALID_ARG;
+    // the bias pointer itself is checked by the call (a plan query needs only the modes)
+    if (o.bias_mode < 0 || o.bias_mode > 2 || o.activation < 0 || o.activation > 2 || o.bias_stride < 0 ||
+        reinterpret_cast<uintptr_t>(o.bias) % 4)
+        return TG_ERR_INVALID_ARG;
     if (some && strip_n + strip_m > 0 && splits == 1) {
         if (o.tail_gemm == 2) {
             const int64_t n_main = p.tiles_n * d.bn, m_main = p.tiles_m * d.bm;
@@ -386,15 +412,20 @@ bool offsets_fit(const tg_plan_info &p, int64_t K, int64_t lda, int64_t ldb, int
            (int64_t)p.block_m * ldc + p.block_n < lim;
 }
 
-template <class C, int DEPTH, int SWZ>
+template <class C, int DEPTH, int SWZ, bool TAIL = false>
 tg_status launch_one(const GemmParams &gp, int64_t grid, hipStream_t stream) {
     if (grid > 0x7fffffffLL) return TG_ERR_UNSUPPORTED;
-    hipLaunchKernelGGL((gemm_kernel<C, DEPTH, SWZ>), dim3((unsigned)grid), dim3(C::THREADS), 0, stream, gp);
+    hipLaunchKernelGGL((gemm_kernel<C, DEPTH, SWZ, TAIL>), dim3((unsigned)grid), dim3(C::THREADS), 0, stream, gp);
     return hipGetLastError() == hipSuccess ? TG_OK : TG_ERR_LAUNCH;
 }
 
+// tail: the fused-tail instantiation (built for the default depth and swizzle only)
 template <class C>
-tg_status launch_variants(const GemmParams &gp, const tg_plan_info &p, hipStream_t s) {
+tg_status launch_variants(const GemmParams &gp, const tg_plan_info &p, hipStream_t s, bool tail) {
+    if (tail) {
+        if (p.pipeline_depth == 2 && p.swizzle == SWZ_XOR) return launch_one<C, 2, SWZ_XOR, true>(gp, p.grid, s);
+        return TG_ERR_UNSUPPORTED;
+    }
     if (p.pipeline_depth == 2 && p.swizzle == SWZ_XOR) return launch_one<C, 2, SWZ_XOR>(gp, p.grid, s);
     if (p.pipeline_depth == 1 && p.swizzle == SWZ_XOR) return launch_one<C, 1, SWZ_XOR>(gp, p.grid, s);
     if (p.pipeline_depth == 2 && p.swizzle == SWZ_NONE) return launch_one<C, 2, SWZ_NONE>(gp, p.grid, s);
@@ -402,18 +433,28 @@ tg_status launch_variants(const GemmParams &gp, const tg_plan_info &p, hipStream
     return TG_ERR_UNSUPPORTED;
 }
 
-template <class C, int STAGES, int SWZ, int SCHED>
+template <class C, int STAGES, int SWZ, int SCHED, bool TAIL = false>
 tg_status launch_ring_one(const GemmParams &gp, int64_t grid, hipStream_t stream) {
     if (grid > 0x7fffffffLL) return TG_ERR_UNSUPPORTED;
-    hipLaunchKernelGGL((gemm_ring_kernel<C, STAGES, SWZ, SCHED>), dim3((unsigned)grid), dim3(C::THREADS), 0, stream, gp);
+    hipLaunchKernelGGL((gemm_ring_kernel<C, STAGES, SWZ, SCHED, TAIL>), dim3((unsigned)grid), dim3(C::THREADS), 0,
+                       stream, gp);
     return hipGetLastError() == hipSuccess ? TG_OK : TG_ERR_LAUNCH;
 }
 
 // SWPIPE: the 256 x 256 tile (one wave per SIMD, a whole K tile of fragments
 // in registers) whenever it has two or more LDS copies; RING otherwise.
 template <class C, bool SWPIPE>
-tg_status launch_ring(const GemmParams &gp, const tg_plan_info &p, hipStream_t s) {
+tg_status launch_ring(const GemmParams &gp, const tg_plan_info &p, hipStream_t s, bool tail) {
     constexpr int SCHED = SWPIPE ? SCHED_SWPIPE : SCHED_RING;
+    if (tail) {
+        if constexpr (SWPIPE) {
+            return TG_ERR_UNSUPPORTED;      // the 256 x 256 tile: not built with the tail
+        } else {
+            if (p.pipeline_depth == 4 && p.swizzle == SWZ_XOR)
+                return launch_ring_one<C, 4, SWZ_XOR, SCHED, true>(gp, p.grid, s);
+            return TG_ERR_UNSUPPORTED;
+        }
+    }
     if (p.swizzle == SWZ_XOR) {
         switch (p.pipeline_depth) {
             case 5:
@@ -431,38 +472,43 @@ tg_status launch_ring(const GemmParams &gp, const tg_plan_info &p, hipStream_t s
 
 template <int P>
 tg_status launch_combine_p(const float *W, float *C, int64_t M, int64_t N, int64_t ldc, int64_t sC,
-                           int64_t problems, int S, float alpha, float beta, hipStream_t stream) {
+                           int64_t problems, int S, float alpha, float beta, const float *bias,
+                           int64_t bias_stride, int bias_mode, int act, hipStream_t stream) {
     const int64_t total = problems * M * N;
     const int64_t blocks = cdiv(total, 256) < 8192 ? cdiv(total, 256) : 8192;
     hipLaunchKernelGGL((splitk_combine_kernel<P>), dim3((unsigned)blocks), dim3(256), 0, stream, W, C, M, N, ldc,
-                       sC, problems, S, alpha, beta);
+                       sC, problems, S, alpha, beta, bias, bias_stride, bias_mode, act);
     return hipGetLastError() == hipSuccess ? TG_OK : TG_ERR_LAUNCH;
 }
 
 tg_status launch_combine(const float *W, float *C, int64_t M, int64_t N, int64_t ldc, int64_t sC,
-                         int64_t problems, int S, float alpha, float beta, hipStream_t stream) {
-    if (S <= 2) return launch_combine_p<2>(W, C, M, N, ldc, sC, problems, S, alpha, beta, stream);
-    if (S <= 4) return launch_combine_p<4>(W, C, M, N, ldc, sC, problems, S, alpha, beta, stream);
-    if (S <= 8) return launch_combine_p<8>(W, C, M, N, ldc, sC, problems, S, alpha, beta, stream);
-    if (S <= 16) return launch_combine_p<16>(W, C, M, N, ldc, sC, problems, S, alpha, beta, stream);
-    if (S <= 32) return launch_combine_p<32>(W, C, M, N, ldc, sC, problems, S, alpha, beta, stream);
-    if (S <= 64) return launch_combine_p<64>(W, C, M, N, ldc, sC, problems, S, alpha, beta, stream);
+                         int64_t problems, int S, float alpha, float beta, const float *bias, int64_t bias_stride,
+                         int bias_mode, int act, hipStream_t stream) {
+#define TG_COMBINE(P) launch_combine_p<P>(W, C, M, N, ldc, sC, problems, S, alpha, beta, bias, bias_stride, bias_mode, act, stream)
+    if (S <= 2) return TG_COMBINE(2);
+    if (S <= 4) return TG_COMBINE(4);
+    if (S <= 8) return TG_COMBINE(8);
+    if (S <= 16) return TG_COMBINE(16);
+    if (S <= 32) return TG_COMBINE(32);
+    if (S <= 64) return TG_COMBINE(64);
+#undef TG_COMBINE
     return TG_ERR_INTERNAL;
 }
 
 template <int DT>
-tg_status launch_dtype(const GemmParams &gp, const tg_plan_info &p, hipStream_t s) {
+tg_status launch_dtype(const GemmParams &gp, const tg_plan_info &p, hipStream_t s, bool tail) {
     if (p.persistent) {
         if (p.config != TG_CFG_256x256 || p.pipeline_depth != 4 || p.swizzle != SWZ_XOR) return TG_ERR_INTERNAL;
         using C = Ring256<DT>;
+        if (tail) return TG_ERR_INTERNAL;   // the plan never pairs the persistent grid with a tail
         hipLaunchKernelGGL((gemm_ring_persistent_kernel<C, 4, SWZ_XOR>), dim3((unsigned)p.grid), dim3(C::THREADS), 0,
                            s, gp);
         return hipGetLastError() == hipSuccess ? TG_OK : TG_ERR_LAUNCH;
     }
     switch (p.config) {
-        case TG_CFG_256x256: return launch_ring<Ring256<DT>, true>(gp, p, s);
-        case TG_CFG_128x128: return launch_ring<Ring128<DT>, false>(gp, p, s);
-        case TG_CFG_64x64: return launch_ring<Ring64<DT>, false>(gp, p, s);
+        case TG_CFG_256x256: return launch_ring<Ring256<DT>, true>(gp, p, s, tail);
+        case TG_CFG_128x128: return launch_ring<Ring128<DT>, false>(gp, p, s, tail);
+        case TG_CFG_64x64: return launch_ring<Ring64<DT>, false>(gp, p, s, tail);
         default: return TG_ERR_UNSUPPORTED;
     }
 }
@@ -476,6 +522,10 @@ tg_status run(int64_t batch, int64_t M, int64_t N, int64_t K, tg_dtype dtype,
     Plan plan;
     st = make_plan(batch, M, N, K, dtype, opt, lda, reinterpret_cast<uintptr_t>(A) % 16 == 0, plan);
     if (st != TG_OK) return st;
+    // the fused tail (modes validated by make_plan): the caller's struct may predate it
+    tg_options to{};
+    if (opt) std::memcpy(&to, opt, opt->struct_size < (int)sizeof to ? (size_t)opt->struct_size : sizeof to);
+    if ((to.bias_mode == 0) != (to.bias == nullptr)) return TG_ERR_INVALID_ARG;
     if (batch == 0 || M == 0 || N == 0) return TG_OK;
     if (!offsets_fit(plan.info, K, lda, ldb, ldc, dtype == TG_F32 ? 4 : 2)) return TG_ERR_UNSUPPORTED;
     const bool split = plan.info.split_k > 1;
@@ -498,6 +548,13 @@ tg_status run(int64_t batch, int64_t M, int64_t N, int64_t K, tg_dtype dtype,
     }
     st = current_device_ok();
     if (st != TG_OK) return st;
+
+    if (to.bias_mode != 0) {
+        const int64_t len = to.bias_mode == 1 ? N : M;
+        const Range rb{reinterpret_cast<uintptr_t>(to.bias),
+                       reinterpret_cast<uintptr_t>(to.bias + (batch - 1) * to.bias_stride + len)};
+        if (overlaps(rb, span(C, batch, M, N, ldc, sC, 4))) return TG_ERR_INVALID_ARG;
+    }
 
     GemmParams gp;
     gp.A = static_cast<const char *>(A);
@@ -533,6 +590,10 @@ tg_status run(int64_t batch, int64_t M, int64_t N, int64_t K, tg_dtype dtype,
     gp.strip_m = plan.strip_m;
     gp.n_main = plan.info.tiles_n * plan.info.block_n;
     gp.m_main = plan.info.tiles_m * plan.info.block_m;
+    gp.bias = to.bias;
+    gp.bias_stride = to.bias_stride;
+    gp.bias_mode = to.bias_mode;
+    gp.act = to.activation;
     if (split) gp.batch = batch * plan.info.split_k;   // (slice, problem) pairs
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (pack) {
@@ -546,16 +607,20 @@ tg_status run(int64_t batch, int64_t M, int64_t N, int64_t K, tg_dtype dtype,
         gp.sA = M * plan.lda_packed;
         gp.W = nullptr;
     }
+    // the fused tail in the GEMM's own epilogue; a split call leaves it to the combine
+    const bool tail = (to.bias_mode != 0 || to.activation != 0) && !split;
     switch (dtype) {
-        case TG_BF16: st = launch_dtype<DT_BF16>(gp, plan.info, s); break;
-        case TG_F16: st = launch_dtype<DT_F16>(gp, plan.info, s); break;
+        case TG_BF16: st = launch_dtype<DT_BF16>(gp, plan.info, s, tail); break;
+        case TG_F16: st = launch_dtype<DT_F16>(gp, plan.info, s, tail); break;
         case TG_F32:
             if (plan.info.config != TG_CFG_F32_64x64) return TG_ERR_UNSUPPORTED;
-            return launch_variants<CfgF32>(gp, plan.info, s);
+            return launch_variants<CfgF32>(gp, plan.info, s, tail);
         default: return TG_ERR_INVALID_ARG;
     }
     if (st != TG_OK) return st;
-    if (split) return launch_combine(gp.W, C, M, N, ldc, sC, batch, plan.info.split_k, alpha, beta, s);
+    if (split)
+        return launch_combine(gp.W, C, M, N, ldc, sC, batch, plan.info.split_k, alpha, beta, to.bias,
+                              to.bias_stride, to.bias_mode, to.activation, s);
     // the thin remainders' own GEMMs (on the A copy when there is one)
     for (const Tail *t : {&plan.tail_n, &plan.tail_m}) {
         if (t->splits == 0) continue;
@@ -567,6 +632,11 @@ tg_status run(int64_t batch, int64_t M, int64_t N, int64_t K, tg_dtype dtype,
         sub.workspace_bytes = t->ws_bytes;
         sub.pack_a = 1;
         sub.tail_gemm = 1;
+        // the remainder's own slice of a per-column / per-row bias
+        sub.bias = to.bias_mode == 1 ? to.bias + t->n0 : (to.bias_mode == 2 ? to.bias + t->m0 : nullptr);
+        sub.bias_stride = to.bias_stride;
+        sub.bias_mode = to.bias_mode;
+        sub.activation = to.activation;
         st = run(batch, t->rows, t->cols, K, dtype, gp.A + t->m0 * gp.lda * 2, gp.lda, gp.sA, gp.B + t->n0 * 2, ldb,
                  sB, C + t->m0 * ldc + t->n0, ldc, sC, alpha, beta, stream, &sub);
         if (st != TG_OK) return st;
