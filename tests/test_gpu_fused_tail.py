@@ -119,23 +119,25 @@ def test_fused_tail_parity(dt, M, N, K, batch, cfg, split, alpha, beta, mode, ac
 
 
 @pytest.mark.parametrize("mode,stride", [(1, 0), (1, 300), (2, 0), (2, 250)])
-@pytest.mark.parametrize("split", [1, 2])
-def test_fused_tail_batched(mode, stride, split):
-    p = workloads.custom("bf16", 200, 260, 600, batch=3, ldb_pad=1, alpha=1.25, beta=0.5, seed=31, name="fb")
+@pytest.mark.parametrize("cfg,split", [(tg.TG_CFG_128x128, 1), (tg.TG_CFG_64x64, 1), (tg.TG_CFG_128x128, 2),
+                                       (tg.TG_CFG_F32_64x64, 1)])
+def test_fused_tail_batched(mode, stride, cfg, split):
+    dt = "f32" if cfg == tg.TG_CFG_F32_64x64 else "bf16"
+    p = workloads.custom(dt, 200, 260, 600, batch=3, ldb_pad=1, alpha=1.25, beta=0.5, seed=31, name="fb")
     bias = make_bias(p, mode, stride, seed=stride + mode)
     bias_t = torch.from_numpy(bias).to("cuda")
-    gp = run(p, bias_t, stride, mode, 2, config=tg.TG_CFG_128x128, split_k=split)
+    gp = run(p, bias_t, stride, mode, 2, config=cfg, split_k=split)
     check(p, gp.result(), bias, stride, mode, 2)
     gp.check_guards()
 
 
 def test_auto_choice_leaves_256():
-    # 2048 x 2048 x 2048 takes the 256 x 256 tile on its own; with a tail and no split, 128 x 128
-    base = tg.tile_gemm_plan(1, 2048, 2048, 2048, "bf16")
+    # 4096 x 4096 x 512 takes the 256 x 256 tile on its own; with a tail and no split, 128 x 128
+    base = tg.tile_gemm_plan(1, 4096, 4096, 512, "bf16")
     assert base["config"] == tg.TG_CFG_256x256
-    with_tail = tg.tile_gemm_plan(1, 2048, 2048, 2048, "bf16", bias_mode=1)
-    assert with_tail["config"] == tg.TG_CFG_128x128 and with_tail["split_k"] == 1
-    p = workloads.custom("bf16", 2048, 2048, 2048, alpha=1.0, beta=0.0, seed=4, name="auto")
+    with_tail = tg.tile_gemm_plan(1, 4096, 4096, 512, "bf16", bias_mode=1)
+    assert (with_tail["config"], with_tail["split_k"]) == (tg.TG_CFG_128x128, 1)
+    p = workloads.custom("bf16", 4096, 4096, 512, alpha=1.0, beta=0.0, seed=4, name="auto")
     bias = make_bias(p, 1, 0, seed=4)
     gp = run(p, torch.from_numpy(bias).to("cuda"), 0, 1, 1)
     pts = workloads.sample_points(p, 400)

@@ -763,6 +763,7 @@ __device__ __forceinline__ GemmParams entry_params(const GemmParams &p, int64_t 
         q.A = p.A + b * p.sA * 2;
         q.B = p.B + b * p.sB * 2;
         q.C = p.C + b * p.sC;
+        if (p.bias_mode != 0) q.bias = p.bias + b * p.bias_stride;   // the epilogue then sees entry 0
     }
     return q;
 }
