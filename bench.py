@@ -47,13 +47,24 @@ def parse():
                     help="thin N/M remainder as a GEMM of its own (0, 1 = strips in the grid, 2 = always)")
     ap.add_argument("--persistent", type=int, default=0,
                     help="persistent workgroups (0, 1 = the plain grid; 2 = persistent where the plan allows)")
+    ap.add_argument("--bias-mode", type=int, default=0,
+                    help="fused tail bias: 0 none, 1 one value per column, 2 one per row (seeded normal)")
+    ap.add_argument("--activation", type=int, default=0, help="fused tail activation: 0 none, 1 ReLU, 2 GELU")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after timing, run a plain device copy of this many MiB (3 times) so HBM "
                          "byte counters can be scaled against a kernel of known traffic")
     return ap.parse_args()
 
 
-def cpu_baseline(p, seconds):
+def tail_args(p, bias, bias_mode, activation, row0, rows):
+    """The oracle's fused-tail arguments for output rows [row0, row0 + rows) (one shared bias vector)."""
+    if bias is None:
+        return dict(activation=activation)
+    b = bias if bias_mode == 1 else bias[row0: row0 + rows]
+    return dict(bias=b, bias_stride=0, bias_mode=bias_mode, activation=activation)
+
+
+def cpu_baseline(p, seconds, bias=None, bias_mode=0, activation=0):
     """The oracle on rows [0, R) of the workload's output, R grown until ~`seconds` of work."""
     import numpy as np
 
@@ -70,7 +81,8 @@ def cpu_baseline(p, seconds):
         if p.beta != 0:
             C0 = np.ascontiguousarray(p.C0[rows_done * p.ldc: rows_done * p.ldc + r * p.ldc])
         t = time.perf_counter()
-        oracle.gemm(r, p.N, p.K, p.dtype, A, p.lda, p.B, p.ldb, C0=C0, ldc=p.ldc, alpha=p.alpha, beta=p.beta)
+        oracle.gemm(r, p.N, p.K, p.dtype, A, p.lda, p.B, p.ldb, C0=C0, ldc=p.ldc, alpha=p.alpha, beta=p.beta,
+                    **tail_args(p, bias, bias_mode, activation, rows_done, r))
         t_total += time.perf_counter() - t
         rows_done += r
         flops += 2.0 * r * p.N * p.K
@@ -80,7 +92,7 @@ def cpu_baseline(p, seconds):
                       f"fp64 triple loop, {t_total:.1f} s"}
 
 
-def oracle_rows(p, rows):
+def oracle_rows(p, rows, bias=None, bias_mode=0, activation=0):
     """The oracle's rows [0, rows) of batch entry 0 and their sum_k |a||b| (not timed)."""
     import numpy as np
 
@@ -88,7 +100,7 @@ def oracle_rows(p, rows):
     A = np.ascontiguousarray(p.A[: rows * p.lda])
     C0 = np.ascontiguousarray(p.C0[: rows * p.ldc]) if p.beta != 0 else None
     ref, den = oracle.gemm(rows, p.N, p.K, p.dtype, A, p.lda, p.B, p.ldb, C0=C0, ldc=p.ldc, alpha=p.alpha,
-                           beta=p.beta, with_absden=True)
+                           beta=p.beta, with_absden=True, **tail_args(p, bias, bias_mode, activation, 0, rows))
     return ref[0], den[0]
 
 
@@ -136,17 +148,26 @@ def main():
     stream = torch.cuda.current_stream()
     opts = dict(config=args.config, pipeline_depth=args.pipeline_depth, swizzle=args.swizzle,
                 block_order=args.block_order, split_k=args.split_k, pack_a=args.pack_a, plan_lda=p.lda,
-                tail_gemm=args.tail_gemm, persistent=args.persistent)
+                tail_gemm=args.tail_gemm, persistent=args.persistent, bias_mode=args.bias_mode,
+                activation=args.activation)
+    # fused tail: one seeded bias vector shared by the batch, about the size of alpha * A.B
+    bias_np = None
+    if args.bias_mode:
+        n_bias = p.N if args.bias_mode == 1 else p.M
+        bias_np = (np.random.default_rng(p.seed + 101).standard_normal(n_bias)
+                   * abs(p.alpha) * max(p.K, 1) ** 0.5 / 3).astype(np.float32)
+    call_opts = dict(bias=torch.from_numpy(bias_np).to("cuda") if bias_np is not None else None)
     # workspace (split-K partials, the aligned copy of A, remainder partials): allocated once, outside
     # the timed region, as a caller would
     ws_bytes = tg.tile_gemm_workspace_size(p.batch, p.M, p.N, p.K, p.dtype, **opts)
     if ws_bytes:
         opts["workspace"] = torch.empty(ws_bytes // 4, dtype=torch.float32, device="cuda")
     plan = tg.tile_gemm_plan(p.batch, p.M, p.N, p.K, p.dtype, **opts)
+    call_opts.update(opts)
 
     def step():
         tg.tile_gemm_ex(p.batch, p.M, p.N, p.K, p.dtype, A, p.lda, p.strideA, B, p.ldb, p.strideB,
-                        C, p.ldc, p.strideC, p.alpha, p.beta, stream, **opts)
+                        C, p.ldc, p.strideC, p.alpha, p.beta, stream, **call_opts)
 
     for _ in range(args.warmup):
         step()
@@ -226,16 +247,18 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(p, args.cpu_seconds)
+        cpu = cpu_baseline(p, args.cpu_seconds, bias_np, args.bias_mode, args.activation)
         # the observed parity error on the oracle's first rows: one fresh call
         # (C reset to C0), compared with the stated metric
         rows = min(8, p.M)
         Cf = to_dev(p.C0.copy()) if p.beta != 0 else torch.zeros(p.sizeC(), dtype=torch.float32, device="cuda")
         tg.tile_gemm_ex(p.batch, p.M, p.N, p.K, p.dtype, A, p.lda, p.strideA, B, p.ldb, p.strideB,
-                        Cf, p.ldc, p.strideC, p.alpha, p.beta, stream, **opts)
+                        Cf, p.ldc, p.strideC, p.alpha, p.beta, stream, **call_opts)
         torch.cuda.synchronize()
         got = Cf[: rows * p.ldc].view(rows, p.ldc)[:, : p.N].cpu().numpy().astype(np.float64)
-        ref, den = oracle_rows(p, rows)
+        ref, den = oracle_rows(p, rows, bias_np, args.bias_mode, args.activation)
+        if bias_np is not None:     # the bias is summed into the output too
+            den = den + np.abs(bias_np[None, :] if args.bias_mode == 1 else bias_np[:rows, None])
         cpu["parity_max_rel_err"] = float(np.max(np.abs(got - ref) / (den + 1e-30)))
         cpu["parity_sample"] = f"output rows 0..{rows - 1}, batch 0, metric max |C - C_ref| / (sum |a||b| + 1e-30)"
 
@@ -251,7 +274,7 @@ def main():
                    "pipeline_depth": plan["pipeline_depth"], "split_k": plan["split_k"],
                    "pack_a": plan["pack_a"], "strip_blocks": plan["strip_blocks"],
                    "tail_n_splits": plan["tail_n_splits"], "tail_m_splits": plan["tail_m_splits"],
-                   "persistent": plan["persistent"],
+                   "persistent": plan["persistent"], "bias_mode": args.bias_mode, "activation": args.activation,
                    "grid": plan["grid"]},
         "roofline": roofline,
         "step_stats": step_stats,

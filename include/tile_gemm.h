@@ -162,16 +162,19 @@ typedef enum {
  * read when beta == 0), in fp32.  bias_mode 1: bias[j], one value per column
  * (N floats per problem); 2: bias[i], one per row (M floats); problem b reads
  * its vector at bias + b * bias_stride (0 = one vector shared by the batch).
- * activation 1: ReLU, x < 0 ? 0 : x (NaN passes through); 2: GELU in its erf
- * form, x * Phi(x) = x/2 * (1 + erf(x / sqrt(2))), with the device's erff.
+ * activation 1: ReLU, x < 0 ? 0 : x (NaN passes through); 2: GELU in its exact
+ * form x * Phi(x) = x/2 * (1 + erf(x / sqrt(2))), Phi evaluated through a
+ * Chebyshev fit of erfc with fractional error below 1.2e-7 (Numerical Recipes,
+ * section 6.2): the fp32 result is within 2.4e-7 |x| of x * Phi(x).
  * Without them the epilogue is fma(alpha, acc, beta * C0) as before.  The
  * bias must be 4-byte aligned, non-NULL exactly when bias_mode != 0, and
  * must not overlap C (tile_gemm_plan and tile_gemm_workspace_size do not read
- * it: for them the modes alone shape the plan, and a NULL bias is accepted).  The tail is built for the default pipeline depth and
- * swizzle (others: TG_ERR_UNSUPPORTED) and, without a split, not for the
- * 256 x 256 tile (its accumulators fill the registers): the automatic choice
- * then takes 128 x 128, a forced TG_CFG_256x256 returns TG_ERR_UNSUPPORTED;
- * with a split the combine pass applies the tail for any configuration.
+ * it: for them the modes alone shape the plan, and a NULL bias is accepted).
+ * Every tile configuration carries the tail in its own store-back at the
+ * default pipeline depth and swizzle (others: TG_ERR_UNSUPPORTED unless split);
+ * a split call applies it once in the combine pass; the plan is otherwise the
+ * one the call would take without the tail, except that persistent workgroups
+ * are not used with it.
  *
  * The workspace is caller-owned device memory, 16-byte aligned, that must not
  * overlap A, B or C; its contents on entry do not matter and are undefined

@@ -299,35 +299,29 @@ def _plan_status(*args, **kw):
 
 
 def test_plan_fused_tail():
-    """A tail without a split moves the automatic choice off the 256 x 256 tile; the options it
+    """The tail leaves the plan as it is without it (but for persistent workgroups); the options it
     is not built for are refused; a plan query takes the modes without a bias pointer."""
-    base = tg.tile_gemm_plan(1, 8192, 8192, 8192, "bf16")
-    assert base["config"] == tg.TG_CFG_256x256
-    for kw in (dict(bias_mode=1), dict(bias_mode=2), dict(activation=1), dict(bias_mode=1, activation=2)):
-        p = tg.tile_gemm_plan(1, 8192, 8192, 8192, "bf16", **kw)
-        assert (p["config"], p["split_k"], p["pack_a"], p["persistent"]) == (tg.TG_CFG_128x128, 1, 0, 0), kw
-        assert tg.tile_gemm_plan(1, 8192, 8192, 8192, "bf16", persistent=2, **kw)["persistent"] == 0
-        # a split keeps the tile: the combine pass applies the tail
-        s = tg.tile_gemm_plan(1, 8192, 8192, 8192, "bf16", config=tg.TG_CFG_256x256, split_k=2, **kw)
-        assert (s["config"], s["split_k"]) == (tg.TG_CFG_256x256, 2)
-    # c3's misaligned A would take the repack on the 256 tile; with a tail it takes none
-    ws = tg.tile_gemm_workspace_size(1, 8191, 8193, 8190, "bf16", plan_lda=8193, bias_mode=1)
-    assert ws == 0
-    assert tg.tile_gemm_workspace_size(1, 8191, 8193, 8190, "bf16", plan_lda=8193) > 0
-    # the f32 tile and the smaller 16-bit tiles carry it as they are
-    assert tg.tile_gemm_plan(1, 67, 45, 53, "f32", activation=2)["config"] == tg.TG_CFG_F32_64x64
-    assert tg.tile_gemm_plan(1, 300, 300, 64, "f16", config=tg.TG_CFG_64x64, activation=1)["config"] == \
-        tg.TG_CFG_64x64
+    for shape in [(1, 8192, 8192, 8192, "bf16"), (1, 8191, 8193, 8190, "bf16"), (512, 257, 129, 1000, "f16"),
+                  (1, 512, 512, 131072, "bf16"), (1, 67, 45, 53, "f32"), (1, 300, 2100, 1100, "bf16")]:
+        for extra in ({}, dict(workspace=1 << 40, workspace_bytes=1 << 40), dict(tail_gemm=2),
+                      dict(tail_gemm=2, workspace=1 << 40, workspace_bytes=1 << 40)):
+            base = tg.tile_gemm_plan(*shape, plan_lda=shape[3] + 3, **extra)
+            for kw in (dict(bias_mode=1), dict(bias_mode=2), dict(activation=1), dict(bias_mode=1, activation=2)):
+                assert tg.tile_gemm_plan(*shape, plan_lda=shape[3] + 3, **extra, **kw) == base, (shape, extra, kw)
+                assert tg.tile_gemm_workspace_size(*shape, plan_lda=shape[3] + 3, **kw,
+                                                   tail_gemm=extra.get("tail_gemm", 0)) == \
+                    tg.tile_gemm_workspace_size(*shape, plan_lda=shape[3] + 3, tail_gemm=extra.get("tail_gemm", 0))
+    assert tg.tile_gemm_plan(1, 8192, 8192, 8192, "bf16", config=tg.TG_CFG_256x256, split_k=1,
+                             activation=2)["config"] == tg.TG_CFG_256x256
+    # persistent workgroups are not built with the tail
+    assert tg.tile_gemm_plan(1, 8192, 8192, 8192, "bf16", persistent=2)["persistent"] == 1
+    assert tg.tile_gemm_plan(1, 8192, 8192, 8192, "bf16", persistent=2, bias_mode=1)["persistent"] == 0
     shape = (1, 1024, 1024, 1024, "bf16")
-    assert _plan_status(*shape, config=tg.TG_CFG_256x256, split_k=1, activation=1) == tg.TG_ERR_UNSUPPORTED
     assert _plan_status(*shape, pipeline_depth=2, activation=1) == tg.TG_ERR_UNSUPPORTED
     assert _plan_status(*shape, pipeline_depth=5, config=tg.TG_CFG_128x128, bias_mode=1) == tg.TG_ERR_UNSUPPORTED
     assert _plan_status(*shape, swizzle=1, activation=2) == tg.TG_ERR_UNSUPPORTED
     assert _plan_status(*shape, pipeline_depth=2, split_k=2, activation=1) == tg.TG_OK     # applied by the combine
-    # a split that does not take effect (K in one slice) leaves the 256 tile without the tail
-    assert _plan_status(1, 64, 64, 32, "bf16", config=tg.TG_CFG_256x256, split_k=2, activation=1) == \
-        tg.TG_ERR_UNSUPPORTED
-    assert tg.tile_gemm_plan(1, 64, 64, 32, "bf16", split_k=2, activation=1)["config"] != tg.TG_CFG_256x256
-    assert _plan_status(1, 64, 64, 64, "bf16", config=tg.TG_CFG_256x256, split_k=2, activation=1) == tg.TG_OK
+    assert _plan_status(1, 64, 64, 32, "bf16", config=tg.TG_CFG_256x256, split_k=2, activation=1) == tg.TG_OK
     assert _plan_status(*shape, bias_mode=3) == tg.TG_ERR_INVALID_ARG
     assert _plan_status(*shape, activation=-1) == tg.TG_ERR_INVALID_ARG
+    assert _plan_status(*shape, bias_mode=1, bias_stride=-1) == tg.TG_ERR_INVALID_ARG

@@ -1,15 +1,15 @@
 """The fused elementwise tail C <- act(alpha A.B + bias) + beta C0 (tile_gemm.h), on the GPU.
 
-* every configuration that carries the tail in its own epilogue (128 x 128 and
-  64 x 64 16-bit tiles, the fp32 tile), ragged across several tiles, with a
-  per-column bias, a per-row bias or none, and ReLU, GELU or no activation,
-  beta zero or not: parity with the fp64 oracle over the whole output and no
-  write outside C;
-* split along K, where the combine pass applies the tail (also for the
-  256 x 256 tile), and batched with a bias stride (0: one vector shared);
-* the automatic choice moves off the 256 x 256 tile when the tail is asked
-  for without a split; the argument errors (NULL, misaligned or overlapping
-  bias, unknown modes, options the tail is not built for);
+* every tile configuration (256 x 256 with its thin strips, 128 x 128, 64 x 64,
+  the fp32 tile), ragged across several tiles, with a per-column bias, a
+  per-row bias or none, and ReLU, GELU or no activation, beta zero or not:
+  parity with the fp64 oracle over the whole output and no write outside C;
+* split along K, where the combine pass applies the tail; thin remainders as
+  GEMMs of their own (their slice of the bias); the repacked A; batched with a
+  bias stride (0: one vector shared);
+* the plan is the one taken without the tail; the argument errors (NULL,
+  misaligned or overlapping bias, unknown modes, options the tail is not built
+  for);
 * ReLU passes a NaN through; full size 8191 x 8193 x 8190 (lda = K + 3,
   ldb = N + 5), sampled.
 
@@ -89,6 +89,10 @@ def check(p, got, bias, stride, mode, act, pts=None):
 
 CASES = [
     # dtype, M, N, K, batch, config, split_k, alpha, beta, bias_mode, activation
+    ("bf16", 300, 257, 100, 1, tg.TG_CFG_256x256, 1, 1.0, 0.0, 1, 1),     # an N strip and an M strip
+    ("bf16", 300, 257, 300, 1, tg.TG_CFG_256x256, 1, 1.5, 0.5, 2, 2),
+    ("f16", 520, 600, 700, 1, tg.TG_CFG_256x256, 1, -0.5, 1.0, 1, 2),     # whole fringe tiles
+    ("bf16", 256, 512, 64, 1, tg.TG_CFG_256x256, 1, 1.0, 0.0, 0, 1),      # interior only, one K tile
     ("bf16", 300, 257, 100, 1, tg.TG_CFG_128x128, 1, 1.0, 0.0, 1, 1),
     ("bf16", 300, 257, 100, 1, tg.TG_CFG_128x128, 1, 1.5, 0.5, 2, 2),
     ("bf16", 131, 200, 37, 1, tg.TG_CFG_128x128, 1, -1.0, 1.0, 0, 2),
@@ -131,12 +135,11 @@ def test_fused_tail_batched(mode, stride, cfg, split):
     gp.check_guards()
 
 
-def test_auto_choice_leaves_256():
-    # 4096 x 4096 x 512 takes the 256 x 256 tile on its own; with a tail and no split, 128 x 128
+def test_automatic_plan_256():
+    # 4096 x 4096 x 512 takes the 256 x 256 tile, with the tail as without it
     base = tg.tile_gemm_plan(1, 4096, 4096, 512, "bf16")
     assert base["config"] == tg.TG_CFG_256x256
-    with_tail = tg.tile_gemm_plan(1, 4096, 4096, 512, "bf16", bias_mode=1)
-    assert (with_tail["config"], with_tail["split_k"]) == (tg.TG_CFG_128x128, 1)
+    assert tg.tile_gemm_plan(1, 4096, 4096, 512, "bf16", bias_mode=1) == base
     p = workloads.custom("bf16", 4096, 4096, 512, alpha=1.0, beta=0.0, seed=4, name="auto")
     bias = make_bias(p, 1, 0, seed=4)
     gp = run(p, torch.from_numpy(bias).to("cuda"), 0, 1, 1)
@@ -156,6 +159,28 @@ def test_relu_passes_nan():
     ref, _ = oracle_tail(p, bias, 0, 1, 1)
     assert not np.isnan(got[:, keep]).any()
     assert np.max(np.abs(got[:, keep] - ref[0][:, keep])) <= 4e-3 * (np.abs(ref[0][:, keep]).max() + 1)
+
+
+REMAINDER_CASES = [
+    # M, N, K, lda_pad, tail_gemm, pack_a, bias_mode, activation, expected (tail_n_splits, tail_m_splits, pack_a)
+    (520, 300, 2100, 0, 2, 0, 1, 2, (4, 4, 0)),      # both remainders as GEMMs, split along K
+    (520, 300, 2100, 0, 2, 0, 2, 1, (4, 4, 0)),
+    (300, 2100, 1100, 3, 2, 0, 1, 1, (2, 2, 1)),     # on the repacked A
+    (300, 2100, 1100, 3, 1, 2, 2, 2, (0, 0, 1)),     # strips, repacked A
+]
+
+
+@pytest.mark.parametrize("M,N,K,lpad,tail_gemm,pack,mode,act,expect", REMAINDER_CASES, ids=lambda v: str(v))
+def test_fused_tail_remainders_and_repack(M, N, K, lpad, tail_gemm, pack, mode, act, expect):
+    p = workloads.custom("bf16", M, N, K, lda_pad=lpad, ldb_pad=2, alpha=1.25, beta=0.5, seed=M + N, name="rem")
+    opts = dict(config=tg.TG_CFG_256x256, split_k=1, tail_gemm=tail_gemm, pack_a=pack)
+    plan = tg.tile_gemm_plan(1, M, N, K, "bf16", plan_lda=p.lda, bias_mode=mode, activation=act,
+                             workspace=1 << 40, workspace_bytes=1 << 40, **opts)
+    assert (plan["tail_n_splits"], plan["tail_m_splits"], plan["pack_a"]) == expect, plan
+    bias = make_bias(p, mode, 0, seed=K + mode)
+    gp = run(p, torch.from_numpy(bias).to("cuda"), 0, mode, act, **opts)
+    check(p, gp.result(), bias, 0, mode, act)
+    gp.check_guards()
 
 
 def _status(fn):
@@ -181,7 +206,7 @@ def test_fused_tail_argument_errors():
     assert call(bias_mode=1, bias=bias, bias_stride=-1) == tg.TG_ERR_INVALID_ARG
     assert call(bias_mode=1, bias=bias.data_ptr() + 2) == tg.TG_ERR_INVALID_ARG   # misaligned
     assert call(bias_mode=1, bias=gp.C.data_ptr()) == tg.TG_ERR_INVALID_ARG       # overlaps C
-    assert call(activation=1, config=tg.TG_CFG_256x256, split_k=1) == tg.TG_ERR_UNSUPPORTED
+    assert call(activation=1, config=tg.TG_CFG_256x256, split_k=1) == tg.TG_OK
     assert call(activation=1, pipeline_depth=2) == tg.TG_ERR_UNSUPPORTED
     assert call(activation=1, swizzle=1) == tg.TG_ERR_UNSUPPORTED
     assert call(activation=1, config=tg.TG_CFG_256x256, split_k=2) == tg.TG_OK              # K in two slices
@@ -195,8 +220,9 @@ def test_full_size_ragged_sampled():
     p = workloads.custom("bf16", 8191, 8193, 8190, lda_pad=3, ldb_pad=5, alpha=1.5, beta=0.5, seed=11,
                          name="fused_full")
     bias = make_bias(p, 1, 0, seed=11)
-    plan = tg.tile_gemm_plan(1, p.M, p.N, p.K, p.dtype, plan_lda=p.lda, bias_mode=1, activation=2)
-    assert plan["config"] == tg.TG_CFG_128x128 and plan["split_k"] == 1, plan
+    plan = tg.tile_gemm_plan(1, p.M, p.N, p.K, p.dtype, plan_lda=p.lda, bias_mode=1, activation=2,
+                             workspace=1 << 40, workspace_bytes=1 << 40)
+    assert (plan["config"], plan["split_k"], plan["pack_a"]) == (tg.TG_CFG_256x256, 1, 1), plan
     gp = run(p, torch.from_numpy(bias).to("cuda"), 0, 1, 2)
     pts = workloads.sample_points(p, 300)
     err = check(p, result_points(gp, pts), bias, 0, 1, 2, pts)
@@ -204,15 +230,15 @@ def test_full_size_ragged_sampled():
     gp.check_guards()
 
 
-@pytest.mark.parametrize("cfg,split", [(tg.TG_CFG_128x128, 1), (tg.TG_CFG_64x64, 1), (tg.TG_CFG_256x256, 2),
-                                       (tg.TG_CFG_F32_64x64, 1)])
+@pytest.mark.parametrize("cfg,split", [(tg.TG_CFG_256x256, 1), (tg.TG_CFG_128x128, 1), (tg.TG_CFG_64x64, 1),
+                                       (tg.TG_CFG_256x256, 2), (tg.TG_CFG_F32_64x64, 1)])
 @pytest.mark.parametrize("mode,act", [(1, 0), (2, 1), (1, 2)])
 def test_fused_equals_two_pass(cfg, split, mode, act):
     """OCANNL epilogue fusion: the fused store-back equals the plain GEMM (alpha 1, beta 0, the same
     tile and split) followed by a separate elementwise pass on the GPU.  Bias add and ReLU are
-    single roundings, so bit for bit; GELU goes through the device erff on one side and the
-    runtime's erf on the other: an ulp of erf moves x Phi(x) by |x| / 2 ulp, so within 2 ulp of x
-    (where 1 + erf cancels, an ulp of the small result is far less)."""
+    single roundings, so bit for bit; GELU goes through the library's Chebyshev fit of erfc on one
+    side (within 2.4e-7 |x| of x Phi(x)) and the runtime's erf on the other (within about an ulp
+    of x), so the two agree to 4 ulp of x."""
     dt = "f32" if cfg == tg.TG_CFG_F32_64x64 else "bf16"
     p = workloads.custom(dt, 300, 270, 700, ldb_pad=2, alpha=1.0, beta=0.0, seed=cfg * 10 + mode + act,
                          name="twopass")
@@ -232,7 +258,28 @@ def test_fused_equals_two_pass(cfg, split, mode, act):
         ax = torch.abs(x)
         ulp = torch.nextafter(ax, torch.full_like(ax, float("inf"))) - ax
         err = torch.abs(got - y)
-        assert bool(torch.all(err <= 2 * ulp)), float(torch.max(err / ulp))
+        assert bool(torch.all(err <= 4 * ulp)), float(torch.max(err / ulp))
     else:
         assert torch.equal(got.contiguous().view(torch.int32), y.contiguous().view(torch.int32))
     fused.check_guards()
+
+
+@pytest.mark.parametrize("split", [1, 2])
+def test_gelu_accuracy(split):
+    """A = 0, so every output is GELU(bias): a dense grid of x in [-12, 12] plus small and large
+    magnitudes, against the oracle's exact erf, to 2.5e-7 |x| (the store-back for split 1, the
+    combine pass for split 2)."""
+    grid = np.concatenate([np.linspace(-12, 12, 60001), np.geomspace(1e-6, 40, 2000),
+                           -np.geomspace(1e-6, 40, 2000), [0.0, -0.0]]).astype(np.float32)
+    N = len(grid)
+    p = workloads.custom("bf16", 3, N, 64, seed=5, name="gelu")
+    p.A = np.zeros_like(p.A)
+    gp = run(p, torch.from_numpy(grid).to("cuda"), 0, 1, 2, config=tg.TG_CFG_256x256, split_k=split)
+    got = gp.result()[0]
+    ref, _ = oracle_tail(p, grid, 0, 1, 2)
+    err = np.abs(got - ref[0])
+    bound = 2.5e-7 * np.abs(grid.astype(np.float64))[None, :]
+    worst = float(np.max(err / np.maximum(bound, 1e-300)))
+    print(f"split {split}: GELU error at most {worst:.3f} of 2.5e-7 |x|")
+    assert np.all(err <= bound), worst
+    gp.check_guards()

@@ -225,10 +225,11 @@ def tile_gemm_status(fn: str, *args) -> int:
 
 def tile_gemm_plan(batch, M, N, K, dtype, config=0, pipeline_depth=0, swizzle=0, block_order=0,
                    split_k=0, workspace=None, workspace_bytes=None, pack_a=0, plan_lda=0, tail_gemm=0,
-                   persistent=0, bias_mode=0, activation=0) -> dict:
+                   persistent=0, bias_mode=0, activation=0, bias_stride=0) -> dict:
     info = PlanInfo()
     opt = _options(config, pipeline_depth, swizzle, block_order, split_k, workspace, workspace_bytes, pack_a,
-                   plan_lda, tail_gemm, persistent, bias_mode=bias_mode, activation=activation)
+                   plan_lda, tail_gemm, persistent, bias_stride=bias_stride, bias_mode=bias_mode,
+                   activation=activation)
     _check(_lib().tile_gemm_plan(batch, M, N, K, _dtype(dtype), ctypes.byref(opt), ctypes.byref(info)),
            "tile_gemm_plan")
     return info.as_dict()
@@ -236,12 +237,12 @@ def tile_gemm_plan(batch, M, N, K, dtype, config=0, pipeline_depth=0, swizzle=0,
 
 def tile_gemm_workspace_size(batch, M, N, K, dtype, config=0, pipeline_depth=0, swizzle=0, block_order=0,
                              split_k=0, pack_a=0, plan_lda=0, tail_gemm=0, persistent=0, bias_mode=0,
-                             activation=0) -> int:
+                             activation=0, bias_stride=0) -> int:
     """Bytes of workspace a call with these arguments would use (split-K partials, the
     aligned copy of A and the remainder GEMMs' partials; 0: none)."""
     n = ctypes.c_int64(0)
     opt = _options(config, pipeline_depth, swizzle, block_order, split_k, None, None, pack_a, plan_lda, tail_gemm,
-                   persistent, bias_mode=bias_mode, activation=activation)
+                   persistent, bias_stride=bias_stride, bias_mode=bias_mode, activation=activation)
     _check(_lib().tile_gemm_workspace_size(batch, M, N, K, _dtype(dtype), ctypes.byref(opt), ctypes.byref(n)),
            "tile_gemm_workspace_size")
     return int(n.value)

@@ -88,11 +88,36 @@ struct GemmParams {
     int bias_mode, act;
 };
 
-// The tail's activation: 1 = ReLU (x < 0 ? 0 : x, so a NaN stays NaN), 2 =
-// GELU in its erf form, x * Phi(x) = x / 2 * (1 + erf(x / sqrt 2)).
+// GELU in its exact form x * Phi(x), Phi the standard normal CDF, branch-free:
+// with z = |x| / sqrt 2, h = erfc(z) / 2 = Phi(-|x|) and Phi(x) = x >= 0 ? 1 - h : h.
+// erfc(z) for z >= 0 is t * exp(P(t) - z^2), t = 1 / (1 + z / 2), P the degree-9
+// Chebyshev fit whose fractional error stays below 1.2e-7 (Press, Teukolsky,
+// Vetterling and Flannery, Numerical Recipes, 2nd ed., section 6.2): one
+// reciprocal, nine fma and one exp2, against a library erff that branches on
+// |z| < 1 and runs both sides when the lanes of a wave differ.  The error is
+// relative, so the negative tail keeps its accuracy, where x / 2 * (1 + erf)
+// cancels; in fp32 the result is within 2.4e-7 |x| of x * Phi(x).
+__device__ __forceinline__ float gelu(float x) {
+    const float z = __builtin_fabsf(x) * 0.70710678118654752f;
+    const float t = __builtin_amdgcn_rcpf(__builtin_fmaf(0.5f, z, 1.0f));
+    float q = 0.17087277f;
+    q = __builtin_fmaf(q, t, -0.82215223f);
+    q = __builtin_fmaf(q, t, 1.48851587f);
+    q = __builtin_fmaf(q, t, -1.13520398f);
+    q = __builtin_fmaf(q, t, 0.27886807f);
+    q = __builtin_fmaf(q, t, -0.18628806f);
+    q = __builtin_fmaf(q, t, 0.09678418f);
+    q = __builtin_fmaf(q, t, 0.37409196f);
+    q = __builtin_fmaf(q, t, 1.00002368f);
+    q = __builtin_fmaf(q, t, -1.26551223f);
+    const float h = 0.5f * t * __builtin_amdgcn_exp2f((q - z * z) * 1.4426950408889634f);
+    return x * (x >= 0.0f ? 1.0f - h : h);
+}
+
+// The tail's activation: 1 = ReLU (x < 0 ? 0 : x, so a NaN stays NaN), 2 = GELU.
 __device__ __forceinline__ float tail_activation(float x, int act) {
     if (act == 1) return x < 0.0f ? 0.0f : x;
-    if (act == 2) return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f));
+    if (act == 2) return gelu(x);
     return x;
 }
 
@@ -260,9 +285,117 @@ __device__ __forceinline__ void mfma_chunk(const u32x4 &a, const u32x4 &b, f32x4
 // per lane whose C0 loads are all issued before any of the chunk's stores:
 // one memory round trip per chunk instead of one per MFMA tile.
 // `acc(i, j, v)` is value v of MFMA tile (i, j) of this lane.
+template <int I, int END, int STEP, class F>
+__device__ __forceinline__ void static_for(const F &f) {
+    if constexpr (I < END) {
+        f(std::integral_constant<int, I>{});
+        static_for<I + STEP, END, STEP>(f);
+    }
+}
+
+// The fused tail C = act(fma(alpha, acc, bias)) + beta * C0 (C0 not read when
+// beta == 0), one instantiation per activation and per beta == 0 / != 0, so the
+// per-value code is straight-line.  A lane's output column depends on its MFMA
+// tile column j alone and its row on the tile row i and value index v alone
+// (acc_coord), so the bias values it needs, TN of them per column or TM x V per
+// row, are loaded once before any store.  No load is masked per lane: a masked
+// load sits in a branch whose join waits for every memory operation in flight,
+// stores included; bias indices are clamped into the vector instead, and a lane
+// outside C reads C0 at the tile's origin (always inside C) and discards it.
+// The chunk index is a template constant: with the activation inlined per value
+// the epilogue is longer than the loop unroller accepts, and a rolled chunk
+// loop would index the accumulators at run time, which moves them to scratch.
+template <class C, bool FRINGE, class AccFn, int CHUNK_VALUES, int ACT, bool BETA>
+__device__ __forceinline__ void store_tile_tail_as(const GemmParams &p, const AccFn &acc, int64_t b,
+                                                   int64_t m0, int64_t n0, int wave, int lane) {
+    float *Cblk = p.C + b * p.sC + m0 * p.ldc + n0;
+    const int ldc = (int)p.ldc;
+    const float alpha = p.alpha, beta = p.beta;
+    const int64_t M = p.M, N = p.N;
+    const float *bias = p.bias + b * p.bias_stride;
+    const int bias_mode = p.bias_mode;
+    constexpr int V = C::ACC_PER_MFMA;
+    constexpr int TN = C::TN;
+    constexpr int TILES = C::TM * C::TN;
+    constexpr int CH = CHUNK_VALUES / V < TILES ? CHUNK_VALUES / V : TILES;   // MFMA tiles per chunk
+    static_assert(TILES % CH == 0, "whole chunks");
+    float bcol[TN], brow[C::TM][V];
+#pragma unroll
+    for (int j = 0; j < TN; ++j) bcol[j] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+        for (int v = 0; v < V; ++v) brow[i][v] = 0.0f;
+    if (bias_mode == 1) {
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            int row, col;
+            acc_coord<C>(wave, lane, j * V, row, col);
+            const int64_t n = n0 + col;
+            bcol[j] = bias[FRINGE && n >= N ? N - 1 : n];
+        }
+    } else if (bias_mode == 2) {
+#pragma unroll
+        for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+            for (int v = 0; v < V; ++v) {
+                int row, col;
+                acc_coord<C>(wave, lane, i * TN * V + v, row, col);
+                const int64_t m = m0 + row;
+                brow[i][v] = bias[FRINGE && m >= M ? M - 1 : m];
+            }
+    }
+    static_for<0, TILES, CH>([&](auto chunk) {
+        constexpr int c0t = decltype(chunk)::value;
+        int off[CH][V];
+        bool ok[CH][V];
+        float cv[CH][V];
+#pragma unroll
+        for (int t = 0; t < CH; ++t)
+#pragma unroll
+            for (int v = 0; v < V; ++v) {
+                int row, col;
+                acc_coord<C>(wave, lane, (c0t + t) * V + v, row, col);
+                off[t][v] = row * ldc + col;
+                ok[t][v] = !FRINGE || (m0 + row < M && n0 + col < N);
+                if constexpr (BETA) cv[t][v] = Cblk[ok[t][v] ? off[t][v] : 0];
+            }
+#pragma unroll
+        for (int t = 0; t < CH; ++t)
+#pragma unroll
+            for (int v = 0; v < V; ++v) {
+                const int i = (c0t + t) / TN, j = (c0t + t) % TN;
+                const float bv = bias_mode == 1 ? bcol[j] : brow[i][v];
+                float y = tail_activation(__builtin_fmaf(alpha, acc(i, j, v), bv), ACT);
+                if constexpr (BETA) y = __builtin_fmaf(beta, cv[t][v], y);
+                if (ok[t][v]) Cblk[off[t][v]] = y;
+            }
+    });
+}
+
+template <class C, bool FRINGE, class AccFn, int CHUNK_VALUES>
+__device__ __forceinline__ void store_tile_tail(const GemmParams &p, const AccFn &acc, int64_t b,
+                                                int64_t m0, int64_t n0, int wave, int lane) {
+#define TG_TAIL_AS(A, BT) store_tile_tail_as<C, FRINGE, AccFn, CHUNK_VALUES, A, BT>(p, acc, b, m0, n0, wave, lane)
+    if (p.beta != 0.0f) {
+        if (p.act == 2) TG_TAIL_AS(2, true);
+        else if (p.act == 1) TG_TAIL_AS(1, true);
+        else TG_TAIL_AS(0, true);
+    } else {
+        if (p.act == 2) TG_TAIL_AS(2, false);
+        else if (p.act == 1) TG_TAIL_AS(1, false);
+        else TG_TAIL_AS(0, false);
+    }
+#undef TG_TAIL_AS
+}
+
 template <class C, bool FRINGE, class AccFn, int CHUNK_VALUES = 64, bool TAIL = false>
 __device__ __forceinline__ void store_tile_epilogue(const GemmParams &p, const AccFn &acc, int64_t b,
                                                     int64_t m0, int64_t n0, int wave, int lane) {
+    if constexpr (TAIL) {
+        store_tile_tail<C, FRINGE, AccFn, CHUNK_VALUES>(p, acc, b, m0, n0, wave, lane);
+        return;
+    }
     float *Cblk = p.C + b * p.sC + m0 * p.ldc + n0;
     const int ldc = (int)p.ldc;
     const float alpha = p.alpha, beta = p.beta;
@@ -284,29 +417,6 @@ __device__ __forceinline__ void store_tile_epilogue(const GemmParams &p, const A
                 off[t][v] = row * ldc + col;
                 ok[t][v] = !FRINGE || (m0 + row < M && n0 + col < N);
             }
-        if constexpr (TAIL) {
-            // fused tail: the chunk's bias values and C0 loads first, then the outputs
-            const float *bias = p.bias + b * p.bias_stride;
-            float bv[CH][V], cv[CH][V];
-#pragma unroll
-            for (int t = 0; t < CH; ++t)
-#pragma unroll
-                for (int v = 0; v < V; ++v) {
-                    int row, col;
-                    acc_coord<C>(wave, lane, (c0t + t) * V + v, row, col);
-                    const int64_t bi = p.bias_mode == 1 ? n0 + col : m0 + row;
-                    bv[t][v] = ok[t][v] && p.bias_mode != 0 ? bias[bi] : 0.0f;
-                    cv[t][v] = ok[t][v] && beta != 0.0f ? Cblk[off[t][v]] : 0.0f;
-                }
-#pragma unroll
-            for (int t = 0; t < CH; ++t)
-#pragma unroll
-                for (int v = 0; v < V; ++v) {
-                    const int i = (c0t + t) / C::TN, j = (c0t + t) % C::TN;
-                    if (ok[t][v]) Cblk[off[t][v]] = tail_value(acc(i, j, v), alpha, bv[t][v], p.act, beta, cv[t][v]);
-                }
-            continue;
-        }
         if (beta != 0.0f) {
             float cv[CH][V];
 #pragma unroll

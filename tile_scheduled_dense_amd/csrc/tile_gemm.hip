@@ -185,22 +185,7 @@ tg_status make_plan(int64_t batch, int64_t M, int64_t N, int64_t K, tg_dtype dty
         want = o.split_k < kMaxSplits ? o.split_k : kMaxSplits;
     }
     if (!config) config = choose_config(batch, M, N, dtype);
-    // A fused tail in the GEMM's own epilogue (no split) is built for every
-    // configuration but the 256 x 256 tile: there its 256 accumulators per
-    // lane leave no registers for the tail, and the compiler would move
-    // accumulators to scratch right behind the (inline, hazard-unaware) MFMAs.
-    // The automatic choice then takes 128 x 128; a forced 256 x 256 with a
-    // tail needs a split (the combine pass applies the tail).
-    const bool tail_req = o.bias_mode != 0 || o.activation != 0;
-    if (tail_req && config == TG_CFG_256x256) {
-        // the split that takes effect: a K that fits one slice is not split
-        const int64_t bk = cfg_dims(TG_CFG_256x256).bk;
-        const int64_t eff = K > 0 ? cdiv(K, cdiv(cdiv(K, want), bk) * bk) : 1;
-        if (eff == 1) {
-            if (o.config) return TG_ERR_UNSUPPORTED;
-            config = TG_CFG_128x128;
-        }
-    }
+    const bool tail_req = o.bias_mode != 0 || o.activation != 0;   // the fused tail (tile_gemm.h)
     if (config < TG_CFG_256x256 || config > TG_CFG_F32_64x64) return TG_ERR_INVALID_ARG;
     if ((dtype == TG_F32) != (config == TG_CFG_F32_64x64)) return TG_ERR_UNSUPPORTED;
     // pipeline depth = LDS copies of the K tile (window = depth - 1)
@@ -353,8 +338,8 @@ tg_status make_plan(int64_t batch, int64_t M, int64_t N, int64_t K, tg_dtype dty
     // interior tiles of one problem, K in whole groups of four K tiles, at
     // least two tiles per workgroup.
     constexpr int64_t kPersistentBlocks = 256;
-    if (sixteen && some && o.persistent == 2 && config == TG_CFG_256x256 && depth == 4 && swz == SWZ_XOR &&
-        order == 0 && batch == 1 && splits == 1 && !p.pack_a && p.strip_blocks == 0 && M % 256 == 0 &&
+    if (sixteen && some && o.persistent == 2 && !tail_req && config == TG_CFG_256x256 && depth == 4 &&
+        swz == SWZ_XOR && order == 0 && batch == 1 && splits == 1 && !p.pack_a && p.strip_blocks == 0 && M % 256 == 0 &&
         N % 256 == 0 && K % (4 * d.bk) == 0 && K >= 8 * d.bk && p.tiles_m * p.tiles_n >= 2 * kPersistentBlocks) {
         p.persistent = 1;
         p.grid = kPersistentBlocks;
@@ -446,14 +431,10 @@ tg_status launch_ring_one(const GemmParams &gp, int64_t grid, hipStream_t stream
 template <class C, bool SWPIPE>
 tg_status launch_ring(const GemmParams &gp, const tg_plan_info &p, hipStream_t s, bool tail) {
     constexpr int SCHED = SWPIPE ? SCHED_SWPIPE : SCHED_RING;
-    if (tail) {
-        if constexpr (SWPIPE) {
-            return TG_ERR_UNSUPPORTED;      // the 256 x 256 tile: not built with the tail
-        } else {
-            if (p.pipeline_depth == 4 && p.swizzle == SWZ_XOR)
-                return launch_ring_one<C, 4, SWZ_XOR, SCHED, true>(gp, p.grid, s);
-            return TG_ERR_UNSUPPORTED;
-        }
+    if (tail) {     // built at the default depth and swizzle (make_plan refuses the others)
+        if (p.pipeline_depth == 4 && p.swizzle == SWZ_XOR)
+            return launch_ring_one<C, 4, SWZ_XOR, SCHED, true>(gp, p.grid, s);
+        return TG_ERR_UNSUPPORTED;
     }
     if (p.swizzle == SWZ_XOR) {
         switch (p.pipeline_depth) {
