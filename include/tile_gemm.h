@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define TILE_GEMM_ABI_VERSION 6
+#define TILE_GEMM_ABI_VERSION 7
 
 typedef enum { TG_F32 = 0, TG_BF16 = 1, TG_F16 = 2 } tg_dtype;
 
@@ -319,6 +319,41 @@ int tile_gemm_acc_coord(int config, int wave, int lane, int slot, int64_t *row, 
 
 const char *tile_gemm_status_string(tg_status s);
 int tile_gemm_abi_version(void);
+
+/*
+ * Hoisted pre-pack of B (OCANNL "Module Ir.Schedule", the Stage paragraph's
+ * hoisted option: a staged copy of an operand the loop nest does not change
+ * is made once, outside it).  For callers that multiply by the same B many
+ * times: tile_gemm_pack_b writes B once into rows of a multiple of 16 bytes
+ * (16-byte aligned, zero-filled past N), the layout the tile copies read at
+ * full rate, and every later call passes the packed copy as an ordinary B:
+ *     B = packed, ldb = tile_gemm_packed_b_ld(N, dtype), strideB = K * ldb,
+ * to tile_gemm / tile_gemm_strided_batched / tile_gemm_ex.  The values are
+ * unchanged, so a call on the packed copy computes the same MFMA sequence and
+ * a bitwise identical C.  The pack can also take B as stored transposed (an
+ * N x K row-major matrix, as a layer's weight often is), which the GEMM itself
+ * does not read.
+ *
+ * tile_gemm_packed_b_ld: the packed row length in elements, roundup(max(N, 1),
+ *   16 / element size); -1 for a negative N or an unknown dtype.
+ * tile_gemm_packed_b_size: *bytes = batch * K * tile_gemm_packed_b_ld(N) *
+ *   element size (host only).
+ * tile_gemm_pack_b: B is batch matrices of K x N (transposed == 0: element
+ *   (k, n) at B[b * strideB + k * ldb + n], ldb >= N) or stored transposed
+ *   (transposed == 1: element (k, n) at B[b * strideB + n * ldb + k], ldb >= K),
+ *   fp32 / bf16 / fp16 storage, read only.  packed is caller-owned device
+ *   memory, 256-byte aligned, packed_bytes >= tile_gemm_packed_b_size, not
+ *   overlapping B; element (b, k, n) lands at packed[(b * K + k) * ld + n].
+ *   Asynchronous on `stream`.  Errors: TG_ERR_INVALID_ARG for negative
+ *   extents or stride, ldb too small, NULL or misaligned pointers, too small
+ *   a buffer, an overlap or transposed not 0 / 1 (checked before any device
+ *   work); TG_ERR_UNSUPPORTED without a gfx950 device or for more than 65535
+ *   transposed batch entries.  An empty B (batch, K or N 0) does nothing.
+ */
+int64_t tile_gemm_packed_b_ld(int64_t N, tg_dtype dtype);
+tg_status tile_gemm_packed_b_size(int64_t batch, int64_t K, int64_t N, tg_dtype dtype, int64_t *bytes);
+tg_status tile_gemm_pack_b(int64_t batch, int64_t K, int64_t N, tg_dtype dtype, const void *B, int64_t ldb,
+                           int64_t strideB, int transposed, void *packed, int64_t packed_bytes, void *stream);
 
 #ifdef __cplusplus
 }

@@ -28,7 +28,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert tg.abi_version() == 6
+    assert tg.abi_version() == 7
     for s in range(5):
         assert tg.STATUS_NAMES[s] in tg.status_string(s)
 
@@ -325,3 +325,47 @@ def test_plan_fused_tail():
     assert _plan_status(*shape, bias_mode=3) == tg.TG_ERR_INVALID_ARG
     assert _plan_status(*shape, activation=-1) == tg.TG_ERR_INVALID_ARG
     assert _plan_status(*shape, bias_mode=1, bias_stride=-1) == tg.TG_ERR_INVALID_ARG
+
+
+def test_packed_b_ld_and_size():
+    """Packed rows are a multiple of 16 bytes; the size is batch x K rows of them."""
+    assert tg.tile_gemm_packed_b_ld(8193, "bf16") == 8200
+    assert tg.tile_gemm_packed_b_ld(8192, "f16") == 8192
+    assert tg.tile_gemm_packed_b_ld(45, "f32") == 48
+    assert tg.tile_gemm_packed_b_ld(0, "bf16") == 8 and tg.tile_gemm_packed_b_ld(0, "f32") == 4
+    assert tg.tile_gemm_packed_b_size(3, 100, 129, "f16") == 3 * 100 * 136 * 2
+    assert tg.tile_gemm_packed_b_size(2, 53, 45, "f32") == 2 * 53 * 48 * 4
+    assert tg.tile_gemm_packed_b_size(0, 53, 45, "f32") == 0
+    with pytest.raises(tg.TileGemmError):
+        tg.tile_gemm_packed_b_ld(-1, "bf16")
+    for args in [(-1, 4, 4, "bf16"), (1, -4, 4, "bf16"), (1, 4, -4, "bf16"), (1, 4, 4, 7)]:
+        with pytest.raises(tg.TileGemmError):
+            tg.tile_gemm_packed_b_size(*args)
+
+
+def test_pack_b_argument_errors():
+    """Rejected before any device work (placeholder addresses are never dereferenced)."""
+    B, P = 0x10000000, 0x20000000
+    K, N = 64, 100
+    need = tg.tile_gemm_packed_b_size(1, K, N, "bf16")
+
+    def st(batch=1, k=K, n=N, dt=tg.TG_BF16, b=B, ldb=N, sb=0, tr=0, p=P, pb=need):
+        return tg.tile_gemm_status("tile_gemm_pack_b", batch, k, n, dt, b, ldb, sb, tr, p, pb, None)
+    bad = tg.TG_ERR_INVALID_ARG
+    assert st(b=None) == bad
+    assert st(p=None) == bad
+    assert st(p=P + 128) == bad                   # not 256-byte aligned
+    assert st(pb=need - 1) == bad
+    assert st(ldb=N - 1) == bad
+    assert st(tr=1, ldb=K - 1) == bad             # the transposed source's rows hold K elements
+    assert st(tr=2) == bad
+    assert st(sb=-1) == bad
+    assert st(batch=-1) == bad and st(k=-1) == bad and st(n=-1) == bad
+    assert st(dt=9) == bad
+    assert st(b=P + 256) == bad                   # B inside the packed buffer
+    assert st(batch=0) == tg.TG_OK and st(k=0) == tg.TG_OK and st(n=0) == tg.TG_OK
+    # valid arguments reach the device check; only where no GPU is visible (the placeholder
+    # addresses must never reach a kernel)
+    import torch
+    if torch.cuda.device_count() == 0:
+        assert st() == tg.TG_ERR_UNSUPPORTED

@@ -43,7 +43,8 @@ LAYOUT_MAX_SWIZZLES = 2
 # every symbol include/tile_gemm.h declares
 EXPORTED = ["tile_gemm", "tile_gemm_strided_batched", "tile_gemm_ex", "tile_gemm_plan",
             "tile_gemm_workspace_size", "tg_layout_eval", "tile_gemm_describe_layout", "tile_gemm_lds_offset",
-            "tile_gemm_acc_coord", "tile_gemm_status_string", "tile_gemm_abi_version"]
+            "tile_gemm_acc_coord", "tile_gemm_status_string", "tile_gemm_abi_version", "tile_gemm_packed_b_ld",
+            "tile_gemm_packed_b_size", "tile_gemm_pack_b"]
 
 
 class TileGemmError(RuntimeError):
@@ -138,6 +139,12 @@ def _lib():
     lib.tile_gemm_status_string.argtypes = [ci]
     lib.tile_gemm_status_string.restype = ctypes.c_char_p
     lib.tile_gemm_abi_version.restype = ci
+    lib.tile_gemm_packed_b_ld.argtypes = [i64, ci]
+    lib.tile_gemm_packed_b_ld.restype = i64
+    lib.tile_gemm_packed_b_size.argtypes = [i64, i64, i64, ci, ctypes.POINTER(i64)]
+    lib.tile_gemm_packed_b_size.restype = ci
+    lib.tile_gemm_pack_b.argtypes = [i64, i64, i64, ci, vp, i64, i64, ci, vp, i64, vp]
+    lib.tile_gemm_pack_b.restype = ci
     _lib_handle = lib
     return lib
 
@@ -246,6 +253,30 @@ def tile_gemm_workspace_size(batch, M, N, K, dtype, config=0, pipeline_depth=0, 
     _check(_lib().tile_gemm_workspace_size(batch, M, N, K, _dtype(dtype), ctypes.byref(opt), ctypes.byref(n)),
            "tile_gemm_workspace_size")
     return int(n.value)
+
+
+def tile_gemm_packed_b_ld(N, dtype) -> int:
+    """Row length (elements) of B packed by tile_gemm_pack_b: rows of a multiple of 16 bytes."""
+    ld = int(_lib().tile_gemm_packed_b_ld(N, _dtype(dtype)))
+    if ld < 0:
+        raise TileGemmError(TG_ERR_INVALID_ARG, "tile_gemm_packed_b_ld")
+    return ld
+
+
+def tile_gemm_packed_b_size(batch, K, N, dtype) -> int:
+    n = ctypes.c_int64(0)
+    _check(_lib().tile_gemm_packed_b_size(batch, K, N, _dtype(dtype), ctypes.byref(n)), "tile_gemm_packed_b_size")
+    return int(n.value)
+
+
+def tile_gemm_pack_b(batch, K, N, dtype, B, ldb, strideB, packed, packed_bytes=None, transposed=0,
+                     stream=None) -> None:
+    """Pack B (K x N, or stored transposed as N x K with transposed=1) into `packed` once; later
+    calls pass `packed` as B with ldb = tile_gemm_packed_b_ld(N, dtype) and strideB = K * ldb."""
+    if packed_bytes is None:
+        packed_bytes = packed.numel() * packed.element_size() if hasattr(packed, "numel") else 0
+    _check(_lib().tile_gemm_pack_b(batch, K, N, _dtype(dtype), _addr(B), ldb, strideB, int(transposed),
+                                   _addr(packed), int(packed_bytes), _stream(stream)), "tile_gemm_pack_b")
 
 
 def make_layout(shape, shard, replica=(), offset=None, swizzle=None) -> Layout:

@@ -494,6 +494,9 @@ tg_status launch_dtype(const GemmParams &gp, const tg_plan_info &p, hipStream_t 
     }
 }
 
+tg_status launch_pack_rows(int esz, const void *src, int64_t ld, int64_t stride, void *dst, int64_t ld_out,
+                           int64_t rows, int64_t cols, int64_t total_rows, hipStream_t s);
+
 tg_status run(int64_t batch, int64_t M, int64_t N, int64_t K, tg_dtype dtype,
               const void *A, int64_t lda, int64_t sA, const void *B, int64_t ldb, int64_t sB,
               float *C, int64_t ldc, int64_t sC, float alpha, float beta, void *stream,
@@ -579,10 +582,8 @@ tg_status run(int64_t batch, int64_t M, int64_t N, int64_t K, tg_dtype dtype,
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (pack) {
         // A -> aligned rows of lda_packed elements in the workspace, then the GEMM on that copy
-        hipLaunchKernelGGL(pack_rows_kernel, dim3((unsigned)(batch * M)), dim3(256), 0, s,
-                           static_cast<const char *>(A), lda, sA, static_cast<char *>(plan.workspace),
-                           plan.lda_packed, M, K);
-        if (hipGetLastError() != hipSuccess) return TG_ERR_LAUNCH;
+        st = launch_pack_rows(2, A, lda, sA, plan.workspace, plan.lda_packed, M, K, batch * M, s);
+        if (st != TG_OK) return st;
         gp.A = static_cast<const char *>(plan.workspace);
         gp.lda = plan.lda_packed;
         gp.sA = M * plan.lda_packed;
@@ -623,6 +624,76 @@ tg_status run(int64_t batch, int64_t M, int64_t N, int64_t K, tg_dtype dtype,
         if (st != TG_OK) return st;
     }
     return TG_OK;
+}
+
+// Hoisted pack of B (tile_gemm.h): rows of a multiple of 16 bytes.
+
+// Threads per row for pack_rows_kernel: whole waves, enough for the row's chunks.
+int pack_group(int64_t chunks) { return chunks > 128 ? 256 : (chunks > 64 ? 128 : 64); }
+
+tg_status launch_pack_rows(int esz, const void *src, int64_t ld, int64_t stride, void *dst, int64_t ld_out,
+                           int64_t rows, int64_t cols, int64_t total_rows, hipStream_t s) {
+    const int group = pack_group(ld_out * esz / 16);
+    const int64_t blocks = cdiv(total_rows, 256 / group);
+    if (blocks > 0x7fffffffLL || ld_out * esz > 0x7fffffffLL) return TG_ERR_UNSUPPORTED;
+    if (esz == 4)
+        hipLaunchKernelGGL(pack_rows_kernel<4>, dim3((unsigned)blocks), dim3(256), 0, s,
+                           static_cast<const char *>(src), ld, stride, static_cast<char *>(dst), ld_out, rows, cols,
+                           total_rows, group);
+    else
+        hipLaunchKernelGGL(pack_rows_kernel<2>, dim3((unsigned)blocks), dim3(256), 0, s,
+                           static_cast<const char *>(src), ld, stride, static_cast<char *>(dst), ld_out, rows, cols,
+                           total_rows, group);
+    return hipGetLastError() == hipSuccess ? TG_OK : TG_ERR_LAUNCH;
+}
+int64_t packed_ld(int64_t N, tg_dtype dtype) {
+    const int64_t per = dtype == TG_F32 ? 4 : 8;     // elements per 16 bytes
+    const int64_t n = N > 1 ? N : 1;
+    return (n + per - 1) / per * per;
+}
+
+tg_status packed_bytes_of(int64_t batch, int64_t K, int64_t N, tg_dtype dtype, int64_t &bytes) {
+    if (batch < 0 || K < 0 || N < 0) return TG_ERR_INVALID_ARG;
+    if (dtype != TG_F32 && dtype != TG_BF16 && dtype != TG_F16) return TG_ERR_INVALID_ARG;
+    const int64_t esz = dtype == TG_F32 ? 4 : 2, ldp = packed_ld(N, dtype);
+    if (N > (int64_t(1) << 40) || K > (int64_t(1) << 40) || batch > (int64_t(1) << 40) ||
+        (K > 0 && batch > (int64_t(1) << 60) / K / ldp / esz))
+        return TG_ERR_INVALID_ARG;
+    bytes = batch * K * ldp * esz;
+    return TG_OK;
+}
+
+tg_status pack_b(int64_t batch, int64_t K, int64_t N, tg_dtype dtype, const void *B, int64_t ldb, int64_t sB,
+                 int transposed, void *packed, int64_t packed_size, void *stream) {
+    int64_t bytes = 0;
+    tg_status st = packed_bytes_of(batch, K, N, dtype, bytes);
+    if (st != TG_OK) return st;
+    if (transposed != 0 && transposed != 1) return TG_ERR_INVALID_ARG;
+    if (batch == 0 || K == 0 || N == 0) return TG_OK;
+    const int esz = dtype == TG_F32 ? 4 : 2;
+    const int64_t rows = transposed ? N : K, cols = transposed ? K : N;   // the source as stored
+    if (!B || !packed || ldb < cols || sB < 0) return TG_ERR_INVALID_ARG;
+    if (reinterpret_cast<uintptr_t>(packed) % 256 || packed_size < bytes) return TG_ERR_INVALID_ARG;
+    const Range rp{reinterpret_cast<uintptr_t>(packed), reinterpret_cast<uintptr_t>(packed) + (uintptr_t)bytes};
+    if (overlaps(span(B, batch, rows, cols, ldb, sB, esz), rp)) return TG_ERR_INVALID_ARG;
+    const int64_t ldp = packed_ld(N, dtype);
+    if (ldp * esz > 0x7fffffffLL) return TG_ERR_UNSUPPORTED;
+    st = current_device_ok();
+    if (st != TG_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (!transposed) return launch_pack_rows(esz, B, ldb, sB, packed, ldp, K, N, batch * K, s);
+    {
+        const int64_t gk = cdiv(K, 64), gn = cdiv(ldp, 64);
+        if (gk > 0x7fffffffLL || gn > 65535 || batch > 65535) return TG_ERR_UNSUPPORTED;
+        const dim3 grid((unsigned)gk, (unsigned)gn, (unsigned)batch);
+        if (esz == 4)
+            hipLaunchKernelGGL(pack_transposed_kernel<uint32_t>, grid, dim3(256), 0, s,
+                               static_cast<const uint32_t *>(B), ldb, sB, static_cast<uint32_t *>(packed), ldp, K, N);
+        else
+            hipLaunchKernelGGL(pack_transposed_kernel<uint16_t>, grid, dim3(256), 0, s,
+                               static_cast<const uint16_t *>(B), ldb, sB, static_cast<uint16_t *>(packed), ldp, K, N);
+    }
+    return hipGetLastError() == hipSuccess ? TG_OK : TG_ERR_LAUNCH;
 }
 
 }  // namespace
@@ -697,5 +768,27 @@ const char *tile_gemm_status_string(tg_status s) {
 }
 
 int tile_gemm_abi_version(void) { return TILE_GEMM_ABI_VERSION; }
+
+int64_t tile_gemm_packed_b_ld(int64_t N, tg_dtype dtype) {
+    if (N < 0 || (dtype != TG_F32 && dtype != TG_BF16 && dtype != TG_F16)) return -1;
+    return packed_ld(N, dtype);
+}
+
+tg_status tile_gemm_packed_b_size(int64_t batch, int64_t K, int64_t N, tg_dtype dtype, int64_t *bytes) {
+    if (!bytes) return TG_ERR_INVALID_ARG;
+    int64_t b = 0;
+    const tg_status st = packed_bytes_of(batch, K, N, dtype, b);
+    if (st == TG_OK) *bytes = b;
+    return st;
+}
+
+tg_status tile_gemm_pack_b(int64_t batch, int64_t K, int64_t N, tg_dtype dtype, const void *B, int64_t ldb,
+                           int64_t strideB, int transposed, void *packed, int64_t packed_bytes, void *stream) {
+    try {
+        return pack_b(batch, K, N, dtype, B, ldb, strideB, transposed, packed, packed_bytes, stream);
+    } catch (...) {
+        return TG_ERR_INTERNAL;
+    }
+}
 
 }  // extern "C"
