@@ -108,19 +108,26 @@ def oracle_rows(p, rows, bias=None, bias_mode=0, activation=0):
 
 
 def rocm_environment():
-    """ROCm version and a sample of the GPU clocks (rocm-smi), best effort."""
-    import subprocess
+    """ROCm version and the GPU clock levels from the driver's sysfs files, best effort.
+
+    Files only: no program is started from this process, which has the GPU open."""
+    import glob
     env = {"rocm_version": None, "clocks": None}
     try:
         with open("/opt/rocm/.info/version") as f:
             env["rocm_version"] = f.read().strip()
     except OSError:
         pass
-    try:
-        out = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=15).stdout
-        env["clocks"] = [l.strip() for l in out.splitlines() if "sclk" in l or "mclk" in l or "fclk" in l][:4] or None
-    except (OSError, subprocess.SubprocessError):
-        pass
+    clocks = []
+    for kind in ("sclk", "mclk", "fclk"):
+        for path in sorted(glob.glob(f"/sys/class/drm/card*/device/pp_dpm_{kind}"))[:1]:
+            try:
+                with open(path) as f:
+                    cur = [l.strip() for l in f if l.strip().endswith("*")]
+                clocks.append(f"{kind}: {cur[0] if cur else 'unknown'}")
+            except OSError:
+                pass
+    env["clocks"] = clocks or None
     return env
 
 
@@ -137,6 +144,9 @@ def main():
     import tile_scheduled_dense_amd as tg
     import workloads
 
+    if not args.no_cpu_baseline:
+        import oracle
+        oracle.load()       # compiled, if it must be, before the GPU is opened
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)

@@ -173,6 +173,13 @@ def _lib() -> OracleLibrary:
     return _default
 
 
+def load() -> OracleLibrary:
+    """The oracle library, compiled first if missing or older than its source.  Call it before
+    the process opens the GPU: compiling starts gcc, and a process that has the GPU open starts
+    no other program."""
+    return _lib()
+
+
 def gemm(*a, **kw):
     return _lib().gemm(*a, **kw)
 

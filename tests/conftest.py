@@ -9,5 +9,8 @@ if ROOT not in sys.path:
 
 
 def pytest_configure(config):
+    # the oracle library is compiled (if it must be) before any test opens the GPU
+    import oracle
+    oracle.load()
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU; runs through the C ABI")
     config.addinivalue_line("markers", "slow: takes more than a few seconds on the CPU")
