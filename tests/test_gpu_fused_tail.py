@@ -283,3 +283,26 @@ def test_gelu_accuracy(split):
     print(f"split {split}: GELU error at most {worst:.3f} of 2.5e-7 |x|")
     assert np.all(err <= bound), worst
     gp.check_guards()
+
+
+EDGE_CASES = [
+    # dtype, M, N, K, batch, config, split_k, alpha, beta, bias_mode, activation
+    ("bf16", 100, 70, 0, 1, 0, 0, 1.5, 0.5, 1, 2),        # K = 0: act(bias) + beta C0
+    ("f32", 33, 17, 0, 2, 0, 0, 1.0, 0.0, 2, 1),
+    ("bf16", 1, 300, 64, 1, 0, 0, 1.0, 0.5, 1, 1),        # one row
+    ("f16", 300, 1, 64, 1, 0, 0, 1.0, 0.0, 2, 2),         # one column
+    ("bf16", 1, 1, 1, 3, 0, 0, -2.0, 1.0, 1, 2),          # one element per problem, K = 1
+    ("f32", 1, 1, 1, 1, 0, 0, 1.0, 0.0, 2, 1),
+]
+
+
+@pytest.mark.parametrize("dt,M,N,K,batch,cfg,split,alpha,beta,mode,act", EDGE_CASES, ids=lambda v: str(v))
+def test_fused_tail_degenerate(dt, M, N, K, batch, cfg, split, alpha, beta, mode, act):
+    p = workloads.custom(dt, M, N, K, batch=batch, alpha=alpha, beta=beta, seed=M + 3 * N + K, name="edge")
+    stride = N if mode == 1 else M
+    bias = make_bias(p, mode, stride, seed=7)
+    if K == 0:      # the bias alone sets the activation's input: give it both signs at a useful size
+        bias = np.random.default_rng(8).standard_normal(len(bias)).astype(np.float32) * 2
+    gp = run(p, torch.from_numpy(bias).to("cuda"), stride, mode, act, config=cfg, split_k=split)
+    check(p, gp.result(), bias, stride, mode, act)
+    gp.check_guards()
