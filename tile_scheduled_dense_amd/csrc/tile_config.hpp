@@ -163,9 +163,12 @@ struct RingCfg {
     static constexpr bool B_HALF_SWZ = MT_ == 16;            // (k >> 3) & 1 into the 32-byte half
     // Workgroups per CU the kernel is compiled for (its register budget): the
     // 256 x 256 tile takes a whole CU (512 registers per lane, 128 KiB of
-    // LDS); the smaller tiles leave room for two and four, which memory-bound
-    // problems need for the bytes in flight.
-    static constexpr int OCCUPANCY = BM_ * BN_ >= 256 * 256 ? 1 : (BM_ * BN_ >= 128 * 128 ? 2 : 4);
+    // LDS); the smaller tiles leave room for two, which memory-bound problems
+    // need for the bytes in flight.  (A budget of four for the 64 x 64 tile
+    // was never met: its software pipeline needs more than 128 registers, so
+    // it ran two per CU anyway and spilled on the way; mid-size problems
+    // measured the same either way.)
+    static constexpr int OCCUPANCY = BM_ * BN_ >= 256 * 256 ? 1 : 2;
 
     static_assert(BM % (WAVES_M * MT) == 0 && BN % (WAVES_N * MT) == 0, "wave tiling");
     static_assert(A_TILE_BYTES % (1024 * WAVES) == 0 && A_DMA >= 1, "A copy split");
