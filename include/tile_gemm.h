@@ -54,7 +54,7 @@ typedef enum { TG_F32 = 0, TG_BF16 = 1, TG_F16 = 2 } tg_dtype;
 typedef enum {
     TG_OK = 0,
     TG_ERR_INVALID_ARG = 1,  /* extents, strides, pointers, dtype or overlap rejected */
-    TG_ERR_UNSUPPORTED = 2,  /* no visible gfx950 device, or an option this build lacks */
+    TG_ERR_UNSUPPORTED = 2,  /* no visible gfx950 device, or an option not built     */
     TG_ERR_LAUNCH = 3,       /* the HIP runtime refused the launch */
     TG_ERR_INTERNAL = 4      /* unexpected failure inside the library */
 } tg_status;

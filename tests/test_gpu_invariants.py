@@ -161,5 +161,5 @@ def test_stream_argument_is_used():
 
 
 def test_negative_status_on_device_for_bad_args():
-    # argument errors are caught before any device work, also on a GPU machine
+    # argument errors are caught before any device work, also with a GPU present
     assert tg.tile_gemm_status("tile_gemm", 4, 4, 4, 1, 0, 4, 0, 4, 0, 3, 1.0, 0.0, 0) == tg.TG_ERR_INVALID_ARG
