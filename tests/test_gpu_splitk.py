@@ -80,8 +80,11 @@ def test_split_integer_exact(dt, M, N, K, batch, cfg, S):
     assert np.array_equal(got, ref)
 
 
-def test_split_equals_slices_folded_in_tree_order():
-    dt, M, N, K, cfg, S, alpha = "bf16", 200, 150, 2600, tg.TG_CFG_64x64, 6, 1.5
+@pytest.mark.parametrize("M,N,K,S", [(200, 150, 2600, 6), (101, 99, 2600, 5), (64, 64, 4096, 7),
+                                     (96, 80, 4096, 13), (33, 65, 2048, 3), (64, 32, 8192, 64)])
+def test_split_equals_slices_folded_in_tree_order(M, N, K, S):
+    # M x N a multiple of 4 takes the combine's 16-byte loads, otherwise one element a thread
+    dt, cfg, alpha = "bf16", tg.TG_CFG_64x64, 1.5
     p = workloads.custom(dt, M, N, K, lda_pad=3, ldb_pad=5, alpha=alpha, beta=0.0, name="split_tree")
     plan = tg.tile_gemm_plan(1, M, N, K, dt, config=cfg, split_k=S)
     S_eff, ks = plan["split_k"], plan["k_slice"]
