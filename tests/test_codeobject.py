@@ -16,6 +16,8 @@ import pytest
 
 import tile_scheduled_dense_amd as tg
 
+pytestmark = pytest.mark.spawns
+
 OBJDUMP = "/opt/rocm/llvm/bin/llvm-objdump"
 
 

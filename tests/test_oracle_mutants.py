@@ -14,6 +14,8 @@ import pytest
 
 import oracle
 
+pytestmark = pytest.mark.spawns
+
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 MUTANTS = {
