@@ -111,6 +111,9 @@ typedef enum {
  *   split_k == 0: automatic -- split only when the plan has too few output
  *                 tiles to fill the GPU, K is deep, and `workspace` holds the
  *                 partials (tile_gemm_workspace_size says how many bytes);
+ *                 without a forced config, each tile size is weighed with its
+ *                 own split and the one whose workgroups best fill the GPU
+ *                 (ties: the larger tile) is taken;
  *   split_k == 1: never split;
  *   split_k >= 2: at most split_k slices (fewer when K is short); the call
  *                 fails with TG_ERR_INVALID_ARG if the workspace is too small.
