@@ -369,3 +369,24 @@ def test_pack_b_argument_errors():
     import torch
     if torch.cuda.device_count() == 0:
         assert st() == tg.TG_ERR_UNSUPPORTED
+
+
+def test_plan_automatic_split_across_tiles():
+    """Without a forced tile, each tile size is weighed with its own automatic split and the best
+    fill of the 256 CUs wins (ties: the larger tile); the workloads keep their plans."""
+    big = dict(workspace=1 << 40, workspace_bytes=1 << 40)
+    cases = [((1, 1024, 1024, 4096, "bf16"), (tg.TG_CFG_128x128, 4, 256)),   # not 256x256 split 4 (64 blocks)
+             ((1, 512, 2048, 2048, "bf16"), (tg.TG_CFG_64x64, 1, 256)),      # not 256x256 split 2 (32 blocks)
+             ((1, 512, 512, 131072, "bf16"), (tg.TG_CFG_256x256, 64, 256)),  # a tie at 256: the larger tile
+             ((1, 8192, 8192, 8192, "bf16"), (tg.TG_CFG_256x256, 1, 1024)),
+             ((512, 257, 129, 1000, "f16"), (tg.TG_CFG_256x256, 1, 1024)),
+             ((1, 1000, 1000, 1000, "bf16"), (tg.TG_CFG_64x64, 1, 256))]
+    for shape, want in cases:
+        p = tg.tile_gemm_plan(*shape, **big)
+        assert (p["config"], p["split_k"], p["grid"]) == want, (shape, p)
+    # a forced tile keeps its own split; without a workspace there is no split at all
+    p = tg.tile_gemm_plan(1, 1024, 1024, 4096, "bf16", config=tg.TG_CFG_256x256, **big)
+    assert (p["config"], p["split_k"]) == (tg.TG_CFG_256x256, 4)
+    assert tg.tile_gemm_plan(1, 1024, 1024, 4096, "bf16")["split_k"] == 1
+    assert tg.tile_gemm_workspace_size(1, 1024, 1024, 4096, "bf16") == 4 * 1024 * 1024 * 4
+    assert tg.tile_gemm_workspace_size(1, 512, 2048, 2048, "bf16") == 0
