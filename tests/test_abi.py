@@ -390,3 +390,12 @@ def test_plan_automatic_split_across_tiles():
     assert tg.tile_gemm_plan(1, 1024, 1024, 4096, "bf16")["split_k"] == 1
     assert tg.tile_gemm_workspace_size(1, 1024, 1024, 4096, "bf16") == 4 * 1024 * 1024 * 4
     assert tg.tile_gemm_workspace_size(1, 512, 2048, 2048, "bf16") == 0
+
+
+def test_plan_single_round_of_256():
+    """256 x 256 when its tiles fill at least half the CUs and 128 x 128 would need a second round."""
+    for shape in [(1, 3000, 3000, 3000, "bf16"), (1, 3072, 3072, 3072, "bf16"), (1, 4096, 2560, 2048, "bf16"),
+                  (1, 3840, 3840, 1024, "bf16"), (4, 1536, 1536, 1024, "bf16")]:
+        assert tg.tile_gemm_plan(*shape)["config"] == tg.TG_CFG_256x256, shape
+    for shape in [(1, 2048, 2048, 2048, "bf16"), (1, 4096, 2048, 2048, "bf16")]:    # one round of 128 x 128
+        assert tg.tile_gemm_plan(*shape)["config"] == tg.TG_CFG_128x128, shape
