@@ -380,7 +380,9 @@ def test_plan_automatic_split_across_tiles():
              ((1, 512, 512, 131072, "bf16"), (tg.TG_CFG_256x256, 64, 256)),  # a tie at 256: the larger tile
              ((1, 8192, 8192, 8192, "bf16"), (tg.TG_CFG_256x256, 1, 1024)),
              ((512, 257, 129, 1000, "f16"), (tg.TG_CFG_256x256, 1, 1024)),
-             ((1, 1000, 1000, 1000, "bf16"), (tg.TG_CFG_64x64, 1, 256))]
+             ((1, 1000, 1000, 1000, "bf16"), (tg.TG_CFG_64x64, 1, 256)),
+             ((1, 384, 4096, 4096, "bf16"), (tg.TG_CFG_128x128, 4, 384)),     # 512 slots for the smaller tiles
+             ((1, 256, 256, 65536, "bf16"), (tg.TG_CFG_64x64, 32, 512))]
     for shape, want in cases:
         p = tg.tile_gemm_plan(*shape, **big)
         assert (p["config"], p["split_k"], p["grid"]) == want, (shape, p)

@@ -122,14 +122,17 @@ constexpr int kOptionsV1Size = 5 * (int)sizeof(int);
 constexpr int64_t kMaxSplits = 64;
 
 // Automatic split count: split only when the output tiles cannot fill the
-// GPU's 256 CUs, doubling while the blocks still fit in one round and each
-// slice keeps at least 1024 of K.
-int64_t auto_splits(int64_t tiles, int64_t K) {
+// GPU, doubling while the blocks still fit in one round (`slots` workgroups at
+// once) and each slice keeps at least 1024 of K.
+int64_t auto_splits(int64_t tiles, int64_t K, int64_t slots) {
     if (tiles >= 128) return 1;
     int64_t s = 1;
-    while (2 * s <= kMaxSplits && tiles * 2 * s <= 256 && K / (2 * s) >= 1024) s *= 2;
+    while (2 * s <= kMaxSplits && tiles * 2 * s <= slots && K / (2 * s) >= 1024) s *= 2;
     return s;
 }
+
+// Workgroups the GPU runs at once for a 16-bit tile: its workgroups per CU times 256 CUs.
+int64_t cfg_slots(int config) { return config == TG_CFG_256x256 ? 256 : 512; }
 
 // A thin remainder computed by a GEMM of its own (see tile_gemm.h): its
 // extents, where it starts in C, and its K split and workspace region.
@@ -174,8 +177,9 @@ tg_status make_plan(int64_t batch, int64_t M, int64_t N, int64_t K, tg_dtype dty
     int config = o.config;
     if (sixteen && some && o.split_k == 0) {
         // With a forced tile, that tile's own count.  Otherwise each tile with its
-        // own count, and the one whose workgroups fill the most of the GPU's 256
-        // CUs (ties: the larger tile, fewer re-reads of A and B); no split when
+        // own count, and the one whose workgroups fill the most of the slots it
+        // has (256 for 256 x 256, 512 for the smaller tiles at two per CU; ties:
+        // the larger tile, fewer re-reads of A and B); no split when
         // that one needs none (the plain choice below then picks the tile).
         // 1024 x 1024 x 4096 bf16: 128 x 128 split 4 (256 workgroups) takes
         // 25.6 us where 256 x 256 split 4 (64) took 35.6; 512 x 2048 x 2048: the
@@ -186,8 +190,9 @@ tg_status make_plan(int64_t batch, int64_t M, int64_t N, int64_t K, tg_dtype dty
             for (int c = TG_CFG_256x256; c <= TG_CFG_64x64; ++c) {
                 const CfgDims dd = cfg_dims(c);
                 const int64_t tiles = cdiv(M, dd.bm) * cdiv(N, dd.bn) * batch;
-                const int64_t blocks = tiles * auto_splits(tiles, K);
-                const int64_t fill = blocks < 256 ? blocks : 256;
+                const int64_t slots = cfg_slots(c);
+                const int64_t blocks = tiles * auto_splits(tiles, K, slots);
+                const int64_t fill = (blocks < slots ? blocks : slots) * 512 / slots;   // in 512ths
                 if (fill > best_fill) {
                     best_fill = fill;
                     cfg = c;
@@ -196,7 +201,7 @@ tg_status make_plan(int64_t batch, int64_t M, int64_t N, int64_t K, tg_dtype dty
         }
         if (cfg >= TG_CFG_256x256 && cfg <= TG_CFG_64x64) {
             const CfgDims dd = cfg_dims(cfg);
-            const int64_t s_auto = auto_splits(cdiv(M, dd.bm) * cdiv(N, dd.bn) * batch, K);
+            const int64_t s_auto = auto_splits(cdiv(M, dd.bm) * cdiv(N, dd.bn) * batch, K, cfg_slots(cfg));
             const int64_t slice = cdiv(cdiv(K, s_auto), dd.bk) * dd.bk;
             const int64_t s_eff = cdiv(K, slice);
             wanted_bytes = s_eff > 1 ? s_eff * batch * M * N * 4 : 0;
