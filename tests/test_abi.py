@@ -382,7 +382,11 @@ def test_plan_automatic_split_across_tiles():
              ((512, 257, 129, 1000, "f16"), (tg.TG_CFG_256x256, 1, 1024)),
              ((1, 1000, 1000, 1000, "bf16"), (tg.TG_CFG_64x64, 1, 256)),
              ((1, 384, 4096, 4096, "bf16"), (tg.TG_CFG_128x128, 4, 384)),     # 512 slots for the smaller tiles
-             ((1, 256, 256, 65536, "bf16"), (tg.TG_CFG_64x64, 32, 512))]
+             ((1, 256, 256, 65536, "bf16"), (tg.TG_CFG_64x64, 32, 512)),
+             # skinny: the 256 x 256 tile's padding would be mostly zeros
+             ((1, 8192, 64, 8192, "bf16"), (tg.TG_CFG_64x64, 4, 512)),
+             ((1, 64, 8192, 8192, "bf16"), (tg.TG_CFG_64x64, 4, 512)),
+             ((1, 16384, 96, 4096, "bf16"), (tg.TG_CFG_128x128, 4, 512))]
     for shape, want in cases:
         p = tg.tile_gemm_plan(*shape, **big)
         assert (p["config"], p["split_k"], p["grid"]) == want, (shape, p)

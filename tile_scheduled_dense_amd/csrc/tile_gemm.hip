@@ -121,11 +121,11 @@ int choose_config(int64_t batch, int64_t M, int64_t N, tg_dtype dtype) {
 constexpr int kOptionsV1Size = 5 * (int)sizeof(int);
 constexpr int64_t kMaxSplits = 64;
 
-// Automatic split count: split only when the output tiles cannot fill the
-// GPU, doubling while the blocks still fit in one round (`slots` workgroups at
-// once) and each slice keeps at least 1024 of K.
+// Automatic split count: split only when the output tiles fill less than
+// half the `slots` workgroups the GPU runs at once, doubling while the blocks
+// still fit in one round and each slice keeps at least 1024 of K.
 int64_t auto_splits(int64_t tiles, int64_t K, int64_t slots) {
-    if (tiles >= 128) return 1;
+    if (2 * tiles >= slots) return 1;
     int64_t s = 1;
     while (2 * s <= kMaxSplits && tiles * 2 * s <= slots && K / (2 * s) >= 1024) s *= 2;
     return s;
@@ -184,17 +184,22 @@ tg_status make_plan(int64_t batch, int64_t M, int64_t N, int64_t K, tg_dtype dty
         // 1024 x 1024 x 4096 bf16: 128 x 128 split 4 (256 workgroups) takes
         // 25.6 us where 256 x 256 split 4 (64) took 35.6; 512 x 2048 x 2048: the
         // 64 x 64 tile unsplit (256) 19.4 us where 256 x 256 split 2 (32) took 33.7.
+        // The fill is weighed by the share of the padded tiles that is output
+        // (a 256 x 256 tile over 64 columns multiplies three quarters zeros):
+        // 8192 x 64 x 8192 bf16 takes 64 x 64 split 4, 27.0 us, where 256 x 256
+        // split 8 took 54.5.
         int cfg = o.config;
         if (!cfg) {
-            int64_t best_fill = -1;
+            double best = -1.0;
             for (int c = TG_CFG_256x256; c <= TG_CFG_64x64; ++c) {
                 const CfgDims dd = cfg_dims(c);
-                const int64_t tiles = cdiv(M, dd.bm) * cdiv(N, dd.bn) * batch;
+                const int64_t tm = cdiv(M, dd.bm), tn = cdiv(N, dd.bn), tiles = tm * tn * batch;
                 const int64_t slots = cfg_slots(c);
                 const int64_t blocks = tiles * auto_splits(tiles, K, slots);
-                const int64_t fill = (blocks < slots ? blocks : slots) * 512 / slots;   // in 512ths
-                if (fill > best_fill) {
-                    best_fill = fill;
+                const double fill = (double)(blocks < slots ? blocks : slots) / (double)slots;
+                const double useful = (double)M * (double)N / ((double)(tm * dd.bm) * (double)(tn * dd.bn));
+                if (fill * useful > best * (1.0 + 1e-9)) {
+                    best = fill * useful;
                     cfg = c;
                 }
             }
