@@ -47,10 +47,19 @@
 extern "C" {
 #endif
 
-#define TILE_GEMM_ABI_VERSION 7
+#define TILE_GEMM_ABI_VERSION 8
 
 typedef enum { TG_F32 = 0, TG_BF16 = 1, TG_F16 = 2 } tg_dtype;
 
+/*
+ * Every call reports its outcome as a tg_status and never prints or aborts.
+ * A schedule operation that cannot apply fails loudly rather than computing
+ * something else (OCANNL "Module Ir.Schedule", Interchange paragraph), and a
+ * target refuses an execution scope it does not have rather than substituting
+ * one (LuisaCompute "Execution Nests and coordinates", Ordering strength and
+ * sibling scopes); a status of its own for each kind of refusal is that rule
+ * across a C boundary.
+ */
 typedef enum {
     TG_OK = 0,
     TG_ERR_INVALID_ARG = 1,  /* extents, strides, pointers, dtype or overlap rejected */
@@ -72,7 +81,10 @@ tg_status tile_gemm(int64_t M, int64_t N, int64_t K, tg_dtype dtype,
  * `batch` independent problems in one launch: problem b uses A + b*strideA,
  * B + b*strideB and C + b*strideC (element strides, >= 0).  The C ranges of
  * distinct b must not overlap each other (checked).  A stride of 0 shares an
- * operand across the batch.
+ * operand across the batch.  The batch is one more independent parallel axis
+ * of the same contraction: the problems are disjoint children of a `parallel`
+ * region (LuisaCompute "Execution Nests and coordinates", structured-region
+ * calculus), so they run in one launch with no ordering between them.
  */
 tg_status tile_gemm_strided_batched(int64_t batch, int64_t M, int64_t N, int64_t K, tg_dtype dtype,
                                     const void *A, int64_t lda, int64_t strideA,
@@ -80,7 +92,9 @@ tg_status tile_gemm_strided_batched(int64_t batch, int64_t M, int64_t N, int64_t
                                     float *C, int64_t ldc, int64_t strideC,
                                     float alpha, float beta, void *stream);
 
-/* Schedule knobs, for tests and measurements; zero-initialise for defaults. */
+/* Schedule knobs, for tests and measurements; zero-initialise for defaults.
+ * The tile configurations are block tiles of the M and N loops (OCANNL "Module
+ * Ir.Schedule", Split paragraph) with their MFMA register tiles (Tensorize). */
 typedef enum {
     TG_CFG_AUTO = 0,
     TG_CFG_256x256 = 1,     /* 16-bit inputs: 256x256 block tile, 4 waves, 16x16x32 MFMA */
@@ -95,8 +109,20 @@ typedef enum {
  * fields past it read as zero.
  *
  * pipeline_depth is the number of LDS copies of the K tile (the window is one
- * less): 16-bit inputs take 1, 2 or 4 (default 4), fp32 inputs 1 or 2 (default
- * 2).  Depth 1 is the unpipelined form.
+ * less; OCANNL "Module Ir.Schedule", Stage paragraph, pipeline_depth, and
+ * LuisaCompute "Pipelines and stage boundaries", window): 16-bit inputs take 1,
+ * 2 or 4 (default 4; 5 for TG_CFG_128x128 and TG_CFG_64x64), fp32 inputs 1 or 2
+ * (default 2).  Depth 1 is the unpipelined form.
+ *
+ * swizzle is the placement of the staged tiles in LDS (OCANNL Stage paragraph,
+ * swizzle and pad_stride; TVM TIRx "Tensor Layout", SwizzleLayout): 0 the
+ * default (XOR); 1 none, the row-major tile; 2 pad_stride, the row-major tile
+ * with its minor dimension rounded up by one 16-byte unit (A rows of 32 k at a
+ * pitch of 40, B rows of BN n at BN + 8; built for TG_CFG_256x256 at depth 4,
+ * UNSUPPORTED elsewhere); 3 the XOR swizzle of 16-byte units (Swizzle_b128
+ * flavour).  Placement changes which LDS bytes hold a value, never the value:
+ * every placement gives a bitwise identical C.  (Version 7 and earlier: 2 was
+ * the XOR swizzle.)
  *
  * Split-K (16-bit inputs): the deterministic two-pass split reduction of the
  * OCANNL "Module Ir.Schedule" page (paragraph of that name).  The K range is
@@ -186,9 +212,9 @@ typedef enum {
  */
 typedef struct {
     int struct_size;
-    int config;          /* tg_config; TG_CFG_AUTO picks by dtype and shape           */
+    int force_cfg;       /* tg_config; TG_CFG_AUTO picks by dtype and shape           */
     int pipeline_depth;  /* 0 = default (see above)                                   */
-    int swizzle;         /* 0 = default (XOR); 1 = none (row-major tile); 2 = XOR   */
+    int swizzle;         /* 0 = default (XOR); 1 = none; 2 = pad_stride; 3 = XOR     */
     int block_order;     /* 0 = default (XCD-grouped); 1 = plain row-major          */
     int split_k;         /* 0 = automatic, 1 = off, S >= 2 = at most S K slices      */
     void *workspace;     /* device memory for split-K partials or the A copy, or NULL */
@@ -238,7 +264,9 @@ typedef struct {
     int tail_n_splits;            /* 0: no N-remainder GEMM; S >= 1: one, with S K slices */
     int tail_m_splits;            /* the same for the M remainder                  */
     int persistent;               /* 1: persistent workgroups (grid = their count) */
-    int pad_;
+    int per_cu;                   /* workgroups of this configuration one CU holds at once
+                                     (registers and LDS of the built kernel); the automatic
+                                     split counts 256 times this many slots */
 } tg_plan_info;
 
 tg_status tile_gemm_plan(int64_t batch, int64_t M, int64_t N, int64_t K, tg_dtype dtype,
@@ -320,7 +348,13 @@ int64_t tile_gemm_lds_offset(int config, int swizzle, int operand, int64_t row, 
  * or -1 for an invalid request. */
 int tile_gemm_acc_coord(int config, int wave, int lane, int slot, int64_t *row, int64_t *col);
 
+/* A fixed description of a status, for messages: never NULL, owned by the
+ * library (the failure reports the status codes above stand for). */
 const char *tile_gemm_status_string(tg_status s);
+
+/* TILE_GEMM_ABI_VERSION of the built library, so a caller can refuse a library
+ * built from another header instead of misreading its structs (the same
+ * refuse-rather-than-guess rule as the status codes above). */
 int tile_gemm_abi_version(void);
 
 /*

@@ -28,7 +28,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert tg.abi_version() == 7
+    assert tg.abi_version() == tg.ABI_VERSION == 8
     for s in range(5):
         assert tg.STATUS_NAMES[s] in tg.status_string(s)
 
@@ -217,7 +217,12 @@ def test_plan_pack_a():
     assert tg.tile_gemm_plan(1, 8191, 1000, 8190, "bf16", plan_lda=8193, **big)["pack_a"] == 0
     # forced: only for the 16-bit 256 x 256 configuration without a split
     assert tg.tile_gemm_plan(1, 100, 100, 100, "bf16", config=tg.TG_CFG_256x256, pack_a=2)["pack_a"] == 1
-    for kw in (dict(config=tg.TG_CFG_128x128), dict(config=tg.TG_CFG_256x256, split_k=4)):
+    # with the tile left to the library, a forced repack takes that tile unsplit, whatever the shape
+    # and workspace would choose otherwise
+    for shape in [(1, 1024, 1024, 4096), (1, 2048, 2048, 8192), (1, 8192, 64, 8192), (3, 257, 129, 1000)]:
+        p = tg.tile_gemm_plan(*shape, "bf16", pack_a=2, workspace=1 << 40, workspace_bytes=1 << 40)
+        assert (p["config"], p["split_k"], p["pack_a"]) == (tg.TG_CFG_256x256, 1, 1), shape
+    for kw in (dict(config=tg.TG_CFG_128x128), dict(config=tg.TG_CFG_256x256, split_k=4), dict(split_k=4)):
         with pytest.raises(tg.TileGemmError):
             tg.tile_gemm_plan(1, 512, 512, 4096, "bf16", pack_a=2, **kw)
     with pytest.raises(tg.TileGemmError):
@@ -405,3 +410,21 @@ def test_plan_single_round_of_256():
         assert tg.tile_gemm_plan(*shape)["config"] == tg.TG_CFG_256x256, shape
     for shape in [(1, 2048, 2048, 2048, "bf16"), (1, 4096, 2048, 2048, "bf16")]:    # one round of 128 x 128
         assert tg.tile_gemm_plan(*shape)["config"] == tg.TG_CFG_128x128, shape
+
+
+def test_plan_placements():
+    """swizzle codes: 0 default (XOR), 1 none, 2 pad_stride, 3 XOR; pad_stride only on the 256 x 256
+    tile at depth 4, whose LDS copies then hold the padded rows (A 256 x 80 bytes = 20 KiB, B 32 x
+    528 bytes in 17 KiB)."""
+    base = tg.tile_gemm_plan(1, 8192, 8192, 8192, "bf16")
+    assert base["swizzle"] == tg.SWZ_XOR == 3
+    assert tg.tile_gemm_plan(1, 8192, 8192, 8192, "bf16", swizzle=tg.SWZ_XOR) == base
+    pad = tg.tile_gemm_plan(1, 8192, 8192, 8192, "bf16", swizzle=tg.SWZ_PAD)
+    assert pad["swizzle"] == tg.SWZ_PAD and pad["lds_bytes"] == 4 * (20 + 17) * 1024
+    assert {k: v for k, v in pad.items() if k not in ("swizzle", "lds_bytes")} == \
+           {k: v for k, v in base.items() if k not in ("swizzle", "lds_bytes")}
+    for kw in (dict(config=tg.TG_CFG_128x128), dict(pipeline_depth=2), dict(config=tg.TG_CFG_64x64)):
+        assert _plan_status(1, 1024, 1024, 1024, "bf16", swizzle=tg.SWZ_PAD, **kw) == tg.TG_ERR_UNSUPPORTED
+    assert _plan_status(1, 64, 64, 64, "f32", swizzle=tg.SWZ_PAD) == tg.TG_ERR_UNSUPPORTED
+    assert _plan_status(1, 64, 64, 64, "bf16", swizzle=4) == tg.TG_ERR_INVALID_ARG
+

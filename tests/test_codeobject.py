@@ -122,3 +122,81 @@ def test_accumulator_hazard_scan_finds_an_early_read():
     assert accumulator_hazards(settled) == []
     other = early[:2] + ["v_accvgpr_read_b32 v60, a12"]           # a different accumulator
     assert accumulator_hazards(other) == []
+
+
+# ---- register, scratch and LDS use of the built kernels -------------------------
+# The kernel descriptors' metadata (llvm-readelf --notes): .vgpr_count is the
+# whole register allocation of a wave (VGPRs and AGPRs), .private_segment_fixed_size
+# its scratch per lane, .group_segment_fixed_size its LDS per workgroup.
+READELF = "/opt/rocm/llvm/bin/llvm-readelf"
+_RING = re.compile(r"gemm_ring_kernelINS_7RingCfgILi(\d)ELi(\d+)ELi(\d+)ELi(\d)ELi(\d)ELi(\d+)EEELi(\d)ELi(\d)ELi(\d)ELb(\d)E")
+_F32 = re.compile(r"gemm_kernelINS_7TileCfgILi0ELi64ELi64ELi2ELi2EEELi(\d)ELi(\d)ELb(\d)E")
+
+
+def _kernels(tmp_path):
+    lib = tg.library_path()
+    if not os.path.exists(OBJDUMP) or not os.path.exists(READELF):
+        pytest.skip("llvm tools not installed")
+    local = tmp_path / "lib.so"
+    shutil.copy(lib, local)
+    subprocess.run([OBJDUMP, "--offloading", str(local)], check=True, capture_output=True, cwd=tmp_path)
+    objs = [p for p in tmp_path.iterdir() if "amdgcn" in p.name and "gfx950" in p.name]
+    notes = subprocess.run([READELF, "--notes", str(objs[0])], check=True, capture_output=True, text=True).stdout
+    out, cur = {}, None
+    for line in notes.splitlines():
+        m = re.match(r"\s+(?:- )?\.(name|vgpr_count|agpr_count|group_segment_fixed_size|"
+                     r"private_segment_fixed_size|max_flat_workgroup_size):\s+(\S+)", line)
+        if not m:
+            continue
+        key, val = m.group(1), m.group(2)
+        if line.lstrip().startswith("- "):
+            cur = {}
+        if cur is None:
+            continue
+        cur[key] = val
+        if key == "name":
+            out[val] = cur
+    return {n: {k: (int(v) if k != "name" else v) for k, v in d.items()} for n, d in out.items()}
+
+
+def _opt_in(name):
+    """Kernels only an explicit option reaches: persistent workgroups and the pad_stride ablation."""
+    if "persistent" in name:
+        return True
+    m = _RING.search(name)
+    return bool(m) and int(m.group(8)) == 2
+
+
+def test_no_scratch_outside_opt_in_variants(tmp_path):
+    ks = _kernels(tmp_path)
+    assert len(ks) > 40
+    spills = {n: d["private_segment_fixed_size"] for n, d in ks.items() if d["private_segment_fixed_size"] > 0}
+    assert all(_opt_in(n) for n in spills), {n: v for n, v in spills.items() if not _opt_in(n)}
+
+
+CFG_OF = {(256, 256): tg.TG_CFG_256x256, (128, 128): tg.TG_CFG_128x128, (64, 64): tg.TG_CFG_64x64}
+
+
+def test_per_cu_table_matches_code_object(tmp_path):
+    """The plan's workgroups per CU equal what each built kernel's registers and LDS allow:
+    min(4 SIMDs x floor(512 / registers per wave) / waves per workgroup, floor(160 KiB / LDS))."""
+    ks = _kernels(tmp_path)
+    checked = 0
+    for name, d in ks.items():
+        m = _RING.search(name)
+        f = _F32.search(name)
+        if m and "persistent" not in name:
+            bm, bn, wm, wn, stages, swz = (int(m.group(i)) for i in (2, 3, 4, 5, 7, 8))
+            if (bm, bn) not in CFG_OF or swz == 2:
+                continue
+            cfg, waves, depth, dt = CFG_OF[(bm, bn)], wm * wn, stages, "bf16" if m.group(1) == "1" else "f16"
+        elif f:
+            cfg, waves, depth, dt = tg.TG_CFG_F32_64x64, 4, int(f.group(1)), "f32"
+        else:
+            continue
+        by_regs = 4 * (512 // d["vgpr_count"]) // waves
+        by_lds = (160 * 1024) // max(d["group_segment_fixed_size"], 1)
+        plan = tg.tile_gemm_plan(1, 1024, 1024, 1024, dt, config=cfg, pipeline_depth=depth)
+        assert plan["per_cu"] == min(by_regs, by_lds), (name, d, plan["per_cu"])
+        checked += 1
+    assert checked >= 20

@@ -194,7 +194,10 @@ def b_transpose_bytes(cfg, swz, mt, wcol, j, s, half):
 # MFMA shapes (zero conflicts with the XOR placement).
 @pytest.mark.parametrize("cfg,bm,bn,waves,mt", RING)
 def test_ring_b_transpose_reads_conflict_free(cfg, bm, bn, waves, mt):
-    for swz, expect in [(tg.SWZ_XOR, True), (tg.SWZ_NONE, False)]:
+    placements = [(tg.SWZ_XOR, True), (tg.SWZ_NONE, False)]
+    if cfg in PAD_CFGS:
+        placements.append((tg.SWZ_PAD, False))
+    for swz, expect in placements:
         for wcol in range(0, bn, mt):
             for s in range(BK // (512 // mt)):
                 for half in (0, 1):
@@ -203,6 +206,52 @@ def test_ring_b_transpose_reads_conflict_free(cfg, bm, bn, waves, mt):
                     assert all(o % 8 == 0 for o in offs)
                     free = all(banks_distinct(offs[g:g + 32], 8) for g in (0, 32))
                     assert free == expect, (swz, wcol, s, half)
+
+
+# pad_stride (OCANNL Stage paragraph): the row stride is the minor dimension
+# rounded up by one 16-byte unit; the extents stay as they are and the padded
+# slots are never addressed.  Built for the 256 x 256 tile and its strips.
+PAD_CFGS = (tg.TG_CFG_256x256, tg.LAYOUT_CFG_STRIP_N, tg.LAYOUT_CFG_STRIP_M)
+
+
+@pytest.mark.parametrize("cfg,bm,bn,waves,mt", [r for r in RING if r[0] in PAD_CFGS])
+def test_pad_stride_placement(cfg, bm, bn, waves, mt):
+    for operand, kind, rows_, cols_ in [(0, tg.LAYOUT_LDS_A, bm, BK), (1, tg.LAYOUT_LDS_B, BK, bn)]:
+        L = tg.tile_gemm_describe_layout(cfg, tg.SWZ_PAD, kind)
+        pitch = cols_ + 8
+        assert (L.shape[0], L.shape[1], L.n_swizzle) == (rows_, cols_, 0)
+        assert (L.shard[0].extent, L.shard[0].stride, L.shard[1].stride) == (rows_, pitch, 1)
+        seen = set()
+        for r in range(rows_):
+            for c in range(cols_):
+                (coord,) = tg.tg_layout_eval(L, (r, c))
+                off = tg.tile_gemm_lds_offset(cfg, tg.SWZ_PAD, operand, r, c)
+                assert off == coord[M] == r * pitch + c
+                seen.add(off)
+        assert len(seen) == rows_ * cols_ and all(o % pitch < cols_ for o in seen)
+    # the tiles built without it refuse it
+    assert tg.tile_gemm_lds_offset(tg.TG_CFG_128x128, tg.SWZ_PAD, 0, 0, 0) == -1
+    with pytest.raises(tg.TileGemmError):
+        tg.tile_gemm_describe_layout(tg.TG_CFG_64x64, tg.SWZ_PAD, tg.LAYOUT_LDS_A)
+
+
+@pytest.mark.parametrize("cfg,bm,bn,waves,mt", [r for r in RING if r[0] in PAD_CFGS and r[2] >= 256])
+def test_pad_stride_b_reads_at_most_two_way(cfg, bm, bn, waves, mt):
+    # no linear pitch separates the rows k and k + 8 one transposing read pairs
+    # from rows k .. k + 3 (the XOR does): under the 32-lanes-per-cycle model the
+    # pad_stride pitch leaves each bank at most twice per cycle
+    worst = 0
+    for wcol in range(0, bn, mt):
+        for half in (0, 1):
+            offs = b_transpose_bytes(cfg, tg.SWZ_PAD, mt, wcol, 0, 0, half)
+            for g in (0, 32):
+                banks = {}
+                for b in offs[g:g + 32]:
+                    for w in range(2):
+                        bank = (b // 4 + w) % 64
+                        banks[bank] = banks.get(bank, 0) + 1
+                worst = max(worst, max(banks.values()))
+    assert worst == 2
 
 
 @pytest.mark.parametrize("cfg,bm,bn,waves,mt", RING)

@@ -25,11 +25,12 @@ DTYPES = {"f32": TG_F32, "bf16": TG_BF16, "f16": TG_F16}
 TG_OK, TG_ERR_INVALID_ARG, TG_ERR_UNSUPPORTED, TG_ERR_LAUNCH, TG_ERR_INTERNAL = range(5)
 STATUS_NAMES = {0: "TG_OK", 1: "TG_ERR_INVALID_ARG", 2: "TG_ERR_UNSUPPORTED", 3: "TG_ERR_LAUNCH",
                 4: "TG_ERR_INTERNAL"}
+ABI_VERSION = 8
 
 TG_CFG_AUTO, TG_CFG_256x256, TG_CFG_128x128, TG_CFG_64x64, TG_CFG_F32_64x64 = range(5)
 # layout-introspection ids of the thin fringe-strip blocks of TG_CFG_256x256
 LAYOUT_CFG_STRIP_N, LAYOUT_CFG_STRIP_M = 101, 102
-SWZ_DEFAULT, SWZ_NONE, SWZ_XOR = 0, 1, 2
+SWZ_DEFAULT, SWZ_NONE, SWZ_PAD, SWZ_XOR = 0, 1, 2, 3
 BIAS_NONE, BIAS_PER_COLUMN, BIAS_PER_ROW = 0, 1, 2
 ACT_NONE, ACT_RELU, ACT_GELU = 0, 1, 2
 
@@ -54,7 +55,7 @@ class TileGemmError(RuntimeError):
 
 
 class Options(ctypes.Structure):
-    _fields_ = [("struct_size", ctypes.c_int), ("config", ctypes.c_int), ("pipeline_depth", ctypes.c_int),
+    _fields_ = [("struct_size", ctypes.c_int), ("force_cfg", ctypes.c_int), ("pipeline_depth", ctypes.c_int),
                 ("swizzle", ctypes.c_int), ("block_order", ctypes.c_int), ("split_k", ctypes.c_int),
                 ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_int64),
                 ("pack_a", ctypes.c_int), ("pad0_", ctypes.c_int), ("plan_lda", ctypes.c_int64),
@@ -77,7 +78,7 @@ class PlanInfo(ctypes.Structure):
                 ("split_k", ctypes.c_int), ("k_slice", ctypes.c_int64), ("workspace_bytes", ctypes.c_int64),
                 ("mfma_m", ctypes.c_int), ("mfma_n", ctypes.c_int), ("mfma_k", ctypes.c_int), ("pack_a", ctypes.c_int),
                 ("strip_blocks", ctypes.c_int64), ("tail_n_splits", ctypes.c_int),
-                ("tail_m_splits", ctypes.c_int), ("persistent", ctypes.c_int), ("pad_", ctypes.c_int)]
+                ("tail_m_splits", ctypes.c_int), ("persistent", ctypes.c_int), ("per_cu", ctypes.c_int)]
 
     def as_dict(self):
         return {f: getattr(self, f) for f, _ in self._fields_}
@@ -214,11 +215,12 @@ def tile_gemm_ex(batch, M, N, K, dtype, A, lda, strideA, B, ldb, strideB, C, ldc
                  alpha=1.0, beta=0.0, stream=None, config=0, pipeline_depth=0, swizzle=0,
                  block_order=0, split_k=0, workspace=None, workspace_bytes=None, pack_a=0,
                  plan_lda=0, tail_gemm=0, persistent=0, bias=None, bias_stride=0, bias_mode=0,
-                 activation=0) -> None:
+                 activation=0, force_cfg=None) -> None:
     """`workspace`: a device tensor or address for split-K partials or the
     aligned copy of A (its byte size is taken from the tensor unless
-    `workspace_bytes` is given)."""
-    opt = _options(config, pipeline_depth, swizzle, block_order, split_k, workspace, workspace_bytes, pack_a,
+    `workspace_bytes` is given).  `force_cfg` (tg_options.force_cfg) may also be
+    given as `config`."""
+    opt = _options(config if force_cfg is None else force_cfg, pipeline_depth, swizzle, block_order, split_k, workspace, workspace_bytes, pack_a,
                    plan_lda, tail_gemm, persistent, bias, bias_stride, bias_mode, activation)
     _check(_lib().tile_gemm_ex(batch, M, N, K, _dtype(dtype), _addr(A), lda, strideA, _addr(B), ldb, strideB,
                                _addr(C), ldc, strideC, alpha, beta, _stream(stream), ctypes.byref(opt)),
@@ -232,9 +234,9 @@ def tile_gemm_status(fn: str, *args) -> int:
 
 def tile_gemm_plan(batch, M, N, K, dtype, config=0, pipeline_depth=0, swizzle=0, block_order=0,
                    split_k=0, workspace=None, workspace_bytes=None, pack_a=0, plan_lda=0, tail_gemm=0,
-                   persistent=0, bias_mode=0, activation=0, bias_stride=0) -> dict:
+                   persistent=0, bias_mode=0, activation=0, bias_stride=0, force_cfg=None) -> dict:
     info = PlanInfo()
-    opt = _options(config, pipeline_depth, swizzle, block_order, split_k, workspace, workspace_bytes, pack_a,
+    opt = _options(config if force_cfg is None else force_cfg, pipeline_depth, swizzle, block_order, split_k, workspace, workspace_bytes, pack_a,
                    plan_lda, tail_gemm, persistent, bias_stride=bias_stride, bias_mode=bias_mode,
                    activation=activation)
     _check(_lib().tile_gemm_plan(batch, M, N, K, _dtype(dtype), ctypes.byref(opt), ctypes.byref(info)),
@@ -244,11 +246,11 @@ def tile_gemm_plan(batch, M, N, K, dtype, config=0, pipeline_depth=0, swizzle=0,
 
 def tile_gemm_workspace_size(batch, M, N, K, dtype, config=0, pipeline_depth=0, swizzle=0, block_order=0,
                              split_k=0, pack_a=0, plan_lda=0, tail_gemm=0, persistent=0, bias_mode=0,
-                             activation=0, bias_stride=0) -> int:
+                             activation=0, bias_stride=0, force_cfg=None) -> int:
     """Bytes of workspace a call with these arguments would use (split-K partials, the
     aligned copy of A and the remainder GEMMs' partials; 0: none)."""
     n = ctypes.c_int64(0)
-    opt = _options(config, pipeline_depth, swizzle, block_order, split_k, None, None, pack_a, plan_lda, tail_gemm,
+    opt = _options(config if force_cfg is None else force_cfg, pipeline_depth, swizzle, block_order, split_k, None, None, pack_a, plan_lda, tail_gemm,
                    persistent, bias_stride=bias_stride, bias_mode=bias_mode, activation=activation)
     _check(_lib().tile_gemm_workspace_size(batch, M, N, K, _dtype(dtype), ctypes.byref(opt), ctypes.byref(n)),
            "tile_gemm_workspace_size")

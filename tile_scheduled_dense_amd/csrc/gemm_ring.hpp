@@ -106,7 +106,7 @@ __device__ __forceinline__ i32x4 rsrc_words_u(uint64_t base, int64_t nbytes) {
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
 template <int G>
-__device__ __forceinline__ void copy_group_to_lds(i32x4 rs, uint32_t lds_addr, const int (&voff)[G]) {
+__device__ __forceinline__ void copy_group_to_lds(i32x4 rs, uint32_t lds_addr, const int *voff) {
     static_assert(G == 1 || G == 2 || G == 4, "1, 2 or 4 copies per group");
     // both operands are uniform by construction; say so for the SGPR constraints
     lds_addr = __builtin_amdgcn_readfirstlane(lds_addr);
@@ -227,17 +227,28 @@ struct RingBlock {
     int lda, ldb;
     const char *Ablk, *Bblk;
     int64_t a_valid, b_valid;
-    int a_row[C::A_DMA], a_k[C::A_DMA], a_off[C::A_DMA], a_voff[C::A_DMA];
-    int b_k[C::B_DMA], b_n[C::B_DMA], b_off[C::B_DMA], b_voff[C::B_DMA];
+    // the copy plan of each operand tile under this placement (tile_config.hpp)
+    using CA = RingCopy<C, SWZ, 0>;
+    using CB = RingCopy<C, SWZ, 1>;
+    static constexpr int A_PER = CA::PER, B_PER = CB::PER;
+    static constexpr int COPIES = A_PER + B_PER;             // copy instructions per wave per K tile
+    static constexpr int A_PITCH = CA::PITCH, B_PITCH = CB::PITCH;
+    static constexpr int A_STAGE = CA::REGION, B_STAGE = CB::REGION;   // LDS bytes per pipeline copy
+    // A padded slot (fetched as zeros) keeps a k of kPadSlot: past every K (the
+    // host keeps K below 2^30), so the register path of the last K tile loads
+    // nothing for it either.
+    static constexpr int kPadSlot = 1 << 30;
+    int a_row[A_PER], a_k[A_PER], a_off[A_PER], a_voff[A_PER];
+    int b_k[B_PER], b_n[B_PER], b_off[B_PER], b_voff[B_PER];
     // a group's resource base sits this far below the tile's first byte
-    static constexpr int A_SHIFT = (C::A_DMA - 1) * 1024, B_SHIFT = (C::B_DMA - 1) * 1024;
+    static constexpr int A_SHIFT = (CA::GMAX - 1) * 1024, B_SHIFT = (CB::GMAX - 1) * 1024;
     uint64_t a_base, b_base;    // Ablk, Bblk as workgroup-uniform integers
     uint32_t lds0;              // LDS address of smem
     int64_t b_step;             // bytes of B per K tile
     i32x4 rsa, rsb;             // interior blocks: resources of the next K tile to copy
     uint32_t a_rd[C::KSTEPS];           // LDS address of this lane's A fragment of row tile 0, copy 0
     uint32_t b_rd[C::KSTEPS][C::TN];    // ... of its B fragment (first read) of column tile j, copy 0
-    u32x4 tail[C::COPIES];
+    u32x4 tail[COPIES];
     AccTiles<C, (STAGES > 1)> acc;
 
     // LDS: the STAGES copies of the B tile, then the STAGES copies of the A
@@ -245,11 +256,13 @@ struct RingBlock {
     // offset that fits the 16-bit immediate of a DS instruction.  B goes first:
     // its reads need one base register per MFMA column tile (the swizzle XOR
     // depends on it), A's a single one, which then absorbs the region offset.
-    static constexpr int A_REGION = STAGES * C::B_TILE_BYTES;
-    static constexpr int a_tile(int stage) { return A_REGION + stage * C::A_TILE_BYTES; }
-    static constexpr int b_tile(int stage) { return stage * C::B_TILE_BYTES; }
-    static_assert((STAGES - 1) * C::A_TILE_BYTES + C::A_TILE_BYTES <= 65536 &&
-                  (STAGES - 1) * C::B_TILE_BYTES + 4 * C::B_ROW_BYTES < 65536, "DS immediate offsets");
+    // (Under pad_stride the A offsets exceed the 16-bit immediate for the later
+    // copies; the compiler then adds them in a register, which only costs time.)
+    static constexpr int A_REGION = STAGES * B_STAGE;
+    static constexpr int a_tile(int stage) { return A_REGION + stage * A_STAGE; }
+    static constexpr int b_tile(int stage) { return stage * B_STAGE; }
+    static_assert(SWZ == SWZ_PAD || ((STAGES - 1) * A_STAGE + C::A_TILE_BYTES <= 65536 &&
+                                     (STAGES - 1) * B_STAGE + 4 * B_PITCH < 65536), "DS immediate offsets");
 
     __device__ __forceinline__ RingBlock(const GemmParams &p_, char *smem_, int64_t b_, int64_t tm, int64_t tn)
         : p(p_), smem(smem_), b(b_) {
@@ -294,16 +307,18 @@ struct RingBlock {
         }
         acc.zero();
 #pragma unroll
-        for (int d = 0; d < C::A_DMA; ++d) {
-            ring_a_source<C>(ring_block<C>(d, wave, C::A_DMA), lane, SWZ, a_row[d], a_k[d]);
-            a_off[d] = (FRINGE && m0 + a_row[d] >= p.M) ? kOutOfRange : (a_row[d] * lda + a_k[d]) * E;
-            a_voff[d] = a_off[d] + A_SHIFT - 1024 * d;
+        for (int d = 0; d < A_PER; ++d) {
+            const bool ok = ring_a_source<C>(CA::block(d, wave), lane, SWZ, a_row[d], a_k[d]);
+            a_off[d] = (!ok || (FRINGE && m0 + a_row[d] >= p.M)) ? kOutOfRange : (a_row[d] * lda + a_k[d]) * E;
+            a_voff[d] = a_off[d] + A_SHIFT - 1024 * CA::pos(d);
+            if (!ok) a_k[d] = kPadSlot;
         }
 #pragma unroll
-        for (int d = 0; d < C::B_DMA; ++d) {
-            ring_b_source<C>(ring_block<C>(d, wave, C::B_DMA), lane, SWZ, b_k[d], b_n[d]);
-            b_off[d] = (FRINGE && n0 + b_n[d] >= p.N) ? kOutOfRange : (b_k[d] * ldb + b_n[d]) * E;
-            b_voff[d] = b_off[d] + B_SHIFT - 1024 * d;
+        for (int d = 0; d < B_PER; ++d) {
+            const bool ok = ring_b_source<C>(CB::block(d, wave), lane, SWZ, b_k[d], b_n[d]);
+            b_off[d] = (!ok || (FRINGE && n0 + b_n[d] >= p.N)) ? kOutOfRange : (b_k[d] * ldb + b_n[d]) * E;
+            b_voff[d] = b_off[d] + B_SHIFT - 1024 * CB::pos(d);
+            if (!ok) b_k[d] = kPadSlot;
         }
     }
 
@@ -323,6 +338,24 @@ struct RingBlock {
         rs.y = (int)(uint32_t)(a >> 32);
     }
 
+    // The copies of one operand under resource rs into the LDS copy at `region`:
+    // the wave's own run of Q adjacent blocks in groups of at most four under
+    // one M0 value each, then the shared block, if any.
+    template <class CP, int NPER>
+    __device__ __forceinline__ void copy_operand(i32x4 rs, uint32_t region, const int (&voff)[NPER]) const {
+        static_assert(NPER == CP::PER, "copy plan");
+        constexpr int G0 = CP::Q < 4 ? CP::Q : 4;
+        copy_group_to_lds<G0>(rs, region + CP::block(0, wave) * 1024, &voff[0]);
+        if constexpr (CP::Q > 4) {
+            constexpr int G1 = CP::Q - 4;
+            static_assert(G1 == 1 || G1 == 2 || G1 == 4, "second group of the run");
+            copy_group_to_lds<G1>(rs, region + CP::block(4, wave) * 1024, &voff[4]);
+        }
+        if constexpr (CP::SHARED) {
+            copy_group_to_lds<1>(rs, region + (CP::NB - 1) * 1024, &voff[CP::Q]);
+        }
+    }
+
     // this wave's copies of one operand (0 = A, 1 = B) of K tile kt into LDS copy `stage`.
     // Every schedule copies the K tiles in increasing order, each once.
     __device__ __forceinline__ void dma_operand(int64_t kt, int stage, int operand) {
@@ -331,21 +364,21 @@ struct RingBlock {
         // advanced by one K tile per copy; a fringe block's limit ends at the
         // last valid element (past it reads as 0).
         if (operand == 0) {
-            const uint32_t dst = lds0 + a_tile(stage) + ring_block<C>(0, wave, C::A_DMA) * 1024;
+            const uint32_t region = lds0 + a_tile(stage);
             if (FRINGE) {
                 const int64_t adv = kt * (C::BK * E);
-                copy_group_to_lds<C::A_DMA>(rsrc_words_u(a_base + adv - A_SHIFT, a_valid - adv + A_SHIFT), dst, a_voff);
+                copy_operand<CA>(rsrc_words_u(a_base + adv - A_SHIFT, a_valid - adv + A_SHIFT), region, a_voff);
             } else {
-                copy_group_to_lds<C::A_DMA>(rsa, dst, a_voff);
+                copy_operand<CA>(rsa, region, a_voff);
                 advance(rsa, C::BK * E);
             }
         } else {
-            const uint32_t dst = lds0 + b_tile(stage) + ring_block<C>(0, wave, C::B_DMA) * 1024;
+            const uint32_t region = lds0 + b_tile(stage);
             if (FRINGE) {
                 const int64_t adv = kt * b_step;
-                copy_group_to_lds<C::B_DMA>(rsrc_words_u(b_base + adv - B_SHIFT, b_valid - adv + B_SHIFT), dst, b_voff);
+                copy_operand<CB>(rsrc_words_u(b_base + adv - B_SHIFT, b_valid - adv + B_SHIFT), region, b_voff);
             } else {
-                copy_group_to_lds<C::B_DMA>(rsb, dst, b_voff);
+                copy_operand<CB>(rsb, region, b_voff);
                 advance(rsb, (uint64_t)b_step);
             }
         }
@@ -363,29 +396,29 @@ struct RingBlock {
         const rsrc_t ra = make_rsrc_n(Ablk + k0 * E, a_valid - k0 * E);
         const rsrc_t rb = make_rsrc_n(Bblk + k0 * p.ldb * E, b_valid - k0 * p.ldb * E);
 #pragma unroll
-        for (int d = 0; d < C::A_DMA; ++d) {
+        for (int d = 0; d < A_PER; ++d) {
             const int64_t left = p.K - (k0 + a_k[d]);
             const bool row_ok = m0 + a_row[d] < p.M;
             const int n = !row_ok || left <= 0 ? 0 : (left >= C::CHUNK ? C::CHUNK : (int)left);
-            tail[d] = bload16_n<E>(ra, (a_row[d] * lda + a_k[d]) * E, 0, n);
+            tail[d] = bload16_n<E>(ra, n > 0 ? (a_row[d] * lda + a_k[d]) * E : 0, 0, n);
         }
 #pragma unroll
-        for (int d = 0; d < C::B_DMA; ++d) {
+        for (int d = 0; d < B_PER; ++d) {
             const int64_t cols = p.N - (n0 + b_n[d]);
             const bool k_ok = k0 + b_k[d] < p.K;
             const int n = !k_ok || cols <= 0 ? 0 : (cols >= C::CHUNK ? C::CHUNK : (int)cols);
-            tail[C::A_DMA + d] = bload16_n<E>(rb, (b_k[d] * ldb + b_n[d]) * E, 0, n);
+            tail[A_PER + d] = bload16_n<E>(rb, n > 0 ? (b_k[d] * ldb + b_n[d]) * E : 0, 0, n);
         }
     }
     __device__ __forceinline__ void tail_store(int stage) {
         char *sA = smem + a_tile(stage);
         char *sB = smem + b_tile(stage);
 #pragma unroll
-        for (int d = 0; d < C::A_DMA; ++d)
-            *(u32x4 *)(sA + ring_block<C>(d, wave, C::A_DMA) * 1024 + 16 * lane) = tail[d];
+        for (int d = 0; d < A_PER; ++d)
+            *(u32x4 *)(sA + CA::block(d, wave) * 1024 + 16 * lane) = tail[d];
 #pragma unroll
-        for (int d = 0; d < C::B_DMA; ++d)
-            *(u32x4 *)(sB + ring_block<C>(d, wave, C::B_DMA) * 1024 + 16 * lane) = tail[C::A_DMA + d];
+        for (int d = 0; d < B_PER; ++d)
+            *(u32x4 *)(sB + CB::block(d, wave) * 1024 + 16 * lane) = tail[A_PER + d];
     }
 
     // Wait until this wave's share of tile t is in LDS (its copies, or for
@@ -395,9 +428,9 @@ struct RingBlock {
     __device__ __forceinline__ void land_tile(int64_t t, int stage) {
         if (t < ndma) {
             const int64_t later = ndma - 1 - t;
-            if (AHEAD >= 3 && later >= 3) wait_vmcnt<3 * C::COPIES>();
-            else if (AHEAD >= 2 && later >= 2) wait_vmcnt<2 * C::COPIES>();
-            else if (AHEAD >= 1 && later >= 1) wait_vmcnt<C::COPIES>();
+            if (AHEAD >= 3 && later >= 3) wait_vmcnt<3 * COPIES>();
+            else if (AHEAD >= 2 && later >= 2) wait_vmcnt<2 * COPIES>();
+            else if (AHEAD >= 1 && later >= 1) wait_vmcnt<COPIES>();
             else wait_vmcnt<0>();
         } else {
             wait_vmcnt<0>();
@@ -410,12 +443,12 @@ struct RingBlock {
     // lies i * MT rows on (the swizzle XOR is the same for it), so its address
     // is a_rd[s] plus a constant
     __device__ __forceinline__ u32x4 read_a(int stage, int s, int i) const {
-        const uint32_t addr = a_rd[s] + stage * C::A_TILE_BYTES + i * C::MT * C::A_ROW_BYTES;
+        const uint32_t addr = a_rd[s] + stage * A_STAGE + i * C::MT * A_PITCH;
         return *(const __attribute__((address_space(3))) u32x4 *)(uintptr_t)addr;
     }
     // one of the two transposing B reads (half: 4 k rows on, the same XOR)
     __device__ __forceinline__ u32x2 read_b(int stage, int s, int j, int half) const {
-        const uint32_t addr = b_rd[s][j] + stage * C::B_TILE_BYTES + half * 4 * C::B_ROW_BYTES;
+        const uint32_t addr = b_rd[s][j] + stage * B_STAGE + half * 4 * B_PITCH;
         const v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16 *)(uintptr_t)addr);
         return __builtin_bit_cast(u32x2, v);
     }
@@ -534,8 +567,14 @@ __device__ __forceinline__ void ring_tile(const GemmParams &p, char *smem, int64
         }
         blk.acc.settle();
     }
+    // Values per store-back chunk: 64 (the C0 loads of a chunk go out together)
+    // for 16x16 tiles, whose accumulators sit in AGPRs; 32 for 32x32 tiles,
+    // whose 64 accumulators per lane share the VGPRs with the chunk's offsets and
+    // C0 values (a chunk of 64 took the 128 x 128 kernel past 256 registers, into
+    // scratch).
+    constexpr int CHUNK_VALUES = TAIL ? 16 : (C::MT == 32 ? 32 : 64);
     auto get = [&](int i, int j, int v) { return blk.acc.get(i, j, v); };
-    store_tile_epilogue<C, FRINGE, decltype(get), TAIL ? 16 : 64, TAIL>(p, get, b, blk.m0, blk.n0, blk.wave, blk.lane);
+    store_tile_epilogue<C, FRINGE, decltype(get), CHUNK_VALUES, TAIL>(p, get, b, blk.m0, blk.n0, blk.wave, blk.lane);
 }
 
 // SCHED_SWPIPE (software pipeline, one wave per SIMD, large wave tiles): the
@@ -568,7 +607,7 @@ struct SwPipe {
         const bool more = STEADY || t + 1 < nk;
         if (STEADY) {
             // tile t + 1 is a copied tile with STAGES - 2 copied tiles issued after it
-            wait_vmcnt<(STAGES - 2) * C::COPIES>();
+            wait_vmcnt<(STAGES - 2) * Blk::COPIES>();
             wait_lds();
         } else if (more) {
             blk.template land_tile<STAGES - 2>(t + 1, nxt_read);
@@ -738,7 +777,7 @@ __device__ __forceinline__ void ring_persistent(const GemmParams &p, char *smem)
 
 template <class C, int STAGES, int SWZ, bool TAIL = false>
 __global__ __launch_bounds__(C::THREADS, C::OCCUPANCY) void gemm_ring_persistent_kernel(GemmParams p) {
-    __shared__ __attribute__((aligned(1024))) char smem[STAGES * C::STAGE_BYTES];
+    __shared__ __attribute__((aligned(1024))) char smem[STAGES * ring_stage_bytes<C, SWZ>()];
     ring_persistent<C, STAGES, SWZ, TAIL>(p, smem);
 }
 
@@ -778,13 +817,14 @@ template <class C, int STAGES, int SWZ, int SCHED, bool TAIL = false>
 __global__ __launch_bounds__(C::THREADS, C::OCCUPANCY) void gemm_ring_kernel(GemmParams p) {
     static_assert(STAGES >= 1 && STAGES <= 5, "1 to 5 LDS copies");
     static_assert(SCHED == SCHED_RING || SCHED == SCHED_SWPIPE, "schedule");
-    __shared__ __attribute__((aligned(1024))) char smem[STAGES * C::STAGE_BYTES];
+    __shared__ __attribute__((aligned(1024))) char smem[STAGES * ring_stage_bytes<C, SWZ>()];
     if constexpr (std::is_same<C, Ring256<C::DT>>::value) {
         // thin fringe strips (Partition: a narrow block for a narrow remainder)
         using SN = Strip256xN<C::DT>;
         using SM = StripMx256<C::DT>;
         static_assert(SN::THREADS == C::THREADS && SM::THREADS == C::THREADS, "one workgroup size");
-        static_assert(SN::STAGE_BYTES <= C::STAGE_BYTES && SM::STAGE_BYTES <= C::STAGE_BYTES, "LDS");
+        static_assert(ring_stage_bytes<SN, SWZ>() <= ring_stage_bytes<C, SWZ>() &&
+                      ring_stage_bytes<SM, SWZ>() <= ring_stage_bytes<C, SWZ>(), "LDS");
         const int64_t main_blocks = p.tiles_m * p.tiles_n * p.batch;
         if ((int64_t)blockIdx.x >= main_blocks) {
             const int64_t per = p.strip_n + p.strip_m;

@@ -126,7 +126,9 @@ void describe_ring_lds(tg_layout *L, int operand, int swz) {
     L->shape[0] = rows;
     L->shape[1] = cols;
     L->n_shard = 2;
-    L->shard[0] = {rows, cols, TG_AXIS_M, 0};
+    // pad_stride: the row stride is the padded pitch (in elements); no swizzle
+    const int pitch = (operand == 0 ? ring_a_pitch<C>(swz) : ring_b_pitch<C>(swz)) / 2;
+    L->shard[0] = {rows, pitch, TG_AXIS_M, 0};
     L->shard[1] = {cols, 1, TG_AXIS_M, 0};
     if (swz != SWZ_XOR) return;
     L->n_swizzle = 1;
@@ -156,12 +158,15 @@ void describe_ring_copy_a(tg_layout *L) {
     L->shape[1] = C::A_ROW_BYTES / 16;
     L->n_shard = 3;
     L->shard[0] = {C::WAVES, 1, TG_AXIS_WAVE, 0};
-    L->shard[1] = {C::A_DMA, 1, TG_AXIS_M, 0};
+    L->shard[1] = {RingCopy<C, SWZ_XOR, 0>::Q, 1, TG_AXIS_M, 0};
     L->shard[2] = {64, 1, TG_AXIS_LANE, 0};
 }
 
 template <class C>
 tg_status describe_ring(int swz, int kind, tg_layout *out) {
+    // pad_stride is built for the 256 x 256 tile and its strips only; its copies
+    // (padded slots, one block every wave copies) are not one shard layout
+    if (swz == SWZ_PAD && (C::BM * C::BN < 256 * 64 || kind == TG_LAYOUT_COPY_A)) return TG_ERR_UNSUPPORTED;
     switch (kind) {
         case TG_LAYOUT_LDS_A: describe_ring_lds<C>(out, 0, swz); return TG_OK;
         case TG_LAYOUT_LDS_B: describe_ring_lds<C>(out, 1, swz); return TG_OK;
@@ -247,7 +252,10 @@ int64_t tg_layout_eval(const tg_layout *L, const int64_t *x, int64_t *out, int64
 tg_status tile_gemm_describe_layout(int config, int swizzle, int kind, tg_layout *out) {
     if (!out) return TG_ERR_INVALID_ARG;
     if (swizzle == 0) swizzle = SWZ_XOR;
-    if (swizzle != SWZ_NONE && swizzle != SWZ_XOR) return TG_ERR_INVALID_ARG;
+    if (swizzle != SWZ_NONE && swizzle != SWZ_PAD && swizzle != SWZ_XOR) return TG_ERR_INVALID_ARG;
+    if (swizzle == SWZ_PAD && config != TG_CFG_256x256 && config != TG_LAYOUT_CFG_STRIP_N &&
+        config != TG_LAYOUT_CFG_STRIP_M)
+        return TG_ERR_UNSUPPORTED;
     std::memset(out, 0, sizeof *out);
     switch (config) {
         case TG_CFG_256x256: return describe_ring<Ring256<DT_BF16>>(swizzle, kind, out);
@@ -262,7 +270,10 @@ tg_status tile_gemm_describe_layout(int config, int swizzle, int kind, tg_layout
 
 int64_t tile_gemm_lds_offset(int config, int swizzle, int operand, int64_t row, int64_t k) {
     if (swizzle == 0) swizzle = SWZ_XOR;
-    if ((swizzle != SWZ_NONE && swizzle != SWZ_XOR) || (operand != 0 && operand != 1)) return -1;
+    if ((swizzle != SWZ_NONE && swizzle != SWZ_PAD && swizzle != SWZ_XOR) || (operand != 0 && operand != 1)) return -1;
+    if (swizzle == SWZ_PAD && config != TG_CFG_256x256 && config != TG_LAYOUT_CFG_STRIP_N &&
+        config != TG_LAYOUT_CFG_STRIP_M)
+        return -1;
     switch (config) {
         case TG_CFG_256x256: return ring_lds_offset<Ring256<DT_BF16>>(swizzle, operand, row, k);
         case TG_LAYOUT_CFG_STRIP_N: return ring_lds_offset<Strip256xN<DT_BF16>>(swizzle, operand, row, k);

@@ -66,7 +66,9 @@ struct TileCfg {
 // configurations are the RingCfg family below.
 using CfgF32 = TileCfg<DT_F32, 64, 64, 2, 2>;                  // 4 waves, wave tile 32 x 32 (16x16 MFMA)
 
-enum Swz : int { SWZ_NONE = 1, SWZ_XOR = 2 };
+// LDS placement of a staged tile (the swizzle codes of tg_options): 1 none (row-major),
+// 2 pad_stride (row-major with a padded row pitch), 3 XOR swizzle.
+enum Swz : int { SWZ_NONE = 1, SWZ_PAD = 2, SWZ_XOR = 3 };
 
 // ---------------------------------------------------------------------------
 // LDS placement of one operand tile (rows x BK, k contiguous).
@@ -100,7 +102,7 @@ TG_HD int swizzle_row_mask(int row) { return (row & 7) ^ ((row >> 3) & 3); }
 template <class C>
 TG_HD int lds_elem(int row, int k, int swz) {
     int m = row * C::BK + k;
-    if (swz == SWZ_NONE) return m;
+    if (swz != SWZ_XOR) return m;
     constexpr int M = C::ELEM == 2 ? 3 : 2;
     return (int)swizzle_apply(swizzle_apply(m, M, 3, 3), M, 2, 6);
 }
@@ -109,7 +111,7 @@ TG_HD int lds_elem(int row, int k, int swz) {
 // LDS write and fragment read moves).
 template <class C>
 TG_HD int lds_chunk_byte(int row, int chunk, int swz) {
-    int c = swz == SWZ_NONE ? chunk : (chunk ^ swizzle_row_mask(row));
+    int c = swz != SWZ_XOR ? chunk : (chunk ^ swizzle_row_mask(row));
     return (row * C::CPR + c) * 16;
 }
 
@@ -196,14 +198,30 @@ template <int DT> using Ring64 = RingCfg<DT, 64, 64, 1, 2>;      // 2 waves, wav
 // l / 16); the other choice costs one extra cycle in two.
 template <class C>
 TG_HD int ring_a_mask(int r, int swz) {
-    if (swz == SWZ_NONE) return 0;
+    if (swz != SWZ_XOR) return 0;
     return C::MT == 32 ? ((r >> 2) & 3) : ((r >> 1) & 3);
 }
+
+// pad_stride placement (OCANNL "Module Ir.Schedule", Stage paragraph, pad_stride):
+// the tile's minor dimension is rounded up by one 16-byte unit -- A rows of 32 k
+// to a pitch of 40 elements (80 bytes), B rows of BN n to BN + 8 -- which changes
+// the row stride while the iterated extents stay as they are; the padded slots
+// are never read.  A pitch that stays a multiple of 16 bytes keeps every
+// 16-byte chunk of a row contiguous, as the copies and fragment reads need.
+// With an 80-byte A pitch, 16 consecutive rows start on 16 distinct 4-bank
+// groups of the 64 banks (row r at bank 20 r mod 64).  No row pitch makes the
+// transposing B read conflict-free: it reads rows k and k + 8 in one cycle, and
+// a linear pitch that separates rows k .. k + 3 maps k + 8 onto k's banks or
+// half-overlaps them; +16 bytes leaves two-way conflicts (the XOR has none).
+template <class C>
+TG_HD constexpr int ring_a_pitch(int swz) { return C::A_ROW_BYTES + (swz == SWZ_PAD ? 16 : 0); }
+template <class C>
+TG_HD constexpr int ring_b_pitch(int swz) { return C::B_ROW_BYTES + (swz == SWZ_PAD ? 16 : 0); }
 
 // A tile: byte offset of logical chunk c (0..3) of row r.
 template <class C>
 TG_HD int ring_a_byte(int r, int c, int swz) {
-    return r * C::A_ROW_BYTES + 16 * (c ^ ring_a_mask<C>(r, swz));
+    return r * ring_a_pitch<C>(swz) + 16 * (c ^ ring_a_mask<C>(r, swz));
 }
 
 // B tile: the XOR applied to the 64-byte unit index of k row k.
@@ -213,7 +231,7 @@ TG_HD int ring_a_byte(int r, int c, int swz) {
 //    k + 8 (the half swizzle below then takes (k >> 1) & 1).
 template <class C>
 TG_HD int ring_b_mask(int k, int swz) {
-    if (swz == SWZ_NONE) return 0;
+    if (swz != SWZ_XOR) return 0;
     if (C::B_UNITS >= 4) return k & 3;
     return C::MT == 32 ? ((k >> 1) & 1) : ((k >> 3) & 1);
 }
@@ -224,7 +242,7 @@ TG_HD int ring_b_mask(int k, int swz) {
 // quarters of a bank line.
 template <class C>
 TG_HD int ring_b_half_mask(int k, int swz) {
-    if (!C::B_HALF_SWZ || swz == SWZ_NONE) return 0;
+    if (!C::B_HALF_SWZ || swz != SWZ_XOR) return 0;
     return C::B_UNITS >= 4 ? ((k >> 3) & 1) : ((k >> 1) & 1);
 }
 
@@ -232,35 +250,72 @@ TG_HD int ring_b_half_mask(int k, int swz) {
 template <class C>
 TG_HD int ring_b_byte(int k, int n, int swz) {
     const int w = n / 32, half = ((n % 32) / 16) ^ ring_b_half_mask<C>(k, swz), in_half = (n % 16) * 2;
-    return k * C::B_ROW_BYTES + 64 * (w ^ ring_b_mask<C>(k, swz)) + 32 * half + in_half;
+    return k * ring_b_pitch<C>(swz) + 64 * (w ^ ring_b_mask<C>(k, swz)) + 32 * half + in_half;
 }
 
-// Which LDS bytes copy d (0 <= d < per_wave, per_wave = A_DMA or B_DMA) of
-// wave w fills: 1 KiB block J = w * per_wave + d of the operand's region.  A
-// wave's copies of one operand are adjacent, so they can share one LDS base
-// address and differ only by an immediate offset.
-template <class C>
-TG_HD int ring_block(int d, int wave, int per_wave) { return wave * per_wave + d; }
+// The copies of one operand tile (OP 0 = A, 1 = B) into one LDS pipeline copy:
+// the tile's rows x pitch bytes in 1 KiB blocks, each filled by one copy
+// instruction (lane l writes bytes 16 l .. 16 l + 15 of its block).  Wave w
+// copies the Q adjacent blocks w * Q .. w * Q + Q - 1, so they share one LDS
+// base and differ only by an immediate offset.  When the blocks do not divide
+// evenly among the waves (a padded pitch), exactly one block is left over and
+// every wave copies it as well: the same source bytes to the same LDS bytes, so
+// the concurrent writes agree.
+template <class C, int SWZ, int OP>
+struct RingCopy {
+    static constexpr int PITCH = OP == 0 ? ring_a_pitch<C>(SWZ) : ring_b_pitch<C>(SWZ);
+    static constexpr int ROWS = OP == 0 ? C::BM : C::BK;
+    static constexpr int ROW_BYTES = OP == 0 ? C::A_ROW_BYTES : C::B_ROW_BYTES;   // valid bytes per row
+    static constexpr int NB = (ROWS * PITCH + 1023) / 1024;     // 1 KiB blocks
+    static constexpr int Q = NB / C::WAVES;                      // blocks of a wave's own run
+    static constexpr int SHARED = NB - Q * C::WAVES;             // 0, or 1 block every wave copies
+    static constexpr int PER = Q + SHARED;                       // copies per wave per K tile
+    static constexpr int REGION = NB * 1024;                     // LDS bytes per pipeline copy
+    static constexpr int GMAX = Q < 4 ? Q : 4;                   // copies under one M0 value at most
+    static_assert(Q >= 1 && SHARED <= 1 && Q <= 8, "copy split");
+    // the block copy d of wave `wave` fills
+    TG_HD static constexpr int block(int d, int wave) { return d < Q ? wave * Q + d : NB - 1; }
+    // copy d's position within its group of adjacent copies (groups of at most four)
+    TG_HD static constexpr int pos(int d) { return d < Q ? d % 4 : 0; }
+};
 
-// The A element (row, first k of the chunk) lane l of block J must fetch.
+// The A element (row, first k of the chunk) lane l of block J must fetch;
+// false for a padded slot or a byte past the tile (fetched as zeros).
 template <class C>
-TG_HD void ring_a_source(int J, int lane, int swz, int &row, int &k) {
+TG_HD bool ring_a_source(int J, int lane, int swz, int &row, int &k) {
+    const int pitch = ring_a_pitch<C>(swz);
     const int byte = J * 1024 + 16 * lane;
-    row = byte / C::A_ROW_BYTES;
-    const int p = (byte % C::A_ROW_BYTES) / 16;
+    row = byte / pitch;
+    const int p = (byte % pitch) / 16;
+    if (row >= C::BM || 16 * p >= C::A_ROW_BYTES) {
+        k = 0;
+        return false;
+    }
     k = 8 * (p ^ ring_a_mask<C>(row, swz));
+    return true;
 }
 
-// The B element (k, first n of the chunk) lane l of block J must fetch.
+// The B element (k, first n of the chunk) lane l of block J must fetch; false
+// for a padded slot or a byte past the tile.
 template <class C>
-TG_HD void ring_b_source(int J, int lane, int swz, int &k, int &n) {
+TG_HD bool ring_b_source(int J, int lane, int swz, int &k, int &n) {
+    const int pitch = ring_b_pitch<C>(swz);
     const int byte = J * 1024 + 16 * lane;
-    k = byte / C::B_ROW_BYTES;
-    const int b = byte % C::B_ROW_BYTES;
+    k = byte / pitch;
+    const int b = byte % pitch;
+    if (k >= C::BK || b >= C::B_ROW_BYTES) {
+        n = 0;
+        return false;
+    }
     const int w = (b / 64) ^ ring_b_mask<C>(k, swz);
     const int half = ((b % 64) / 32) ^ ring_b_half_mask<C>(k, swz);
     n = 32 * w + 16 * half + (b % 32) / 2;
+    return true;
 }
+
+// LDS bytes of one pipeline copy (A and B tiles) under a placement.
+template <class C, int SWZ>
+TG_HD constexpr int ring_stage_bytes() { return RingCopy<C, SWZ, 0>::REGION + RingCopy<C, SWZ, 1>::REGION; }
 
 // ---------------------------------------------------------------------------
 // MFMA register tiles.  Wave w owns the wave tile at

@@ -131,7 +131,42 @@ int64_t auto_splits(int64_t tiles, int64_t K, int64_t slots) {
     return s;
 }
 
-// Workgroups the GPU runs at once for a 16-bit tile: its workgroups per CU times 256 CUs.
+// Workgroups of a configuration one CU holds at once, the lesser of what its
+// registers and its LDS allow (a SIMD holds 512 registers per lane for its
+// waves, a CU 160 KiB of LDS); the built kernels' register counts are checked
+// against this table by a code-object test.
+//   256 x 256: 510 registers a wave, 4 waves: one per CU.
+//   128 x 128: under 256 registers, 4 waves: two waves per SIMD, two per CU
+//              (LDS 64 / 80 KiB at depth 4 / 5 allows two as well).
+//   64 x 64:   under 168 registers, 2 waves: three waves per SIMD, six per CU by
+//              registers; LDS 8 KiB per depth: 5 at depth 4, 4 at depth 5.
+int cfg_per_cu(int config, int depth) {
+    switch (config) {
+        case TG_CFG_256x256: return 1;
+        case TG_CFG_128x128: return 2;
+        case TG_CFG_64x64: {
+            const int by_lds = (160 * 1024) / (depth * 8 * 1024);
+            return by_lds < 6 ? by_lds : 6;
+        }
+        case TG_CFG_F32_64x64:
+            // 4 waves; depth 1 under 104 registers (five waves per SIMD, five per
+            // CU; 16 KiB of LDS), depth 2 under 128 (four; 32 KiB allows five)
+            return depth == 1 ? 5 : 4;
+        default: return 1;
+    }
+}
+
+// Workgroups the automatic split aims to fill: 256 for the 256 x 256 tile, 512
+// for the smaller ones.  These are split targets that measured best, not the
+// residency (cfg_per_cu): the 64 x 64 tile holds 5 workgroups per CU at depth
+// 4, yet filling them all measured slower on every shape it changed (us):
+// 8192 x 64 x 8192 35.8 against 29.6, 64 x 8192 x 8192 38.6 / 33.2,
+// 256 x 256 x 65536 31.5 / 28.7, 512 x 2048 x 2048 23.4 / 21.2; more slices
+// cost more partials while one wave per SIMD already feeds its matrix core.
+// One wave per SIMD for the 128 x 128 tile as well (256) measured slower on
+// 16384 x 96 x 4096 (55.2 against 39.7: the 64 x 64 tile unsplit won the
+// comparison) and 384 x 4096 x 4096 (36.9 against 33.0), faster only on
+// 8192 x 128 x 8192 (38.5 against 43.0).
 int64_t cfg_slots(int config) { return config == TG_CFG_256x256 ? 256 : 512; }
 
 // A thin remainder computed by a GEMM of its own (see tile_gemm.h): its
@@ -174,13 +209,17 @@ tg_status make_plan(int64_t batch, int64_t M, int64_t N, int64_t K, tg_dtype dty
     const bool sixteen = dtype != TG_F32;
     const bool some = K > 0 && M > 0 && N > 0 && batch > 0;
     int64_t want = 1, wanted_bytes = 0;
-    int config = o.config;
-    if (sixteen && some && o.split_k == 0) {
+    int config = o.force_cfg;
+    // An always-repacked A (pack_a == 2) is built for the unsplit 256 x 256
+    // tile: with the tile left to the library, that is the tile, unsplit.
+    const bool pin256 = sixteen && o.pack_a == 2 && config == TG_CFG_AUTO;
+    if (pin256) config = TG_CFG_256x256;
+    if (sixteen && some && o.split_k == 0 && !pin256) {
         // With a forced tile, that tile's own count.  Otherwise each tile with its
-        // own count, and the one whose workgroups fill the most of the slots it
-        // has (256 for 256 x 256, 512 for the smaller tiles at two per CU; ties:
-        // the larger tile, fewer re-reads of A and B); no split when
-        // that one needs none (the plain choice below then picks the tile).
+        // own count, and the one whose workgroups fill the most of its slots
+        // (cfg_slots, the measured split targets; ties: the larger tile, fewer
+        // re-reads of A and B); no split when that one needs none (the plain
+        // choice below then picks the tile).
         // 1024 x 1024 x 4096 bf16: 128 x 128 split 4 (256 workgroups) takes
         // 25.6 us where 256 x 256 split 4 (64) took 35.6; 512 x 2048 x 2048: the
         // 64 x 64 tile unsplit (256) 19.4 us where 256 x 256 split 2 (32) took 33.7.
@@ -188,7 +227,7 @@ tg_status make_plan(int64_t batch, int64_t M, int64_t N, int64_t K, tg_dtype dty
         // (a 256 x 256 tile over 64 columns multiplies three quarters zeros):
         // 8192 x 64 x 8192 bf16 takes 64 x 64 split 4, 27.0 us, where 256 x 256
         // split 8 took 54.5.
-        int cfg = o.config;
+        int cfg = o.force_cfg;
         if (!cfg) {
             double best = -1.0;
             for (int c = TG_CFG_256x256; c <= TG_CFG_64x64; ++c) {
@@ -232,8 +271,10 @@ tg_status make_plan(int64_t batch, int64_t M, int64_t N, int64_t K, tg_dtype dty
                               : (depth == 1 || depth == 2 || depth == 4 || (depth == 5 && config != TG_CFG_256x256));
     if (!depth_ok) return TG_ERR_UNSUPPORTED;
     const int swz = o.swizzle ? o.swizzle : SWZ_XOR;
-    if (swz != SWZ_NONE && swz != SWZ_XOR) return TG_ERR_UNSUPPORTED;
+    if (swz < 0 || swz > SWZ_XOR) return TG_ERR_INVALID_ARG;
     if (!f32 && swz == SWZ_NONE && depth != 4) return TG_ERR_UNSUPPORTED;   // ablation built at depth 4 only
+    // pad_stride: the 256 x 256 tile at depth 4 (the placement ablation of the default kernel)
+    if (swz == SWZ_PAD && (config != TG_CFG_256x256 || depth != 4)) return TG_ERR_UNSUPPORTED;
     const int order = o.block_order;
     if (order != 0 && order != 1) return TG_ERR_UNSUPPORTED;
 
@@ -273,7 +314,8 @@ tg_status make_plan(int64_t batch, int64_t M, int64_t N, int64_t K, tg_dtype dty
     p.mfma_k = d.mfma_k;
     p.k_tiles = cdiv(K, d.bk);
     p.k_tail = K % d.bk;
-    p.lds_bytes = depth * d.stage_bytes;
+    p.lds_bytes = depth * (swz == SWZ_PAD ? ring_stage_bytes<Ring256<DT_BF16>, SWZ_PAD>() : d.stage_bytes);
+    p.per_cu = cfg_per_cu(config, depth);
 
     // split-K
     if (f32 && o.split_k >= 2) return TG_ERR_UNSUPPORTED;
@@ -479,8 +521,10 @@ tg_status launch_ring(const GemmParams &gp, const tg_plan_info &p, hipStream_t s
             case 2: return launch_ring_one<C, 2, SWZ_XOR, SCHED>(gp, p.grid, s);
             case 1: return launch_ring_one<C, 1, SWZ_XOR, SCHED_RING>(gp, p.grid, s);
         }
-    } else if (p.pipeline_depth == 4) {
+    } else if (p.pipeline_depth == 4 && p.swizzle == SWZ_NONE) {
         return launch_ring_one<C, 4, SWZ_NONE, SCHED>(gp, p.grid, s);
+    } else if (p.pipeline_depth == 4 && p.swizzle == SWZ_PAD) {
+        if constexpr (SWPIPE) return launch_ring_one<C, 4, SWZ_PAD, SCHED>(gp, p.grid, s);
     }
     return TG_ERR_UNSUPPORTED;
 }
@@ -642,7 +686,7 @@ tg_status run(int64_t batch, int64_t M, int64_t N, int64_t K, tg_dtype dtype,
         if (t->splits == 0) continue;
         tg_options sub{};
         sub.struct_size = (int)sizeof sub;
-        sub.config = TG_CFG_64x64;
+        sub.force_cfg = TG_CFG_64x64;
         sub.split_k = (int)t->splits;
         sub.workspace = t->ws_bytes ? static_cast<char *>(plan.workspace) + t->ws_offset : nullptr;
         sub.workspace_bytes = t->ws_bytes;
