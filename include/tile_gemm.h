@@ -65,7 +65,8 @@ typedef enum {
     TG_ERR_INVALID_ARG = 1,  /* extents, strides, pointers, dtype or overlap rejected */
     TG_ERR_UNSUPPORTED = 2,  /* no visible gfx950 device, or an option not built     */
     TG_ERR_LAUNCH = 3,       /* the HIP runtime refused the launch */
-    TG_ERR_INTERNAL = 4      /* unexpected failure inside the library */
+    TG_ERR_INTERNAL = 4,     /* unexpected failure inside the library */
+    TG_ERR_SCRATCH_LIMIT = 5 /* tile_gemm_ex_noalloc: the call needs more scratch than the library holds */
 } tg_status;
 
 /*
@@ -391,6 +392,36 @@ int64_t tile_gemm_packed_b_ld(int64_t N, tg_dtype dtype);
 tg_status tile_gemm_packed_b_size(int64_t batch, int64_t K, int64_t N, tg_dtype dtype, int64_t *bytes);
 tg_status tile_gemm_pack_b(int64_t batch, int64_t K, int64_t N, tg_dtype dtype, const void *B, int64_t ldb,
                            int64_t strideB, int transposed, void *packed, int64_t packed_bytes, void *stream);
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): tile_gemm_ex with the
+ * library's own scratch instead of a caller workspace.
+ *
+ * The scratch is one file-scope device array of TILE_GEMM_NOALLOC_SCRATCH_BYTES
+ * (64 MiB), held by every GPU the library runs on until the process ends; its
+ * device address is looked up once per device on the first call there.  The
+ * call takes the same arguments as tile_gemm_ex and computes the same plan as
+ * tile_gemm_ex given a workspace of that size, so its C is bitwise the one
+ * tile_gemm_ex writes with such a workspace: automatic split-K and the repack
+ * of A happen only when they fit.  opt->workspace must be NULL and
+ * opt->workspace_bytes 0 (TG_ERR_INVALID_ARG otherwise).  A call that would
+ * need more scratch than the array holds (a forced split_k, pack_a == 2 or
+ * tail_gemm == 2 whose partials or copy exceed it) returns TG_ERR_SCRATCH_LIMIT
+ * before any device work.  It allocates nothing: no hipMalloc, no hipFree, no
+ * allocating library routine, and no memset (nothing in the scratch has to
+ * start at zero: split partials are written whole before they are read).
+ * Every call on one GPU shares that GPU's array, which keeps the last call's
+ * contents: calls that overlap in time on one GPU (different streams, or
+ * several host threads without ordering) race on it and must not be issued.
+ */
+#define TILE_GEMM_NOALLOC_SCRATCH_BYTES (64LL << 20)
+
+tg_status tile_gemm_ex_noalloc(int64_t batch, int64_t M, int64_t N, int64_t K, tg_dtype dtype,
+                               const void *A, int64_t lda, int64_t strideA,
+                               const void *B, int64_t ldb, int64_t strideB,
+                               float *C, int64_t ldc, int64_t strideC,
+                               float alpha, float beta, void *stream, const tg_options *opt);
 
 #ifdef __cplusplus
 }

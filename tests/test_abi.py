@@ -29,7 +29,7 @@ def test_exports_every_declared_symbol():
 
 def test_abi_version_and_status_strings():
     assert tg.abi_version() == tg.ABI_VERSION == 8
-    for s in range(5):
+    for s in range(6):
         assert tg.STATUS_NAMES[s] in tg.status_string(s)
 
 
@@ -428,3 +428,28 @@ def test_plan_placements():
     assert _plan_status(1, 64, 64, 64, "f32", swizzle=tg.SWZ_PAD) == tg.TG_ERR_UNSUPPORTED
     assert _plan_status(1, 64, 64, 64, "bf16", swizzle=4) == tg.TG_ERR_INVALID_ARG
 
+
+def noalloc(batch=1, M=512, N=512, K=8192, opt=None, A=FAKE, B=FAKE * 4096, C=FAKE * 65536 * 64):
+    return tg.tile_gemm_status("tile_gemm_ex_noalloc", batch, M, N, K, tg.TG_BF16, A, K, M * K, B, N, K * N,
+                               C, N, M * N, 1.0, 0.0, 0, ctypes.byref(opt) if opt is not None else None)
+
+
+def test_noalloc_limits_checked_before_any_device():
+    """tile_gemm_ex_noalloc refuses, with no device work, a call whose scratch need exceeds the
+    library's array, and a caller workspace; a call that fits only lacks the GPU here."""
+    assert tg.NOALLOC_SCRATCH_BYTES == 64 << 20
+    # 32 planes of 1024 x 1024 fp32 = 128 MiB of split partials
+    assert noalloc(M=1024, N=1024, opt=tg._options(split_k=32)) == tg.TG_ERR_SCRATCH_LIMIT
+    # 64 planes of 512 x 512 = 64 MiB: fits
+    import torch
+    fits = tg.TG_OK if torch.cuda.is_available() else tg.TG_ERR_UNSUPPORTED
+    if not torch.cuda.is_available():
+        assert noalloc(opt=tg._options(split_k=64)) == fits
+        assert noalloc() == fits
+    # a forced repack of a 16384 x 4099 A (134 MB) does not fit
+    assert noalloc(M=16384, N=256, K=4099, opt=tg._options(pack_a=2)) == tg.TG_ERR_SCRATCH_LIMIT
+    # a caller workspace, and argument errors, as tile_gemm_ex would report them
+    assert noalloc(opt=tg._options(workspace=FAKE * 65536 * 1024, workspace_bytes=1 << 20)) == \
+        tg.TG_ERR_INVALID_ARG
+    assert noalloc(M=-1) == tg.TG_ERR_INVALID_ARG
+    assert noalloc(M=0) == tg.TG_OK

@@ -22,10 +22,12 @@ LIB_PATH = os.path.join(_HERE, "libtile_gemm.so")
 TG_F32, TG_BF16, TG_F16 = 0, 1, 2
 DTYPES = {"f32": TG_F32, "bf16": TG_BF16, "f16": TG_F16}
 
-TG_OK, TG_ERR_INVALID_ARG, TG_ERR_UNSUPPORTED, TG_ERR_LAUNCH, TG_ERR_INTERNAL = range(5)
+TG_OK, TG_ERR_INVALID_ARG, TG_ERR_UNSUPPORTED, TG_ERR_LAUNCH, TG_ERR_INTERNAL, TG_ERR_SCRATCH_LIMIT = range(6)
 STATUS_NAMES = {0: "TG_OK", 1: "TG_ERR_INVALID_ARG", 2: "TG_ERR_UNSUPPORTED", 3: "TG_ERR_LAUNCH",
-                4: "TG_ERR_INTERNAL"}
+                4: "TG_ERR_INTERNAL", 5: "TG_ERR_SCRATCH_LIMIT"}
 ABI_VERSION = 8
+# bytes of the library's own scratch that tile_gemm_ex_noalloc works in (TILE_GEMM_NOALLOC_SCRATCH_BYTES)
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 TG_CFG_AUTO, TG_CFG_256x256, TG_CFG_128x128, TG_CFG_64x64, TG_CFG_F32_64x64 = range(5)
 # layout-introspection ids of the thin fringe-strip blocks of TG_CFG_256x256
@@ -45,7 +47,7 @@ LAYOUT_MAX_SWIZZLES = 2
 EXPORTED = ["tile_gemm", "tile_gemm_strided_batched", "tile_gemm_ex", "tile_gemm_plan",
             "tile_gemm_workspace_size", "tg_layout_eval", "tile_gemm_describe_layout", "tile_gemm_lds_offset",
             "tile_gemm_acc_coord", "tile_gemm_status_string", "tile_gemm_abi_version", "tile_gemm_packed_b_ld",
-            "tile_gemm_packed_b_size", "tile_gemm_pack_b"]
+            "tile_gemm_packed_b_size", "tile_gemm_pack_b", "tile_gemm_ex_noalloc"]
 
 
 class TileGemmError(RuntimeError):
@@ -125,6 +127,9 @@ def _lib():
     lib.tile_gemm_ex.argtypes = [i64, i64, i64, i64, ci, vp, i64, i64, vp, i64, i64, vp, i64, i64,
                                  f32, f32, vp, ctypes.POINTER(Options)]
     lib.tile_gemm_ex.restype = ci
+    lib.tile_gemm_ex_noalloc.argtypes = [i64, i64, i64, i64, ci, vp, i64, i64, vp, i64, i64, vp, i64, i64,
+                                         f32, f32, vp, ctypes.POINTER(Options)]
+    lib.tile_gemm_ex_noalloc.restype = ci
     lib.tile_gemm_plan.argtypes = [i64, i64, i64, i64, ci, ctypes.POINTER(Options), ctypes.POINTER(PlanInfo)]
     lib.tile_gemm_plan.restype = ci
     lib.tile_gemm_workspace_size.argtypes = [i64, i64, i64, i64, ci, ctypes.POINTER(Options), ctypes.POINTER(i64)]
@@ -225,6 +230,18 @@ def tile_gemm_ex(batch, M, N, K, dtype, A, lda, strideA, B, ldb, strideB, C, ldc
     _check(_lib().tile_gemm_ex(batch, M, N, K, _dtype(dtype), _addr(A), lda, strideA, _addr(B), ldb, strideB,
                                _addr(C), ldc, strideC, alpha, beta, _stream(stream), ctypes.byref(opt)),
            "tile_gemm_ex")
+
+
+def tile_gemm_ex_noalloc(batch, M, N, K, dtype, A, lda, strideA, B, ldb, strideB, C, ldc, strideC,
+                         alpha=1.0, beta=0.0, stream=None, config=0, pipeline_depth=0, swizzle=0,
+                         block_order=0, split_k=0, pack_a=0, plan_lda=0, tail_gemm=0, persistent=0, bias=None,
+                         bias_stride=0, bias_mode=0, activation=0, force_cfg=None) -> None:
+    """tile_gemm_ex in the library's own scratch (no workspace argument, nothing allocated)."""
+    opt = _options(config if force_cfg is None else force_cfg, pipeline_depth, swizzle, block_order, split_k,
+                   None, 0, pack_a, plan_lda, tail_gemm, persistent, bias, bias_stride, bias_mode, activation)
+    _check(_lib().tile_gemm_ex_noalloc(batch, M, N, K, _dtype(dtype), _addr(A), lda, strideA, _addr(B), ldb,
+                                       strideB, _addr(C), ldc, strideC, alpha, beta, _stream(stream),
+                                       ctypes.byref(opt)), "tile_gemm_ex_noalloc")
 
 
 def tile_gemm_status(fn: str, *args) -> int:

@@ -22,6 +22,7 @@ constexpr int kMaxDevices = 64;
 struct DeviceState {
     bool probed = false;
     bool gfx950 = false;
+    void *scratch = nullptr;   // this device's address of `scratch` (tile_gemm_ex_noalloc)
 };
 
 std::mutex g_mutex;
@@ -51,6 +52,33 @@ tg_status current_device_ok() {
         d.probed = true;
     }
     return d.gfx950 ? TG_OK : TG_ERR_UNSUPPORTED;
+}
+
+// The scratch of tile_gemm_ex_noalloc (tile_gemm.h): split-K partials, the
+// aligned copy of A and the remainder partials of calls that cannot allocate.
+// Each device holds its own copy of the array at its own address; in host code
+// the name stands for a host-side shadow, so the device address is looked up
+// once per device (with that device current) and only that address is used.
+static __device__ __align__(256) char scratch[TILE_GEMM_NOALLOC_SCRATCH_BYTES];
+
+tg_status current_device_scratch(void **out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        (void)hipGetLastError();
+        return TG_ERR_UNSUPPORTED;
+    }
+    std::lock_guard<std::mutex> lock(g_mutex);
+    DeviceState &d = g_devices[dev];
+    if (!d.scratch) {
+        void *ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) {
+            (void)hipGetLastError();
+            return TG_ERR_INTERNAL;
+        }
+        d.scratch = ptr;
+    }
+    *out = d.scratch;
+    return TG_OK;
 }
 
 struct CfgDims {
@@ -774,6 +802,43 @@ tg_status pack_b(int64_t batch, int64_t K, int64_t N, tg_dtype dtype, const void
     return hipGetLastError() == hipSuccess ? TG_OK : TG_ERR_LAUNCH;
 }
 
+// tile_gemm_ex_noalloc (tile_gemm.h): the plan tile_gemm_ex would make with a
+// workspace of the scratch's size, checked against that size before any device
+// work, then the same call with the scratch as its workspace.
+tg_status run_noalloc(int64_t batch, int64_t M, int64_t N, int64_t K, tg_dtype dtype,
+                      const void *A, int64_t lda, int64_t sA, const void *B, int64_t ldb, int64_t sB,
+                      float *C, int64_t ldc, int64_t sC, float alpha, float beta, void *stream,
+                      const tg_options *opt) {
+    tg_options o{};
+    if (opt) {
+        if (opt->struct_size < kOptionsV1Size) return TG_ERR_INVALID_ARG;
+        std::memcpy(&o, opt, opt->struct_size < (int)sizeof o ? (size_t)opt->struct_size : sizeof o);
+    }
+    if (o.workspace != nullptr || o.workspace_bytes != 0) return TG_ERR_INVALID_ARG;
+    o.struct_size = (int)sizeof o;
+    tg_status st = validate(batch, M, N, K, dtype, A, lda, sA, B, ldb, sB, C, ldc, sC);
+    if (st != TG_OK) return st;
+    {
+        // the plan only asks whether a workspace is there and how large it is
+        tg_options q = o;
+        q.workspace = reinterpret_cast<void *>(uintptr_t(256));
+        q.workspace_bytes = TILE_GEMM_NOALLOC_SCRATCH_BYTES;
+        Plan plan;
+        st = make_plan(batch, M, N, K, dtype, &q, lda, reinterpret_cast<uintptr_t>(A) % 16 == 0, plan);
+        if (st != TG_OK) return st;
+        if (plan.info.workspace_bytes > TILE_GEMM_NOALLOC_SCRATCH_BYTES) return TG_ERR_SCRATCH_LIMIT;
+    }
+    if (batch == 0 || M == 0 || N == 0) return TG_OK;
+    st = current_device_ok();
+    if (st != TG_OK) return st;
+    void *ws = nullptr;
+    st = current_device_scratch(&ws);
+    if (st != TG_OK) return st;
+    o.workspace = ws;
+    o.workspace_bytes = TILE_GEMM_NOALLOC_SCRATCH_BYTES;
+    return run(batch, M, N, K, dtype, A, lda, sA, B, ldb, sB, C, ldc, sC, alpha, beta, stream, &o);
+}
+
 }  // namespace
 
 extern "C" {
@@ -786,6 +851,19 @@ tg_status tile_gemm_ex(int64_t batch, int64_t M, int64_t N, int64_t K, tg_dtype 
     try {
         return run(batch, M, N, K, dtype, A, lda, strideA, B, ldb, strideB, C, ldc, strideC, alpha, beta,
                    stream, opt);
+    } catch (...) {
+        return TG_ERR_INTERNAL;
+    }
+}
+
+tg_status tile_gemm_ex_noalloc(int64_t batch, int64_t M, int64_t N, int64_t K, tg_dtype dtype,
+                               const void *A, int64_t lda, int64_t strideA,
+                               const void *B, int64_t ldb, int64_t strideB,
+                               float *C, int64_t ldc, int64_t strideC,
+                               float alpha, float beta, void *stream, const tg_options *opt) {
+    try {
+        return run_noalloc(batch, M, N, K, dtype, A, lda, strideA, B, ldb, strideB, C, ldc, strideC, alpha, beta,
+                           stream, opt);
     } catch (...) {
         return TG_ERR_INTERNAL;
     }
@@ -841,6 +919,9 @@ const char *tile_gemm_status_string(tg_status s) {
         case TG_ERR_UNSUPPORTED: return "TG_ERR_UNSUPPORTED: no gfx950 device visible, or option not available";
         case TG_ERR_LAUNCH: return "TG_ERR_LAUNCH: the HIP runtime refused the kernel launch";
         case TG_ERR_INTERNAL: return "TG_ERR_INTERNAL: unexpected failure inside the library";
+        case TG_ERR_SCRATCH_LIMIT:
+            return "TG_ERR_SCRATCH_LIMIT: the call needs more scratch than tile_gemm_ex_noalloc holds "
+                   "(TILE_GEMM_NOALLOC_SCRATCH_BYTES)";
     }
     return "unknown tg_status";
 }
