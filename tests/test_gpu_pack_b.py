@@ -15,7 +15,7 @@ import torch
 import tile_scheduled_dense_amd as tg
 import workloads
 from tests.gpu_util import GpuProblem, check_parity, device_tensor, need_gpu, oracle_points, parity_error, \
-    result_points
+    parity_error_rounded, result_points
 
 pytestmark = pytest.mark.gpu
 
@@ -144,5 +144,5 @@ def test_full_size_ragged_packed_b():
     vals = result_points(got, pts)
     o, den = oracle_points(p, pts)
     c0 = p.C0[pts[:, 1] * p.ldc + pts[:, 2]].astype(np.float64)
-    assert parity_error(vals, o, abs(p.alpha) * den + abs(p.beta) * np.abs(c0)) <= 4e-3
+    assert parity_error_rounded(vals, o, den, p.beta, c0) <= 4e-3
     got.check_guards()

@@ -14,7 +14,8 @@ import torch
 
 import tile_scheduled_dense_amd as tg
 import workloads
-from tests.gpu_util import GpuProblem, check_parity, need_gpu, oracle_points, parity_error, result_points
+from tests.gpu_util import (GpuProblem, check_parity, need_gpu, oracle_points, parity_error,
+                            parity_error_rounded, result_points)
 
 pytestmark = pytest.mark.gpu
 
@@ -83,7 +84,7 @@ def test_full_size_m_remainder_sampled():
     got = result_points(gp, pts)
     ref, den = oracle_points(p, pts)
     c0 = p.C0[pts[:, 1] * p.ldc + pts[:, 2]].astype(np.float64)
-    err = parity_error(got, ref, abs(p.alpha) * den + abs(p.beta) * np.abs(c0))
+    err = parity_error_rounded(got, ref, den, p.beta, c0)
     print(f"8193 x 8192 x 8192: sampled parity error {err:.3e} over {len(pts)} outputs")
     assert err <= 4e-3
     gp.check_guards()

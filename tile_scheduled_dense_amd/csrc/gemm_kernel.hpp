@@ -9,8 +9,10 @@
 //  1. block order: the hardware hands consecutive workgroup ids to the eight
 //     XCDs in turn; the id is remapped so each XCD receives a contiguous run of
 //     tiles, walked in groups of GROUP_M tile rows, so tiles that share A and B
-//     panels are resident on one XCD's L2 at the same time (the ParallelMap
-//     "reshape, permute or swizzle child coordinates" of the LuisaCompute page).
+//     panels are resident on one XCD's L2 at the same time: a remapping of the
+//     parallel children's coordinates, which the ParallelMap of the LuisaCompute
+//     "Execution Nests and coordinates" page permits (Ordering strength and
+//     sibling scopes).
 //  2. pad-to-tile + partition (OCANNL Pad and Partition paragraphs): the
 //     extents are padded to the tile; a block whose tile lies inside M x N runs
 //     the guard-free instantiation, a block crossing M or N runs the one whose

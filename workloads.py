@@ -178,14 +178,21 @@ def custom(dtype, M, N, K, batch=1, lda_pad=0, ldb_pad=0, ldc_pad=0, alpha=1.0, 
 
 
 def sample_points(p: Problem, n: int, seed: int = 1) -> np.ndarray:
-    """n (b, i, j) output coordinates: corners and fringe rows/columns first, then random."""
+    """(b, i, j) output coordinates: the whole last row and last column of every batch entry
+    (of the first and last when that would exceed 300k points), where thin fringe strips and
+    fringe tiles end; corners and middles; then n random points."""
     rng = np.random.default_rng(seed)
     fixed = []
     for b in sorted({0, p.batch - 1}):
         for i in sorted({0, p.M - 1, max(0, p.M // 2)}):
             for j in sorted({0, p.N - 1, max(0, p.N // 2)}):
                 fixed.append((b, i, j))
-    rest = max(0, n - len(fixed))
+    edge_entries = range(p.batch) if p.batch * (p.M + p.N) <= 300000 else sorted({0, p.batch - 1})
+    for b in edge_entries:
+        fixed += [(b, p.M - 1, j) for j in range(p.N)]
+        fixed += [(b, i, p.N - 1) for i in range(p.M)]
+    fixed = sorted(set(fixed))
+    rest = n
     rnd = np.stack([rng.integers(0, p.batch, rest), rng.integers(0, p.M, rest),
                     rng.integers(0, p.N, rest)], axis=1) if rest else np.zeros((0, 3), np.int64)
     pts = np.concatenate([np.array(fixed, dtype=np.int64).reshape(-1, 3), rnd.astype(np.int64)])
