@@ -101,7 +101,9 @@ typedef enum {
     TG_CFG_256x256 = 1,     /* 16-bit inputs: 256x256 block tile, 4 waves, 16x16x32 MFMA */
     TG_CFG_128x128 = 2,     /* 16-bit inputs: 128x128 block tile, 4 waves        */
     TG_CFG_64x64 = 3,       /* 16-bit inputs: 64x64 block tile, 2 waves          */
-    TG_CFG_F32_64x64 = 4    /* fp32 inputs: 64x64 block tile, 4 waves            */
+    TG_CFG_F32_64x64 = 4,   /* fp32 inputs: 64x64 block tile, 4 waves            */
+    TG_CFG_288x160 = 5      /* 16-bit inputs: 288x160 block tile, 4 waves, 16x16x32: one
+                               block per problem of up to 288 x 160 (batched small GEMMs) */
 } tg_config;
 
 /*
@@ -112,8 +114,9 @@ typedef enum {
  * pipeline_depth is the number of LDS copies of the K tile (the window is one
  * less; OCANNL "Module Ir.Schedule", Stage paragraph, pipeline_depth, and
  * LuisaCompute "Pipelines and stage boundaries", window): 16-bit inputs take 1,
- * 2 or 4 (default 4; 5 for TG_CFG_128x128 and TG_CFG_64x64), fp32 inputs 1 or 2
- * (default 2).  Depth 1 is the unpipelined form.
+ * 2 or 4 (default 4; 5 for TG_CFG_128x128 and TG_CFG_64x64; 2 or 4 for
+ * TG_CFG_288x160), fp32 inputs 1 or 2 (default 2).  Depth 1 is the unpipelined
+ * form.
  *
  * swizzle is the placement of the staged tiles in LDS (OCANNL Stage paragraph,
  * swizzle and pad_stride; TVM TIRx "Tensor Layout", SwizzleLayout): 0 the

@@ -384,7 +384,7 @@ def test_plan_automatic_split_across_tiles():
              ((1, 512, 2048, 2048, "bf16"), (tg.TG_CFG_64x64, 1, 256)),      # not 256x256 split 2 (32 blocks)
              ((1, 512, 512, 131072, "bf16"), (tg.TG_CFG_256x256, 64, 256)),  # a tie at 256: the larger tile
              ((1, 8192, 8192, 8192, "bf16"), (tg.TG_CFG_256x256, 1, 1024)),
-             ((512, 257, 129, 1000, "f16"), (tg.TG_CFG_256x256, 1, 1024)),
+             ((512, 257, 129, 1000, "f16"), (tg.TG_CFG_288x160, 1, 512)),   # one block per problem
              ((1, 1000, 1000, 1000, "bf16"), (tg.TG_CFG_64x64, 1, 256)),
              ((1, 384, 4096, 4096, "bf16"), (tg.TG_CFG_128x128, 4, 384)),     # 512 slots for the smaller tiles
              ((1, 256, 256, 65536, "bf16"), (tg.TG_CFG_64x64, 32, 512)),
@@ -453,3 +453,25 @@ def test_noalloc_limits_checked_before_any_device():
         tg.TG_ERR_INVALID_ARG
     assert noalloc(M=-1) == tg.TG_ERR_INVALID_ARG
     assert noalloc(M=0) == tg.TG_OK
+
+
+def test_plan_one_block_per_small_problem():
+    """Batched problems that fit one 288 x 160 tile, at least half of it output, take one block
+    per problem; the batched workload 512 x (257 x 129 x 1000) is one such."""
+    p = tg.tile_gemm_plan(512, 257, 129, 1000, "f16")
+    assert (p["config"], p["block_m"], p["block_n"], p["tiles_m"], p["tiles_n"], p["grid"]) == \
+           (tg.TG_CFG_288x160, 288, 160, 1, 1, 512)
+    assert (p["interior_blocks"], p["fringe_blocks"], p["strip_blocks"], p["lds_bytes"], p["per_cu"]) == \
+           (0, 1, 0, 4 * (18 + 10) * 1024, 1)
+    assert (p["mfma_m"], p["mfma_k"], p["k_tiles"], p["k_tail"]) == (16, 32, 32, 8)
+    # too few problems, too small a share of the tile, or too large: another tile
+    assert tg.tile_gemm_plan(64, 257, 129, 1000, "f16")["config"] != tg.TG_CFG_288x160
+    assert tg.tile_gemm_plan(512, 100, 100, 1000, "f16")["config"] != tg.TG_CFG_288x160
+    assert tg.tile_gemm_plan(512, 300, 129, 1000, "f16")["config"] != tg.TG_CFG_288x160
+    # depths 2 and 4 are built, and the none placement at depth 4
+    for d in (2, 4):
+        assert tg.tile_gemm_plan(8, 257, 129, 100, "bf16", config=tg.TG_CFG_288x160, pipeline_depth=d)["grid"] == 8
+    assert _plan_status(8, 257, 129, 100, "bf16", config=tg.TG_CFG_288x160, pipeline_depth=1) == tg.TG_ERR_UNSUPPORTED
+    assert _plan_status(8, 257, 129, 100, "bf16", config=tg.TG_CFG_288x160, swizzle=tg.SWZ_PAD) == \
+        tg.TG_ERR_UNSUPPORTED
+    assert _plan_status(8, 257, 129, 100, "f32", config=tg.TG_CFG_288x160) == tg.TG_ERR_UNSUPPORTED

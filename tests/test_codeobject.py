@@ -174,7 +174,8 @@ def test_no_scratch_outside_opt_in_variants(tmp_path):
     assert all(_opt_in(n) for n in spills), {n: v for n, v in spills.items() if not _opt_in(n)}
 
 
-CFG_OF = {(256, 256): tg.TG_CFG_256x256, (128, 128): tg.TG_CFG_128x128, (64, 64): tg.TG_CFG_64x64}
+CFG_OF = {(256, 256): tg.TG_CFG_256x256, (128, 128): tg.TG_CFG_128x128, (64, 64): tg.TG_CFG_64x64,
+          (288, 160): tg.TG_CFG_288x160}
 
 
 def test_per_cu_table_matches_code_object(tmp_path):

@@ -22,7 +22,7 @@ from tests.gpu_util import GpuProblem, check_parity, need_gpu
 
 pytestmark = pytest.mark.gpu
 
-CFG16 = [tg.TG_CFG_256x256, tg.TG_CFG_128x128, tg.TG_CFG_64x64]
+CFG16 = [tg.TG_CFG_256x256, tg.TG_CFG_128x128, tg.TG_CFG_64x64, tg.TG_CFG_288x160]
 
 
 @pytest.fixture(autouse=True)
@@ -70,6 +70,7 @@ def padded(p, Mp, Np, Kp):
 @pytest.mark.parametrize("cfg,dt,tile", [(tg.TG_CFG_256x256, "bf16", (256, 256, 32)),
                                          (tg.TG_CFG_128x128, "f16", (128, 128, 32)),
                                          (tg.TG_CFG_64x64, "bf16", (64, 64, 32)),
+                                         (tg.TG_CFG_288x160, "f16", (288, 160, 32)),
                                          (0, "f32", (64, 64, 32))])
 @pytest.mark.parametrize("shape", [(300, 333, 130), (67, 45, 53), (257, 129, 1000)], ids=str)
 def test_ragged_equals_cropped_padded(cfg, dt, tile, shape):
@@ -89,6 +90,8 @@ def test_depth_swizzle_order_are_bitwise_invisible(cfg, dt):
     p = workloads.custom(dt, 531, 389, 333, lda_pad=1, ldb_pad=2, alpha=0.75, beta=-1.25, seed=3)
     ref = run(p, config=cfg)
     variants = [dict(pipeline_depth=1), dict(pipeline_depth=2), dict(swizzle=tg.SWZ_NONE), dict(block_order=1)]
+    if cfg == tg.TG_CFG_288x160:           # built at depths 2 and 4
+        variants = variants[1:]
     if dt == "f32":
         variants.append(dict(pipeline_depth=1, swizzle=tg.SWZ_NONE, block_order=1))
     if cfg == tg.TG_CFG_256x256:

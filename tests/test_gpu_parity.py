@@ -17,7 +17,7 @@ from tests.gpu_util import (GpuProblem, check_parity, need_gpu, oracle_full, ora
 
 pytestmark = pytest.mark.gpu
 
-CFG16 = [tg.TG_CFG_256x256, tg.TG_CFG_128x128, tg.TG_CFG_64x64]
+CFG16 = [tg.TG_CFG_256x256, tg.TG_CFG_128x128, tg.TG_CFG_64x64, tg.TG_CFG_288x160]
 
 
 @pytest.fixture(autouse=True)

@@ -93,7 +93,7 @@ def test_admission_and_invalid():
 # configuration have layout-only ids.
 RING = [(tg.TG_CFG_256x256, 256, 256, 4, 16), (tg.LAYOUT_CFG_STRIP_N, 256, 64, 4, 16),
         (tg.LAYOUT_CFG_STRIP_M, 64, 256, 4, 16), (tg.TG_CFG_128x128, 128, 128, 4, 32),
-        (tg.TG_CFG_64x64, 64, 64, 2, 32)]
+        (tg.TG_CFG_64x64, 64, 64, 2, 32), (tg.TG_CFG_288x160, 288, 160, 4, 16)]
 BK = 32
 PLANNED = [r for r in RING if r[0] < 100] + [(tg.TG_CFG_F32_64x64, 64, 64, 4, 16)]
 
@@ -111,6 +111,8 @@ def test_kernel_lds_placement_matches_layout(cfg, bm, bn, waves, mt, swz):
     # the address the kernel computes (same inline function as the device code)
     # equals the TileLayout + swizzle description, and is a bijection onto the tile
     for operand, kind in [(0, tg.LAYOUT_LDS_A), (1, tg.LAYOUT_LDS_B)]:
+        if cfg == tg.TG_CFG_288x160 and operand == 1 and swz == tg.SWZ_XOR:
+            continue        # no TIRx description (test_320_byte_b_rows below)
         L = tg.tile_gemm_describe_layout(cfg, swz, kind)
         rows_, cols_ = L.shape[0], L.shape[1]
         seen = set()
@@ -254,7 +256,25 @@ def test_pad_stride_b_reads_at_most_two_way(cfg, bm, bn, waves, mt):
     assert worst == 2
 
 
-@pytest.mark.parametrize("cfg,bm,bn,waves,mt", RING)
+def test_320_byte_b_rows():
+    """The 288 x 160 tile's B rows are 320 bytes (5 units of 64): row k starts on bank 16 k, so
+    rows k .. k + 3 are apart already, and the 32-byte half XOR of bit 3 of k moves k + 8 off k's
+    banks.  Its placement is a bijection of the 32 x 160 tile onto 32 rows of 160 elements, and it
+    is no TIRx swizzle of the linear address (the row pitch is no power of two), so it has no
+    layout description."""
+    cfg = tg.TG_CFG_288x160
+    seen = set()
+    for k in range(BK):
+        for n in range(160):
+            off = tg.tile_gemm_lds_offset(cfg, tg.SWZ_XOR, 1, k, n)
+            assert off // 160 == k and (off % 160) // 16 == (n // 16) ^ ((k >> 3) & 1) and off % 16 == n % 16
+            seen.add(off)
+    assert seen == set(range(BK * 160))
+    with pytest.raises(tg.TileGemmError):
+        tg.tile_gemm_describe_layout(cfg, tg.SWZ_XOR, tg.LAYOUT_LDS_B)
+
+
+@pytest.mark.parametrize("cfg,bm,bn,waves,mt", [r for r in RING if r[0] != tg.TG_CFG_288x160])
 def test_ring_copy_ownership(cfg, bm, bn, waves, mt):
     # every physical 16-byte chunk of the A tile is filled by exactly one
     # (copy instruction, wave, lane); a copy instruction fills 1 KiB, lane l

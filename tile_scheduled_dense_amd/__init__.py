@@ -29,7 +29,7 @@ ABI_VERSION = 8
 # bytes of the library's own scratch that tile_gemm_ex_noalloc works in (TILE_GEMM_NOALLOC_SCRATCH_BYTES)
 NOALLOC_SCRATCH_BYTES = 64 << 20
 
-TG_CFG_AUTO, TG_CFG_256x256, TG_CFG_128x128, TG_CFG_64x64, TG_CFG_F32_64x64 = range(5)
+TG_CFG_AUTO, TG_CFG_256x256, TG_CFG_128x128, TG_CFG_64x64, TG_CFG_F32_64x64, TG_CFG_288x160 = range(6)
 # layout-introspection ids of the thin fringe-strip blocks of TG_CFG_256x256
 LAYOUT_CFG_STRIP_N, LAYOUT_CFG_STRIP_M = 101, 102
 SWZ_DEFAULT, SWZ_NONE, SWZ_PAD, SWZ_XOR = 0, 1, 2, 3

@@ -261,7 +261,7 @@ struct RingBlock {
     static constexpr int A_REGION = STAGES * B_STAGE;
     static constexpr int a_tile(int stage) { return A_REGION + stage * A_STAGE; }
     static constexpr int b_tile(int stage) { return stage * B_STAGE; }
-    static_assert(SWZ == SWZ_PAD || ((STAGES - 1) * A_STAGE + C::A_TILE_BYTES <= 65536 &&
+    static_assert(SWZ == SWZ_PAD || ((STAGES - 1) * A_STAGE + (C::TM - 1) * C::MT * A_PITCH + 48 < 65536 &&
                                      (STAGES - 1) * B_STAGE + 4 * B_PITCH < 65536), "DS immediate offsets");
 
     __device__ __forceinline__ RingBlock(const GemmParams &p_, char *smem_, int64_t b_, int64_t tm, int64_t tn)
@@ -352,7 +352,7 @@ struct RingBlock {
             copy_group_to_lds<G1>(rs, region + CP::block(4, wave) * 1024, &voff[4]);
         }
         if constexpr (CP::SHARED) {
-            copy_group_to_lds<1>(rs, region + (CP::NB - 1) * 1024, &voff[CP::Q]);
+            copy_group_to_lds<1>(rs, region + CP::block(CP::Q, wave) * 1024, &voff[CP::Q]);
         }
     }
 
@@ -528,6 +528,21 @@ struct RingBlock {
     }
 };
 
+// Values per store-back chunk (the C0 loads of a chunk go out together): up
+// to 64 for 16x16 tiles, whose accumulators sit in AGPRs; up to 32 for 32x32
+// tiles, whose 64 accumulators per lane share the VGPRs with the chunk's
+// offsets and C0 values (a chunk of 64 took the 128 x 128 kernel past 256
+// registers, into scratch); up to 16 with the fused tail.  The chunk is a
+// whole number of MFMA tiles that divides the wave's tiles (45 for the
+// 288 x 160 tile: 15 per chunk, 5 with the tail).
+template <class C, bool TAIL>
+constexpr int chunk_values() {
+    const int cap = (TAIL ? 16 : (C::MT == 32 ? 32 : 64)) / C::ACC_PER_MFMA;
+    int ch = cap < C::TM * C::TN ? cap : C::TM * C::TN;
+    while ((C::TM * C::TN) % ch) --ch;
+    return ch * C::ACC_PER_MFMA;
+}
+
 // SCHED_RING (all waves in step): iteration kt waits for tile kt, one
 // barrier (tile kt visible, copy of tile kt-1 released), issues tile
 // kt + STAGES - 1, multiplies tile kt.  STAGES == 1 is the unpipelined form.
@@ -567,14 +582,9 @@ __device__ __forceinline__ void ring_tile(const GemmParams &p, char *smem, int64
         }
         blk.acc.settle();
     }
-    // Values per store-back chunk: 64 (the C0 loads of a chunk go out together)
-    // for 16x16 tiles, whose accumulators sit in AGPRs; 32 for 32x32 tiles,
-    // whose 64 accumulators per lane share the VGPRs with the chunk's offsets and
-    // C0 values (a chunk of 64 took the 128 x 128 kernel past 256 registers, into
-    // scratch).
-    constexpr int CHUNK_VALUES = TAIL ? 16 : (C::MT == 32 ? 32 : 64);
     auto get = [&](int i, int j, int v) { return blk.acc.get(i, j, v); };
-    store_tile_epilogue<C, FRINGE, decltype(get), CHUNK_VALUES, TAIL>(p, get, b, blk.m0, blk.n0, blk.wave, blk.lane);
+    store_tile_epilogue<C, FRINGE, decltype(get), chunk_values<C, TAIL>(), TAIL>(p, get, b, blk.m0, blk.n0, blk.wave,
+                                                                                blk.lane);
 }
 
 // SCHED_SWPIPE (software pipeline, one wave per SIMD, large wave tiles): the
@@ -592,7 +602,6 @@ struct SwPipe {
     static constexpr int NMFMA = C::KSTEPS * C::TM * C::TN;
     static constexpr int READS = Blk::READS;
     static_assert(READS <= NMFMA, "one fragment read per MFMA at most");
-    static_assert(NMFMA % 4 == 0, "copy groups after a quarter and three quarters of the MFMAs");
 
     // One iteration: multiply tile t from (fa, fb) while reading tile t + 1
     // into (na, nb).  STEADY: tile t + 1 exists and tile t + STAGES is copied
@@ -699,7 +708,8 @@ __device__ __forceinline__ void ring_tile_swpipe(const GemmParams &p, char *smem
         blk.acc.settle();
     }
     auto get = [&](int i, int j, int v) { return blk.acc.get(i, j, v); };
-    store_tile_epilogue<C, FRINGE, decltype(get), TAIL ? 16 : 64, TAIL>(p, get, b, blk.m0, blk.n0, blk.wave, blk.lane);
+    store_tile_epilogue<C, FRINGE, decltype(get), chunk_values<C, TAIL>(), TAIL>(p, get, b, blk.m0, blk.n0, blk.wave,
+                                                                                blk.lane);
 }
 
 // Persistent form of the software pipeline for a grid of interior tiles of

@@ -167,6 +167,11 @@ tg_status describe_ring(int swz, int kind, tg_layout *out) {
     // pad_stride is built for the 256 x 256 tile and its strips only; its copies
     // (padded slots, one block every wave copies) are not one shard layout
     if (swz == SWZ_PAD && (C::BM * C::BN < 256 * 64 || kind == TG_LAYOUT_COPY_A)) return TG_ERR_UNSUPPORTED;
+    // 320-byte B rows (the 288 x 160 tile): the 32-byte half XOR of row k's bit 3
+    // is not a swizzle of the linear address of a row pitch that is no power of
+    // two, and the A copies end with blocks copied by several waves
+    if (C::B_UNITS == 5 && ((kind == TG_LAYOUT_LDS_B && swz == SWZ_XOR) || kind == TG_LAYOUT_COPY_A))
+        return TG_ERR_UNSUPPORTED;
     switch (kind) {
         case TG_LAYOUT_LDS_A: describe_ring_lds<C>(out, 0, swz); return TG_OK;
         case TG_LAYOUT_LDS_B: describe_ring_lds<C>(out, 1, swz); return TG_OK;
@@ -263,6 +268,7 @@ tg_status tile_gemm_describe_layout(int config, int swizzle, int kind, tg_layout
         case TG_LAYOUT_CFG_STRIP_M: return describe_ring<StripMx256<DT_BF16>>(swizzle, kind, out);
         case TG_CFG_128x128: return describe_ring<Ring128<DT_BF16>>(swizzle, kind, out);
         case TG_CFG_64x64: return describe_ring<Ring64<DT_BF16>>(swizzle, kind, out);
+        case TG_CFG_288x160: return describe_ring<Ring288x160<DT_BF16>>(swizzle, kind, out);
         case TG_CFG_F32_64x64: return describe<CfgF32>(swizzle, kind, out);
     }
     return TG_ERR_INVALID_ARG;
@@ -280,6 +286,7 @@ int64_t tile_gemm_lds_offset(int config, int swizzle, int operand, int64_t row, 
         case TG_LAYOUT_CFG_STRIP_M: return ring_lds_offset<StripMx256<DT_BF16>>(swizzle, operand, row, k);
         case TG_CFG_128x128: return ring_lds_offset<Ring128<DT_BF16>>(swizzle, operand, row, k);
         case TG_CFG_64x64: return ring_lds_offset<Ring64<DT_BF16>>(swizzle, operand, row, k);
+        case TG_CFG_288x160: return ring_lds_offset<Ring288x160<DT_BF16>>(swizzle, operand, row, k);
         case TG_CFG_F32_64x64: return lds_offset<CfgF32>(swizzle, operand, row, k);
     }
     return -1;
@@ -292,6 +299,7 @@ int tile_gemm_acc_coord(int config, int wave, int lane, int slot, int64_t *row, 
         case TG_LAYOUT_CFG_STRIP_M: return acc_coord_checked<StripMx256<DT_BF16>>(wave, lane, slot, row, col);
         case TG_CFG_128x128: return acc_coord_checked<Ring128<DT_BF16>>(wave, lane, slot, row, col);
         case TG_CFG_64x64: return acc_coord_checked<Ring64<DT_BF16>>(wave, lane, slot, row, col);
+        case TG_CFG_288x160: return acc_coord_checked<Ring288x160<DT_BF16>>(wave, lane, slot, row, col);
         case TG_CFG_F32_64x64: return acc_coord_checked<CfgF32>(wave, lane, slot, row, col);
     }
     return -1;

@@ -157,9 +157,6 @@ struct RingCfg {
     static constexpr int A_TILE_BYTES = BM * A_ROW_BYTES;
     static constexpr int B_TILE_BYTES = BK * B_ROW_BYTES;
     static constexpr int STAGE_BYTES = A_TILE_BYTES + B_TILE_BYTES;
-    static constexpr int A_DMA = A_TILE_BYTES / 1024 / WAVES;   // 1 KiB copies per wave per tile
-    static constexpr int B_DMA = B_TILE_BYTES / 1024 / WAVES;
-    static constexpr int COPIES = A_DMA + B_DMA;
     // acc_coord() below is shared with TileCfg
     static constexpr int LANE_GROUPS = 64 / MT_;             // lanes sharing a row: 2 or 4
     static constexpr bool B_HALF_SWZ = MT_ == 16;            // (k >> 3) & 1 into the 32-byte half
@@ -170,13 +167,15 @@ struct RingCfg {
     // was never met: its software pipeline needs more than 128 registers, so
     // it ran two per CU anyway and spilled on the way; mid-size problems
     // measured the same either way.)
-    static constexpr int OCCUPANCY = BM_ * BN_ >= 256 * 256 ? 1 : 2;
+    // The rule: more than 128 accumulators per lane (256 for 256 x 256, 180 for
+    // 288 x 160) take a whole CU; a tile sized by area alone compiled the
+    // 288 x 160 kernel at depth 2 for two per CU and spilled accumulators.
+    static constexpr int OCCUPANCY = WTM * WTN / 64 > 128 ? 1 : 2;
 
     static_assert(BM % (WAVES_M * MT) == 0 && BN % (WAVES_N * MT) == 0, "wave tiling");
-    static_assert(A_TILE_BYTES % (1024 * WAVES) == 0 && A_DMA >= 1, "A copy split");
-    static_assert(B_TILE_BYTES % (1024 * WAVES) == 0 && B_DMA >= 1, "B copy split");
-    static_assert(B_UNITS == 2 || B_UNITS == 4 || B_UNITS == 8, "B row of 2, 4 or 8 units");
-    static_assert(A_DMA <= 4 && B_DMA <= 4, "a wave's copies of one operand span at most 4 KiB");
+    static_assert(B_ROW_BYTES % 64 == 0, "B rows of whole 64-byte units");
+    static_assert(B_UNITS == 2 || B_UNITS == 4 || B_UNITS == 8 || (B_UNITS == 5 && MT_ == 16),
+                  "B rows of 2, 4 or 8 units (XOR of the unit index), or of 5 (half XOR only)");
 
 };
 
@@ -189,6 +188,10 @@ template <int DT> using Strip256xN = RingCfg<DT, 256, 64, 4, 1, 16>;
 template <int DT> using StripMx256 = RingCfg<DT, 64, 256, 1, 4, 16>;
 template <int DT> using Ring128 = RingCfg<DT, 128, 128, 2, 2>;   // 4 waves, wave tile 64 x 64
 template <int DT> using Ring64 = RingCfg<DT, 64, 64, 1, 2>;      // 2 waves, wave tile 64 x 32
+// One workgroup per small problem: a 288 x 160 tile (18 x 10 MFMA tiles of 16 x 16; 4 waves,
+// wave tile 144 x 80) covers a whole problem of up to 288 x 160, e.g. 257 x 129 in one block
+// with no strip and no second tile, so A and B are each read once.
+template <int DT> using Ring288x160 = RingCfg<DT, 288, 160, 2, 2, 16>;
 
 // A tile: the XOR applied to the 16-byte chunk index of row r.  Which row
 // bits make the fragment reads conflict-free depends on the MFMA lane pattern
@@ -232,6 +235,9 @@ TG_HD int ring_a_byte(int r, int c, int swz) {
 template <class C>
 TG_HD int ring_b_mask(int k, int swz) {
     if (swz != SWZ_XOR) return 0;
+    // 5 units (320-byte rows): rows k .. k + 3 already start 16 banks apart; the
+    // half XOR below separates k from k + 8
+    if (C::B_UNITS == 5) return 0;
     if (C::B_UNITS >= 4) return k & 3;
     return C::MT == 32 ? ((k >> 1) & 1) : ((k >> 3) & 1);
 }
@@ -258,9 +264,10 @@ TG_HD int ring_b_byte(int k, int n, int swz) {
 // instruction (lane l writes bytes 16 l .. 16 l + 15 of its block).  Wave w
 // copies the Q adjacent blocks w * Q .. w * Q + Q - 1, so they share one LDS
 // base and differ only by an immediate offset.  When the blocks do not divide
-// evenly among the waves (a padded pitch), exactly one block is left over and
-// every wave copies it as well: the same source bytes to the same LDS bytes, so
-// the concurrent writes agree.
+// evenly among the waves (a padded pitch, a tile of 18 or 10 KiB), the SHARED
+// blocks left over are copied once more each by every wave w, block
+// Q * WAVES + w % SHARED: a block copied by several waves gets the same source
+// bytes at the same LDS bytes from each, so the concurrent writes agree.
 template <class C, int SWZ, int OP>
 struct RingCopy {
     static constexpr int PITCH = OP == 0 ? ring_a_pitch<C>(SWZ) : ring_b_pitch<C>(SWZ);
@@ -268,13 +275,15 @@ struct RingCopy {
     static constexpr int ROW_BYTES = OP == 0 ? C::A_ROW_BYTES : C::B_ROW_BYTES;   // valid bytes per row
     static constexpr int NB = (ROWS * PITCH + 1023) / 1024;     // 1 KiB blocks
     static constexpr int Q = NB / C::WAVES;                      // blocks of a wave's own run
-    static constexpr int SHARED = NB - Q * C::WAVES;             // 0, or 1 block every wave copies
-    static constexpr int PER = Q + SHARED;                       // copies per wave per K tile
+    static constexpr int SHARED = NB - Q * C::WAVES;             // blocks left over (< WAVES)
+    static constexpr int PER = Q + (SHARED ? 1 : 0);             // copies per wave per K tile
     static constexpr int REGION = NB * 1024;                     // LDS bytes per pipeline copy
     static constexpr int GMAX = Q < 4 ? Q : 4;                   // copies under one M0 value at most
-    static_assert(Q >= 1 && SHARED <= 1 && Q <= 8, "copy split");
+    static_assert(Q >= 1 && Q <= 8, "copy split");
     // the block copy d of wave `wave` fills
-    TG_HD static constexpr int block(int d, int wave) { return d < Q ? wave * Q + d : NB - 1; }
+    TG_HD static constexpr int block(int d, int wave) {
+        return d < Q ? wave * Q + d : Q * C::WAVES + (SHARED ? wave % SHARED : 0);
+    }
     // copy d's position within its group of adjacent copies (groups of at most four)
     TG_HD static constexpr int pos(int d) { return d < Q ? d % 4 : 0; }
 };

@@ -96,6 +96,7 @@ CfgDims cfg_dims(int config) {
         case TG_CFG_128x128: return dims_of<Ring128<DT_BF16>>(Ring128<DT_BF16>::MK);
         case TG_CFG_64x64: return dims_of<Ring64<DT_BF16>>(Ring64<DT_BF16>::MK);
         case TG_CFG_F32_64x64: return dims_of<CfgF32>(4);
+        case TG_CFG_288x160: return dims_of<Ring288x160<DT_BF16>>(Ring288x160<DT_BF16>::MK);
         default: return {0, 0, 0, 0, 0, 0, 0};
     }
 }
@@ -131,6 +132,11 @@ Partition256 partition256(int64_t M, int64_t N) {
 // of the 384 x 256 it pads to in 128-wide tiles.
 int choose_config(int64_t batch, int64_t M, int64_t N, tg_dtype dtype) {
     if (dtype == TG_F32) return TG_CFG_F32_64x64;
+    // Many small problems that each fit one 288 x 160 tile, at least half of it
+    // output: one block per problem reads its A and B once (the 256 x 256 tile
+    // plus a strip read B twice and multiplied 2.5 times the output of a
+    // 257 x 129 problem).
+    if (batch >= 128 && M <= 288 && N <= 160 && 2 * M * N >= 288 * 160) return TG_CFG_288x160;
     const Partition256 q = partition256(M, N);
     const int64_t big = (q.tiles_m * q.tiles_n + q.strip_n + q.strip_m) * batch;
     const int64_t mid = cdiv(M, 128) * cdiv(N, 128) * batch;
@@ -171,6 +177,7 @@ int64_t auto_splits(int64_t tiles, int64_t K, int64_t slots) {
 int cfg_per_cu(int config, int depth) {
     switch (config) {
         case TG_CFG_256x256: return 1;
+        case TG_CFG_288x160: return 1;   // 417 registers a wave, 4 waves, 28 KiB per depth
         case TG_CFG_128x128: return 2;
         case TG_CFG_64x64: {
             const int by_lds = (160 * 1024) / (depth * 8 * 1024);
@@ -195,7 +202,7 @@ int cfg_per_cu(int config, int depth) {
 // 16384 x 96 x 4096 (55.2 against 39.7: the 64 x 64 tile unsplit won the
 // comparison) and 384 x 4096 x 4096 (36.9 against 33.0), faster only on
 // 8192 x 128 x 8192 (38.5 against 43.0).
-int64_t cfg_slots(int config) { return config == TG_CFG_256x256 ? 256 : 512; }
+int64_t cfg_slots(int config) { return config == TG_CFG_256x256 || config == TG_CFG_288x160 ? 256 : 512; }
 
 // A thin remainder computed by a GEMM of its own (see tile_gemm.h): its
 // extents, where it starts in C, and its K split and workspace region.
@@ -287,7 +294,7 @@ tg_status make_plan(int64_t batch, int64_t M, int64_t N, int64_t K, tg_dtype dty
     }
     if (!config) config = choose_config(batch, M, N, dtype);
     const bool tail_req = o.bias_mode != 0 || o.activation != 0;   // the fused tail (tile_gemm.h)
-    if (config < TG_CFG_256x256 || config > TG_CFG_F32_64x64) return TG_ERR_INVALID_ARG;
+    if (config < TG_CFG_256x256 || config > TG_CFG_288x160) return TG_ERR_INVALID_ARG;
     if ((dtype == TG_F32) != (config == TG_CFG_F32_64x64)) return TG_ERR_UNSUPPORTED;
     // pipeline depth = LDS copies of the K tile (window = depth - 1)
     const bool f32 = config == TG_CFG_F32_64x64;
@@ -296,7 +303,8 @@ tg_status make_plan(int64_t batch, int64_t M, int64_t N, int64_t K, tg_dtype dty
     // workgroups per CU still fit 160 KiB of LDS; the 256 x 256 tile's software
     // pipeline cycles its copies four at a time
     const bool depth_ok = f32 ? (depth == 1 || depth == 2)
-                              : (depth == 1 || depth == 2 || depth == 4 || (depth == 5 && config != TG_CFG_256x256));
+                          : config == TG_CFG_288x160 ? (depth == 2 || depth == 4)
+                          : (depth == 1 || depth == 2 || depth == 4 || (depth == 5 && config != TG_CFG_256x256));
     if (!depth_ok) return TG_ERR_UNSUPPORTED;
     const int swz = o.swizzle ? o.swizzle : SWZ_XOR;
     if (swz < 0 || swz > SWZ_XOR) return TG_ERR_INVALID_ARG;
@@ -596,6 +604,20 @@ tg_status launch_dtype(const GemmParams &gp, const tg_plan_info &p, hipStream_t 
         case TG_CFG_256x256: return launch_ring<Ring256<DT>, true>(gp, p, s, tail);
         case TG_CFG_128x128: return launch_ring<Ring128<DT>, false>(gp, p, s, tail);
         case TG_CFG_64x64: return launch_ring<Ring64<DT>, false>(gp, p, s, tail);
+        case TG_CFG_288x160: {
+            // the software pipeline at depth 2 or 4; the placement ablation at depth 4
+            using C = Ring288x160<DT>;
+            if (tail) {
+                if (p.pipeline_depth == 4 && p.swizzle == SWZ_XOR)
+                    return launch_ring_one<C, 4, SWZ_XOR, SCHED_SWPIPE, true>(gp, p.grid, s);
+                return TG_ERR_UNSUPPORTED;
+            }
+            if (p.swizzle == SWZ_XOR && p.pipeline_depth == 4) return launch_ring_one<C, 4, SWZ_XOR, SCHED_SWPIPE>(gp, p.grid, s);
+            if (p.swizzle == SWZ_XOR && p.pipeline_depth == 2) return launch_ring_one<C, 2, SWZ_XOR, SCHED_SWPIPE>(gp, p.grid, s);
+            if (p.swizzle == SWZ_NONE && p.pipeline_depth == 4)
+                return launch_ring_one<C, 4, SWZ_NONE, SCHED_SWPIPE>(gp, p.grid, s);
+            return TG_ERR_UNSUPPORTED;
+        }
         default: return TG_ERR_UNSUPPORTED;
     }
 }
