@@ -352,6 +352,7 @@ def main():
     stream = torch.cuda.current_stream()
     opts = dict(config=args.config, pipeline_depth=args.pipeline_depth, swizzle=args.swizzle,
                 block_order=args.block_order, split_k=args.split_k, pack_a=args.pack_a, plan_lda=p.lda,
+                plan_ldb=p.ldb,
                 tail_gemm=args.tail_gemm, persistent=args.persistent, bias_mode=args.bias_mode,
                 activation=args.activation)
     # fused tail: one seeded bias vector shared by the batch, about the size of alpha * A.B
@@ -409,7 +410,7 @@ def main():
         q = workloads.config(args.ragged)
         print(f"# workload {q.name}: {q.batch}x{q.M}x{q.N}x{q.K} {q.dtype}", file=sys.stderr, flush=True)
         qA, qB, qC, _ = upload(q)
-        qopts = dict(plan_lda=q.lda, pipeline_depth=args.pipeline_depth, swizzle=args.swizzle,
+        qopts = dict(plan_lda=q.lda, plan_ldb=q.ldb, pipeline_depth=args.pipeline_depth, swizzle=args.swizzle,
                      block_order=args.block_order)
         q_ws = tg.tile_gemm_workspace_size(q.batch, q.M, q.N, q.K, q.dtype, **qopts)
         if q_ws:

@@ -161,6 +161,12 @@ typedef enum {
  *                workspace; TG_ERR_UNSUPPORTED for another configuration).
  * plan_lda is the lda that tile_gemm_plan and tile_gemm_workspace_size assume
  * (0: a multiple of 8); tile_gemm_ex uses its own lda and A.
+ * Repack of B: the same for B's rows when they are only 2-byte aligned (an odd
+ * ldb, or B itself on an odd 2-byte boundary) and the plan has at least 8 tile
+ * rows; B is copied into `workspace` after the A copy, with rows of
+ * roundup(N, 8) elements (batch entries packed, zero past N).  pack_b 0 / 1 / 2
+ * as pack_a (2 also for rows on 4- or 8-byte boundaries); plan_ldb is the ldb
+ * the plan queries assume (0: a multiple of 8).
  * Thin remainders (TG_CFG_256x256): an N tail of at most 64 columns (N >= 256)
  * and an M tail of at most 64 rows (M >= 256) are fringe partitions of their
  * own (OCANNL "Module Ir.Schedule": index-set splitting of a block loop at
@@ -173,7 +179,14 @@ typedef enum {
  * partials (after the A copy, N tail first).  The value is the same
  * contraction; the tail's k sum may be regrouped by its split.
  *   tail_gemm == 0 or 1: strips in the grid;
- *   tail_gemm == 2: the remainder GEMMs whenever there is a thin remainder.
+ *   tail_gemm == 2: the remainder GEMMs whenever there is a thin remainder;
+ *   tail_gemm == 3: strips in the grid, each split along K into S slices (K
+ *                   slices of a multiple of 32, S up to 16) that write unscaled
+ *                   partials into `workspace` (after the copies of A and B),
+ *                   and a combine pass over the strip region adds them in the
+ *                   fixed tree order of the split reduction and applies the
+ *                   epilogue and fused tail (the strips' k sum is regrouped);
+ *                   unsplit when the workspace is too small.
  * Persistent workgroups (16-bit, TG_CFG_256x256, depth 4, XOR swizzle, the
  * grouped block order, one problem, no split, no repack, no strips, every
  * tile interior (M and N multiples of 256), K a multiple of 128 and at least
@@ -232,6 +245,9 @@ typedef struct {
     int64_t bias_stride; /* floats between the bias vectors of batch entries          */
     int bias_mode;       /* 0 = none, 1 = per column (bias[j]), 2 = per row (bias[i]) */
     int activation;      /* 0 = none, 1 = ReLU, 2 = GELU (erf form)                  */
+    int pack_b;          /* 0 = automatic, 1 = never, 2 = always (see above)        */
+    int pad1_;
+    int64_t plan_ldb;    /* ldb assumed by the plan queries (0: a multiple of 8)    */
 } tg_options;
 
 /* tile_gemm_strided_batched with explicit schedule knobs (opt may be NULL).
@@ -269,8 +285,9 @@ typedef struct {
     int tail_m_splits;            /* the same for the M remainder                  */
     int persistent;               /* 1: persistent workgroups (grid = their count) */
     int per_cu;                   /* workgroups of this configuration one CU holds at once
-                                     (registers and LDS of the built kernel); the automatic
-                                     split counts 256 times this many slots */
+                                     (registers and LDS of the built kernel) */
+    int pack_b;                   /* 1: B is first copied to aligned rows in the workspace */
+    int strip_splits;             /* K slices of each strip block (1: not split)   */
 } tg_plan_info;
 
 tg_status tile_gemm_plan(int64_t batch, int64_t M, int64_t N, int64_t K, tg_dtype dtype,

@@ -241,6 +241,10 @@ def test_plan_tail_gemm():
         p = tg.tile_gemm_plan(*args, tail_gemm=t, **big)
         assert (p["strip_blocks"], p["tail_n_splits"], p["tail_m_splits"], p["grid"]) == (32, 0, 0, 1056)
         assert tg.tile_gemm_workspace_size(*args, tail_gemm=t) == 0
+    # split strips (3): 8 K slices of each of the 32 strip blocks, partials 8 x 8191 x 1
+    p = tg.tile_gemm_plan(*args, tail_gemm=3, **big)
+    assert (p["strip_blocks"], p["strip_splits"], p["grid"]) == (32, 8, 1024 + 8 * 32)
+    assert tg.tile_gemm_workspace_size(*args, tail_gemm=3) == tail_bytes
     # forced: 8 K slices of the one-column GEMM (about 1024 workgroups of 64 x 64)
     p = tg.tile_gemm_plan(*args, tail_gemm=2, **big)
     assert (p["strip_blocks"], p["tail_n_splits"], p["tail_m_splits"], p["grid"]) == (0, 8, 0, 1024)
@@ -264,7 +268,7 @@ def test_plan_tail_gemm():
     p = tg.tile_gemm_plan(1, 8192, 8192, 8192, "bf16", tail_gemm=2, **big)
     assert (p["strip_blocks"], p["tail_n_splits"], p["tail_m_splits"]) == (0, 0, 0)
     with pytest.raises(tg.TileGemmError):
-        tg.tile_gemm_plan(*args, tail_gemm=3)
+        tg.tile_gemm_plan(*args, tail_gemm=4)
 
 
 def test_plan_persistent():
@@ -475,3 +479,37 @@ def test_plan_one_block_per_small_problem():
     assert _plan_status(8, 257, 129, 100, "bf16", config=tg.TG_CFG_288x160, swizzle=tg.SWZ_PAD) == \
         tg.TG_ERR_UNSUPPORTED
     assert _plan_status(8, 257, 129, 100, "f32", config=tg.TG_CFG_288x160) == tg.TG_ERR_UNSUPPORTED
+
+
+def test_plan_b_repack_and_split_strips():
+    """The repack of B takes rows that are only 2-byte aligned (odd ldb) on plans with at least
+    8 tile rows; the ragged workload's ldb = N + 5 (rows 4-byte aligned) is left in place.  Its
+    32 strip blocks split into 8 K slices only on request (tail_gemm = 3)."""
+    args = (1, 8191, 8193, 8190, "bf16")
+    a_bytes = -(-8191 * 8192 * 2 // 256) * 256
+    b_bytes = -(-8190 * 8200 * 2 // 256) * 256
+    s_bytes = -(-8 * 8191 * 1 * 4 // 256) * 256
+    kw = dict(plan_lda=8193, plan_ldb=8198)
+    assert tg.tile_gemm_workspace_size(*args, **kw) == a_bytes
+    p = tg.tile_gemm_plan(*args, workspace=1 << 40, workspace_bytes=1 << 40, **kw)
+    assert (p["pack_a"], p["pack_b"], p["strip_splits"], p["grid"]) == (1, 0, 1, 1024 + 32)
+    # an odd ldb: B repacked after the A copy
+    kw = dict(plan_lda=8193, plan_ldb=8197)
+    n = tg.tile_gemm_workspace_size(*args, **kw)
+    assert n == a_bytes + b_bytes
+    p = tg.tile_gemm_plan(*args, workspace=1 << 40, workspace_bytes=n, **kw)
+    assert (p["pack_a"], p["pack_b"], p["workspace_bytes"]) == (1, 1, n)
+    # forced (2) also for 4-byte aligned rows; never (1)
+    assert tg.tile_gemm_plan(*args, workspace=1 << 40, workspace_bytes=1 << 40, pack_b=2, plan_ldb=8198)["pack_b"] == 1
+    assert tg.tile_gemm_plan(*args, workspace=1 << 40, workspace_bytes=1 << 40, pack_b=1, plan_ldb=8197)["pack_b"] == 0
+    # split strips on request, after both copies
+    n = tg.tile_gemm_workspace_size(*args, tail_gemm=3, **kw)
+    assert n == a_bytes + b_bytes + s_bytes
+    p = tg.tile_gemm_plan(*args, workspace=1 << 40, workspace_bytes=n, tail_gemm=3, **kw)
+    assert (p["pack_a"], p["pack_b"], p["strip_blocks"], p["strip_splits"], p["grid"]) == (1, 1, 32, 8, 1024 + 8 * 32)
+    # few tile rows: no B copy
+    assert tg.tile_gemm_plan(1, 1000, 8193, 8190, "bf16", workspace=1 << 40, workspace_bytes=1 << 40,
+                             plan_ldb=8197)["pack_b"] == 0
+    assert _plan_status(*args, pack_b=3) == tg.TG_ERR_INVALID_ARG
+    assert _plan_status(*args, pack_b=2, config=tg.TG_CFG_128x128) == tg.TG_ERR_UNSUPPORTED
+    assert _plan_status(*args, tail_gemm=4) == tg.TG_ERR_INVALID_ARG

@@ -1,8 +1,8 @@
 """Seeded random sweep of the call's options against the fp64 oracle, on the GPU.
 
 Each case draws, from its own fixed seed, a dtype, ragged extents (1 to 600), a batch of 1 to 3,
-leading-dimension padding, alpha and beta, a tile configuration, a split-K count, the repack of
-A, remainder GEMMs and a fused tail (bias per column or per row with a batch stride, ReLU or
+leading-dimension padding, alpha and beta, a tile configuration, a split-K count, the repacks of
+A and B, remainder GEMMs or split strips and a fused tail (bias per column or per row with a batch stride, ReLU or
 GELU).  A combination the plan refuses (TG_ERR_UNSUPPORTED) is skipped; every other case must
 match the oracle over the whole output and write nothing outside C.  The seeds are fixed, so
 the sweep is the same on every run.
@@ -47,6 +47,12 @@ def draw(seed):
     act = int(r.choice([0, 0, 1, 2]))
     if dt != "f32" and r.integers(0, 6) == 0:      # drawn last, so the draws above stay as they were
         opts["config"] = tg.TG_CFG_288x160
+    if dt != "f32":
+        opts["pack_b"] = int(r.choice([0, 0, 1, 2]))
+        if opts["pack_b"] == 2 and opts["config"] not in (0, tg.TG_CFG_256x256):
+            opts["pack_b"] = 0                      # built for the 256 x 256 tile only
+        if r.integers(0, 5) == 0:
+            opts["tail_gemm"] = 3
     return dt, M, N, K, batch, pads, alpha, beta, opts, mode, act
 
 
@@ -63,18 +69,18 @@ def test_random_case(seed):
                 * max(K, 1) ** 0.5 / 3).astype(np.float32)
     tail = dict(bias_mode=mode, activation=act)
     try:
-        tg.tile_gemm_plan(batch, M, N, K, dt, plan_lda=p.lda, workspace=1 << 40, workspace_bytes=1 << 40,
-                          **opts, **tail)
+        tg.tile_gemm_plan(batch, M, N, K, dt, plan_lda=p.lda, plan_ldb=p.ldb, workspace=1 << 40,
+                          workspace_bytes=1 << 40, **opts, **tail)
     except tg.TileGemmError as e:
         if e.status == tg.TG_ERR_UNSUPPORTED:
             pytest.skip(f"combination not built: {opts} {tail}")
         raise
-    n = tg.tile_gemm_workspace_size(batch, M, N, K, dt, plan_lda=p.lda, **opts, **tail)
+    n = tg.tile_gemm_workspace_size(batch, M, N, K, dt, plan_lda=p.lda, plan_ldb=p.ldb, **opts, **tail)
     ws = torch.empty(max(n, 16) // 4 + 4, dtype=torch.float32, device="cuda")
     gp = GpuProblem(p)
     gp.reset_c()
     try:
-        gp.run(workspace=ws, plan_lda=p.lda, bias=torch.from_numpy(bias).cuda() if bias is not None else None,
+        gp.run(workspace=ws, plan_lda=p.lda, plan_ldb=p.ldb, bias=torch.from_numpy(bias).cuda() if bias is not None else None,
                bias_stride=stride, **opts, **tail)
     except tg.TileGemmError as e:
         if e.status == tg.TG_ERR_UNSUPPORTED:

@@ -63,7 +63,8 @@ class Options(ctypes.Structure):
                 ("pack_a", ctypes.c_int), ("pad0_", ctypes.c_int), ("plan_lda", ctypes.c_int64),
                 ("tail_gemm", ctypes.c_int), ("persistent", ctypes.c_int),
                 ("bias", ctypes.c_void_p), ("bias_stride", ctypes.c_int64), ("bias_mode", ctypes.c_int),
-                ("activation", ctypes.c_int)]
+                ("activation", ctypes.c_int), ("pack_b", ctypes.c_int), ("pad1_", ctypes.c_int),
+                ("plan_ldb", ctypes.c_int64)]
 
 
 # size of the options struct in ABI version 1 (the first five ints)
@@ -80,7 +81,8 @@ class PlanInfo(ctypes.Structure):
                 ("split_k", ctypes.c_int), ("k_slice", ctypes.c_int64), ("workspace_bytes", ctypes.c_int64),
                 ("mfma_m", ctypes.c_int), ("mfma_n", ctypes.c_int), ("mfma_k", ctypes.c_int), ("pack_a", ctypes.c_int),
                 ("strip_blocks", ctypes.c_int64), ("tail_n_splits", ctypes.c_int),
-                ("tail_m_splits", ctypes.c_int), ("persistent", ctypes.c_int), ("per_cu", ctypes.c_int)]
+                ("tail_m_splits", ctypes.c_int), ("persistent", ctypes.c_int), ("per_cu", ctypes.c_int),
+                ("pack_b", ctypes.c_int), ("strip_splits", ctypes.c_int)]
 
     def as_dict(self):
         return {f: getattr(self, f) for f, _ in self._fields_}
@@ -182,13 +184,16 @@ def _dtype(d) -> int:
 
 def _options(config=0, pipeline_depth=0, swizzle=0, block_order=0, split_k=0, workspace=None,
              workspace_bytes=None, pack_a=0, plan_lda=0, tail_gemm=0, persistent=0, bias=None, bias_stride=0,
-             bias_mode=0, activation=0) -> Options:
+             bias_mode=0, activation=0, pack_b=0, plan_ldb=0, force_cfg=None) -> Options:
+    """tg_options from keyword arguments (`force_cfg` may also be given as `config`)."""
     ws = _addr(workspace)
     if workspace_bytes is None:
         workspace_bytes = workspace.numel() * workspace.element_size() if hasattr(workspace, "numel") else 0
-    return Options(ctypes.sizeof(Options), int(config), int(pipeline_depth), int(swizzle), int(block_order),
+    cfg = config if force_cfg is None else force_cfg
+    return Options(ctypes.sizeof(Options), int(cfg), int(pipeline_depth), int(swizzle), int(block_order),
                    int(split_k), ws, int(workspace_bytes), int(pack_a), 0, int(plan_lda), int(tail_gemm),
-                   int(persistent), _addr(bias), int(bias_stride), int(bias_mode), int(activation))
+                   int(persistent), _addr(bias), int(bias_stride), int(bias_mode), int(activation), int(pack_b), 0,
+                   int(plan_ldb))
 
 
 def _check(status: int, where: str):
@@ -217,28 +222,20 @@ def tile_gemm_strided_batched(batch, M, N, K, dtype, A, lda, strideA, B, ldb, st
 
 
 def tile_gemm_ex(batch, M, N, K, dtype, A, lda, strideA, B, ldb, strideB, C, ldc, strideC,
-                 alpha=1.0, beta=0.0, stream=None, config=0, pipeline_depth=0, swizzle=0,
-                 block_order=0, split_k=0, workspace=None, workspace_bytes=None, pack_a=0,
-                 plan_lda=0, tail_gemm=0, persistent=0, bias=None, bias_stride=0, bias_mode=0,
-                 activation=0, force_cfg=None) -> None:
-    """`workspace`: a device tensor or address for split-K partials or the
-    aligned copy of A (its byte size is taken from the tensor unless
-    `workspace_bytes` is given).  `force_cfg` (tg_options.force_cfg) may also be
-    given as `config`."""
-    opt = _options(config if force_cfg is None else force_cfg, pipeline_depth, swizzle, block_order, split_k, workspace, workspace_bytes, pack_a,
-                   plan_lda, tail_gemm, persistent, bias, bias_stride, bias_mode, activation)
+                 alpha=1.0, beta=0.0, stream=None, **options) -> None:
+    """tg_options as keywords (see _options): `workspace` is a device tensor or address for
+    split-K partials or the aligned copies of A and B (its byte size is taken from the tensor
+    unless `workspace_bytes` is given)."""
+    opt = _options(**options)
     _check(_lib().tile_gemm_ex(batch, M, N, K, _dtype(dtype), _addr(A), lda, strideA, _addr(B), ldb, strideB,
                                _addr(C), ldc, strideC, alpha, beta, _stream(stream), ctypes.byref(opt)),
            "tile_gemm_ex")
 
 
 def tile_gemm_ex_noalloc(batch, M, N, K, dtype, A, lda, strideA, B, ldb, strideB, C, ldc, strideC,
-                         alpha=1.0, beta=0.0, stream=None, config=0, pipeline_depth=0, swizzle=0,
-                         block_order=0, split_k=0, pack_a=0, plan_lda=0, tail_gemm=0, persistent=0, bias=None,
-                         bias_stride=0, bias_mode=0, activation=0, force_cfg=None) -> None:
+                         alpha=1.0, beta=0.0, stream=None, **options) -> None:
     """tile_gemm_ex in the library's own scratch (no workspace argument, nothing allocated)."""
-    opt = _options(config if force_cfg is None else force_cfg, pipeline_depth, swizzle, block_order, split_k,
-                   None, 0, pack_a, plan_lda, tail_gemm, persistent, bias, bias_stride, bias_mode, activation)
+    opt = _options(**options)
     _check(_lib().tile_gemm_ex_noalloc(batch, M, N, K, _dtype(dtype), _addr(A), lda, strideA, _addr(B), ldb,
                                        strideB, _addr(C), ldc, strideC, alpha, beta, _stream(stream),
                                        ctypes.byref(opt)), "tile_gemm_ex_noalloc")
@@ -249,26 +246,21 @@ def tile_gemm_status(fn: str, *args) -> int:
     return int(getattr(_lib(), fn)(*args))
 
 
-def tile_gemm_plan(batch, M, N, K, dtype, config=0, pipeline_depth=0, swizzle=0, block_order=0,
-                   split_k=0, workspace=None, workspace_bytes=None, pack_a=0, plan_lda=0, tail_gemm=0,
-                   persistent=0, bias_mode=0, activation=0, bias_stride=0, force_cfg=None) -> dict:
+def tile_gemm_plan(batch, M, N, K, dtype, **options) -> dict:
+    """The plan a call would launch; bias_mode / activation shape it, the bias itself is not read."""
     info = PlanInfo()
-    opt = _options(config if force_cfg is None else force_cfg, pipeline_depth, swizzle, block_order, split_k, workspace, workspace_bytes, pack_a,
-                   plan_lda, tail_gemm, persistent, bias_stride=bias_stride, bias_mode=bias_mode,
-                   activation=activation)
+    opt = _options(**options)
     _check(_lib().tile_gemm_plan(batch, M, N, K, _dtype(dtype), ctypes.byref(opt), ctypes.byref(info)),
            "tile_gemm_plan")
     return info.as_dict()
 
 
-def tile_gemm_workspace_size(batch, M, N, K, dtype, config=0, pipeline_depth=0, swizzle=0, block_order=0,
-                             split_k=0, pack_a=0, plan_lda=0, tail_gemm=0, persistent=0, bias_mode=0,
-                             activation=0, bias_stride=0, force_cfg=None) -> int:
+def tile_gemm_workspace_size(batch, M, N, K, dtype, **options) -> int:
     """Bytes of workspace a call with these arguments would use (split-K partials, the
-    aligned copy of A and the remainder GEMMs' partials; 0: none)."""
+    aligned copies of A and B and the remainder GEMMs' partials; 0: none)."""
     n = ctypes.c_int64(0)
-    opt = _options(config if force_cfg is None else force_cfg, pipeline_depth, swizzle, block_order, split_k, None, None, pack_a, plan_lda, tail_gemm,
-                   persistent, bias_stride=bias_stride, bias_mode=bias_mode, activation=activation)
+    options = {k: v for k, v in options.items() if k not in ("workspace", "workspace_bytes")}
+    opt = _options(**options)
     _check(_lib().tile_gemm_workspace_size(batch, M, N, K, _dtype(dtype), ctypes.byref(opt), ctypes.byref(n)),
            "tile_gemm_workspace_size")
     return int(n.value)

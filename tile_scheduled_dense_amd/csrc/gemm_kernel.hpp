@@ -82,6 +82,14 @@ struct GemmParams {
     // columns 0..).  tiles_m / tiles_n then count the main tiles only.
     int64_t strip_n, strip_m;
     int64_t n_main, m_main;
+    // Strip blocks split along K (strip_splits > 1): the grid holds
+    // strip_splits copies of the strip blocks, slice s multiplying k in
+    // [s * strip_k_slice, ...) into an unscaled fp32 partial in Ws: first the N
+    // strips' region (strip_rows_n x (N - n_main) per slice and problem), then
+    // the M strips' ((M - m_main) x N).
+    int strip_splits;
+    int64_t strip_k_slice, strip_rows_n;
+    float *Ws;
     // Fused elementwise tail (bias_mode or act nonzero): out = act(alpha * acc
     // + bias) + beta * C0, the bias one value per column (bias_mode 1) or per
     // row (2) of each problem, problem b's vector at bias + b * bias_stride.

@@ -817,6 +817,31 @@ __device__ __forceinline__ GemmParams entry_params(const GemmParams &p, int64_t 
     return q;
 }
 
+// A strip block's K slice (strip_splits > 1): its k range, and C pointed at the
+// slice's partial of the strip region so that the strip's own (m0, n0)
+// addressing lands there (row stride: the region's width).
+__device__ __forceinline__ GemmParams strip_slice_params(const GemmParams &p, GemmParams q, int64_t b,
+                                                         int64_t slice, bool n_strip) {
+    const int64_t k0 = slice * p.strip_k_slice;
+    q.A = q.A + k0 * 2;
+    q.B = q.B + k0 * q.ldb * 2;
+    q.K = p.K - k0 < p.strip_k_slice ? p.K - k0 : p.strip_k_slice;
+    q.alpha = 1.0f;
+    q.beta = 0.0f;
+    q.bias_mode = 0;
+    q.act = 0;
+    const int64_t wn = p.N - p.n_main, rows_n = p.strip_rows_n, rows_m = p.M - p.m_main;
+    if (n_strip) {
+        q.C = p.Ws + (slice * p.batch + b) * rows_n * wn - p.n_main;
+        q.ldc = wn;
+    } else {
+        const int64_t n_region = p.strip_n ? p.strip_splits * p.batch * rows_n * wn : 0;
+        q.C = p.Ws + n_region + (slice * p.batch + b) * rows_m * p.N - p.m_main * p.N;
+        q.ldc = p.N;
+    }
+    return q;
+}
+
 template <class C, int STAGES, int SWZ, int SCHED, bool FRINGE, bool TAIL>
 __device__ __forceinline__ void run_tile(const GemmParams &q, char *smem, int64_t tm, int64_t tn) {
     if constexpr (SCHED == SCHED_SWPIPE) ring_tile_swpipe<C, STAGES, SWZ, FRINGE, TAIL>(q, smem, 0, tm, tn);
@@ -838,9 +863,12 @@ __global__ __launch_bounds__(C::THREADS, C::OCCUPANCY) void gemm_ring_kernel(Gem
         const int64_t main_blocks = p.tiles_m * p.tiles_n * p.batch;
         if ((int64_t)blockIdx.x >= main_blocks) {
             const int64_t per = p.strip_n + p.strip_m;
-            const int64_t s = (int64_t)blockIdx.x - main_blocks;
+            int64_t s = (int64_t)blockIdx.x - main_blocks;
+            const int64_t slice = s / (per * p.batch);       // 0 unless the strips are split along K
+            s -= slice * per * p.batch;
             const int64_t b = s / per, r = s - b * per;
-            const GemmParams q = entry_params(p, b);
+            GemmParams q = entry_params(p, b);
+            if (p.strip_splits > 1) q = strip_slice_params(p, q, b, slice, r < p.strip_n);
             if (r < p.strip_n) run_tile<SN, STAGES, SWZ, SCHED, true, TAIL>(q, smem, r, p.n_main / SN::BN);
             else run_tile<SM, STAGES, SWZ, SCHED, true, TAIL>(q, smem, p.m_main / SM::BM, r - p.strip_n);
             return;

@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <cstddef>
 #include <cstring>
 #include <mutex>
 #include <new>
@@ -220,14 +221,18 @@ struct Plan {
     void *workspace = nullptr;         // set when the call splits or repacks A
     int64_t workspace_given = 0;
     int64_t lda_packed = 0;            // row stride of the A copy (elements)
+    int64_t ldb_packed = 0;            // row stride of the B copy (elements)
+    int64_t strip_k_slice = 0, strip_rows_n = 0, strip_ws_offset = 0;   // strips split along K
+    int64_t b_offset = 0;              // workspace bytes before the B copy (the A copy)
 };
 
 inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
-// lda: the call's (or, for the plan queries, the assumed) leading dimension of
-// A; a_aligned: A itself starts on a 16-byte boundary.
+// lda, ldb: the call's (or, for the plan queries, the assumed) leading
+// dimensions of A and B; a_aligned: A itself starts on a 16-byte boundary;
+// b_two_byte: B's rows start on boundaries only 2-byte aligned (odd ldb or B).
 tg_status make_plan(int64_t batch, int64_t M, int64_t N, int64_t K, tg_dtype dtype,
-                    const tg_options *opt, int64_t lda, bool a_aligned, Plan &out) {
+                    const tg_options *opt, int64_t lda, bool a_aligned, int64_t ldb, bool b_two_byte, Plan &out) {
     if (batch < 0 || M < 0 || N < 0 || K < 0) return TG_ERR_INVALID_ARG;
     if (dtype != TG_F32 && dtype != TG_BF16 && dtype != TG_F16) return TG_ERR_INVALID_ARG;
     tg_options o{};
@@ -247,7 +252,7 @@ tg_status make_plan(int64_t batch, int64_t M, int64_t N, int64_t K, tg_dtype dty
     int config = o.force_cfg;
     // An always-repacked A (pack_a == 2) is built for the unsplit 256 x 256
     // tile: with the tile left to the library, that is the tile, unsplit.
-    const bool pin256 = sixteen && o.pack_a == 2 && config == TG_CFG_AUTO;
+    const bool pin256 = sixteen && (o.pack_a == 2 || o.pack_b == 2) && config == TG_CFG_AUTO;
     if (pin256) config = TG_CFG_256x256;
     if (sixteen && some && o.split_k == 0 && !pin256) {
         // With a forced tile, that tile's own count.  Otherwise each tile with its
@@ -395,6 +400,31 @@ tg_status make_plan(int64_t batch, int64_t M, int64_t N, int64_t K, tg_dtype dty
             }
         }
     }
+    // Repack of B (see tile_gemm.h), after the A copy: rows only 2-byte aligned
+    // (an odd ldb, or B itself on an odd 2-byte boundary), a plan whose B panels
+    // are each read by many workgroups (at least 8 tile rows), no split.  Rows on
+    // 4- or 8-byte boundaries cost their copies 17% more, less than the copy of
+    // B: on 8191 x 8193 x 8190 (ldb = N + 5, rows 4-byte aligned) the repack made
+    // the call 1052 us against 1000.
+    if (o.pack_b < 0 || o.pack_b > 2) return TG_ERR_INVALID_ARG;
+    if (o.pack_b == 2 && (!sixteen || config != TG_CFG_256x256 || splits > 1)) return TG_ERR_UNSUPPORTED;
+    if (sixteen && some && config == TG_CFG_256x256 && splits == 1 && o.pack_b != 1) {
+        const int64_t ldp = round_up(N, 8);
+        const int64_t bytes_b = round_up(batch * K * ldp * 2, 256);
+        const bool worth = b_two_byte && p.tiles_m >= 8;
+        if (o.pack_b == 2 || worth) {
+            wanted_pack += bytes_b;
+            out.wanted_workspace = out.wanted_workspace > wanted_pack ? out.wanted_workspace : wanted_pack;
+            if (o.pack_b == 2 || (o.workspace && o.workspace_bytes >= used + bytes_b)) {
+                p.pack_b = 1;
+                out.ldb_packed = ldp;
+                out.b_offset = used;
+                used += bytes_b;
+                p.workspace_bytes = used;
+                out.workspace = o.workspace;
+            }
+        }
+    }
 
     // Thin remainders as GEMMs of their own (tile_gemm.h), when asked: each
     // tail is split along K until it has about 1024 workgroups of the 64 x 64
@@ -402,7 +432,7 @@ tg_status make_plan(int64_t batch, int64_t M, int64_t N, int64_t K, tg_dtype dty
     // copy holds the partials.  Not chosen automatically: on 8191 x 8193 x
     // 8190 the 32 strips that follow the 1024 main tiles cost the grid about
     // 8 us, the separate GEMM and its combine about 33 us.
-    if (o.tail_gemm < 0 || o.tail_gemm > 2) return TG_ERR_INVALID_ARG;
+    if (o.tail_gemm < 0 || o.tail_gemm > 3) return TG_ERR_INVALID_ARG;
     if (o.persistent < 0 || o.persistent > 2) return TG_ERR_INVALID_ARG;
     // the bias pointer itself is checked by the call (a plan query needs only the modes)
     if (o.bias_mode < 0 || o.bias_mode > 2 || o.activation < 0 || o.activation > 2 || o.bias_stride < 0 ||
@@ -446,12 +476,50 @@ tg_status make_plan(int64_t batch, int64_t M, int64_t N, int64_t K, tg_dtype dty
         }
     }
 
+    // Thin strips split along K, on request (tail_gemm == 3, tile_gemm.h): each
+    // strip block becomes S K slices (S doubled while the slices fill at most
+    // the 256 slots and keep at least 512 of K), whose partials follow the
+    // copies in the workspace; a combine pass over the strip region finishes
+    // them.  Not chosen automatically: on 8191 x 8193 x 8190 the 32 strips, a
+    // fifth round after 1024 main tiles, split 8 ways made the call 1011 us
+    // against 1000 (the whole strips overlap the main tiles' uneven ends; the
+    // split ones still read all of A and add a combine pass).
+    p.strip_splits = 1;
+    if (sixteen && some && out.strip_n + out.strip_m > 0 && splits == 1 && o.tail_gemm == 3) {
+        const int64_t strips = (out.strip_n + out.strip_m) * batch;
+        const int64_t slots = cfg_slots(TG_CFG_256x256);
+        int64_t sp = 1;
+        while (2 * sp <= 16 && strips * 2 * sp <= slots && K / (2 * sp) >= 512) sp *= 2;
+        if (sp > 1) {
+            const int64_t k_slice_s = cdiv(cdiv(K, sp), d.bk) * d.bk;
+            const int64_t s_eff = cdiv(K, k_slice_s);
+            const int64_t n_main = p.tiles_n * d.bn, m_main = p.tiles_m * d.bm;
+            const int64_t rows_n = out.strip_m ? m_main : M;
+            const int64_t floats = s_eff * batch * ((out.strip_n ? rows_n * (N - n_main) : 0) +
+                                                    (out.strip_m ? (M - m_main) * N : 0));
+            const int64_t bytes = round_up(floats * 4, 256);
+            const int64_t wanted = wanted_pack + bytes;
+            out.wanted_workspace = out.wanted_workspace > wanted ? out.wanted_workspace : wanted;
+            if (s_eff > 1 && o.workspace && o.workspace_bytes >= used + bytes) {
+                p.strip_splits = (int)s_eff;
+                out.strip_k_slice = k_slice_s;
+                out.strip_rows_n = rows_n;
+                out.strip_ws_offset = used;
+                used += bytes;
+                p.workspace_bytes = used;
+                out.workspace = o.workspace;
+                p.grid += (s_eff - 1) * strips;
+            }
+        }
+    }
+
     // Persistent workgroups (tile_gemm.h), on request: a whole grid of
     // interior tiles of one problem, K in whole groups of four K tiles, at
     // least two tiles per workgroup.
     constexpr int64_t kPersistentBlocks = 256;
     if (sixteen && some && o.persistent == 2 && !tail_req && config == TG_CFG_256x256 && depth == 4 &&
-        swz == SWZ_XOR && order == 0 && batch == 1 && splits == 1 && !p.pack_a && p.strip_blocks == 0 && M % 256 == 0 &&
+        swz == SWZ_XOR && order == 0 && batch == 1 && splits == 1 && !p.pack_a && !p.pack_b && p.strip_blocks == 0 &&
+        M % 256 == 0 &&
         N % 256 == 0 && K % (4 * d.bk) == 0 && K >= 8 * d.bk && p.tiles_m * p.tiles_n >= 2 * kPersistentBlocks) {
         p.persistent = 1;
         p.grid = kPersistentBlocks;
@@ -632,7 +700,8 @@ tg_status run(int64_t batch, int64_t M, int64_t N, int64_t K, tg_dtype dtype,
     tg_status st = validate(batch, M, N, K, dtype, A, lda, sA, B, ldb, sB, C, ldc, sC);
     if (st != TG_OK) return st;
     Plan plan;
-    st = make_plan(batch, M, N, K, dtype, opt, lda, reinterpret_cast<uintptr_t>(A) % 16 == 0, plan);
+    st = make_plan(batch, M, N, K, dtype, opt, lda, reinterpret_cast<uintptr_t>(A) % 16 == 0, ldb,
+                   ldb % 2 != 0 || reinterpret_cast<uintptr_t>(B) % 4 != 0, plan);
     if (st != TG_OK) return st;
     // the fused tail (modes validated by make_plan): the caller's struct may predate it
     tg_options to{};
@@ -642,8 +711,9 @@ tg_status run(int64_t batch, int64_t M, int64_t N, int64_t K, tg_dtype dtype,
     if (!offsets_fit(plan.info, K, lda, ldb, ldc, dtype == TG_F32 ? 4 : 2)) return TG_ERR_UNSUPPORTED;
     const bool split = plan.info.split_k > 1;
     const bool pack = plan.info.pack_a != 0;
-    const bool tail_ws = plan.tail_n.ws_bytes > 0 || plan.tail_m.ws_bytes > 0;
-    if (split || pack || tail_ws) {
+    const bool pack_b = plan.info.pack_b != 0;
+    const bool tail_ws = plan.tail_n.ws_bytes > 0 || plan.tail_m.ws_bytes > 0 || plan.info.strip_splits > 1;
+    if (split || pack || pack_b || tail_ws) {
         // a forced split or repack needs the workspace; an automatic one only happens with it
         if (!plan.workspace || plan.workspace_given < plan.info.workspace_bytes ||
             reinterpret_cast<uintptr_t>(plan.workspace) % 16)
@@ -655,7 +725,11 @@ tg_status run(int64_t batch, int64_t M, int64_t N, int64_t K, tg_dtype dtype,
             overlaps(rw, span(C, batch, M, N, ldc, sC, 4)))
             return TG_ERR_INVALID_ARG;
         if (split && !offsets_fit(plan.info, plan.info.k_slice, lda, ldb, N, esz)) return TG_ERR_UNSUPPORTED;
-        if (pack && (!offsets_fit(plan.info, K, plan.lda_packed, ldb, ldc, esz) || batch * M > 0x7fffffffLL))
+        const int64_t ldb_used = pack_b ? plan.ldb_packed : ldb;
+        if (pack && (!offsets_fit(plan.info, K, plan.lda_packed, ldb_used, ldc, esz) || batch * M > 0x7fffffffLL))
+            return TG_ERR_UNSUPPORTED;
+        if (pack_b && (!offsets_fit(plan.info, K, pack ? plan.lda_packed : lda, ldb_used, ldc, esz) ||
+                       batch * K > 0x7fffffffLL))
             return TG_ERR_UNSUPPORTED;
     }
     st = current_device_ok();
@@ -702,6 +776,12 @@ tg_status run(int64_t batch, int64_t M, int64_t N, int64_t K, tg_dtype dtype,
     gp.strip_m = plan.strip_m;
     gp.n_main = plan.info.tiles_n * plan.info.block_n;
     gp.m_main = plan.info.tiles_m * plan.info.block_m;
+    gp.strip_splits = plan.info.strip_splits;
+    gp.strip_k_slice = plan.strip_k_slice;
+    gp.strip_rows_n = plan.strip_rows_n;
+    gp.Ws = plan.info.strip_splits > 1
+                ? reinterpret_cast<float *>(static_cast<char *>(plan.workspace) + plan.strip_ws_offset)
+                : nullptr;
     gp.bias = to.bias;
     gp.bias_stride = to.bias_stride;
     gp.bias_mode = to.bias_mode;
@@ -715,6 +795,16 @@ tg_status run(int64_t batch, int64_t M, int64_t N, int64_t K, tg_dtype dtype,
         gp.A = static_cast<const char *>(plan.workspace);
         gp.lda = plan.lda_packed;
         gp.sA = M * plan.lda_packed;
+        gp.W = nullptr;
+    }
+    if (pack_b) {
+        // B -> aligned rows of ldb_packed elements after the A copy
+        char *dst = static_cast<char *>(plan.workspace) + plan.b_offset;
+        st = launch_pack_rows(2, B, ldb, sB, dst, plan.ldb_packed, K, N, batch * K, s);
+        if (st != TG_OK) return st;
+        gp.B = dst;
+        gp.ldb = plan.ldb_packed;
+        gp.sB = K * plan.ldb_packed;
         gp.W = nullptr;
     }
     // the fused tail in the GEMM's own epilogue; a split call leaves it to the combine
@@ -731,6 +821,25 @@ tg_status run(int64_t batch, int64_t M, int64_t N, int64_t K, tg_dtype dtype,
     if (split)
         return launch_combine(gp.W, C, M, N, ldc, sC, batch, plan.info.split_k, alpha, beta, to.bias,
                               to.bias_stride, to.bias_mode, to.activation, s);
+    if (plan.info.strip_splits > 1) {
+        // the strip regions' partials: N strips (rows [0, strip_rows_n), columns
+        // [n_main, N)), then M strips (rows [m_main, M), all columns)
+        const int S = plan.info.strip_splits;
+        const int64_t wn = N - gp.n_main, rows_m = M - gp.m_main;
+        const float *bias_n = to.bias_mode == 1 ? to.bias + gp.n_main : to.bias;
+        const float *bias_m = to.bias_mode == 2 ? to.bias + gp.m_main : to.bias;
+        if (plan.strip_n) {
+            st = launch_combine(gp.Ws, C + gp.n_main, gp.strip_rows_n, wn, ldc, sC, batch, S, alpha, beta, bias_n,
+                                to.bias_stride, to.bias_mode, to.activation, s);
+            if (st != TG_OK) return st;
+        }
+        if (plan.strip_m) {
+            const float *w = gp.Ws + (plan.strip_n ? (int64_t)S * batch * gp.strip_rows_n * wn : 0);
+            st = launch_combine(w, C + gp.m_main * ldc, rows_m, N, ldc, sC, batch, S, alpha, beta, bias_m,
+                                to.bias_stride, to.bias_mode, to.activation, s);
+            if (st != TG_OK) return st;
+        }
+    }
     // the thin remainders' own GEMMs (on the A copy when there is one)
     for (const Tail *t : {&plan.tail_n, &plan.tail_m}) {
         if (t->splits == 0) continue;
@@ -747,8 +856,9 @@ tg_status run(int64_t batch, int64_t M, int64_t N, int64_t K, tg_dtype dtype,
         sub.bias_stride = to.bias_stride;
         sub.bias_mode = to.bias_mode;
         sub.activation = to.activation;
-        st = run(batch, t->rows, t->cols, K, dtype, gp.A + t->m0 * gp.lda * 2, gp.lda, gp.sA, gp.B + t->n0 * 2, ldb,
-                 sB, C + t->m0 * ldc + t->n0, ldc, sC, alpha, beta, stream, &sub);
+        sub.pack_b = 1;
+        st = run(batch, t->rows, t->cols, K, dtype, gp.A + t->m0 * gp.lda * 2, gp.lda, gp.sA, gp.B + t->n0 * 2,
+                 gp.ldb, gp.sB, C + t->m0 * ldc + t->n0, ldc, sC, alpha, beta, stream, &sub);
         if (st != TG_OK) return st;
     }
     return TG_OK;
@@ -846,7 +956,8 @@ tg_status run_noalloc(int64_t batch, int64_t M, int64_t N, int64_t K, tg_dtype d
         q.workspace = reinterpret_cast<void *>(uintptr_t(256));
         q.workspace_bytes = TILE_GEMM_NOALLOC_SCRATCH_BYTES;
         Plan plan;
-        st = make_plan(batch, M, N, K, dtype, &q, lda, reinterpret_cast<uintptr_t>(A) % 16 == 0, plan);
+        st = make_plan(batch, M, N, K, dtype, &q, lda, reinterpret_cast<uintptr_t>(A) % 16 == 0, ldb,
+                       ldb % 2 != 0 || reinterpret_cast<uintptr_t>(B) % 4 != 0, plan);
         if (st != TG_OK) return st;
         if (plan.info.workspace_bytes > TILE_GEMM_NOALLOC_SCRATCH_BYTES) return TG_ERR_SCRATCH_LIMIT;
     }
@@ -859,6 +970,17 @@ tg_status run_noalloc(int64_t batch, int64_t M, int64_t N, int64_t K, tg_dtype d
     o.workspace = ws;
     o.workspace_bytes = TILE_GEMM_NOALLOC_SCRATCH_BYTES;
     return run(batch, M, N, K, dtype, A, lda, sA, B, ldb, sB, C, ldc, sC, alpha, beta, stream, &o);
+}
+
+// The leading dimension the plan queries assume for A (or B): plan_lda
+// (plan_ldb) when the caller's struct has it and it is positive, else 8 (a
+// multiple of 8: aligned rows).
+int64_t plan_ld(const tg_options *opt, bool a) {
+    if (!opt) return 8;
+    const size_t need = a ? offsetof(tg_options, plan_lda) + sizeof(int64_t) : offsetof(tg_options, plan_ldb) + sizeof(int64_t);
+    if (opt->struct_size < (int)need) return 8;
+    const int64_t ld = a ? opt->plan_lda : opt->plan_ldb;
+    return ld > 0 ? ld : 8;
 }
 
 }  // namespace
@@ -911,8 +1033,8 @@ tg_status tile_gemm_plan(int64_t batch, int64_t M, int64_t N, int64_t K, tg_dtyp
     if (!out) return TG_ERR_INVALID_ARG;
     try {
         Plan p;
-        tg_status st = make_plan(batch, M, N, K, dtype, opt, opt && opt->struct_size >= (int)sizeof(tg_options) &&
-                                 opt->plan_lda > 0 ? opt->plan_lda : 8, true, p);
+        const int64_t ldb = plan_ld(opt, false);
+        tg_status st = make_plan(batch, M, N, K, dtype, opt, plan_ld(opt, true), true, ldb, ldb % 2 != 0, p);
         if (st == TG_OK) *out = p.info;
         return st;
     } catch (...) {
@@ -925,8 +1047,8 @@ tg_status tile_gemm_workspace_size(int64_t batch, int64_t M, int64_t N, int64_t 
     if (!bytes) return TG_ERR_INVALID_ARG;
     try {
         Plan p;
-        tg_status st = make_plan(batch, M, N, K, dtype, opt, opt && opt->struct_size >= (int)sizeof(tg_options) &&
-                                 opt->plan_lda > 0 ? opt->plan_lda : 8, true, p);
+        const int64_t ldb = plan_ld(opt, false);
+        tg_status st = make_plan(batch, M, N, K, dtype, opt, plan_ld(opt, true), true, ldb, ldb % 2 != 0, p);
         if (st == TG_OK) *bytes = p.wanted_workspace;
         return st;
     } catch (...) {
