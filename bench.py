@@ -10,13 +10,15 @@ The metric covers square and ragged extents, so with the default workload the
 same run then times the ragged problem (bf16 8191 x 8193 x 8190, lda = K + 3,
 ldb = N + 5, alpha = 1.5, beta = 0.5) the same way, W warm-up and K timed
 steps of its own, and reports it in the line's "ragged" object.  During every
-timed region the shader clock is sampled from the GPU's hwmon file
-(freq1_input; a file read, no program is started).
+timed region the driver's current shader-clock level (pp_dpm_sclk) and the
+board power (hwmon power1_input) are sampled (file reads, no program is
+started).
 
   python bench.py [--steps K] [--warmup W] [--workload NAME] [--ragged NAME|none] [--no-cpu-baseline]
 
 The CPU-baseline leg times the fp64 oracle (test infrastructure, untuned) on a
-bounded band of output rows of the same workload.
+bounded band of output rows of the same workload, and on the whole small fp32
+problem (67 x 45 x 53) on one thread and on all of them.
 """
 from __future__ import annotations
 
@@ -102,6 +104,28 @@ def cpu_baseline(p, seconds, bias=None, bias_mode=0, activation=0):
     return {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": f"output rows 0..{rows_done - 1} of {p.name} ({rows_done}x{p.N}x{p.K}, batch 0), "
                       f"fp64 triple loop, {t_total:.1f} s"}
+
+
+def oracle_small_latency(reps=200):
+    """The oracle on the whole small fp32 problem (67x45x53), mean wall time per call on one
+    thread and on all of them (a latency, not a throughput: the problem is 3.2e5 flops)."""
+    import oracle
+    import workloads
+    q = workloads.config("c1_f32_67x45x53")
+    out = {"problem": f"{q.name} ({q.M}x{q.N}x{q.K}, whole output)", "reps": reps}
+    threads = oracle.max_threads()
+    try:
+        for n, key in ((1, "one_thread_us"), (threads, "all_threads_us")):
+            oracle.set_threads(n)
+            oracle.gemm(q.M, q.N, q.K, q.dtype, q.A, q.lda, q.B, q.ldb, ldc=q.ldc)    # warm
+            t = time.perf_counter()
+            for _ in range(reps):
+                oracle.gemm(q.M, q.N, q.K, q.dtype, q.A, q.lda, q.B, q.ldb, ldc=q.ldc)
+            out[key] = round((time.perf_counter() - t) / reps * 1e6, 1)
+        out["threads"] = threads
+    finally:
+        oracle.set_threads(threads)
+    return out
 
 
 def oracle_rows(p, rows, bias=None, bias_mode=0, activation=0):
@@ -487,6 +511,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(p, args.cpu_seconds, bias_np, args.bias_mode, args.activation)
+        cpu["small_fp32_oracle"] = oracle_small_latency()
         # the observed parity error on the oracle's first rows: one fresh call
         # (C reset to C0), compared with the stated metric
         rows = min(8, p.M)

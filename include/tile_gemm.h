@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define TILE_GEMM_ABI_VERSION 8
+#define TILE_GEMM_ABI_VERSION 9
 
 typedef enum { TG_F32 = 0, TG_BF16 = 1, TG_F16 = 2 } tg_dtype;
 
@@ -98,10 +98,13 @@ tg_status tile_gemm_strided_batched(int64_t batch, int64_t M, int64_t N, int64_t
  * Ir.Schedule", Split paragraph) with their MFMA register tiles (Tensorize). */
 typedef enum {
     TG_CFG_AUTO = 0,
-    TG_CFG_256x256 = 1,     /* 16-bit inputs: 256x256 block tile, 4 waves, 16x16x32 MFMA */
-    TG_CFG_128x128 = 2,     /* 16-bit inputs: 128x128 block tile, 4 waves        */
+    TG_CFG_256x256 = 1,     /* 256x256 block tile on the LDS ring, 4 waves: 16x16x32 MFMA for
+                               16-bit inputs, 16x16x4 for fp32 (version 9 and later) */
+    TG_CFG_128x128 = 2,     /* 128x128 block tile on the LDS ring, 4 waves: 32x32x16 MFMA for
+                               16-bit inputs, 16x16x4 for fp32 (version 9 and later) */
     TG_CFG_64x64 = 3,       /* 16-bit inputs: 64x64 block tile, 2 waves          */
-    TG_CFG_F32_64x64 = 4,   /* fp32 inputs: 64x64 block tile, 4 waves            */
+    TG_CFG_F32_64x64 = 4,   /* fp32 inputs: 64x64 block tile, 4 waves, staged through
+                               registers (small problems; no split-K)           */
     TG_CFG_288x160 = 5      /* 16-bit inputs: 288x160 block tile, 4 waves, 16x16x32: one
                                block per problem of up to 288 x 160 (batched small GEMMs) */
 } tg_config;
@@ -115,21 +118,23 @@ typedef enum {
  * less; OCANNL "Module Ir.Schedule", Stage paragraph, pipeline_depth, and
  * LuisaCompute "Pipelines and stage boundaries", window): 16-bit inputs take 1,
  * 2 or 4 (default 4; 5 for TG_CFG_128x128 and TG_CFG_64x64; 2 or 4 for
- * TG_CFG_288x160), fp32 inputs 1 or 2 (default 2).  Depth 1 is the unpipelined
- * form.
+ * TG_CFG_288x160), and so do fp32 inputs on TG_CFG_128x128 (on TG_CFG_256x256:
+ * 2 or 4); fp32 inputs on TG_CFG_F32_64x64 take 1 or 2 (default 2).  Depth 1 is the
+ * unpipelined form.
  *
  * swizzle is the placement of the staged tiles in LDS (OCANNL Stage paragraph,
  * swizzle and pad_stride; TVM TIRx "Tensor Layout", SwizzleLayout): 0 the
  * default (XOR); 1 none, the row-major tile; 2 pad_stride, the row-major tile
  * with its minor dimension rounded up by one 16-byte unit (A rows of 32 k at a
- * pitch of 40, B rows of BN n at BN + 8; built for TG_CFG_256x256 at depth 4,
- * UNSUPPORTED elsewhere); 3 the XOR swizzle of 16-byte units (Swizzle_b128
+ * pitch of 40, B rows of BN n at BN + 8; built for TG_CFG_256x256 with 16-bit
+ * inputs at depth 4, UNSUPPORTED elsewhere); 3 the XOR swizzle of 16-byte units (Swizzle_b128
  * flavour).  Placement changes which LDS bytes hold a value, never the value:
  * every placement gives a bitwise identical C.  (Version 7 and earlier: 2 was
  * the XOR swizzle.)
  *
- * Split-K (16-bit inputs): the deterministic two-pass split reduction of the
- * OCANNL "Module Ir.Schedule" page (paragraph of that name).  The K range is
+ * Split-K (16-bit inputs, and fp32 inputs on the ring tiles): the
+ * deterministic two-pass split reduction of the OCANNL "Module Ir.Schedule"
+ * page (paragraph of that name).  The K range is
  * cut into S slices of a multiple of block_k elements (the last one shorter);
  * each slice's product goes, unscaled, to its own fp32 M x N partial in
  * `workspace` (slice s of problem b at float offset (s * batch + b) * M * N),
@@ -355,7 +360,11 @@ typedef enum { TG_LAYOUT_LDS_A = 0, TG_LAYOUT_LDS_B = 1, TG_LAYOUT_ACC = 2,
 /* The introspection calls below take a tg_config, or one of these ids for the
  * thin fringe-strip blocks of TG_CFG_256x256 (256 x 64 for an N tail of at
  * most 64 columns, 64 x 256 for an M tail of at most 64 rows). */
-enum { TG_LAYOUT_CFG_STRIP_N = 101, TG_LAYOUT_CFG_STRIP_M = 102 };
+enum { TG_LAYOUT_CFG_STRIP_N = 101, TG_LAYOUT_CFG_STRIP_M = 102,
+       /* the same tiles for fp32 inputs (K tile 16, 16x16x4 MFMAs): TG_CFG_256x256,
+        * TG_CFG_128x128 and the 256x256 tile's strips (version 9 and later) */
+       TG_LAYOUT_CFG_F32_256 = 103, TG_LAYOUT_CFG_F32_128 = 104,
+       TG_LAYOUT_CFG_F32_STRIP_N = 105, TG_LAYOUT_CFG_F32_STRIP_M = 106 };
 
 tg_status tile_gemm_describe_layout(int config, int swizzle, int kind, tg_layout *out);
 

@@ -82,6 +82,8 @@ class OracleLibrary:
         lib.oracle_decode_f16.argtypes = [ctypes.c_uint16]
         lib.oracle_decode_f16.restype = dbl
         lib.oracle_max_threads.restype = ctypes.c_int
+        lib.oracle_set_threads.argtypes = [ctypes.c_int]
+        lib.oracle_set_threads.restype = None
         lib.oracle_tail.argtypes = [i64, i64, i64, vp, i64, i64, vp, i64, ctypes.c_int, ctypes.c_int,
                                     vp, i64, i64, dbl]
         lib.oracle_tail.restype = ctypes.c_int
@@ -160,6 +162,9 @@ class OracleLibrary:
     def max_threads(self) -> int:
         return int(self.lib.oracle_max_threads())
 
+    def set_threads(self, n: int) -> None:
+        self.lib.oracle_set_threads(int(n))
+
 
 _default = None
 
@@ -194,3 +199,7 @@ def decode(bits, dtype):
 
 def max_threads() -> int:
     return _lib().max_threads()
+
+
+def set_threads(n: int) -> None:
+    _lib().set_threads(n)

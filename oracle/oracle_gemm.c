@@ -248,3 +248,14 @@ int oracle_max_threads(void) {
     return 1;
 #endif
 }
+
+/* Threads for the following calls (n >= 1); a timing control only, the
+ * arithmetic of every output is the same on any number of threads. */
+void oracle_set_threads(int n) {
+#ifdef _OPENMP
+    extern void omp_set_num_threads(int);
+    if (n >= 1) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}

@@ -28,7 +28,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert tg.abi_version() == tg.ABI_VERSION == 8
+    assert tg.abi_version() == tg.ABI_VERSION == 9
     for s in range(6):
         assert tg.STATUS_NAMES[s] in tg.status_string(s)
 
@@ -90,7 +90,11 @@ def test_options_validation():
     with pytest.raises(tg.TileGemmError):
         tg.tile_gemm_plan(1, 8, 8, 8, "bf16", pipeline_depth=3)
     with pytest.raises(tg.TileGemmError):
-        tg.tile_gemm_plan(1, 8, 8, 8, "f32", config=tg.TG_CFG_256x256)   # fp32 has its own tile
+        tg.tile_gemm_plan(1, 8, 8, 8, "f32", config=tg.TG_CFG_64x64)     # the 16-bit 64 x 64 ring tile
+    with pytest.raises(tg.TileGemmError):
+        tg.tile_gemm_plan(1, 8, 8, 8, "f32", config=tg.TG_CFG_288x160)
+    with pytest.raises(tg.TileGemmError):
+        tg.tile_gemm_plan(1, 8, 8, 8, "bf16", config=tg.TG_CFG_F32_64x64)
     with pytest.raises(tg.TileGemmError):
         tg.tile_gemm_plan(1, 8, 8, 8, "bf16", swizzle=5)
 
@@ -513,3 +517,51 @@ def test_plan_b_repack_and_split_strips():
     assert _plan_status(*args, pack_b=3) == tg.TG_ERR_INVALID_ARG
     assert _plan_status(*args, pack_b=2, config=tg.TG_CFG_128x128) == tg.TG_ERR_UNSUPPORTED
     assert _plan_status(*args, tail_gemm=4) == tg.TG_ERR_INVALID_ARG
+
+
+def test_plan_fp32_ring_tiles():
+    # fp32 inputs on the LDS ring: 256 x 256 and 128 x 128 block tiles with 16x16x4 MFMAs and a
+    # K tile of 16 (64-byte A rows), chosen by the 16-bit rule; the register-staged 64 x 64 tile
+    # for problems that fill the GPU with neither
+    info = tg.tile_gemm_plan(1, 8192, 8192, 8192, "f32")
+    assert (info["config"], info["block_m"], info["block_n"], info["block_k"]) == (tg.TG_CFG_256x256, 256, 256, 16)
+    assert (info["mfma_m"], info["mfma_k"], info["grid"], info["k_tiles"]) == (16, 4, 1024, 512)
+    assert (info["pipeline_depth"], info["lds_bytes"], info["per_cu"]) == (4, 4 * (16384 + 16384), 1)
+    info = tg.tile_gemm_plan(1, 2048, 2048, 2048, "f32")
+    assert (info["config"], info["block_k"], info["lds_bytes"], info["per_cu"]) == (tg.TG_CFG_128x128, 16,
+                                                                                      4 * (8192 + 8192), 2)
+    assert tg.tile_gemm_plan(1, 67, 45, 53, "f32")["config"] == tg.TG_CFG_F32_64x64
+    # ragged: thin strips beside the 256 x 256 tiles, as for 16-bit inputs
+    info = tg.tile_gemm_plan(1, 8191, 8193, 8190, "f32")
+    assert (info["config"], info["strip_blocks"], info["k_tail"]) == (tg.TG_CFG_256x256, 32, 8190 % 16)
+    # depths: 2 or 4 on the 256 x 256 tile, 1, 2, 4 or 5 on the 128 x 128 tile
+    for d in (2, 4):
+        assert tg.tile_gemm_plan(1, 4096, 4096, 4096, "f32", config=tg.TG_CFG_256x256, pipeline_depth=d)["lds_bytes"] \
+            == d * 32768
+    for d in (1, 3, 5):
+        with pytest.raises(tg.TileGemmError):
+            tg.tile_gemm_plan(1, 4096, 4096, 4096, "f32", config=tg.TG_CFG_256x256, pipeline_depth=d)
+    for d in (1, 2, 4, 5):
+        assert tg.tile_gemm_plan(1, 4096, 4096, 4096, "f32", config=tg.TG_CFG_128x128,
+                                 pipeline_depth=d)["lds_bytes"] == d * 16384
+    # placements: XOR and none; pad_stride is a 16-bit ablation only
+    assert tg.tile_gemm_plan(1, 4096, 4096, 4096, "f32", config=tg.TG_CFG_256x256, swizzle=tg.SWZ_NONE)["swizzle"] \
+        == tg.SWZ_NONE
+    with pytest.raises(tg.TileGemmError):
+        tg.tile_gemm_plan(1, 4096, 4096, 4096, "f32", config=tg.TG_CFG_256x256, swizzle=tg.SWZ_PAD)
+    # split-K on the ring tiles, forced and automatic (with the workspace it asks for)
+    info = tg.tile_gemm_plan(1, 512, 512, 131072, "f32", config=tg.TG_CFG_256x256, split_k=64)
+    assert (info["split_k"], info["k_slice"], info["grid"]) == (64, 2048, 4 * 64)
+    need = tg.tile_gemm_workspace_size(1, 512, 512, 131072, "f32")
+    assert need > 0
+    info = tg.tile_gemm_plan(1, 512, 512, 131072, "f32", workspace=FAKE, workspace_bytes=need)
+    assert info["split_k"] > 1 and info["config"] in (tg.TG_CFG_256x256, tg.TG_CFG_128x128)
+    # the register-staged tile still has no split; the remainder GEMMs are 16-bit only;
+    # the repacks and the persistent grid stay 16-bit
+    with pytest.raises(tg.TileGemmError):
+        tg.tile_gemm_plan(1, 64, 64, 8192, "f32", config=tg.TG_CFG_F32_64x64, split_k=4)
+    with pytest.raises(tg.TileGemmError):
+        tg.tile_gemm_plan(1, 8191, 8193, 8190, "f32", tail_gemm=2)
+    with pytest.raises(tg.TileGemmError):
+        tg.tile_gemm_plan(1, 4096, 4096, 4096, "f32", pack_a=2)
+    assert tg.tile_gemm_plan(1, 8192, 8192, 8192, "f32", persistent=2)["persistent"] == 0

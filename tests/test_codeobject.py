@@ -63,7 +63,8 @@ def test_m0_only_in_copy_groups(tmp_path):
 # place).  This scans for any instruction other than an MFMA that names an
 # AGPR written by a 16x16x32 MFMA fewer than 19 wait states earlier (an
 # s_nop N counts N + 1, any other instruction 1), along the text of each
-# function.
+# function.  The fp32 ring tiles' 16x16x4 MFMAs are inline assembly too and
+# are held to the same distance.
 _AREG = re.compile(r"\ba(\d+)\b|\ba\[(\d+):(\d+)\]")
 _XDL_WAIT = 19
 
@@ -89,7 +90,7 @@ def accumulator_hazards(lines):
             continue
         parts = l.split(None, 1)
         op, rest = parts[0], parts[1] if len(parts) > 1 else ""
-        if op.startswith("v_mfma_f32_16x16x32"):
+        if op.startswith(("v_mfma_f32_16x16x32", "v_mfma_f32_16x16x4")):
             dst = rest.split(",")[0]
             for p in pending:
                 p[1] += 1
@@ -190,7 +191,8 @@ def test_per_cu_table_matches_code_object(tmp_path):
             bm, bn, wm, wn, stages, swz = (int(m.group(i)) for i in (2, 3, 4, 5, 7, 8))
             if (bm, bn) not in CFG_OF or swz == 2:
                 continue
-            cfg, waves, depth, dt = CFG_OF[(bm, bn)], wm * wn, stages, "bf16" if m.group(1) == "1" else "f16"
+            cfg, waves, depth = CFG_OF[(bm, bn)], wm * wn, stages
+            dt = {"0": "f32", "1": "bf16", "2": "f16"}[m.group(1)]
         elif f:
             cfg, waves, depth, dt = tg.TG_CFG_F32_64x64, 4, int(f.group(1)), "f32"
         else:

@@ -1,7 +1,7 @@
 """The fused elementwise tail C <- act(alpha A.B + bias) + beta C0 (tile_gemm.h), on the GPU.
 
 * every tile configuration (256 x 256 with its thin strips, 128 x 128, 64 x 64,
-  the fp32 tile), ragged across several tiles, with a per-column bias, a
+  the fp32 tiles), ragged across several tiles, with a per-column bias, a
   per-row bias or none, and ReLU, GELU or no activation, beta zero or not:
   parity with the fp64 oracle over the whole output and no write outside C;
 * split along K, where the combine pass applies the tail; thin remainders as
@@ -101,6 +101,9 @@ CASES = [
     ("bf16", 97, 65, 40, 1, tg.TG_CFG_64x64, 1, 1.0, 0.0, 0, 1),
     ("f32", 67, 45, 53, 1, tg.TG_CFG_F32_64x64, 1, 1.0, 0.0, 1, 2),
     ("f32", 130, 70, 200, 1, tg.TG_CFG_F32_64x64, 1, 1.5, 0.5, 2, 1),
+    ("f32", 300, 257, 100, 1, tg.TG_CFG_256x256, 1, 1.0, 0.5, 1, 2),     # fp32 ring tile with its strips
+    ("f32", 131, 200, 37, 1, tg.TG_CFG_128x128, 1, -1.0, 1.0, 2, 1),
+    ("f32", 300, 260, 2100, 1, tg.TG_CFG_256x256, 3, 1.0, 0.5, 1, 2),     # fp32 split: the combine applies it
     ("bf16", 300, 260, 2100, 1, tg.TG_CFG_256x256, 3, 1.0, 0.5, 1, 2),     # combine pass applies it
     ("f16", 257, 300, 1300, 1, tg.TG_CFG_128x128, 2, 1.0, 0.0, 2, 1),
 ]

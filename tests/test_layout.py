@@ -308,3 +308,84 @@ def test_accumulator_layout_matches_epilogue(cfg, bm, bn, waves, mt):
             seen.add((wave, lane, slot))
     if step == 1:
         assert len(seen) == bm * bn
+
+
+# ---- fp32 inputs on the ring tiles (K tile 16, 16x16x4 MFMAs) --------------------------
+F32_RING = [(tg.LAYOUT_CFG_F32_256, 256, 256, 4, tg.TG_CFG_256x256),
+            (tg.LAYOUT_CFG_F32_128, 128, 128, 4, tg.TG_CFG_128x128),
+            (tg.LAYOUT_CFG_F32_STRIP_N, 256, 64, 4, tg.LAYOUT_CFG_STRIP_N),
+            (tg.LAYOUT_CFG_F32_STRIP_M, 64, 256, 4, tg.LAYOUT_CFG_STRIP_M)]
+BK32 = 16
+
+
+@pytest.mark.parametrize("cfg,bm,bn,waves,cfg16", F32_RING)
+@pytest.mark.parametrize("swz", [tg.SWZ_NONE, tg.SWZ_XOR])
+def test_f32_ring_lds_placement_matches_layout(cfg, bm, bn, waves, cfg16, swz):
+    for operand, kind, rows_, cols_ in [(0, tg.LAYOUT_LDS_A, bm, BK32), (1, tg.LAYOUT_LDS_B, BK32, bn)]:
+        L = tg.tile_gemm_describe_layout(cfg, swz, kind)
+        assert (L.shape[0], L.shape[1]) == (rows_, cols_)
+        seen = set()
+        for r in range(rows_):
+            for c in range(cols_):
+                (coord,) = tg.tg_layout_eval(L, (r, c))
+                off = tg.tile_gemm_lds_offset(cfg, swz, operand, r, c)
+                assert off == coord[M], (operand, r, c)
+                seen.add(off)
+        assert seen == set(range(rows_ * cols_))
+    with pytest.raises(tg.TileGemmError):
+        tg.tile_gemm_describe_layout(cfg, tg.SWZ_PAD, tg.LAYOUT_LDS_A)
+
+
+@pytest.mark.parametrize("cfg,bm,bn,waves,cfg16", F32_RING)
+def test_f32_ring_a_tile_is_the_16bit_a_tile(cfg, bm, bn, waves, cfg16):
+    # 64-byte rows either way: fp32 element (r, k) sits at the bytes of 16-bit element
+    # (r, 2k) of the 16x16x32 tile, so the same ds_read_b128 lane pattern (row l % 16,
+    # chunk l // 16) reads it, with the same measured conflict-free XOR; a lane's chunk
+    # holds its 4 consecutive k
+    for swz in (tg.SWZ_NONE, tg.SWZ_XOR):
+        for r in range(bm):
+            for k in range(BK32):
+                byte = 4 * tg.tile_gemm_lds_offset(cfg, swz, 0, r, k)
+                mask = ((r >> 1) & 3) if swz == tg.SWZ_XOR else 0
+                assert byte == 64 * r + 16 * ((k // 4) ^ mask) + 4 * (k % 4)
+                if cfg16 != tg.TG_CFG_128x128:     # (the 16-bit 128 x 128 tile takes 32x32x16 MFMAs)
+                    assert byte == 2 * tg.tile_gemm_lds_offset(cfg16, swz, 0, r, 2 * k)
+    assert MEASURED_B128_EXTRA_CYCLES[16]["(r>>1)&3"] == 0
+    assert MEASURED_B128_EXTRA_CYCLES[16]["0"] > 0
+    for lane in range(64):
+        row, k0 = lane % 16, 4 * (lane // 16)
+        offs = [tg.tile_gemm_lds_offset(cfg, tg.SWZ_XOR, 0, row, k0 + e) for e in range(4)]
+        assert offs == list(range(offs[0], offs[0] + 4)) and offs[0] % 4 == 0
+
+
+@pytest.mark.parametrize("cfg,bm,bn,waves,cfg16", F32_RING)
+def test_f32_ring_b_reads_conflict_free(cfg, bm, bn, waves, cfg16):
+    # MFMA step e's B operand: lane L = 16 g + i reads the 4 bytes of B[4 g + e][n0 + i]
+    # (ds_read_b32, 64 lanes over the 64 banks at once).  The XOR of the 64-byte unit
+    # with (k >> 2) & 3 = g sends the four lane groups to four distinct bank quarters;
+    # row-major, all four land on the same 16 banks (four-way conflicts)
+    for swz, expect in [(tg.SWZ_XOR, True), (tg.SWZ_NONE, False)]:
+        for n0 in range(0, bn, 16):
+            for e in range(4):
+                offs = [4 * tg.tile_gemm_lds_offset(cfg, swz, 1, 4 * (L // 16) + e, n0 + L % 16) for L in range(64)]
+                assert banks_distinct(offs, 4) == expect, (swz, n0, e)
+
+
+@pytest.mark.parametrize("cfg,bm,bn,waves,cfg16", F32_RING)
+def test_f32_ring_copies_and_accumulators(cfg, bm, bn, waves, cfg16):
+    # the A copies own each 16-byte chunk once, as for the 16-bit tile; the accumulator
+    # layout (16x16 MFMA output) is the epilogue's
+    L = tg.tile_gemm_describe_layout(cfg, 0, tg.LAYOUT_COPY_A)
+    owners = set()
+    per_wave = bm * 64 // 1024 // waves
+    for r in range(bm):
+        for p in range(4):
+            (coord,) = tg.tg_layout_eval(L, (r, p))
+            assert (r * 64) + 16 * p == (coord[WAVE] * per_wave + coord[M]) * 1024 + 16 * coord[LANE]
+            owners.add((coord[M], coord[WAVE], coord[LANE]))
+    assert len(owners) == bm * 4
+    L = tg.tile_gemm_describe_layout(cfg, 0, tg.LAYOUT_ACC)
+    for r in range(0, bm, 3):
+        for c in range(0, bn, 5):
+            (coord,) = tg.tg_layout_eval(L, (r, c))
+            assert tg.tile_gemm_acc_coord(cfg, coord[WAVE], coord[LANE], coord[M]) == (r, c)

@@ -25,13 +25,15 @@ DTYPES = {"f32": TG_F32, "bf16": TG_BF16, "f16": TG_F16}
 TG_OK, TG_ERR_INVALID_ARG, TG_ERR_UNSUPPORTED, TG_ERR_LAUNCH, TG_ERR_INTERNAL, TG_ERR_SCRATCH_LIMIT = range(6)
 STATUS_NAMES = {0: "TG_OK", 1: "TG_ERR_INVALID_ARG", 2: "TG_ERR_UNSUPPORTED", 3: "TG_ERR_LAUNCH",
                 4: "TG_ERR_INTERNAL", 5: "TG_ERR_SCRATCH_LIMIT"}
-ABI_VERSION = 8
+ABI_VERSION = 9
 # bytes of the library's own scratch that tile_gemm_ex_noalloc works in (TILE_GEMM_NOALLOC_SCRATCH_BYTES)
 NOALLOC_SCRATCH_BYTES = 64 << 20
 
 TG_CFG_AUTO, TG_CFG_256x256, TG_CFG_128x128, TG_CFG_64x64, TG_CFG_F32_64x64, TG_CFG_288x160 = range(6)
-# layout-introspection ids of the thin fringe-strip blocks of TG_CFG_256x256
+# layout-introspection ids of the thin fringe-strip blocks of TG_CFG_256x256, and of the
+# fp32 ring tiles (TG_CFG_256x256, TG_CFG_128x128 and the strips with fp32 inputs)
 LAYOUT_CFG_STRIP_N, LAYOUT_CFG_STRIP_M = 101, 102
+LAYOUT_CFG_F32_256, LAYOUT_CFG_F32_128, LAYOUT_CFG_F32_STRIP_N, LAYOUT_CFG_F32_STRIP_M = 103, 104, 105, 106
 SWZ_DEFAULT, SWZ_NONE, SWZ_PAD, SWZ_XOR = 0, 1, 2, 3
 BIAS_NONE, BIAS_PER_COLUMN, BIAS_PER_ROW = 0, 1, 2
 ACT_NONE, ACT_RELU, ACT_GELU = 0, 1, 2

@@ -165,7 +165,7 @@ __device__ __forceinline__ uint32_t lds_address(const char *p) {
 // next to an MFMA the compiler cannot see would read its result too early.
 template <class C, bool INLINE = true>
 struct AccTiles {
-    static constexpr bool ASM = INLINE && C::MT == 16 && C::DT != DT_F32;
+    static constexpr bool ASM = INLINE && C::MT == 16;
     typename AccT<C>::type r[C::TM][C::TN];
     __device__ __forceinline__ void zero() {
 #pragma unroll
@@ -173,10 +173,22 @@ struct AccTiles {
 #pragma unroll
             for (int j = 0; j < C::TN; ++j) r[i][j] = typename AccT<C>::type{};
     }
-    // r[i][j] += a . b, or r[i][j] = a . b for the first K step (FIRST)
+    // r[i][j] += a . b, or r[i][j] = a . b for the first K step (FIRST).  fp32:
+    // one 16x16x4 MFMA on element e of both fragments (the same k).
     template <bool FIRST>
-    __device__ __forceinline__ void mma(int i, int j, const u32x4 &a, const u32x4 &b) {
-        if constexpr (ASM) {
+    __device__ __forceinline__ void mma(int i, int j, const u32x4 &a, const u32x4 &b, int e = 0) {
+        if constexpr (C::DT == DT_F32) {
+            if constexpr (ASM) {
+                if (FIRST) asm volatile("v_mfma_f32_16x16x4_f32 %0, %1, %2, 0" : "=a"(r[i][j]) : "v"(a[e]), "v"(b[e]));
+                else asm volatile("v_mfma_f32_16x16x4_f32 %0, %1, %2, %0" : "+a"(r[i][j]) : "v"(a[e]), "v"(b[e]));
+            } else {
+                // the element copied out first: a bit_cast of a vector-element
+                // lvalue reads element 0
+                const uint32_t ae = a[e], be = b[e];
+                r[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(__builtin_bit_cast(float, ae),
+                                                             __builtin_bit_cast(float, be), r[i][j], 0, 0, 0);
+            }
+        } else if constexpr (ASM) {
             if constexpr (C::DT == DT_BF16) {
                 if (FIRST) asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=a"(r[i][j]) : "v"(a), "v"(b));
                 else asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(r[i][j]) : "v"(a), "v"(b));
@@ -219,7 +231,7 @@ struct AccTiles {
 // schedules below.
 template <class C, int STAGES, int SWZ, bool FRINGE>
 struct RingBlock {
-    static constexpr int E = 2;
+    static constexpr int E = C::ELEM;
     const GemmParams &p;
     char *smem;
     int lane, wave;
@@ -446,6 +458,11 @@ struct RingBlock {
         const uint32_t addr = a_rd[s] + stage * A_STAGE + i * C::MT * A_PITCH;
         return *(const __attribute__((address_space(3))) u32x4 *)(uintptr_t)addr;
     }
+    // fp32: B element of MFMA step e (e rows on from the read step's first, the same XOR)
+    __device__ __forceinline__ uint32_t read_b32(int stage, int s, int j, int e) const {
+        const uint32_t addr = b_rd[s][j] + stage * B_STAGE + e * B_PITCH;
+        return *(const __attribute__((address_space(3))) uint32_t *)(uintptr_t)addr;
+    }
     // one of the two transposing B reads (half: 4 k rows on, the same XOR)
     __device__ __forceinline__ u32x2 read_b(int stage, int s, int j, int half) const {
         const uint32_t addr = b_rd[s][j] + stage * B_STAGE + half * 4 * B_PITCH;
@@ -459,8 +476,13 @@ struct RingBlock {
         for (int i = 0; i < C::TM; ++i) af[i] = read_a(stage, s, i);
 #pragma unroll
         for (int j = 0; j < C::TN; ++j) {
-            const u32x2 l2 = read_b(stage, s, j, 0), h2 = read_b(stage, s, j, 1);
-            bfr[j] = u32x4{l2.x, l2.y, h2.x, h2.y};
+            if constexpr (C::DT == DT_F32) {
+                bfr[j] = u32x4{read_b32(stage, s, j, 0), read_b32(stage, s, j, 1), read_b32(stage, s, j, 2),
+                               read_b32(stage, s, j, 3)};
+            } else {
+                const u32x2 l2 = read_b(stage, s, j, 0), h2 = read_b(stage, s, j, 1);
+                bfr[j] = u32x4{l2.x, l2.y, h2.x, h2.y};
+            }
         }
     }
 
@@ -474,7 +496,12 @@ struct RingBlock {
     __device__ __forceinline__ int a_frag_chunk(int s) const { return C::LANE_GROUPS * s + lane / C::MT; }
     __device__ __forceinline__ void b_frag_src(int wcol, int j, int s, int half, int &k, int &n) const {
         const int grp = lane / 16, gi = lane % 16;
-        if (C::MT == 32) {
+        if (C::DT == DT_F32) {
+            // fp32: lane L = 16 g + i reads B[4 g + e][column i] for MFMA step e
+            // (`half` is e here); the rows of one read step are 4 g .. 4 g + 3
+            k = C::MK * C::MFMA_PER_READ * s + 4 * grp + half;
+            n = wcol + j * 16 + gi;
+        } else if (C::MT == 32) {
             k = 16 * s + 8 * (grp / 2) + gi / 4 + 4 * half;
             n = wcol + j * 32 + 16 * (grp % 2) + 4 * (gi % 4);
         } else {
@@ -484,15 +511,19 @@ struct RingBlock {
     }
 
     // Fragment piece r of K tile `stage` (r < READS): A pieces first
-    // (s, i), then B half-reads (s, j, half); B pieces fill one half of a
-    // u32x4 each.
-    static constexpr int READS = C::KSTEPS * (C::TM + 2 * C::TN);
+    // (s, i), then B reads (s, j, piece); a 16-bit B piece fills one half of a
+    // u32x4, an fp32 one one element.
+    static constexpr int READS = C::KSTEPS * (C::TM + C::B_PIECES * C::TN);
     __device__ __forceinline__ void read_piece(int stage, int r, u32x4 (&af)[C::KSTEPS][C::TM],
                                                u32x4 (&bfr)[C::KSTEPS][C::TN]) const {
         constexpr int NA = C::KSTEPS * C::TM;
         if (r < NA) {
             const int s = r / C::TM, i = r % C::TM;
             af[s][i] = read_a(stage, s, i);
+        } else if constexpr (C::DT == DT_F32) {
+            const int q = r - NA;
+            const int s = q / (4 * C::TN), j = (q / 4) % C::TN, e = q % 4;
+            bfr[s][j][e] = read_b32(stage, s, j, e);
         } else {
             const int q = r - NA;
             const int s = q / (2 * C::TN), j = (q / 2) % C::TN, half = q % 2;
@@ -507,12 +538,16 @@ struct RingBlock {
         }
     }
 
+    // the MFMAs of one read step: MFMA step e outermost, so an accumulator's
+    // consecutive MFMAs are TM x TN apart
     template <bool FIRST>
     __device__ __forceinline__ void mfmas(const u32x4 (&af)[C::TM], const u32x4 (&bfr)[C::TN]) {
-#pragma unroll
-        for (int i = 0; i < C::TM; ++i)
-#pragma unroll
-            for (int j = 0; j < C::TN; ++j) acc.template mma<FIRST>(i, j, af[i], bfr[j]);
+        static_for<0, C::MFMA_PER_READ * C::TM * C::TN, 1>([&](auto qc) {
+            constexpr int q = decltype(qc)::value;
+            constexpr int e = q / (C::TM * C::TN), i = (q / C::TN) % C::TM, j = q % C::TN;
+            if constexpr (FIRST && e == 0) acc.template mma<true>(i, j, af[i], bfr[j], e);
+            else acc.template mma<false>(i, j, af[i], bfr[j], e);
+        });
     }
 
     // the MFMAs of LDS copy `stage`; FIRST: the block's first K tile
@@ -599,7 +634,7 @@ __device__ __forceinline__ void ring_tile(const GemmParams &p, char *smem, int64
 template <class C, int STAGES, int SWZ, bool FRINGE>
 struct SwPipe {
     using Blk = RingBlock<C, STAGES, SWZ, FRINGE>;
-    static constexpr int NMFMA = C::KSTEPS * C::TM * C::TN;
+    static constexpr int NMFMA = C::KSTEPS * C::MFMA_PER_READ * C::TM * C::TN;
     static constexpr int READS = Blk::READS;
     static_assert(READS <= NMFMA, "one fragment read per MFMA at most");
 
@@ -627,27 +662,33 @@ struct SwPipe {
         __builtin_amdgcn_sched_barrier(0);
         const int64_t tc = t + STAGES;          // copy into tile t's LDS copy
         if (STEADY) {
-#pragma unroll
-            for (int q = 0; q < NMFMA; ++q) {
-                const int s = q / (C::TM * C::TN), i = (q / C::TN) % C::TM, j = q % C::TN;
-                if (FIRST && s == 0) blk.acc.template mma<true>(i, j, fa[s][i], fb[s][j]);
-                else blk.acc.template mma<false>(i, j, fa[s][i], fb[s][j]);
-                if (READ && q < READS) blk.read_piece(nxt_read, q, na, nb);
-                if (q == NMFMA / 4 - 1 || q == 3 * NMFMA / 4 - 1) blk.dma_operand(tc, cur, q < NMFMA / 2 ? 0 : 1);
+            // a compile-time loop: every accumulator and fragment index is a
+            // constant however long the stream (a loop the unroller declines
+            // would index the accumulators at run time, i.e. in scratch)
+            static_for<0, NMFMA, 1>([&](auto qc) {
+                constexpr int q = decltype(qc)::value;
+                constexpr int se = q / (C::TM * C::TN), i = (q / C::TN) % C::TM, j = q % C::TN;
+                constexpr int s = se / C::MFMA_PER_READ, e = se % C::MFMA_PER_READ;
+                if constexpr (FIRST && se == 0) blk.acc.template mma<true>(i, j, fa[s][i], fb[s][j], e);
+                else blk.acc.template mma<false>(i, j, fa[s][i], fb[s][j], e);
+                if constexpr (READ && q < READS) blk.read_piece(nxt_read, q, na, nb);
+                if constexpr (q == NMFMA / 4 - 1 || q == 3 * NMFMA / 4 - 1)
+                    blk.dma_operand(tc, cur, q < NMFMA / 2 ? 0 : 1);
                 __builtin_amdgcn_sched_barrier(0);
-            }
+            });
         } else {
             if (more) {
 #pragma unroll
                 for (int r = 0; r < READS; ++r) blk.read_piece(nxt_read, r, na, nb);
             }
             if (tc < ndma) blk.dma(tc, cur);
-#pragma unroll
-            for (int q = 0; q < NMFMA; ++q) {
-                const int s = q / (C::TM * C::TN), i = (q / C::TN) % C::TM, j = q % C::TN;
-                if (FIRST && s == 0) blk.acc.template mma<true>(i, j, fa[s][i], fb[s][j]);
-                else blk.acc.template mma<false>(i, j, fa[s][i], fb[s][j]);
-            }
+            static_for<0, NMFMA, 1>([&](auto qc) {
+                constexpr int q = decltype(qc)::value;
+                constexpr int se = q / (C::TM * C::TN), i = (q / C::TN) % C::TM, j = q % C::TN;
+                constexpr int s = se / C::MFMA_PER_READ, e = se % C::MFMA_PER_READ;
+                if constexpr (FIRST && se == 0) blk.acc.template mma<true>(i, j, fa[s][i], fb[s][j], e);
+                else blk.acc.template mma<false>(i, j, fa[s][i], fb[s][j], e);
+            });
         }
     }
 };
@@ -793,14 +834,15 @@ __global__ __launch_bounds__(C::THREADS, C::OCCUPANCY) void gemm_ring_persistent
 
 // The problem of grid batch entry b with its batch offsets folded into the
 // pointers; for a split-K pass, its K slice, written unscaled to its fp32
-// partial.
+// partial.  E: bytes per input element.
+template <int E>
 __device__ __forceinline__ GemmParams entry_params(const GemmParams &p, int64_t b) {
     GemmParams q = p;
     if (p.splits > 1) {
         const int64_t s = b / p.problems, pb = b - s * p.problems;
         const int64_t k0 = s * p.k_slice;
-        q.A = p.A + (pb * p.sA + k0) * 2;
-        q.B = p.B + (pb * p.sB + k0 * p.ldb) * 2;
+        q.A = p.A + (pb * p.sA + k0) * E;
+        q.B = p.B + (pb * p.sB + k0 * p.ldb) * E;
         q.K = p.K - k0 < p.k_slice ? p.K - k0 : p.k_slice;
         q.C = p.W + b * p.M * p.N;
         q.ldc = p.N;
@@ -809,8 +851,8 @@ __device__ __forceinline__ GemmParams entry_params(const GemmParams &p, int64_t 
         q.bias_mode = 0;        // the tail belongs to the combine pass
         q.act = 0;
     } else {
-        q.A = p.A + b * p.sA * 2;
-        q.B = p.B + b * p.sB * 2;
+        q.A = p.A + b * p.sA * E;
+        q.B = p.B + b * p.sB * E;
         q.C = p.C + b * p.sC;
         if (p.bias_mode != 0) q.bias = p.bias + b * p.bias_stride;   // the epilogue then sees entry 0
     }
@@ -820,11 +862,12 @@ __device__ __forceinline__ GemmParams entry_params(const GemmParams &p, int64_t 
 // A strip block's K slice (strip_splits > 1): its k range, and C pointed at the
 // slice's partial of the strip region so that the strip's own (m0, n0)
 // addressing lands there (row stride: the region's width).
+template <int E>
 __device__ __forceinline__ GemmParams strip_slice_params(const GemmParams &p, GemmParams q, int64_t b,
                                                          int64_t slice, bool n_strip) {
     const int64_t k0 = slice * p.strip_k_slice;
-    q.A = q.A + k0 * 2;
-    q.B = q.B + k0 * q.ldb * 2;
+    q.A = q.A + k0 * E;
+    q.B = q.B + k0 * q.ldb * E;
     q.K = p.K - k0 < p.strip_k_slice ? p.K - k0 : p.strip_k_slice;
     q.alpha = 1.0f;
     q.beta = 0.0f;
@@ -867,8 +910,8 @@ __global__ __launch_bounds__(C::THREADS, C::OCCUPANCY) void gemm_ring_kernel(Gem
             const int64_t slice = s / (per * p.batch);       // 0 unless the strips are split along K
             s -= slice * per * p.batch;
             const int64_t b = s / per, r = s - b * per;
-            GemmParams q = entry_params(p, b);
-            if (p.strip_splits > 1) q = strip_slice_params(p, q, b, slice, r < p.strip_n);
+            GemmParams q = entry_params<C::ELEM>(p, b);
+            if (p.strip_splits > 1) q = strip_slice_params<C::ELEM>(p, q, b, slice, r < p.strip_n);
             if (r < p.strip_n) run_tile<SN, STAGES, SWZ, SCHED, true, TAIL>(q, smem, r, p.n_main / SN::BN);
             else run_tile<SM, STAGES, SWZ, SCHED, true, TAIL>(q, smem, p.m_main / SM::BM, r - p.strip_n);
             return;
@@ -876,7 +919,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCCUPANCY) void gemm_ring_kernel(Gem
     }
     int64_t b, tm, tn;
     block_coords(p, b, tm, tn);
-    const GemmParams q = entry_params(p, b);
+    const GemmParams q = entry_params<C::ELEM>(p, b);
     const bool interior = (tm + 1) * C::BM <= p.M && (tn + 1) * C::BN <= p.N;
     if (interior) run_tile<C, STAGES, SWZ, SCHED, false, TAIL>(q, smem, tm, tn);
     else run_tile<C, STAGES, SWZ, SCHED, true, TAIL>(q, smem, tm, tn);

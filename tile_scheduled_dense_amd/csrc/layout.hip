@@ -116,8 +116,13 @@ tg_status describe(int swz, int kind, tg_layout *out) {
     return TG_ERR_INVALID_ARG;
 }
 
-// The 16-bit ring family: A [BM][32] under Swizzle(3, 2, 4); B [32][BN] under
-// Swizzle(5, B, S) on 64-byte units; copies own physical 16-byte chunks.
+constexpr int log2i(int x) { return x <= 1 ? 0 : 1 + log2i(x / 2); }
+
+// The ring family: A [BM][BK] (64-byte rows) under Swizzle(3, 2, 4) or (M, 2, 3)
+// with M = 3 for 16-bit, 2 for fp32 elements (the 16-byte chunk index); 16-bit
+// B [32][BN] under Swizzle(5, B, S) on 64-byte units, fp32 B [16][BN] under
+// Swizzle(4, 2, log2(units) + 2) (unit ^= (k >> 2) & 3); copies own physical
+// 16-byte chunks.
 template <class C>
 void describe_ring_lds(tg_layout *L, int operand, int swz) {
     const int rows = operand == 0 ? C::BM : C::BK;
@@ -127,14 +132,17 @@ void describe_ring_lds(tg_layout *L, int operand, int swz) {
     L->shape[1] = cols;
     L->n_shard = 2;
     // pad_stride: the row stride is the padded pitch (in elements); no swizzle
-    const int pitch = (operand == 0 ? ring_a_pitch<C>(swz) : ring_b_pitch<C>(swz)) / 2;
+    const int pitch = (operand == 0 ? ring_a_pitch<C>(swz) : ring_b_pitch<C>(swz)) / C::ELEM;
     L->shard[0] = {rows, pitch, TG_AXIS_M, 0};
     L->shard[1] = {cols, 1, TG_AXIS_M, 0};
     if (swz != SWZ_XOR) return;
     L->n_swizzle = 1;
+    constexpr int CM = log2i(C::CHUNK);                     // element bits of a 16-byte chunk
     if (operand == 0) {
-        if (C::MT == 32) L->swizzle[0] = {3, 2, 4};         // chunk ^= (row >> 2) & 3
-        else L->swizzle[0] = {3, 2, 3};                     // chunk ^= (row >> 1) & 3
+        if (C::MT == 32) L->swizzle[0] = {CM, 2, 4};        // chunk ^= (row >> 2) & 3
+        else L->swizzle[0] = {CM, 2, 3};                    // chunk ^= (row >> 1) & 3
+    } else if (C::ELEM == 4) {
+        L->swizzle[0] = {4, 2, log2i(C::B_UNITS) + 2};      // 64-byte unit ^= (k >> 2) & 3
     } else if (C::B_UNITS >= 4) {
         L->swizzle[0] = {5, 2, C::B_UNITS == 8 ? 3 : 2};    // 64-byte unit ^= k & 3
         if (C::B_HALF_SWZ) {                                // 32-byte half ^= (k >> 3) & 1
@@ -194,10 +202,10 @@ template <class C>
 int64_t ring_lds_offset(int swz, int operand, int64_t i, int64_t j) {
     if (operand == 0) {
         if (i < 0 || i >= C::BM || j < 0 || j >= C::BK) return -1;
-        return ring_a_byte<C>((int)i, (int)(j / 8), swz) / 2 + j % 8;
+        return ring_a_byte<C>((int)i, (int)(j / C::CHUNK), swz) / C::ELEM + j % C::CHUNK;
     }
     if (i < 0 || i >= C::BK || j < 0 || j >= C::BN) return -1;
-    return ring_b_byte<C>((int)i, (int)j, swz) / 2;
+    return ring_b_byte<C>((int)i, (int)j, swz) / C::ELEM;
 }
 
 template <class C>
@@ -263,6 +271,10 @@ tg_status tile_gemm_describe_layout(int config, int swizzle, int kind, tg_layout
         return TG_ERR_UNSUPPORTED;
     std::memset(out, 0, sizeof *out);
     switch (config) {
+        case TG_LAYOUT_CFG_F32_256: return describe_ring<RingF32_256>(swizzle, kind, out);
+        case TG_LAYOUT_CFG_F32_128: return describe_ring<RingF32_128>(swizzle, kind, out);
+        case TG_LAYOUT_CFG_F32_STRIP_N: return describe_ring<Strip256xN<DT_F32>>(swizzle, kind, out);
+        case TG_LAYOUT_CFG_F32_STRIP_M: return describe_ring<StripMx256<DT_F32>>(swizzle, kind, out);
         case TG_CFG_256x256: return describe_ring<Ring256<DT_BF16>>(swizzle, kind, out);
         case TG_LAYOUT_CFG_STRIP_N: return describe_ring<Strip256xN<DT_BF16>>(swizzle, kind, out);
         case TG_LAYOUT_CFG_STRIP_M: return describe_ring<StripMx256<DT_BF16>>(swizzle, kind, out);
@@ -281,6 +293,10 @@ int64_t tile_gemm_lds_offset(int config, int swizzle, int operand, int64_t row, 
         config != TG_LAYOUT_CFG_STRIP_M)
         return -1;
     switch (config) {
+        case TG_LAYOUT_CFG_F32_256: return ring_lds_offset<RingF32_256>(swizzle, operand, row, k);
+        case TG_LAYOUT_CFG_F32_128: return ring_lds_offset<RingF32_128>(swizzle, operand, row, k);
+        case TG_LAYOUT_CFG_F32_STRIP_N: return ring_lds_offset<Strip256xN<DT_F32>>(swizzle, operand, row, k);
+        case TG_LAYOUT_CFG_F32_STRIP_M: return ring_lds_offset<StripMx256<DT_F32>>(swizzle, operand, row, k);
         case TG_CFG_256x256: return ring_lds_offset<Ring256<DT_BF16>>(swizzle, operand, row, k);
         case TG_LAYOUT_CFG_STRIP_N: return ring_lds_offset<Strip256xN<DT_BF16>>(swizzle, operand, row, k);
         case TG_LAYOUT_CFG_STRIP_M: return ring_lds_offset<StripMx256<DT_BF16>>(swizzle, operand, row, k);
@@ -294,6 +310,10 @@ int64_t tile_gemm_lds_offset(int config, int swizzle, int operand, int64_t row, 
 
 int tile_gemm_acc_coord(int config, int wave, int lane, int slot, int64_t *row, int64_t *col) {
     switch (config) {
+        case TG_LAYOUT_CFG_F32_256: return acc_coord_checked<RingF32_256>(wave, lane, slot, row, col);
+        case TG_LAYOUT_CFG_F32_128: return acc_coord_checked<RingF32_128>(wave, lane, slot, row, col);
+        case TG_LAYOUT_CFG_F32_STRIP_N: return acc_coord_checked<Strip256xN<DT_F32>>(wave, lane, slot, row, col);
+        case TG_LAYOUT_CFG_F32_STRIP_M: return acc_coord_checked<StripMx256<DT_F32>>(wave, lane, slot, row, col);
         case TG_CFG_256x256: return acc_coord_checked<Ring256<DT_BF16>>(wave, lane, slot, row, col);
         case TG_LAYOUT_CFG_STRIP_N: return acc_coord_checked<Strip256xN<DT_BF16>>(wave, lane, slot, row, col);
         case TG_LAYOUT_CFG_STRIP_M: return acc_coord_checked<StripMx256<DT_BF16>>(wave, lane, slot, row, col);

@@ -136,21 +136,37 @@ TG_HD int lds_chunk_byte(int row, int chunk, int swz) {
 //    k rows 8g.. of the same 16 columns, so groups 0 and 1 (read in one cycle)
 //    touch rows k and k + 8; a second swizzle term XORs the 32-byte half of
 //    each 64-byte unit with (k >> 3) & 1 to keep them on distinct banks.
+//  * fp32 inputs (DT_F32, 16x16x4 MFMAs only): the same 64-byte A rows hold a
+//    K tile of 16, so the A tile, its swizzle and its ds_read_b128 fragment
+//    reads are those of the 16-bit 16x16x32 kernel byte for byte; lane l's
+//    chunk holds k 4 (l / 16) .. + 3 and its element e feeds MFMA step e, which
+//    thus sums k = 4 g + e over the lane groups g.  B rows are BN fp32 (64-byte
+//    units of 16 n); the partner of that A element, B[4 g + e][n], is one
+//    ds_read_b32 per step (no 32-bit transposing read exists), and the unit
+//    XOR (k >> 2) & 3 puts the four lane groups' rows on four distinct
+//    16-bank quarters of the bank line.
 // ---------------------------------------------------------------------------
 template <int DT_, int BM_, int BN_, int WAVES_M_, int WAVES_N_, int MT_ = 32>
 struct RingCfg {
     static constexpr int DT = DT_;
-    static constexpr int ELEM = 2;
-    static constexpr int BM = BM_, BN = BN_, BK = 32;
-    static constexpr int CHUNK = 8;                          // elements per 16 bytes
+    static constexpr int ELEM = DT_ == DT_F32 ? 4 : 2;       // bytes per input element
+    static constexpr int BM = BM_, BN = BN_, BK = 64 / ELEM;  // K tile: 64-byte A rows (32 or 16 k)
+    static constexpr int CHUNK = 16 / ELEM;                  // elements per 16 bytes
     static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
     static constexpr int WAVES = WAVES_M_ * WAVES_N_;
     static constexpr int THREADS = 64 * WAVES;
     static constexpr int MT = MT_, ACC_PER_MFMA = MT_ * MT_ / 64;
-    static constexpr int MK = 512 / MT_;                     // k per MFMA: 16 (32x32) or 32 (16x16)
+    // k per MFMA: 16 (32x32x16), 32 (16x16x32) or 4 (fp32 16x16x4)
+    static constexpr int MK = DT_ == DT_F32 ? 4 : 512 / MT_;
     static constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
     static constexpr int TM = WTM / MT, TN = WTN / MT;
-    static constexpr int KSTEPS = BK / MK;                   // MFMA K steps per K tile
+    // MFMAs per (row tile, column tile) per fragment read (the fp32 chunk's 4 k)
+    static constexpr int MFMA_PER_READ = DT_ == DT_F32 ? 4 : 1;
+    // fragment read steps per K tile (one 16-byte A chunk per lane each)
+    static constexpr int KSTEPS = BK / (MK * MFMA_PER_READ);
+    // B reads per column tile and read step: two transposing 8-byte reads
+    // (16-bit), four 4-byte reads (fp32, one per MFMA step)
+    static constexpr int B_PIECES = DT_ == DT_F32 ? 4 : 2;
     static constexpr int A_ROW_BYTES = BK * ELEM;            // 64
     static constexpr int B_ROW_BYTES = BN * ELEM;
     static constexpr int B_UNITS = B_ROW_BYTES / 64;         // 64-byte units per B row
@@ -159,7 +175,7 @@ struct RingCfg {
     static constexpr int STAGE_BYTES = A_TILE_BYTES + B_TILE_BYTES;
     // acc_coord() below is shared with TileCfg
     static constexpr int LANE_GROUPS = 64 / MT_;             // lanes sharing a row: 2 or 4
-    static constexpr bool B_HALF_SWZ = MT_ == 16;            // (k >> 3) & 1 into the 32-byte half
+    static constexpr bool B_HALF_SWZ = MT_ == 16 && DT_ != DT_F32;   // (k >> 3) & 1 into the 32-byte half
     // Workgroups per CU the kernel is compiled for (its register budget): the
     // 256 x 256 tile takes a whole CU (512 registers per lane, 128 KiB of
     // LDS); the smaller tiles leave room for two, which memory-bound problems
@@ -174,8 +190,10 @@ struct RingCfg {
 
     static_assert(BM % (WAVES_M * MT) == 0 && BN % (WAVES_N * MT) == 0, "wave tiling");
     static_assert(B_ROW_BYTES % 64 == 0, "B rows of whole 64-byte units");
-    static_assert(B_UNITS == 2 || B_UNITS == 4 || B_UNITS == 8 || (B_UNITS == 5 && MT_ == 16),
-                  "B rows of 2, 4 or 8 units (XOR of the unit index), or of 5 (half XOR only)");
+    static_assert(DT_ == DT_F32 ? (MT_ == 16 && (B_UNITS == 4 || B_UNITS == 8 || B_UNITS == 16))
+                                : (B_UNITS == 2 || B_UNITS == 4 || B_UNITS == 8 || (B_UNITS == 5 && MT_ == 16)),
+                  "16-bit B rows of 2, 4 or 8 units (XOR of the unit index) or of 5 (half XOR only); "
+                  "fp32: 16x16x4 MFMAs, B rows of 4, 8 or 16 units");
 
 };
 
@@ -192,6 +210,10 @@ template <int DT> using Ring64 = RingCfg<DT, 64, 64, 1, 2>;      // 2 waves, wav
 // wave tile 144 x 80) covers a whole problem of up to 288 x 160, e.g. 257 x 129 in one block
 // with no strip and no second tile, so A and B are each read once.
 template <int DT> using Ring288x160 = RingCfg<DT, 288, 160, 2, 2, 16>;
+// fp32 inputs on the ring (16x16x4 MFMAs, K tile 16): the 256 x 256 tile (its
+// strips as above) and the 128 x 128 tile, 4 waves each.
+using RingF32_256 = RingCfg<DT_F32, 256, 256, 2, 2, 16>;
+using RingF32_128 = RingCfg<DT_F32, 128, 128, 2, 2, 16>;
 
 // A tile: the XOR applied to the 16-byte chunk index of row r.  Which row
 // bits make the fragment reads conflict-free depends on the MFMA lane pattern
@@ -235,6 +257,9 @@ TG_HD int ring_a_byte(int r, int c, int swz) {
 template <class C>
 TG_HD int ring_b_mask(int k, int swz) {
     if (swz != SWZ_XOR) return 0;
+    // fp32: a B read takes rows 4 g + e of the four lane groups g (one MFMA step
+    // e): XOR (k >> 2) & 3 = g moves group g's 16 columns to bank quarter g
+    if (C::ELEM == 4) return (k >> 2) & 3;
     // 5 units (320-byte rows): rows k .. k + 3 already start 16 banks apart; the
     // half XOR below separates k from k + 8
     if (C::B_UNITS == 5) return 0;
@@ -255,6 +280,7 @@ TG_HD int ring_b_half_mask(int k, int swz) {
 // B tile: byte offset of element (k, n).
 template <class C>
 TG_HD int ring_b_byte(int k, int n, int swz) {
+    if (C::ELEM == 4) return k * ring_b_pitch<C>(swz) + 64 * ((n / 16) ^ ring_b_mask<C>(k, swz)) + 4 * (n % 16);
     const int w = n / 32, half = ((n % 32) / 16) ^ ring_b_half_mask<C>(k, swz), in_half = (n % 16) * 2;
     return k * ring_b_pitch<C>(swz) + 64 * (w ^ ring_b_mask<C>(k, swz)) + 32 * half + in_half;
 }
@@ -300,7 +326,7 @@ TG_HD bool ring_a_source(int J, int lane, int swz, int &row, int &k) {
         k = 0;
         return false;
     }
-    k = 8 * (p ^ ring_a_mask<C>(row, swz));
+    k = C::CHUNK * (p ^ ring_a_mask<C>(row, swz));
     return true;
 }
 
@@ -317,6 +343,10 @@ TG_HD bool ring_b_source(int J, int lane, int swz, int &k, int &n) {
         return false;
     }
     const int w = (b / 64) ^ ring_b_mask<C>(k, swz);
+    if (C::ELEM == 4) {
+        n = 16 * w + (b % 64) / 4;
+        return true;
+    }
     const int half = ((b % 64) / 32) ^ ring_b_half_mask<C>(k, swz);
     n = 32 * w + 16 * half + (b % 32) / 2;
     return true;

@@ -91,10 +91,15 @@ CfgDims dims_of(int mfma_k) {
     return {C::BM, C::BN, C::BK, C::WAVES, C::STAGE_BYTES, C::MT, mfma_k};
 }
 
-CfgDims cfg_dims(int config) {
+// The tile of a configuration; the 256 x 256 and 128 x 128 ring tiles take
+// fp32 inputs too (16x16x4 MFMAs, a K tile of 16).
+CfgDims cfg_dims(int config, tg_dtype dtype) {
+    const bool f32 = dtype == TG_F32;
     switch (config) {
-        case TG_CFG_256x256: return dims_of<Ring256<DT_BF16>>(Ring256<DT_BF16>::MK);
-        case TG_CFG_128x128: return dims_of<Ring128<DT_BF16>>(Ring128<DT_BF16>::MK);
+        case TG_CFG_256x256:
+            return f32 ? dims_of<RingF32_256>(RingF32_256::MK) : dims_of<Ring256<DT_BF16>>(Ring256<DT_BF16>::MK);
+        case TG_CFG_128x128:
+            return f32 ? dims_of<RingF32_128>(RingF32_128::MK) : dims_of<Ring128<DT_BF16>>(Ring128<DT_BF16>::MK);
         case TG_CFG_64x64: return dims_of<Ring64<DT_BF16>>(Ring64<DT_BF16>::MK);
         case TG_CFG_F32_64x64: return dims_of<CfgF32>(4);
         case TG_CFG_288x160: return dims_of<Ring288x160<DT_BF16>>(Ring288x160<DT_BF16>::MK);
@@ -126,13 +131,18 @@ Partition256 partition256(int64_t M, int64_t N) {
     return q;
 }
 
-// Default choice (fp32 has one configuration): the largest tile that still
-// gives about one workgroup per CU (240 of the 256) and pads the output by at
-// most a quarter more than the next smaller tile.  The 256-wide padding counts
-// its strips: a 257 x 129 problem covers 256 x 256 plus a 64 x 256 strip, 5/6
-// of the 384 x 256 it pads to in 128-wide tiles.
+// Default choice: the largest tile that still gives about one workgroup per
+// CU (240 of the 256) and pads the output by at most a quarter more than the
+// next smaller tile.  The 256-wide padding counts its strips: a 257 x 129
+// problem covers 256 x 256 plus a 64 x 256 strip, 5/6 of the 384 x 256 it pads
+// to in 128-wide tiles.  fp32 takes the same rule over its ring tiles (256 x 256,
+// 128 x 128) with the register-staged 64 x 64 tile in place of the 16-bit
+// 64 x 64 ring tile.
 int choose_config(int64_t batch, int64_t M, int64_t N, tg_dtype dtype) {
-    if (dtype == TG_F32) return TG_CFG_F32_64x64;
+    if (dtype == TG_F32) {
+        const int c = choose_config(batch, M, N, TG_BF16);
+        return c == TG_CFG_256x256 || c == TG_CFG_128x128 ? c : TG_CFG_F32_64x64;
+    }
     // Many small problems that each fit one 288 x 160 tile, at least half of it
     // output: one block per problem reads its A and B once (the 256 x 256 tile
     // plus a strip read B twice and multiplied 2.5 times the output of a
@@ -248,13 +258,20 @@ tg_status make_plan(int64_t batch, int64_t M, int64_t N, int64_t K, tg_dtype dty
     if (o.split_k < 0) return TG_ERR_INVALID_ARG;
     const bool sixteen = dtype != TG_F32;
     const bool some = K > 0 && M > 0 && N > 0 && batch > 0;
+    // the configurations this input type has: the ring tiles, and for fp32 the
+    // register-staged 64 x 64 tile (no split) in place of the 16-bit 64 x 64
+    const int small_cfg = sixteen ? TG_CFG_64x64 : TG_CFG_F32_64x64;
+    auto cfg_ok = [&](int c) {
+        return sixteen ? (c == TG_CFG_256x256 || c == TG_CFG_128x128 || c == TG_CFG_64x64 || c == TG_CFG_288x160)
+                       : (c == TG_CFG_256x256 || c == TG_CFG_128x128 || c == TG_CFG_F32_64x64);
+    };
     int64_t want = 1, wanted_bytes = 0;
     int config = o.force_cfg;
     // An always-repacked A (pack_a == 2) is built for the unsplit 256 x 256
     // tile: with the tile left to the library, that is the tile, unsplit.
     const bool pin256 = sixteen && (o.pack_a == 2 || o.pack_b == 2) && config == TG_CFG_AUTO;
     if (pin256) config = TG_CFG_256x256;
-    if (sixteen && some && o.split_k == 0 && !pin256) {
+    if (some && o.split_k == 0 && !pin256) {
         // With a forced tile, that tile's own count.  Otherwise each tile with its
         // own count, and the one whose workgroups fill the most of its slots
         // (cfg_slots, the measured split targets; ties: the larger tile, fewer
@@ -270,11 +287,12 @@ tg_status make_plan(int64_t batch, int64_t M, int64_t N, int64_t K, tg_dtype dty
         int cfg = o.force_cfg;
         if (!cfg) {
             double best = -1.0;
-            for (int c = TG_CFG_256x256; c <= TG_CFG_64x64; ++c) {
-                const CfgDims dd = cfg_dims(c);
+            for (int c : {(int)TG_CFG_256x256, (int)TG_CFG_128x128, small_cfg}) {
+                const CfgDims dd = cfg_dims(c, dtype);
                 const int64_t tm = cdiv(M, dd.bm), tn = cdiv(N, dd.bn), tiles = tm * tn * batch;
                 const int64_t slots = cfg_slots(c);
-                const int64_t blocks = tiles * auto_splits(tiles, K, slots);
+                // the register-staged fp32 tile does not split
+                const int64_t blocks = tiles * (c == TG_CFG_F32_64x64 ? 1 : auto_splits(tiles, K, slots));
                 const double fill = (double)(blocks < slots ? blocks : slots) / (double)slots;
                 const double useful = (double)M * (double)N / ((double)(tm * dd.bm) * (double)(tn * dd.bn));
                 if (fill * useful > best * (1.0 + 1e-9)) {
@@ -283,8 +301,8 @@ tg_status make_plan(int64_t batch, int64_t M, int64_t N, int64_t K, tg_dtype dty
                 }
             }
         }
-        if (cfg >= TG_CFG_256x256 && cfg <= TG_CFG_64x64) {
-            const CfgDims dd = cfg_dims(cfg);
+        if (cfg >= TG_CFG_256x256 && cfg <= TG_CFG_64x64 && cfg_ok(cfg)) {
+            const CfgDims dd = cfg_dims(cfg, dtype);
             const int64_t s_auto = auto_splits(cdiv(M, dd.bm) * cdiv(N, dd.bn) * batch, K, cfg_slots(cfg));
             const int64_t slice = cdiv(cdiv(K, s_auto), dd.bk) * dd.bk;
             const int64_t s_eff = cdiv(K, slice);
@@ -294,32 +312,36 @@ tg_status make_plan(int64_t batch, int64_t M, int64_t N, int64_t K, tg_dtype dty
                 config = cfg;
             }
         }
-    } else if (sixteen && some && o.split_k >= 2) {
+    } else if (some && o.split_k >= 2) {
         want = o.split_k < kMaxSplits ? o.split_k : kMaxSplits;
     }
     if (!config) config = choose_config(batch, M, N, dtype);
     const bool tail_req = o.bias_mode != 0 || o.activation != 0;   // the fused tail (tile_gemm.h)
     if (config < TG_CFG_256x256 || config > TG_CFG_288x160) return TG_ERR_INVALID_ARG;
-    if ((dtype == TG_F32) != (config == TG_CFG_F32_64x64)) return TG_ERR_UNSUPPORTED;
-    // pipeline depth = LDS copies of the K tile (window = depth - 1)
+    if (!cfg_ok(config)) return TG_ERR_UNSUPPORTED;
+    // pipeline depth = LDS copies of the K tile (window = depth - 1); f32: the
+    // register-staged fp32 tile (the fp32 ring tiles follow the 16-bit rules)
     const bool f32 = config == TG_CFG_F32_64x64;
     const int depth = o.pipeline_depth ? o.pipeline_depth : (f32 ? 2 : 4);
     // depth 5 (a window of 4 tiles) for the smaller 16-bit tiles, whose two
     // workgroups per CU still fit 160 KiB of LDS; the 256 x 256 tile's software
     // pipeline cycles its copies four at a time
+    // (the unpipelined fp32 256 x 256 kernel is not built: its 256 MFMAs per K
+    // tile through the compiler's builtin need scratch)
     const bool depth_ok = f32 ? (depth == 1 || depth == 2)
                           : config == TG_CFG_288x160 ? (depth == 2 || depth == 4)
+                          : !sixteen && config == TG_CFG_256x256 ? (depth == 2 || depth == 4)
                           : (depth == 1 || depth == 2 || depth == 4 || (depth == 5 && config != TG_CFG_256x256));
     if (!depth_ok) return TG_ERR_UNSUPPORTED;
     const int swz = o.swizzle ? o.swizzle : SWZ_XOR;
     if (swz < 0 || swz > SWZ_XOR) return TG_ERR_INVALID_ARG;
     if (!f32 && swz == SWZ_NONE && depth != 4) return TG_ERR_UNSUPPORTED;   // ablation built at depth 4 only
-    // pad_stride: the 256 x 256 tile at depth 4 (the placement ablation of the default kernel)
-    if (swz == SWZ_PAD && (config != TG_CFG_256x256 || depth != 4)) return TG_ERR_UNSUPPORTED;
+    // pad_stride: the 16-bit 256 x 256 tile at depth 4 (the placement ablation of the default kernel)
+    if (swz == SWZ_PAD && (config != TG_CFG_256x256 || depth != 4 || !sixteen)) return TG_ERR_UNSUPPORTED;
     const int order = o.block_order;
     if (order != 0 && order != 1) return TG_ERR_UNSUPPORTED;
 
-    const CfgDims d = cfg_dims(config);
+    const CfgDims d = cfg_dims(config, dtype);
     tg_plan_info &p = out.info;
     std::memset(&p, 0, sizeof p);
     p.config = config;
@@ -439,6 +461,7 @@ tg_status make_plan(int64_t batch, int64_t M, int64_t N, int64_t K, tg_dtype dty
         reinterpret_cast<uintptr_t>(o.bias) % 4)
         return TG_ERR_INVALID_ARG;
     if (some && strip_n + strip_m > 0 && splits == 1) {
+        if (o.tail_gemm == 2 && !sixteen) return TG_ERR_UNSUPPORTED;   // remainder GEMMs: 16-bit 64 x 64 tile
         if (o.tail_gemm == 2) {
             const int64_t n_main = p.tiles_n * d.bn, m_main = p.tiles_m * d.bm;
             int64_t wanted_tail = wanted_pack;
@@ -485,7 +508,7 @@ tg_status make_plan(int64_t batch, int64_t M, int64_t N, int64_t K, tg_dtype dty
     // against 1000 (the whole strips overlap the main tiles' uneven ends; the
     // split ones still read all of A and add a combine pass).
     p.strip_splits = 1;
-    if (sixteen && some && out.strip_n + out.strip_m > 0 && splits == 1 && o.tail_gemm == 3) {
+    if (some && out.strip_n + out.strip_m > 0 && splits == 1 && o.tail_gemm == 3) {
         const int64_t strips = (out.strip_n + out.strip_m) * batch;
         const int64_t slots = cfg_slots(TG_CFG_256x256);
         int64_t sp = 1;
@@ -623,12 +646,14 @@ tg_status launch_ring(const GemmParams &gp, const tg_plan_info &p, hipStream_t s
                 return TG_ERR_UNSUPPORTED;
             case 4: return launch_ring_one<C, 4, SWZ_XOR, SCHED>(gp, p.grid, s);
             case 2: return launch_ring_one<C, 2, SWZ_XOR, SCHED>(gp, p.grid, s);
-            case 1: return launch_ring_one<C, 1, SWZ_XOR, SCHED_RING>(gp, p.grid, s);
+            case 1:
+                if constexpr (SWPIPE && C::DT == DT_F32) return TG_ERR_UNSUPPORTED;   // not built (make_plan)
+                else return launch_ring_one<C, 1, SWZ_XOR, SCHED_RING>(gp, p.grid, s);
         }
     } else if (p.pipeline_depth == 4 && p.swizzle == SWZ_NONE) {
         return launch_ring_one<C, 4, SWZ_NONE, SCHED>(gp, p.grid, s);
     } else if (p.pipeline_depth == 4 && p.swizzle == SWZ_PAD) {
-        if constexpr (SWPIPE) return launch_ring_one<C, 4, SWZ_PAD, SCHED>(gp, p.grid, s);
+        if constexpr (SWPIPE && C::DT != DT_F32) return launch_ring_one<C, 4, SWZ_PAD, SCHED>(gp, p.grid, s);
     }
     return TG_ERR_UNSUPPORTED;
 }
@@ -813,8 +838,12 @@ tg_status run(int64_t batch, int64_t M, int64_t N, int64_t K, tg_dtype dtype,
         case TG_BF16: st = launch_dtype<DT_BF16>(gp, plan.info, s, tail); break;
         case TG_F16: st = launch_dtype<DT_F16>(gp, plan.info, s, tail); break;
         case TG_F32:
-            if (plan.info.config != TG_CFG_F32_64x64) return TG_ERR_UNSUPPORTED;
-            return launch_variants<CfgF32>(gp, plan.info, s, tail);
+            if (plan.info.config == TG_CFG_F32_64x64) return launch_variants<CfgF32>(gp, plan.info, s, tail);
+            if (plan.info.persistent) return TG_ERR_INTERNAL;   // 16-bit only (make_plan)
+            if (plan.info.config == TG_CFG_256x256) st = launch_ring<RingF32_256, true>(gp, plan.info, s, tail);
+            else if (plan.info.config == TG_CFG_128x128) st = launch_ring<RingF32_128, false>(gp, plan.info, s, tail);
+            else return TG_ERR_UNSUPPORTED;
+            break;
         default: return TG_ERR_INVALID_ARG;
     }
     if (st != TG_OK) return st;
