@@ -165,8 +165,16 @@ def materialize(p: Problem) -> Problem:
     return replace(p, A=A, B=B, C0=C0)
 
 
+# Further shapes the benchmark can time (not among the five: the large fp32 problem the fp32
+# ring tiles are measured on).
+EXTRA = {
+    "f32_8192": Problem("f32_8192", "f32", 8192, 8192, 8192, dist="uniform",
+                        note="fp32 in / fp32 out, square 8192^3, beta=0 (fp32 ring tile)"),
+}
+
+
 def config(name: str, seed: int = 0) -> Problem:
-    return materialize(replace(CONFIGS[name], seed=seed))
+    return materialize(replace(CONFIGS[name] if name in CONFIGS else EXTRA[name], seed=seed))
 
 
 def custom(dtype, M, N, K, batch=1, lda_pad=0, ldb_pad=0, ldc_pad=0, alpha=1.0, beta=0.0,
