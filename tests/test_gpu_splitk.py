@@ -191,11 +191,16 @@ def test_workspace_errors():
         assert e.status == tg.TG_ERR_UNSUPPORTED
 
 
-@pytest.mark.parametrize("M,N,K", [(2048, 64, 8192), (64, 2048, 8192), (1024, 96, 4096), (256, 256, 16384)])
-def test_automatic_split_on_skinny_and_deep(M, N, K):
+@pytest.mark.parametrize("dt,M,N,K,cfg", [("bf16", 2048, 64, 8192, tg.TG_CFG_64x64),
+                                          ("bf16", 64, 2048, 8192, tg.TG_CFG_64x64),
+                                          ("bf16", 1024, 96, 4096, tg.TG_CFG_64x64),
+                                          ("bf16", 256, 256, 16384, tg.TG_CFG_64x64),
+                                          ("bf16", 1024, 1024, 4096, tg.TG_CFG_128x128),
+                                          ("f32", 512, 512, 65536, tg.TG_CFG_256x256)])
+def test_automatic_split_on_skinny_and_deep(dt, M, N, K, cfg):
     """The automatic choice with a workspace (tile and split weighed together) against the oracle."""
-    p = workloads.custom("bf16", M, N, K, ldb_pad=3, alpha=1.5, beta=0.5, seed=M + N, name="auto_split")
-    plan = tg.tile_gemm_plan(1, M, N, K, "bf16", workspace=1 << 40, workspace_bytes=1 << 40)
-    assert plan["split_k"] > 1, plan
+    p = workloads.custom(dt, M, N, K, ldb_pad=3, alpha=1.5, beta=0.5, seed=M + N, name="auto_split")
+    plan = tg.tile_gemm_plan(1, M, N, K, dt, workspace=1 << 40, workspace_bytes=1 << 40)
+    assert plan["split_k"] > 1 and plan["config"] == cfg, plan
     got = run_split(p)
     check_parity(p, got)
