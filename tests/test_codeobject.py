@@ -29,10 +29,13 @@ def _disassembly(tmp_path):
     shutil.copy(lib, local)
     # --offloading writes the bundled code objects next to the input
     subprocess.run([OBJDUMP, "--offloading", str(local)], check=True, capture_output=True, cwd=tmp_path)
-    objs = [p for p in tmp_path.iterdir() if "amdgcn" in p.name and "gfx950" in p.name]
+    objs = sorted(p for p in tmp_path.iterdir() if "amdgcn" in p.name and "gfx950" in p.name)
     assert objs, "no gfx950 code object in the library"
-    out = subprocess.run([OBJDUMP, "-d", "--mcpu=gfx950", str(objs[0])], check=True, capture_output=True, text=True)
-    return [l.split("//")[0].strip() for l in out.stdout.splitlines()]
+    lines = []
+    for obj in objs:     # one code object per translation unit with device code
+        out = subprocess.run([OBJDUMP, "-d", "--mcpu=gfx950", str(obj)], check=True, capture_output=True, text=True)
+        lines += [l.split("//")[0].strip() for l in out.stdout.splitlines()]
+    return lines
 
 
 def test_m0_only_in_copy_groups(tmp_path):
@@ -141,8 +144,9 @@ def _kernels(tmp_path):
     local = tmp_path / "lib.so"
     shutil.copy(lib, local)
     subprocess.run([OBJDUMP, "--offloading", str(local)], check=True, capture_output=True, cwd=tmp_path)
-    objs = [p for p in tmp_path.iterdir() if "amdgcn" in p.name and "gfx950" in p.name]
-    notes = subprocess.run([READELF, "--notes", str(objs[0])], check=True, capture_output=True, text=True).stdout
+    objs = sorted(p for p in tmp_path.iterdir() if "amdgcn" in p.name and "gfx950" in p.name)
+    notes = "".join(subprocess.run([READELF, "--notes", str(o)], check=True, capture_output=True, text=True).stdout
+                    for o in objs)
     out, cur = {}, None
     for line in notes.splitlines():
         m = re.match(r"\s+(?:- )?\.(name|vgpr_count|agpr_count|group_segment_fixed_size|"
