@@ -3,6 +3,7 @@ bench.py reports.
 
   python -m tile_scheduled_dense_amd.rocprof_summary trace  <kernel_stats.csv> <out.txt> <command...>
   python -m tile_scheduled_dense_amd.rocprof_summary timed  <kernel_stats.csv> <kernel_trace.csv> <K> <out.txt> <command...>
+  python -m tile_scheduled_dense_amd.rocprof_summary window <kernel_stats.csv> <kernel_trace.csv> <label:first:count,...> <out.txt> <command...>
   python -m tile_scheduled_dense_amd.rocprof_summary counters <fetch_dir> <write_dir> <copy_mib> <out.txt> <command...>
   python -m tile_scheduled_dense_amd.rocprof_summary sq <sq_dir> <trace_kernel_stats.csv> <out.txt> <command...>
 
@@ -16,6 +17,11 @@ only while the sources still match.
 `timed` is `trace` plus the mean duration of the last K dispatches of the GEMM
 kernel (the K timed steps of a bench.py run, after its warm-up), the figure to
 set beside bench.py's own HIP-event time per launch.
+
+`window` is `trace` plus the mean duration of GEMM dispatches first .. first +
+count - 1 for each labelled window: the timed steps of a bench.py run by their
+position (W warm-up steps come first; the ragged workload's steps, cache-flushed
+calls or a parity call may follow).
 
 `sq` averages the SQ/GRBM counters of one --pmc run over the GEMM dispatches
 and derives the shader clock (GRBM_GUI_ACTIVE counts cycles on each of the 8
@@ -164,6 +170,17 @@ def timed_average_ns(trace_csv, k):
     return sum(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in last) / len(last), len(rows)
 
 
+def window_average_ns(trace_csv, first, count):
+    """Mean duration of GEMM dispatches first .. first + count - 1 (in dispatch order): the timed
+    steps of a bench.py run, which follow its warm-up steps (further calls may come after)."""
+    rows = [r for r in _rows(trace_csv) if GEMM_KERNEL_TAG in r["Kernel_Name"]]
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    sel = rows[first:first + count]
+    if len(sel) < count:
+        raise SystemExit(f"only {len(rows)} GEMM dispatches, window {first}+{count}")
+    return sum(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in sel) / len(sel), len(rows)
+
+
 def main(argv):
     mode = argv[1]
     if mode == "timed":
@@ -175,6 +192,21 @@ def main(argv):
                          f"min_us={d['min_ns'] / 1e3:.2f} max_us={d['max_ns'] / 1e3:.2f} pct={d['percentage']:.2f}")
         avg, n = timed_average_ns(trace, k)
         kv[f"gemm_timed_average_us (last {k} of {n} GEMM dispatches)"] = f"{avg / 1e3:.2f}"
+        kv["kernel_source_sha256"] = kernel_source_hash()
+        write_kv(out, "rocprofv3 --kernel-trace --stats summary", cmd, kv)
+    elif mode == "window":
+        # windows: label:first:count[,label:first:count...]
+        stats, trace, windows, out, cmd = argv[2], argv[3], argv[4], argv[5], " ".join(argv[6:])
+        kv = {}
+        for name, d in summarize_trace(stats).items():
+            short = name if len(name) < 120 else name[:117] + "..."
+            kv[short] = (f"calls={d['calls']} average_us={d['average_ns'] / 1e3:.2f} "
+                         f"min_us={d['min_ns'] / 1e3:.2f} max_us={d['max_ns'] / 1e3:.2f} pct={d['percentage']:.2f}")
+        for w in windows.split(","):
+            label, first, count = w.split(":")
+            avg, n = window_average_ns(trace, int(first), int(count))
+            kv[f"gemm_timed_average_us {label} (GEMM dispatches {first}..{int(first) + int(count) - 1} of {n})"] = \
+                f"{avg / 1e3:.2f}"
         kv["kernel_source_sha256"] = kernel_source_hash()
         write_kv(out, "rocprofv3 --kernel-trace --stats summary", cmd, kv)
     elif mode == "trace":
