@@ -53,6 +53,10 @@ def draw(seed):
             opts["pack_b"] = 0                      # built for the 256 x 256 tile only
         if r.integers(0, 5) == 0:
             opts["tail_gemm"] = 3
+    if dt == "f32" and r.integers(0, 2) == 0:       # the fp32 ring tiles, with a split or split strips
+        opts["config"] = int(r.choice([tg.TG_CFG_256x256, tg.TG_CFG_128x128]))
+        opts["split_k"] = int(r.choice([0, 1, 2, 3, 5]))
+        opts["tail_gemm"] = int(r.choice([0, 0, 3]))
     return dt, M, N, K, batch, pads, alpha, beta, opts, mode, act
 
 
