@@ -84,17 +84,21 @@ tg_status launch_dtype(const GemmParams &gp, const tg_plan_info &p, hipStream_t 
         case TG_CFG_128x128: return launch_ring<Ring128<DT>, false>(gp, p, s, tail);
         case TG_CFG_64x64: return launch_ring<Ring64<DT>, false>(gp, p, s, tail);
         case TG_CFG_288x160: {
-            // the software pipeline at depth 2 or 4; the placement ablation at depth 4
+            // the plain ring (all waves in step, fragments read per K tile) at depth 2
+            // or 4; the placement ablation at depth 4.  This tile serves batches of
+            // small problems, bound by memory, where the software pipeline's second
+            // fragment set only costs registers (118 against 122 us on 512 problems
+            // of 257 x 129 x 1000, the same MFMA order and result).
             using C = Ring288x160<DT>;
             if (tail) {
                 if (p.pipeline_depth == 4 && p.swizzle == SWZ_XOR)
-                    return launch_ring_one<C, 4, SWZ_XOR, SCHED_SWPIPE, true>(gp, p.grid, s);
+                    return launch_ring_one<C, 4, SWZ_XOR, SCHED_RING, true>(gp, p.grid, s);
                 return TG_ERR_UNSUPPORTED;
             }
-            if (p.swizzle == SWZ_XOR && p.pipeline_depth == 4) return launch_ring_one<C, 4, SWZ_XOR, SCHED_SWPIPE>(gp, p.grid, s);
-            if (p.swizzle == SWZ_XOR && p.pipeline_depth == 2) return launch_ring_one<C, 2, SWZ_XOR, SCHED_SWPIPE>(gp, p.grid, s);
+            if (p.swizzle == SWZ_XOR && p.pipeline_depth == 4) return launch_ring_one<C, 4, SWZ_XOR, SCHED_RING>(gp, p.grid, s);
+            if (p.swizzle == SWZ_XOR && p.pipeline_depth == 2) return launch_ring_one<C, 2, SWZ_XOR, SCHED_RING>(gp, p.grid, s);
             if (p.swizzle == SWZ_NONE && p.pipeline_depth == 4)
-                return launch_ring_one<C, 4, SWZ_NONE, SCHED_SWPIPE>(gp, p.grid, s);
+                return launch_ring_one<C, 4, SWZ_NONE, SCHED_RING>(gp, p.grid, s);
             return TG_ERR_UNSUPPORTED;
         }
         default: return TG_ERR_UNSUPPORTED;

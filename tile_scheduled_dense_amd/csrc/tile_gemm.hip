@@ -188,7 +188,7 @@ int64_t auto_splits(int64_t tiles, int64_t K, int64_t slots) {
 int cfg_per_cu(int config, int depth) {
     switch (config) {
         case TG_CFG_256x256: return 1;
-        case TG_CFG_288x160: return 1;   // 417 registers a wave, 4 waves, 28 KiB per depth
+        case TG_CFG_288x160: return 1;   // 320 registers a wave, 4 waves, 28 KiB per depth
         case TG_CFG_128x128: return 2;
         case TG_CFG_64x64: {
             const int by_lds = (160 * 1024) / (depth * 8 * 1024);
