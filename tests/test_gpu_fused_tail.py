@@ -1,7 +1,7 @@
 """The fused elementwise tail C <- act(alpha A.B + bias) + beta C0 (tile_gemm.h), on the GPU.
 
 * every tile configuration (256 x 256 with its thin strips, 128 x 128, 64 x 64,
-  the fp32 tiles), ragged across several tiles, with a per-column bias, a
+  288 x 160, the fp32 tiles), ragged across several tiles, with a per-column bias, a
   per-row bias or none, and ReLU, GELU or no activation, beta zero or not:
   parity with the fp64 oracle over the whole output and no write outside C;
 * split along K, where the combine pass applies the tail; thin remainders as
@@ -106,6 +106,9 @@ CASES = [
     ("f32", 300, 260, 2100, 1, tg.TG_CFG_256x256, 3, 1.0, 0.5, 1, 2),     # fp32 split: the combine applies it
     ("bf16", 300, 260, 2100, 1, tg.TG_CFG_256x256, 3, 1.0, 0.5, 1, 2),     # combine pass applies it
     ("f16", 257, 300, 1300, 1, tg.TG_CFG_128x128, 2, 1.0, 0.0, 2, 1),
+    ("f16", 257, 129, 1000, 4, tg.TG_CFG_288x160, 1, 1.0, -0.5, 1, 2),   # one block per problem
+    ("bf16", 200, 100, 77, 3, tg.TG_CFG_288x160, 1, 1.5, 0.0, 2, 1),
+    ("bf16", 300, 170, 90, 1, tg.TG_CFG_288x160, 1, -1.0, 1.0, 0, 2),    # fringe blocks across both axes
 ]
 
 
@@ -127,7 +130,7 @@ def test_fused_tail_parity(dt, M, N, K, batch, cfg, split, alpha, beta, mode, ac
 
 @pytest.mark.parametrize("mode,stride", [(1, 0), (1, 300), (2, 0), (2, 250)])
 @pytest.mark.parametrize("cfg,split", [(tg.TG_CFG_128x128, 1), (tg.TG_CFG_64x64, 1), (tg.TG_CFG_128x128, 2),
-                                       (tg.TG_CFG_F32_64x64, 1)])
+                                       (tg.TG_CFG_F32_64x64, 1), (tg.TG_CFG_288x160, 1)])
 def test_fused_tail_batched(mode, stride, cfg, split):
     dt = "f32" if cfg == tg.TG_CFG_F32_64x64 else "bf16"
     p = workloads.custom(dt, 200, 260, 600, batch=3, ldb_pad=1, alpha=1.25, beta=0.5, seed=31, name="fb")
