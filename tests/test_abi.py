@@ -521,8 +521,9 @@ def test_plan_b_repack_and_split_strips():
 
 def test_plan_fp32_ring_tiles():
     # fp32 inputs on the LDS ring: 256 x 256 and 128 x 128 block tiles with 16x16x4 MFMAs and a
-    # K tile of 16 (64-byte A rows), chosen by the 16-bit rule; the register-staged 64 x 64 tile
-    # for problems that fill the GPU with neither
+    # K tile of 16 (64-byte A rows), chosen by the 16-bit rule except that a part-filled round of
+    # 256 x 256 tiles needs three quarters of the CUs (192 tiles, not 128); the register-staged
+    # 64 x 64 tile for problems that fill the GPU with neither
     info = tg.tile_gemm_plan(1, 8192, 8192, 8192, "f32")
     assert (info["config"], info["block_m"], info["block_n"], info["block_k"]) == (tg.TG_CFG_256x256, 256, 256, 16)
     assert (info["mfma_m"], info["mfma_k"], info["grid"], info["k_tiles"]) == (16, 4, 1024, 512)
@@ -531,6 +532,11 @@ def test_plan_fp32_ring_tiles():
     assert (info["config"], info["block_k"], info["lds_bytes"], info["per_cu"]) == (tg.TG_CFG_128x128, 16,
                                                                                       4 * (8192 + 8192), 2)
     assert tg.tile_gemm_plan(1, 67, 45, 53, "f32")["config"] == tg.TG_CFG_F32_64x64
+    # 144, 169, 196 and 225 tiles of 256 x 256 in one part-filled round
+    for n, cfg in [(3072, tg.TG_CFG_128x128), (3328, tg.TG_CFG_128x128), (3584, tg.TG_CFG_256x256),
+                   (3840, tg.TG_CFG_256x256)]:
+        assert tg.tile_gemm_plan(1, n, n, n, "f32")["config"] == cfg, n
+        assert tg.tile_gemm_plan(1, n, n, n, "bf16")["config"] == tg.TG_CFG_256x256, n
     # ragged: thin strips beside the 256 x 256 tiles, as for 16-bit inputs
     info = tg.tile_gemm_plan(1, 8191, 8193, 8190, "f32")
     assert (info["config"], info["strip_blocks"], info["k_tail"]) == (tg.TG_CFG_256x256, 32, 8190 % 16)

@@ -138,11 +138,9 @@ Partition256 partition256(int64_t M, int64_t N) {
 // to in 128-wide tiles.  fp32 takes the same rule over its ring tiles (256 x 256,
 // 128 x 128) with the register-staged 64 x 64 tile in place of the 16-bit
 // 64 x 64 ring tile.
-int choose_config(int64_t batch, int64_t M, int64_t N, tg_dtype dtype) {
-    if (dtype == TG_F32) {
-        const int c = choose_config(batch, M, N, TG_BF16);
-        return c == TG_CFG_256x256 || c == TG_CFG_128x128 ? c : TG_CFG_F32_64x64;
-    }
+// part_fill: the 256 x 256 tiles that must be busy (of the 256 CUs) before one
+// part-filled round of them is taken over a second round of 128 x 128 tiles.
+static int choose_tile(int64_t batch, int64_t M, int64_t N, int64_t part_fill) {
     // Many small problems that each fit one 288 x 160 tile, at least half of it
     // output: one block per problem reads its A and B once (the 256 x 256 tile
     // plus a strip read B twice and multiplied 2.5 times the output of a
@@ -153,13 +151,27 @@ int choose_config(int64_t batch, int64_t M, int64_t N, tg_dtype dtype) {
     const int64_t mid = cdiv(M, 128) * cdiv(N, 128) * batch;
     const int64_t area_big = q.area() * batch, area_mid = mid * 128 * 128;
     if (big >= 240 && 4 * area_big <= 5 * area_mid) return TG_CFG_256x256;
-    // At least half the CUs busy with 256 x 256 tiles beats a second round of
-    // 128 x 128 ones (two per CU): a 256 x 256 tile does more than twice the
-    // work per CU cycle (3000^3 bf16: 76.5 us against 98.7).
-    if (big >= 128 && mid > 512 && 4 * area_big <= 5 * area_mid) return TG_CFG_256x256;
+    // A part-filled round of 256 x 256 tiles against a second round of 128 x 128
+    // ones (two per CU).
+    if (big >= part_fill && mid > 512 && 4 * area_big <= 5 * area_mid) return TG_CFG_256x256;
     if (mid >= 240) return TG_CFG_128x128;
     if (big >= 240) return TG_CFG_256x256;
     return TG_CFG_64x64;
+}
+
+int choose_config(int64_t batch, int64_t M, int64_t N, tg_dtype dtype) {
+    if (dtype == TG_F32) {
+        // Both fp32 ring tiles run 16x16x4 MFMAs, so a 256 x 256 tile does only
+        // about 1.75 times the work of a 128 x 128 one per CU cycle: a part-filled
+        // round of them wins from three quarters of the CUs (3072^3: 693 us against
+        // 607 at 144 tiles; 3328^3: 748 / 658 at 169; 3584^3: 807 / 923 at 196).
+        const int c = choose_tile(batch, M, N, 192);
+        return c == TG_CFG_256x256 || c == TG_CFG_128x128 ? c : TG_CFG_F32_64x64;
+    }
+    // 16-bit: at least half the CUs busy with 256 x 256 tiles beats a second round
+    // of 128 x 128 ones, whose 32x32x16 MFMAs do less than half the work per CU
+    // cycle (3000^3 bf16: 76.5 us against 98.7).
+    return choose_tile(batch, M, N, 128);
 }
 
 // Size of tg_options in ABI version 1 (five ints, before the split-K fields).
