@@ -532,6 +532,15 @@ def test_plan_fp32_ring_tiles():
     assert (info["config"], info["block_k"], info["lds_bytes"], info["per_cu"]) == (tg.TG_CFG_128x128, 16,
                                                                                       4 * (8192 + 8192), 2)
     assert tg.tile_gemm_plan(1, 67, 45, 53, "f32")["config"] == tg.TG_CFG_F32_64x64
+    # with a workspace, fp32 ring tiles split by the busiest CU's share of slices:
+    # 576 tiles of 128 x 128 are 3 per CU, split 2 makes 2.5 and split 4 2.25
+    big_ws = dict(workspace=1 << 40, workspace_bytes=1 << 40)
+    for (M, N, K), split in [((3072, 3072, 3072), 4), ((3072, 3072, 1024), 2), ((3072, 3072, 800), 1),
+                             ((2048, 2048, 2048), 1), ((2560, 2560, 2560), 1), ((8192, 8192, 8192), 1)]:
+        info = tg.tile_gemm_plan(1, M, N, K, "f32", **big_ws)
+        assert info["split_k"] == split, (M, N, K, info["config"], info["split_k"])
+        assert tg.tile_gemm_plan(1, M, N, K, "f32")["split_k"] == 1
+    assert tg.tile_gemm_plan(1, 3072, 3072, 3072, "bf16", **big_ws)["split_k"] == 1   # 16-bit: unchanged
     # 144, 169, 196 and 225 tiles of 256 x 256 in one part-filled round
     for n, cfg in [(3072, tg.TG_CFG_128x128), (3328, tg.TG_CFG_128x128), (3584, tg.TG_CFG_256x256),
                    (3840, tg.TG_CFG_256x256)]:

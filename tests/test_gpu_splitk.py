@@ -196,7 +196,8 @@ def test_workspace_errors():
                                           ("bf16", 1024, 96, 4096, tg.TG_CFG_64x64),
                                           ("bf16", 256, 256, 16384, tg.TG_CFG_64x64),
                                           ("bf16", 1024, 1024, 4096, tg.TG_CFG_128x128),
-                                          ("f32", 512, 512, 65536, tg.TG_CFG_256x256)])
+                                          ("f32", 512, 512, 65536, tg.TG_CFG_256x256),
+                                          ("f32", 3072, 3072, 1024, tg.TG_CFG_128x128)])
 def test_automatic_split_on_skinny_and_deep(dt, M, N, K, cfg):
     """The automatic choice with a workspace (tile and split weighed together) against the oracle."""
     p = workloads.custom(dt, M, N, K, ldb_pad=3, alpha=1.5, beta=0.5, seed=M + N, name="auto_split")

@@ -188,6 +188,26 @@ int64_t auto_splits(int64_t tiles, int64_t K, int64_t slots) {
     return s;
 }
 
+// fp32 ring tiles are bound by their MFMAs: a CU runs its share of the
+// workgroups one after another, so a call takes about as long as its busiest
+// CU's share, ceil(blocks / 256) slices of 1/s of a tile each.  Split in two or
+// four when that share drops by a tenth or more, each slice keeping at least 512
+// of K (3072^3 on 128 x 128 tiles: 607 us unsplit, 523 split 2, 491 split 4;
+// 2048^3 gains nothing, and none is predicted).
+int64_t f32_round_splits(int64_t tiles, int64_t K) {
+    int64_t best = 1;
+    double share = (double)cdiv(tiles, 256);
+    for (int64_t s = 2; s <= 4; s *= 2) {
+        if (K / s < 512) break;
+        const double c = (double)cdiv(tiles * s, 256) / (double)s;
+        if (c <= 0.9 * share) {
+            best = s;
+            share = c;
+        }
+    }
+    return best;
+}
+
 // Workgroups of a configuration one CU holds at once, the lesser of what its
 // registers and its LDS allow (a SIMD holds 512 registers per lane for its
 // waves, a CU 160 KiB of LDS); the built kernels' register counts are checked
@@ -315,7 +335,10 @@ tg_status make_plan(int64_t batch, int64_t M, int64_t N, int64_t K, tg_dtype dty
         }
         if (cfg >= TG_CFG_256x256 && cfg <= TG_CFG_64x64 && cfg_ok(cfg)) {
             const CfgDims dd = cfg_dims(cfg, dtype);
-            const int64_t s_auto = auto_splits(cdiv(M, dd.bm) * cdiv(N, dd.bn) * batch, K, cfg_slots(cfg));
+            const int64_t tiles = cdiv(M, dd.bm) * cdiv(N, dd.bn) * batch;
+            int64_t s_auto = auto_splits(tiles, K, cfg_slots(cfg));
+            if (!sixteen && s_auto == 1 && (cfg == TG_CFG_256x256 || cfg == TG_CFG_128x128))
+                s_auto = f32_round_splits(tiles, K);
             const int64_t slice = cdiv(cdiv(K, s_auto), dd.bk) * dd.bk;
             const int64_t s_eff = cdiv(K, slice);
             wanted_bytes = s_eff > 1 ? s_eff * batch * M * N * 4 : 0;
