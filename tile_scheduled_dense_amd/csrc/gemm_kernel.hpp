@@ -432,7 +432,10 @@ __device__ __forceinline__ void store_tile_epilogue(const GemmParams &p, const A
 #pragma unroll
             for (int t = 0; t < CH; ++t)
 #pragma unroll
-                for (int v = 0; v < V; ++v) cv[t][v] = ok[t][v] ? Cblk[off[t][v]] : 0.0f;
+                // C0 at the tile's origin for a value outside C (never stored):
+                // a load under a lane mask would be a branch whose join waits for
+                // every memory operation in flight
+                for (int v = 0; v < V; ++v) cv[t][v] = Cblk[ok[t][v] ? off[t][v] : 0];
 #pragma unroll
             for (int t = 0; t < CH; ++t)
 #pragma unroll

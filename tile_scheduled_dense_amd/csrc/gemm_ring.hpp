@@ -229,7 +229,13 @@ struct AccTiles {
 // One workgroup's tile of the 16-bit family: copy sources, the copies, the
 // register-path last tile, fragment reads and the MFMAs, shared by the
 // schedules below.
-template <class C, int STAGES, int SWZ, bool FRINGE>
+// FRINGE: rows past M and 8-column chunks past N are masked (read as 0, not
+// stored).  LIMIT (fringe blocks only): every copy's resource also ends at the
+// operand's last valid element, for a block whose N edge cuts a 16-byte chunk;
+// without it the copies advance one resource per operand, as interior blocks
+// do (the copied K tiles lie inside K, masked rows read nothing, and no chunk
+// reaches past N).
+template <class C, int STAGES, int SWZ, bool FRINGE, bool LIMIT = FRINGE>
 struct RingBlock {
     static constexpr int E = C::ELEM;
     const GemmParams &p;
@@ -373,11 +379,11 @@ struct RingBlock {
     __device__ __forceinline__ void dma_operand(int64_t kt, int stage, int operand) {
         // An interior block's copied tiles lie wholly inside A and B, so its
         // resources need no size limit beyond the 31-bit offsets and are
-        // advanced by one K tile per copy; a fringe block's limit ends at the
+        // advanced by one K tile per copy; a LIMIT block's limit ends at the
         // last valid element (past it reads as 0).
         if (operand == 0) {
             const uint32_t region = lds0 + a_tile(stage);
-            if (FRINGE) {
+            if (LIMIT) {
                 const int64_t adv = kt * (C::BK * E);
                 copy_operand<CA>(rsrc_words_u(a_base + adv - A_SHIFT, a_valid - adv + A_SHIFT), region, a_voff);
             } else {
@@ -386,7 +392,7 @@ struct RingBlock {
             }
         } else {
             const uint32_t region = lds0 + b_tile(stage);
-            if (FRINGE) {
+            if (LIMIT) {
                 const int64_t adv = kt * b_step;
                 copy_operand<CB>(rsrc_words_u(b_base + adv - B_SHIFT, b_valid - adv + B_SHIFT), region, b_voff);
             } else {
@@ -581,9 +587,9 @@ constexpr int chunk_values() {
 // SCHED_RING (all waves in step): iteration kt waits for tile kt, one
 // barrier (tile kt visible, copy of tile kt-1 released), issues tile
 // kt + STAGES - 1, multiplies tile kt.  STAGES == 1 is the unpipelined form.
-template <class C, int STAGES, int SWZ, bool FRINGE, bool TAIL = false>
+template <class C, int STAGES, int SWZ, bool FRINGE, bool TAIL = false, bool LIMIT = FRINGE>
 __device__ __forceinline__ void ring_tile(const GemmParams &p, char *smem, int64_t b, int64_t tm, int64_t tn) {
-    RingBlock<C, STAGES, SWZ, FRINGE> blk(p, smem, b, tm, tn);
+    RingBlock<C, STAGES, SWZ, FRINGE, LIMIT> blk(p, smem, b, tm, tn);
     const int64_t nk = blk.nk, ndma = blk.ndma;
     if (nk > 0) {
         blk.tail_load();
@@ -631,9 +637,9 @@ __device__ __forceinline__ void ring_tile(const GemmParams &p, char *smem, int64
 // copy) placed between them, so the matrix core is fed while LDS and the
 // texture unit work.  Copies run STAGES - 1 tiles ahead of the tile being
 // landed.
-template <class C, int STAGES, int SWZ, bool FRINGE>
+template <class C, int STAGES, int SWZ, bool FRINGE, bool LIMIT = FRINGE>
 struct SwPipe {
-    using Blk = RingBlock<C, STAGES, SWZ, FRINGE>;
+    using Blk = RingBlock<C, STAGES, SWZ, FRINGE, LIMIT>;
     static constexpr int NMFMA = C::KSTEPS * C::MFMA_PER_READ * C::TM * C::TN;
     static constexpr int READS = Blk::READS;
     static_assert(READS <= NMFMA, "one fragment read per MFMA at most");
@@ -693,11 +699,11 @@ struct SwPipe {
     }
 };
 
-template <class C, int STAGES, int SWZ, bool FRINGE, bool TAIL = false>
+template <class C, int STAGES, int SWZ, bool FRINGE, bool TAIL = false, bool LIMIT = FRINGE>
 __device__ __forceinline__ void ring_tile_swpipe(const GemmParams &p, char *smem, int64_t b, int64_t tm, int64_t tn) {
     static_assert(STAGES >= 2, "software pipeline needs at least two LDS copies");
-    using SP = SwPipe<C, STAGES, SWZ, FRINGE>;
-    RingBlock<C, STAGES, SWZ, FRINGE> blk(p, smem, b, tm, tn);
+    using SP = SwPipe<C, STAGES, SWZ, FRINGE, LIMIT>;
+    RingBlock<C, STAGES, SWZ, FRINGE, LIMIT> blk(p, smem, b, tm, tn);
     const int64_t nk = blk.nk, ndma = blk.ndma;
     if (nk > 0) {
         // With at most STAGES copied tiles the last tile is landed by the
@@ -885,10 +891,10 @@ __device__ __forceinline__ GemmParams strip_slice_params(const GemmParams &p, Ge
     return q;
 }
 
-template <class C, int STAGES, int SWZ, int SCHED, bool FRINGE, bool TAIL>
+template <class C, int STAGES, int SWZ, int SCHED, bool FRINGE, bool TAIL, bool LIMIT = FRINGE>
 __device__ __forceinline__ void run_tile(const GemmParams &q, char *smem, int64_t tm, int64_t tn) {
-    if constexpr (SCHED == SCHED_SWPIPE) ring_tile_swpipe<C, STAGES, SWZ, FRINGE, TAIL>(q, smem, 0, tm, tn);
-    else ring_tile<C, STAGES, SWZ, FRINGE, TAIL>(q, smem, 0, tm, tn);
+    if constexpr (SCHED == SCHED_SWPIPE) ring_tile_swpipe<C, STAGES, SWZ, FRINGE, TAIL, LIMIT>(q, smem, 0, tm, tn);
+    else ring_tile<C, STAGES, SWZ, FRINGE, TAIL, LIMIT>(q, smem, 0, tm, tn);
 }
 
 template <class C, int STAGES, int SWZ, int SCHED, bool TAIL = false>
@@ -920,9 +926,17 @@ __global__ __launch_bounds__(C::THREADS, C::OCCUPANCY) void gemm_ring_kernel(Gem
     int64_t b, tm, tn;
     block_coords(p, b, tm, tn);
     const GemmParams q = entry_params<C::ELEM>(p, b);
-    const bool interior = (tm + 1) * C::BM <= p.M && (tn + 1) * C::BN <= p.N;
-    if (interior) run_tile<C, STAGES, SWZ, SCHED, false, TAIL>(q, smem, tm, tn);
-    else run_tile<C, STAGES, SWZ, SCHED, true, TAIL>(q, smem, tm, tn);
+    const bool full_m = (tm + 1) * C::BM <= p.M, full_n = (tn + 1) * C::BN <= p.N;
+    // A block past M only, or past N where N ends on a 16-byte chunk, masks its
+    // rows and chunks and copies like an interior block (the per-copy limits
+    // cost 3% of a 256 x 256 tile's time); only an N edge inside a chunk needs
+    // them.  Not in the kernels with the fused tail, the unpipelined depth or the
+    // pad_stride placement: a third tile body took those into scratch.
+    constexpr bool UNLIMITED_FRINGE = !TAIL && STAGES > 1 && SWZ != SWZ_PAD;
+    if (full_m && full_n) run_tile<C, STAGES, SWZ, SCHED, false, TAIL>(q, smem, tm, tn);
+    else if (UNLIMITED_FRINGE && (full_n || p.N % C::CHUNK == 0))
+        run_tile<C, STAGES, SWZ, SCHED, true, TAIL, !UNLIMITED_FRINGE>(q, smem, tm, tn);
+    else run_tile<C, STAGES, SWZ, SCHED, true, TAIL, true>(q, smem, tm, tn);
 }
 
 }  // namespace tg
