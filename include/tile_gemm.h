@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define TILE_GEMM_ABI_VERSION 9
+#define TILE_GEMM_ABI_VERSION 10
 
 typedef enum { TG_F32 = 0, TG_BF16 = 1, TG_F16 = 2 } tg_dtype;
 
@@ -183,7 +183,13 @@ typedef enum {
  * its own GEMM), split along K as above when the workspace also holds its
  * partials (after the A copy, N tail first).  The value is the same
  * contraction; the tail's k sum may be regrouped by its split.
- *   tail_gemm == 0 or 1: strips in the grid;
+ *   tail_gemm == 0: strips in the grid, split along K as for tail_gemm == 3
+ *                   when the whole strips would run after the main tiles as a
+ *                   part-filled round of their own (the main tiles end a whole
+ *                   round of 256 workgroups, or leave fewer free slots in their
+ *                   last round than there are strips) and `workspace` holds the
+ *                   partials; otherwise whole;
+ *   tail_gemm == 1: strips in the grid, whole;
  *   tail_gemm == 2: the remainder GEMMs whenever there is a thin remainder;
  *   tail_gemm == 3: strips in the grid, each split along K into S slices (K
  *                   slices of a multiple of 32, S up to 16) that write unscaled
@@ -244,7 +250,7 @@ typedef struct {
     int pack_a;          /* 0 = automatic, 1 = never, 2 = always (see above)        */
     int pad0_;
     int64_t plan_lda;    /* lda assumed by the plan queries (0: a multiple of 8)    */
-    int tail_gemm;       /* 0, 1 = strips; 2 = thin remainders as GEMMs (see above)  */
+    int tail_gemm;       /* 0 = strips, split when worth it; 1 = strips; 2 = GEMMs; 3 = split (above) */
     int persistent;      /* 0, 1 = plain grid; 2 = persistent where allowed (above) */
     const float *bias;   /* fused tail bias (see above), NULL when bias_mode == 0    */
     int64_t bias_stride; /* floats between the bias vectors of batch entries          */

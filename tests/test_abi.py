@@ -28,7 +28,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert tg.abi_version() == tg.ABI_VERSION == 9
+    assert tg.abi_version() == tg.ABI_VERSION == 10
     for s in range(6):
         assert tg.STATUS_NAMES[s] in tg.status_string(s)
 
@@ -240,15 +240,18 @@ def test_plan_tail_gemm():
     args = (1, 8191, 8193, 8190, "bf16")
     big = dict(workspace=1 << 40, workspace_bytes=1 << 40)
     tail_bytes = 8 * 8191 * 1 * 4 + 32            # 8 K slices of an 8191 x 1 partial, rounded to 256
-    # by default (0) and never (1): 32 strip blocks after the 1024 main tiles, no workspace
-    for t in (0, 1):
+    # never split (1): 32 strip blocks after the 1024 main tiles, no workspace
+    p = tg.tile_gemm_plan(*args, tail_gemm=1, **big)
+    assert (p["strip_blocks"], p["tail_n_splits"], p["tail_m_splits"], p["grid"]) == (32, 0, 0, 1056)
+    assert tg.tile_gemm_workspace_size(*args, tail_gemm=1) == 0
+    # split strips (3, and by default (0) here: the 1024 main tiles fill the GPU): 8 K slices of
+    # each of the 32 strip blocks, partials 8 x 8191 x 1; whole strips without the workspace
+    for t in (0, 3):
         p = tg.tile_gemm_plan(*args, tail_gemm=t, **big)
-        assert (p["strip_blocks"], p["tail_n_splits"], p["tail_m_splits"], p["grid"]) == (32, 0, 0, 1056)
-        assert tg.tile_gemm_workspace_size(*args, tail_gemm=t) == 0
-    # split strips (3): 8 K slices of each of the 32 strip blocks, partials 8 x 8191 x 1
-    p = tg.tile_gemm_plan(*args, tail_gemm=3, **big)
-    assert (p["strip_blocks"], p["strip_splits"], p["grid"]) == (32, 8, 1024 + 8 * 32)
-    assert tg.tile_gemm_workspace_size(*args, tail_gemm=3) == tail_bytes
+        assert (p["strip_blocks"], p["strip_splits"], p["grid"]) == (32, 8, 1024 + 8 * 32)
+        assert tg.tile_gemm_workspace_size(*args, tail_gemm=t) == tail_bytes
+        p = tg.tile_gemm_plan(*args, tail_gemm=t)
+        assert (p["strip_blocks"], p["strip_splits"], p["grid"]) == (32, 1, 1056)
     # forced: 8 K slices of the one-column GEMM (about 1024 workgroups of 64 x 64)
     p = tg.tile_gemm_plan(*args, tail_gemm=2, **big)
     assert (p["strip_blocks"], p["tail_n_splits"], p["tail_m_splits"], p["grid"]) == (0, 8, 0, 1024)
@@ -488,20 +491,27 @@ def test_plan_one_block_per_small_problem():
 def test_plan_b_repack_and_split_strips():
     """The repack of B takes rows that are only 2-byte aligned (odd ldb) on plans with at least
     8 tile rows; the ragged workload's ldb = N + 5 (rows 4-byte aligned) is left in place.  Its
-    32 strip blocks split into 8 K slices only on request (tail_gemm = 3)."""
+    32 strip blocks split into 8 K slices by default when the workspace holds them (the 1024 main
+    tiles fill the GPU), and on request (tail_gemm = 3)."""
     args = (1, 8191, 8193, 8190, "bf16")
     a_bytes = -(-8191 * 8192 * 2 // 256) * 256
     b_bytes = -(-8190 * 8200 * 2 // 256) * 256
     s_bytes = -(-8 * 8191 * 1 * 4 // 256) * 256
     kw = dict(plan_lda=8193, plan_ldb=8198)
-    assert tg.tile_gemm_workspace_size(*args, **kw) == a_bytes
-    p = tg.tile_gemm_plan(*args, workspace=1 << 40, workspace_bytes=1 << 40, **kw)
+    assert tg.tile_gemm_workspace_size(*args, tail_gemm=1, **kw) == a_bytes
+    assert tg.tile_gemm_workspace_size(*args, **kw) == a_bytes + s_bytes
+    p = tg.tile_gemm_plan(*args, workspace=1 << 40, workspace_bytes=1 << 40, tail_gemm=1, **kw)
     assert (p["pack_a"], p["pack_b"], p["strip_splits"], p["grid"]) == (1, 0, 1, 1024 + 32)
+    p = tg.tile_gemm_plan(*args, workspace=1 << 40, workspace_bytes=1 << 40, **kw)
+    assert (p["pack_a"], p["pack_b"], p["strip_splits"], p["grid"]) == (1, 0, 8, 1024 + 8 * 32)
+    # the A copy fits but not the strip partials after it: the strips stay whole
+    p = tg.tile_gemm_plan(*args, workspace=1 << 40, workspace_bytes=a_bytes, **kw)
+    assert (p["pack_a"], p["strip_splits"], p["workspace_bytes"]) == (1, 1, a_bytes)
     # an odd ldb: B repacked after the A copy
     kw = dict(plan_lda=8193, plan_ldb=8197)
-    n = tg.tile_gemm_workspace_size(*args, **kw)
+    n = tg.tile_gemm_workspace_size(*args, tail_gemm=1, **kw)
     assert n == a_bytes + b_bytes
-    p = tg.tile_gemm_plan(*args, workspace=1 << 40, workspace_bytes=n, **kw)
+    p = tg.tile_gemm_plan(*args, workspace=1 << 40, workspace_bytes=n, tail_gemm=1, **kw)
     assert (p["pack_a"], p["pack_b"], p["workspace_bytes"]) == (1, 1, n)
     # forced (2) also for 4-byte aligned rows; never (1)
     assert tg.tile_gemm_plan(*args, workspace=1 << 40, workspace_bytes=1 << 40, pack_b=2, plan_ldb=8198)["pack_b"] == 1
@@ -517,6 +527,29 @@ def test_plan_b_repack_and_split_strips():
     assert _plan_status(*args, pack_b=3) == tg.TG_ERR_INVALID_ARG
     assert _plan_status(*args, pack_b=2, config=tg.TG_CFG_128x128) == tg.TG_ERR_UNSUPPORTED
     assert _plan_status(*args, tail_gemm=4) == tg.TG_ERR_INVALID_ARG
+
+
+def test_plan_strips_split_automatically_after_a_full_round():
+    # tail_gemm 0 splits the thin strips along K when the main tiles fill a round of the GPU
+    # (256 workgroups) and the workspace holds the partials; 1 keeps them whole; 3 always asks
+    big_ws = dict(workspace=1 << 40, workspace_bytes=1 << 40)
+    c3 = dict(plan_lda=8190 + 3, plan_ldb=8193 + 5)
+    info = tg.tile_gemm_plan(1, 8191, 8193, 8190, "bf16", **c3, **big_ws)
+    assert (info["strip_blocks"], info["strip_splits"]) == (32, 8), info
+    assert tg.tile_gemm_plan(1, 8191, 8193, 8190, "bf16", tail_gemm=1, **c3, **big_ws)["strip_splits"] == 1
+    assert tg.tile_gemm_plan(1, 8191, 8193, 8190, "bf16", **c3)["strip_splits"] == 1        # no workspace
+    n0 = tg.tile_gemm_workspace_size(1, 8191, 8193, 8190, "bf16", tail_gemm=1, **c3)
+    n1 = tg.tile_gemm_workspace_size(1, 8191, 8193, 8190, "bf16", **c3)
+    assert n1 > n0                                                  # it asks for the partials too
+    # strips beside a part-filled last round stay whole unless asked: 144 main tiles and 25
+    # strips (3073^2), 576 main tiles (64 in the last round) and 49 strips (6145^2); 256 main
+    # tiles (4097^2, a whole round): split
+    for n in (3073, 6145):
+        assert tg.tile_gemm_plan(1, n, n, 2048, "bf16", **big_ws)["strip_splits"] == 1, n
+        assert tg.tile_gemm_plan(1, n, n, 2048, "bf16", tail_gemm=3, **big_ws)["strip_splits"] > 1, n
+    assert tg.tile_gemm_plan(1, 4097, 4097, 2048, "bf16", **big_ws)["strip_splits"] > 1
+    # 240 main tiles and 32 strips (3841 x 4097): more strips than free slots, split
+    assert tg.tile_gemm_plan(1, 3841, 4097, 2048, "bf16", **big_ws)["strip_splits"] > 1
 
 
 def test_plan_fp32_ring_tiles():

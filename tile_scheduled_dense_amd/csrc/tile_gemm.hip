@@ -534,16 +534,23 @@ tg_status make_plan(int64_t batch, int64_t M, int64_t N, int64_t K, tg_dtype dty
         }
     }
 
-    // Thin strips split along K, on request (tail_gemm == 3, tile_gemm.h): each
-    // strip block becomes S K slices (S doubled while the slices fill at most
-    // the 256 slots and keep at least 512 of K), whose partials follow the
+    // Thin strips split along K (tail_gemm == 3, or automatically, tile_gemm.h):
+    // each strip block becomes S K slices (S doubled while the slices fill at
+    // most the 256 slots and keep at least 512 of K), whose partials follow the
     // copies in the workspace; a combine pass over the strip region finishes
-    // them.  Not chosen automatically: on 8191 x 8193 x 8190 the 32 strips, a
-    // fifth round after 1024 main tiles, split 8 ways made the call 1011 us
-    // against 1000 (the whole strips overlap the main tiles' uneven ends; the
-    // split ones still read all of A and add a combine pass).
+    // them.  Automatic when the whole strips would run as a part-filled round
+    // of their own after the main tiles (these end a whole round, or leave too
+    // few slots in their last one): 8191 x 8193 x 8190 (32 strips after 1024
+    // main tiles) 953-964 us split 8 ways against 988-992 whole, 8193^2 x 8192
+    // 862-866 against 898-900, 4096 x 4097 x 4096 133 against 160; where the
+    // strips fit beside a part-filled last round they stay whole (6145^2 x 6144,
+    // 49 strips beside 64 of 576 main tiles: 414 us whole, 428 split).
     p.strip_splits = 1;
-    if (some && out.strip_n + out.strip_m > 0 && splits == 1 && o.tail_gemm == 3) {
+    const int64_t main_blocks = p.tiles_m * p.tiles_n * batch, slots256 = cfg_slots(TG_CFG_256x256);
+    const int64_t last_round = main_blocks % slots256;
+    const bool auto_strip_split = o.tail_gemm == 0 && main_blocks > 0 &&
+                                  (last_round == 0 || last_round + (out.strip_n + out.strip_m) * batch > slots256);
+    if (some && out.strip_n + out.strip_m > 0 && splits == 1 && (o.tail_gemm == 3 || auto_strip_split)) {
         const int64_t strips = (out.strip_n + out.strip_m) * batch;
         const int64_t slots = cfg_slots(TG_CFG_256x256);
         int64_t sp = 1;
