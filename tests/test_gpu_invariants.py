@@ -72,7 +72,9 @@ def padded(p, Mp, Np, Kp):
                                          (tg.TG_CFG_64x64, "bf16", (64, 64, 32)),
                                          (tg.TG_CFG_288x160, "f16", (288, 160, 32)),
                                          (0, "f32", (64, 64, 32))])
-@pytest.mark.parametrize("shape", [(300, 333, 130), (67, 45, 53), (257, 129, 1000)], ids=str)
+# (300, 328, 130): an N edge on a 16-byte chunk (the fringe blocks copy like interior ones);
+# N = 333, 45, 129: an N edge inside a chunk (per-copy resources)
+@pytest.mark.parametrize("shape", [(300, 333, 130), (67, 45, 53), (257, 129, 1000), (300, 328, 130)], ids=str)
 def test_ragged_equals_cropped_padded(cfg, dt, tile, shape):
     M, N, K = shape
     p = workloads.custom(dt, M, N, K, batch=2, lda_pad=3, ldb_pad=1, ldc_pad=5, alpha=1.5, beta=0.5, seed=K)
@@ -154,8 +156,9 @@ def test_edge_extents(dt, shape):
         check_parity(p, run(p))
 
 
-def test_beta_zero_never_reads_c_and_nan_padding_never_leaks():
-    p = workloads.custom("bf16", 200, 300, 100, lda_pad=7, ldb_pad=9, ldc_pad=4, alpha=1.0, beta=0.0, seed=4)
+@pytest.mark.parametrize("N", [300, 296])   # an N edge inside a 16-byte chunk, and on one
+def test_beta_zero_never_reads_c_and_nan_padding_never_leaks(N):
+    p = workloads.custom("bf16", 200, N, 100, lda_pad=7, ldb_pad=9, ldc_pad=4, alpha=1.0, beta=0.0, seed=4)
     gp = GpuProblem(p)
     gp.reset_c()            # C = NaN inside the window (beta == 0 must not read it)
     gp.run()
