@@ -168,8 +168,13 @@ __device__ __forceinline__ void block_coords_of(const GemmParams &p, uint32_t w,
         const uint32_t first_m = group * gm;
         const uint32_t rows = (tiles_m - first_m) < gm ? (tiles_m - first_m) : gm;
         const uint32_t in_g = t % (gm * tiles_n);
-        tm = first_m + in_g % rows;
         tn = in_g / rows;
+        // The row order turns by one for every 32 tiles of the group (an XCD's
+        // round), so the blocks of a slower row (a fringe row past M) do not fall
+        // to the same CUs round after round: 8191 x 8193 x 8190 926-928 us
+        // against 910-914 turned, 8191 x 8192 x 8192 826-827 against 812-816.
+        // The turn is the same for all the rows of one column: still a bijection.
+        tm = first_m + (in_g % rows + tn * rows / 32) % rows;
     } else {
         tm = t / tiles_n;
         tn = t % tiles_n;

@@ -930,9 +930,12 @@ __global__ __launch_bounds__(C::THREADS, C::OCCUPANCY) void gemm_ring_kernel(Gem
     // A block past M only, or past N where N ends on a 16-byte chunk, masks its
     // rows and chunks and copies like an interior block (the per-copy limits
     // cost 3% of a 256 x 256 tile's time); only an N edge inside a chunk needs
-    // them.  Not in the kernels with the fused tail, the unpipelined depth or the
-    // pad_stride placement: a third tile body took those into scratch.
-    constexpr bool UNLIMITED_FRINGE = !TAIL && STAGES > 1 && SWZ != SWZ_PAD;
+    // them.  Only in the 256 x 256 kernels, and not in those with the fused tail,
+    // the unpipelined depth or the pad_stride placement: a third tile body took
+    // those into scratch, and the smaller tiles past the register count of the
+    // workgroups per CU they are planned for.
+    constexpr bool UNLIMITED_FRINGE =
+        std::is_same<C, Ring256<C::DT>>::value && !TAIL && STAGES > 1 && SWZ != SWZ_PAD;
     if (full_m && full_n) run_tile<C, STAGES, SWZ, SCHED, false, TAIL>(q, smem, tm, tn);
     else if (UNLIMITED_FRINGE && (full_n || p.N % C::CHUNK == 0))
         run_tile<C, STAGES, SWZ, SCHED, true, TAIL, !UNLIMITED_FRINGE>(q, smem, tm, tn);
