@@ -316,7 +316,7 @@ def plan_config(p, plan, extra=None):
            "inputs": f"{p.dist} seed {p.seed}", "accumulate": "fp32", "output": "fp32",
            "tile": f"{plan['block_m']}x{plan['block_n']}x{plan['block_k']}",
            "pipeline_depth": plan["pipeline_depth"], "split_k": plan["split_k"],
-           "pack_a": plan["pack_a"], "strip_blocks": plan["strip_blocks"],
+           "pack_a": plan["pack_a"], "strip_blocks": plan["strip_blocks"], "strip_splits": plan["strip_splits"],
            "tail_n_splits": plan["tail_n_splits"], "tail_m_splits": plan["tail_m_splits"],
            "persistent": plan["persistent"]}
     cfg.update(extra or {})
