@@ -2,7 +2,8 @@
 
 * repack of B (ldb not a multiple of 8): the same values in aligned rows, the same MFMA
   sequence, so C is bitwise the call without it (pack_b = 1), alone and with the A repack;
-* strips split along K (tail_gemm = 3 with a workspace): the main tiles are bitwise those of
+* strips split along K (tail_gemm = 3 with a workspace, or tail_gemm = 0 where the whole strips
+  would run as a round of their own after the main tiles): the main tiles are bitwise those of
   the unsplit plan (tail_gemm = 1); the strip region is a regrouped k sum, within the stated
   tolerance of the oracle, and bit-exact on integer-valued inputs (every partial sum exact);
   thin N tails, thin M tails with the corner, batches, beta != 0 and the fused tail.
@@ -80,6 +81,21 @@ def test_split_strips(M, N, K, batch):
     assert np.array_equal(bits(got[:, :m_main, :n_main]), bits(ref[:, :m_main, :n_main]))   # main tiles untouched
     pts = strip_points(p)
     check_parity(p, got, points=pts)
+
+
+@pytest.mark.parametrize("M,N,K", [(4097, 4097, 2048), (4096, 4097, 4096)], ids=str)
+def test_automatic_strip_split(M, N, K):
+    """tail_gemm 0 with the workspace it asks for: the strips after a whole round of 256 main
+    tiles are split along K by themselves; the main tiles are bitwise the whole-strip plan's."""
+    p = workloads.custom("bf16", M, N, K, lda_pad=2, ldb_pad=1, alpha=1.5, beta=0.5, seed=M + K)
+    got, plan = run(p)
+    assert plan["strip_blocks"] > 0 and plan["strip_splits"] > 1, plan
+    ref, ref_plan = run(p, tail_gemm=1)
+    assert ref_plan["strip_splits"] == 1
+    n_main = plan["tiles_n"] * 256
+    m_main = plan["tiles_m"] * 256 if M % 256 else M
+    assert np.array_equal(bits(got[:, :m_main, :n_main]), bits(ref[:, :m_main, :n_main]))
+    check_parity(p, got, points=strip_points(p))
 
 
 @pytest.mark.parametrize("M,N,K,batch", STRIP_SHAPES[:4], ids=str)
