@@ -742,8 +742,9 @@ tg_status run(int64_t batch, int64_t M, int64_t N, int64_t K, tg_dtype dtype,
     // tiles are group_m rows by 32 / group_m columns.  Four rows (4 A and 8 B
     // panels per K step, the A panels' 64-byte row segments being the costlier
     // copies) measured 2.6% faster than eight at 8192^3 and with a ragged K,
-    // but 2.5% slower with a fringe tile row and 10% slower on 8191 x 8193 x
-    // 8190: four only when every 256 x 256 tile is whole.
+    // but slower with a fringe tile row (8191 x 8192 x 8192: 1%) and with thin
+    // strips (8191 x 8193 x 8192: 3.5%; 8191 x 8193 x 8190: 2%): four only when
+    // every 256 x 256 tile is whole.
     gp.group_m = plan.info.config == TG_CFG_256x256 && M % 256 == 0 && N % 256 == 0 ? 4 : 8;
     gp.splits = plan.info.split_k;
     gp.problems = batch;
