@@ -63,7 +63,8 @@ typedef enum { TG_F32 = 0, TG_BF16 = 1, TG_F16 = 2 } tg_dtype;
 typedef enum {
     TG_OK = 0,
     TG_ERR_INVALID_ARG = 1,  /* extents, strides, pointers, dtype or overlap rejected */
-    TG_ERR_UNSUPPORTED = 2,  /* no visible gfx950 device, or an option not built     */
+    TG_ERR_UNSUPPORTED = 2,  /* no visible gfx950 device, an option not built, or a  */
+                             /* block's tile of A, B or C spanning 2^31 bytes or more */
     TG_ERR_LAUNCH = 3,       /* the HIP runtime refused the launch */
     TG_ERR_INTERNAL = 4,     /* unexpected failure inside the library */
     TG_ERR_SCRATCH_LIMIT = 5 /* tile_gemm_ex_noalloc: the call needs more scratch than the library holds */

@@ -125,14 +125,16 @@ def test_plan_block_classes(args, expect):
         assert info[k] == v, (k, info)
 
 
-def test_plan_depth_changes_lds_only():
+def test_plan_depth_changes_lds_and_residency_only():
     plans = {d: tg.tile_gemm_plan(1, 1000, 1000, 1000, "bf16", config=tg.TG_CFG_128x128, pipeline_depth=d)
              for d in (1, 2, 4)}
     stage = 128 * 32 * 2 * 2
+    # three workgroups per CU by registers; at depth 4 the LDS holds two
+    assert {d: info["per_cu"] for d, info in plans.items()} == {1: 3, 2: 3, 4: 2}
     for d, info in plans.items():
         assert info["lds_bytes"] == d * stage
-        assert {k: v for k, v in info.items() if k not in ("lds_bytes", "pipeline_depth")} == \
-               {k: v for k, v in plans[1].items() if k not in ("lds_bytes", "pipeline_depth")}
+        assert {k: v for k, v in info.items() if k not in ("lds_bytes", "pipeline_depth", "per_cu")} == \
+               {k: v for k, v in plans[1].items() if k not in ("lds_bytes", "pipeline_depth", "per_cu")}
     with pytest.raises(tg.TileGemmError):
         tg.tile_gemm_plan(1, 64, 64, 64, "bf16", pipeline_depth=3)
     with pytest.raises(tg.TileGemmError):

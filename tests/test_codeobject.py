@@ -198,12 +198,12 @@ def test_per_cu_table_matches_code_object(tmp_path):
             cfg, waves, depth = CFG_OF[(bm, bn)], wm * wn, stages
             dt = {"0": "f32", "1": "bf16", "2": "f16"}[m.group(1)]
         elif f:
-            cfg, waves, depth, dt = tg.TG_CFG_F32_64x64, 4, int(f.group(1)), "f32"
+            cfg, waves, depth, dt, swz = tg.TG_CFG_F32_64x64, 4, int(f.group(1)), "f32", int(f.group(2))
         else:
             continue
         by_regs = 4 * (512 // d["vgpr_count"]) // waves
         by_lds = (160 * 1024) // max(d["group_segment_fixed_size"], 1)
-        plan = tg.tile_gemm_plan(1, 1024, 1024, 1024, dt, config=cfg, pipeline_depth=depth)
+        plan = tg.tile_gemm_plan(1, 1024, 1024, 1024, dt, config=cfg, pipeline_depth=depth, swizzle=swz)
         assert plan["per_cu"] == min(by_regs, by_lds), (name, d, plan["per_cu"])
         checked += 1
     assert checked >= 20

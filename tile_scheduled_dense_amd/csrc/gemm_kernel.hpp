@@ -204,6 +204,19 @@ __device__ __forceinline__ rsrc_t make_rsrc(const char *base) {
     return __builtin_amdgcn_make_buffer_rsrc((void *)u, (short)0, 0x7fffffff, 0x00020000);
 }
 
+// Resource over [base, base + nbytes): offsets past nbytes read as 0, and a
+// store there is dropped.
+__device__ __forceinline__ rsrc_t make_rsrc_n(const char *base, int64_t nbytes) {
+    const uint64_t a = (uint64_t)base;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    const char *u = (const char *)(((uint64_t)hi << 32) | lo);
+    const int n = nbytes > 0x7fffffffLL ? 0x7fffffff : (int)nbytes;
+    return __builtin_amdgcn_make_buffer_rsrc((void *)u, (short)0, __builtin_amdgcn_readfirstlane(n), 0x00020000);
+}
+
+constexpr int kOutOfRange = (int)0x80000000u;   // >= every resource size: reads as 0, stores dropped
+
 __device__ __forceinline__ u32x4 bload16(rsrc_t r, int voff, int soff) {
     return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
 }
@@ -308,6 +321,37 @@ __device__ __forceinline__ void static_for(const F &f) {
     }
 }
 
+// Store-back of a fringe block, through a buffer resource over the block's
+// part of C (from its first element to one past its last valid one).  A
+// value's byte offset is a row base (per MFMA row tile and value index: its
+// row, and the lane's column in column tile 0) plus the column tile's step, a
+// constant that the store and load carry as their immediate offset.  A row
+// outside C gets the base kFar, past every resource size, so its C0 load reads
+// 0 and its store is dropped: no store sits under a lane mask for rows (a
+// masked store is a branch of its own per value -- mask, exec save, store,
+// exec restore -- which made the store-back of the batched 257 x 129 problems
+// 3.9 times as long as unmasked stores of the whole tile).  A column outside C
+// in a row inside C still addresses C (the next row's elements), so a block
+// that cuts N masks its stores per column tile: one branch per MFMA column
+// tile and chunk, not per value; its loads there read elements of C it does
+// not use.  The host keeps every byte offset of a block's tile of C below
+// 2^31 - 4097, so kFar plus a lane's column and the step stays below 2^32.
+struct FringeC {
+    static constexpr uint32_t kFar = 0x7ffff000u;
+    rsrc_t r;
+    __device__ __forceinline__ FringeC(float *Cblk, int64_t rows_left, int64_t cols_left, int64_t ldc)
+        : r(make_rsrc_n((const char *)Cblk, ((rows_left - 1) * ldc + cols_left) * 4)) {}
+    __device__ __forceinline__ static uint32_t base(int row, int col0, int ldc, int64_t rows_left) {
+        return (row < rows_left ? (uint32_t)(row * ldc) * 4u : kFar) + (uint32_t)col0 * 4u;
+    }
+    __device__ __forceinline__ float load(uint32_t voff) const {
+        return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, 0, 0));
+    }
+    __device__ __forceinline__ void put(uint32_t voff, float v) const {
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, (int)voff, 0, 0);
+    }
+};
+
 // The fused tail C = act(fma(alpha, acc, bias)) + beta * C0 (C0 not read when
 // beta == 0), one instantiation per activation and per beta == 0 / != 0, so the
 // per-value code is straight-line.  A lane's output column depends on its MFMA
@@ -329,6 +373,7 @@ __device__ __forceinline__ void store_tile_tail_as(const GemmParams &p, const Ac
     const int64_t M = p.M, N = p.N;
     const float *bias = p.bias + b * p.bias_stride;
     const int bias_mode = p.bias_mode;
+    const FringeC fc(Cblk, M - m0, N - n0, p.ldc);   // used by fringe blocks only
     constexpr int V = C::ACC_PER_MFMA;
     constexpr int TN = C::TN;
     constexpr int TILES = C::TM * C::TN;
@@ -360,10 +405,17 @@ __device__ __forceinline__ void store_tile_tail_as(const GemmParams &p, const Ac
                 brow[i][v] = bias[FRINGE && m >= M ? M - 1 : m];
             }
     }
+    // fringe blocks: this lane's column in column tile 0, and whether the block cuts N
+    int col0 = 0;
+    {
+        int row;
+        acc_coord<C>(wave, lane, 0, row, col0);
+    }
+    const bool cols_whole = n0 + C::BN <= N;
     static_for<0, TILES, CH>([&](auto chunk) {
         constexpr int c0t = decltype(chunk)::value;
-        int off[CH][V];
-        bool ok[CH][V];
+        int off[CH][V];         // element offsets (interior) or byte offsets (fringe)
+        uint32_t rb[CH][V];     // fringe: row bases
         float cv[CH][V];
 #pragma unroll
         for (int t = 0; t < CH; ++t)
@@ -371,20 +423,36 @@ __device__ __forceinline__ void store_tile_tail_as(const GemmParams &p, const Ac
             for (int v = 0; v < V; ++v) {
                 int row, col;
                 acc_coord<C>(wave, lane, (c0t + t) * V + v, row, col);
-                off[t][v] = row * ldc + col;
-                ok[t][v] = !FRINGE || (m0 + row < M && n0 + col < N);
-                if constexpr (BETA) cv[t][v] = Cblk[ok[t][v] ? off[t][v] : 0];
+                if constexpr (FRINGE) {
+                    const int j = (c0t + t) % TN;
+                    rb[t][v] = FringeC::base(row, col0, ldc, M - m0);
+                    off[t][v] = (int)(rb[t][v] + (uint32_t)(j * C::MT * 4));
+                    if constexpr (BETA) cv[t][v] = fc.load((uint32_t)off[t][v]);
+                } else {
+                    off[t][v] = row * ldc + col;
+                    if constexpr (BETA) cv[t][v] = Cblk[off[t][v]];
+                }
             }
+        // the stores form their offsets anew from the row bases (as in
+        // store_tile_epilogue: an opaque column step)
+        uint32_t step = C::MT * 4;
+        if constexpr (FRINGE && BETA) asm volatile("" : "+v"(step));
 #pragma unroll
-        for (int t = 0; t < CH; ++t)
+        for (int t = 0; t < CH; ++t) {
+            const int i = (c0t + t) / TN, j = (c0t + t) % TN;
+            const bool col_ok = !FRINGE || cols_whole || col0 + j * C::MT < N - n0;
 #pragma unroll
             for (int v = 0; v < V; ++v) {
-                const int i = (c0t + t) / TN, j = (c0t + t) % TN;
                 const float bv = bias_mode == 1 ? bcol[j] : brow[i][v];
                 float y = tail_activation(__builtin_fmaf(alpha, acc(i, j, v), bv), ACT);
                 if constexpr (BETA) y = __builtin_fmaf(beta, cv[t][v], y);
-                if (ok[t][v]) Cblk[off[t][v]] = y;
+                if constexpr (FRINGE) {
+                    if (col_ok) fc.put(rb[t][v] + j * step, y);
+                } else {
+                    Cblk[off[t][v]] = y;
+                }
             }
+        }
     });
 }
 
@@ -415,47 +483,71 @@ __device__ __forceinline__ void store_tile_epilogue(const GemmParams &p, const A
     const int ldc = (int)p.ldc;
     const float alpha = p.alpha, beta = p.beta;
     const int64_t M = p.M, N = p.N;
+    const FringeC fc(Cblk, M - m0, N - n0, p.ldc);   // used by fringe blocks only
     constexpr int V = C::ACC_PER_MFMA;
     constexpr int TILES = C::TM * C::TN;
     constexpr int CH = CHUNK_VALUES / V < TILES ? CHUNK_VALUES / V : TILES;   // MFMA tiles per chunk
     static_assert(TILES % CH == 0, "whole chunks");
+    // fringe blocks: this lane's column in column tile 0, and whether the block cuts N
+    int col0 = 0;
+    {
+        int row;
+        acc_coord<C>(wave, lane, 0, row, col0);
+    }
+    const bool cols_whole = n0 + C::BN <= N;
 #pragma unroll
     for (int c0t = 0; c0t < TILES; c0t += CH) {
-        int off[CH][V];
-        bool ok[CH][V];
+        int off[CH][V];         // element offsets (interior) or byte offsets (fringe)
+        uint32_t rb[CH][V];     // fringe: row bases
 #pragma unroll
         for (int t = 0; t < CH; ++t)
 #pragma unroll
             for (int v = 0; v < V; ++v) {
                 int row, col;
                 acc_coord<C>(wave, lane, (c0t + t) * V + v, row, col);
-                off[t][v] = row * ldc + col;
-                ok[t][v] = !FRINGE || (m0 + row < M && n0 + col < N);
+                const int j = (c0t + t) % C::TN;
+                rb[t][v] = FringeC::base(row, col0, ldc, M - m0);
+                off[t][v] = FRINGE ? (int)(rb[t][v] + (uint32_t)(j * C::MT * 4)) : row * ldc + col;
             }
         if (beta != 0.0f) {
             float cv[CH][V];
 #pragma unroll
             for (int t = 0; t < CH; ++t)
 #pragma unroll
-                // C0 at the tile's origin for a value outside C (never stored):
-                // a load under a lane mask would be a branch whose join waits for
-                // every memory operation in flight
-                for (int v = 0; v < V; ++v) cv[t][v] = Cblk[ok[t][v] ? off[t][v] : 0];
+                for (int v = 0; v < V; ++v) cv[t][v] = FRINGE ? fc.load((uint32_t)off[t][v]) : Cblk[off[t][v]];
+            // the stores form their offsets anew from the row bases: an opaque
+            // column step keeps the compiler from holding the loads' offsets,
+            // one register per value, across the loads
+            uint32_t step = C::MT * 4;
+            if constexpr (FRINGE) asm volatile("" : "+v"(step));
 #pragma unroll
-            for (int t = 0; t < CH; ++t)
+            for (int t = 0; t < CH; ++t) {
+                const int i = (c0t + t) / C::TN, j = (c0t + t) % C::TN;
+                const bool col_ok = !FRINGE || cols_whole || col0 + j * C::MT < N - n0;
 #pragma unroll
                 for (int v = 0; v < V; ++v) {
-                    const int i = (c0t + t) / C::TN, j = (c0t + t) % C::TN;
-                    if (ok[t][v]) Cblk[off[t][v]] = __builtin_fmaf(alpha, acc(i, j, v), beta * cv[t][v]);
+                    const float y = __builtin_fmaf(alpha, acc(i, j, v), beta * cv[t][v]);
+                    if constexpr (FRINGE) {
+                        if (col_ok) fc.put(rb[t][v] + j * step, y);
+                    } else {
+                        Cblk[off[t][v]] = y;
+                    }
                 }
+            }
         } else {
 #pragma unroll
-            for (int t = 0; t < CH; ++t)
+            for (int t = 0; t < CH; ++t) {
+                const int i = (c0t + t) / C::TN, j = (c0t + t) % C::TN;
+                const bool col_ok = !FRINGE || cols_whole || col0 + j * C::MT < N - n0;
 #pragma unroll
                 for (int v = 0; v < V; ++v) {
-                    const int i = (c0t + t) / C::TN, j = (c0t + t) % C::TN;
-                    if (ok[t][v]) Cblk[off[t][v]] = alpha * acc(i, j, v);
+                    if constexpr (FRINGE) {
+                        if (col_ok) fc.put(rb[t][v] + (uint32_t)(j * C::MT * 4), alpha * acc(i, j, v));
+                    } else {
+                        Cblk[off[t][v]] = alpha * acc(i, j, v);
+                    }
                 }
+            }
         }
     }
 }

@@ -49,17 +49,6 @@ __device__ __forceinline__ void wait_vmcnt() {
 __device__ __forceinline__ void wait_lds() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 __device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
-// Resource over [base, base + nbytes): offsets past nbytes read as 0.
-__device__ __forceinline__ rsrc_t make_rsrc_n(const char *base, int64_t nbytes) {
-    const uint64_t a = (uint64_t)base;
-    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
-    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
-    const char *u = (const char *)(((uint64_t)hi << 32) | lo);
-    const int n = nbytes > 0x7fffffffLL ? 0x7fffffff : (int)nbytes;
-    return __builtin_amdgcn_make_buffer_rsrc((void *)u, (short)0, __builtin_amdgcn_readfirstlane(n), 0x00020000);
-}
-
-constexpr int kOutOfRange = (int)0x80000000u;   // >= every resource size: reads as 0
 
 // One 1-KiB buffer -> LDS copy: lane l's 16 bytes at byte `voff` of the
 // resource land at LDS byte lds_addr + 16 l.  Issued as inline assembly so the

@@ -217,19 +217,27 @@ int64_t f32_round_splits(int64_t tiles, int64_t K) {
 //              (LDS 64 / 80 KiB at depth 4 / 5 allows two as well).
 //   64 x 64:   under 168 registers, 2 waves: three waves per SIMD, six per CU by
 //              registers; LDS 8 KiB per depth: 5 at depth 4, 4 at depth 5.
-int cfg_per_cu(int config, int depth) {
+int cfg_per_cu(int config, int depth, bool f32, int swz) {
     switch (config) {
         case TG_CFG_256x256: return 1;
         case TG_CFG_288x160: return 1;   // 320 registers a wave, 4 waves, 28 KiB per depth
-        case TG_CFG_128x128: return 2;
+        case TG_CFG_128x128: {
+            // 16-bit: 164 registers a wave (three waves per SIMD); fp32: 193 (two);
+            // 16 KiB of LDS per depth
+            const int by_regs = f32 ? 2 : 3, by_lds = (160 * 1024) / (depth * 16 * 1024);
+            return by_lds < by_regs ? by_lds : by_regs;
+        }
         case TG_CFG_64x64: {
+            // 128 registers a wave (148 with the fused tail, built at depth 4,
+            // where the LDS holds five), 2 waves, 8 KiB of LDS per depth
             const int by_lds = (160 * 1024) / (depth * 8 * 1024);
-            return by_lds < 6 ? by_lds : 6;
+            return by_lds < 8 ? by_lds : 8;
         }
         case TG_CFG_F32_64x64:
-            // 4 waves; depth 1 under 104 registers (five waves per SIMD, five per
-            // CU; 16 KiB of LDS), depth 2 under 128 (four; 32 KiB allows five)
-            return depth == 1 ? 5 : 4;
+            // 4 waves; depth 1 at 100 registers (five waves per SIMD, five per CU;
+            // 16 KiB of LDS), 84 without the swizzle (six), depth 2 at 108 (four;
+            // 32 KiB allows five)
+            return depth == 1 ? (swz == SWZ_NONE ? 6 : 5) : 4;
         default: return 1;
     }
 }
@@ -413,7 +421,7 @@ tg_status make_plan(int64_t batch, int64_t M, int64_t N, int64_t K, tg_dtype dty
     p.k_tiles = cdiv(K, d.bk);
     p.k_tail = K % d.bk;
     p.lds_bytes = depth * (swz == SWZ_PAD ? ring_stage_bytes<Ring256<DT_BF16>, SWZ_PAD>() : d.stage_bytes);
-    p.per_cu = cfg_per_cu(config, depth);
+    p.per_cu = cfg_per_cu(config, depth, !sixteen, swz);
 
     // split-K
     if (f32 && o.split_k >= 2) return TG_ERR_UNSUPPORTED;
@@ -632,14 +640,14 @@ tg_status validate(int64_t batch, int64_t M, int64_t N, int64_t K, tg_dtype dtyp
 }
 
 // Per-thread offsets inside a block are 32-bit: the byte offset of any element
-// of an A or B tile from the tile's first row, and the element offset of any C
-// element from the block's first row, must stay below 2^31, with 4 KiB to
-// spare (the 16-bit kernel adds up to 3 KiB: a copy group's resource base sits
-// below the tile).
+// of an A or B tile from the tile's first row, and of any C element from the
+// block's first row (a fringe block stores C through a buffer resource), must
+// stay below 2^31, with 4 KiB to spare (the 16-bit kernel adds up to 3 KiB: a
+// copy group's resource base sits below the tile).
 bool offsets_fit(const tg_plan_info &p, int64_t K, int64_t lda, int64_t ldb, int64_t ldc, int esz) {
     const int64_t lim = (int64_t(1) << 31) - 1 - 4096;
     return ((int64_t)p.block_m * lda + K) * esz < lim && ((int64_t)p.block_k * ldb + p.block_n) * esz < lim &&
-           (int64_t)p.block_m * ldc + p.block_n < lim;
+           ((int64_t)p.block_m * ldc + p.block_n) * 4 < lim;
 }
 
 template <int P>
