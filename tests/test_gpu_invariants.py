@@ -168,6 +168,28 @@ def test_beta_zero_never_reads_c_and_nan_padding_never_leaks(N):
     check_parity(p, out)
 
 
+@pytest.mark.parametrize("beta", [0.0, 0.5])
+def test_c_row_stride_at_the_tile_offset_limit(beta):
+    """A block's tile of C spans at most 2^31 - 4097 bytes (a fringe block stores C through a
+    buffer resource with 32-bit byte offsets): with 256 x 256 blocks the largest row stride
+    allowed computes (fringe rows and columns, its last row 8 MB from its first), the next
+    is refused before any device work and C is left as it was."""
+    lim = 2**31 - 1 - 4096
+    ldc_max = ((lim - 1) // 4 - 256) // 256
+    assert (256 * ldc_max + 256) * 4 < lim <= (256 * (ldc_max + 1) + 256) * 4
+    p = workloads.custom("bf16", 3, 40, 64, ldc_pad=ldc_max - 40, alpha=1.5, beta=beta, seed=11)
+    check_parity(p, run(p, config=tg.TG_CFG_256x256))
+    q = workloads.custom("bf16", 3, 40, 64, ldc_pad=ldc_max + 1 - 40, alpha=1.5, beta=beta, seed=11)
+    gq = GpuProblem(q)
+    gq.reset_c()
+    before = gq.cbuf.cpu().numpy().copy()
+    with pytest.raises(tg.TileGemmError) as e:
+        gq.run(config=tg.TG_CFG_256x256)
+    assert e.value.status == tg.TG_ERR_UNSUPPORTED
+    torch.cuda.synchronize()
+    assert np.array_equal(gq.cbuf.cpu().numpy().view(np.uint32), before.view(np.uint32))
+
+
 def test_shared_operand_batch_stride_zero():
     p = workloads.custom("f16", 70, 90, 110, batch=3, alpha=1.0, beta=0.0, seed=6)
     p.strideB = 0
