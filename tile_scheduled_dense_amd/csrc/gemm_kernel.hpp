@@ -324,9 +324,9 @@ __device__ __forceinline__ void static_for(const F &f) {
 // Store-back of a fringe block, through a buffer resource over the block's
 // part of C (from its first element to one past its last valid one).  A
 // value's byte offset is a row base (per MFMA row tile and value index: its
-// row, and the lane's column in column tile 0) plus the column tile's step, a
-// constant that the store and load carry as their immediate offset.  A row
-// outside C gets the base kFar, past every resource size, so its C0 load reads
+// row, and the lane's column in column tile 0) plus its column tile's step
+// (MT columns a tile), so a chunk holds one base per row, not one offset per
+// value.  A row outside C gets the base kFar, past every resource size, so its C0 load reads
 // 0 and its store is dropped: no store sits under a lane mask for rows (a
 // masked store is a branch of its own per value -- mask, exec save, store,
 // exec restore -- which made the store-back of the batched 257 x 129 problems
