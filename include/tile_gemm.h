@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define TILE_GEMM_ABI_VERSION 10
+#define TILE_GEMM_ABI_VERSION 11
 
 typedef enum { TG_F32 = 0, TG_BF16 = 1, TG_F16 = 2 } tg_dtype;
 
@@ -210,8 +210,17 @@ typedef enum {
  * the copies a workgroup issues after a tile's C stores can only be waited
  * for once those stores are done, which a fresh workgroup of the plain grid
  * never waits for (8192^3 bf16: 0.797 ms against 0.783 ms).
- *   persistent == 0 or 1: the plain grid;
- *   persistent == 2: persistent workgroups where the conditions hold.
+ * Two batch entries per workgroup (16-bit, TG_CFG_288x160, depth 4, XOR
+ * swizzle, every entry one block of the tile, no split, no repack, more than
+ * 256 and at most 512 entries, at least 4 K tiles): 256 workgroups, workgroup
+ * w takes entry w and then entry w + 256; the first entry's last K iterations
+ * copy the second's first K tiles, so the second does not start cold.  The
+ * same MFMA sequence per entry: bitwise the plain grid's result.  This is the
+ * automatic choice where it applies (512 x 257x129x1000 f16: 111.8 against
+ * 114.9 us for the kernel).
+ *   persistent == 0: the plain grid, or two entries per workgroup where that applies;
+ *   persistent == 1: the plain grid;
+ *   persistent == 2: as 0, and persistent workgroups where their conditions hold.
  * Fused elementwise tail (OCANNL "Module Ir.Schedule", epilogue fusion: the
  * bias add / activation / residual that follows a reduction, folded into its
  * store-back): with bias_mode or activation nonzero every output is
@@ -252,7 +261,7 @@ typedef struct {
     int pad0_;
     int64_t plan_lda;    /* lda assumed by the plan queries (0: a multiple of 8)    */
     int tail_gemm;       /* 0 = strips, split when worth it; 1 = strips; 2 = GEMMs; 3 = split (above) */
-    int persistent;      /* 0, 1 = plain grid; 2 = persistent where allowed (above) */
+    int persistent;      /* 0 automatic, 1 plain grid, 2 persistent where allowed (above) */
     const float *bias;   /* fused tail bias (see above), NULL when bias_mode == 0    */
     int64_t bias_stride; /* floats between the bias vectors of batch entries          */
     int bias_mode;       /* 0 = none, 1 = per column (bias[j]), 2 = per row (bias[i]) */
@@ -295,7 +304,8 @@ typedef struct {
     int64_t strip_blocks;         /* thin fringe-strip blocks per problem (in grid) */
     int tail_n_splits;            /* 0: no N-remainder GEMM; S >= 1: one, with S K slices */
     int tail_m_splits;            /* the same for the M remainder                  */
-    int persistent;               /* 1: persistent workgroups (grid = their count) */
+    int persistent;               /* 1: persistent workgroups or two batch entries per
+                                     workgroup (grid = their count) */
     int per_cu;                   /* workgroups of this configuration one CU holds at once
                                      (registers and LDS of the built kernel) */
     int pack_b;                   /* 1: B is first copied to aligned rows in the workspace */

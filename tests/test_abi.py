@@ -28,7 +28,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert tg.abi_version() == tg.ABI_VERSION == 10
+    assert tg.abi_version() == tg.ABI_VERSION == 11
     for s in range(6):
         assert tg.STATUS_NAMES[s] in tg.status_string(s)
 
@@ -397,7 +397,7 @@ def test_plan_automatic_split_across_tiles():
              ((1, 512, 2048, 2048, "bf16"), (tg.TG_CFG_64x64, 1, 256)),      # not 256x256 split 2 (32 blocks)
              ((1, 512, 512, 131072, "bf16"), (tg.TG_CFG_256x256, 64, 256)),  # a tie at 256: the larger tile
              ((1, 8192, 8192, 8192, "bf16"), (tg.TG_CFG_256x256, 1, 1024)),
-             ((512, 257, 129, 1000, "f16"), (tg.TG_CFG_288x160, 1, 512)),   # one block per problem
+             ((512, 257, 129, 1000, "f16"), (tg.TG_CFG_288x160, 1, 256)),   # two problems per workgroup
              ((1, 1000, 1000, 1000, "bf16"), (tg.TG_CFG_64x64, 1, 256)),
              ((1, 384, 4096, 4096, "bf16"), (tg.TG_CFG_128x128, 4, 384)),     # 512 slots for the smaller tiles
              ((1, 256, 256, 65536, "bf16"), (tg.TG_CFG_64x64, 32, 512)),
@@ -471,7 +471,7 @@ def test_noalloc_limits_checked_before_any_device():
 def test_plan_one_block_per_small_problem():
     """Batched problems that fit one 288 x 160 tile, at least half of it output, take one block
     per problem; the batched workload 512 x (257 x 129 x 1000) is one such."""
-    p = tg.tile_gemm_plan(512, 257, 129, 1000, "f16")
+    p = tg.tile_gemm_plan(512, 257, 129, 1000, "f16", persistent=1)
     assert (p["config"], p["block_m"], p["block_n"], p["tiles_m"], p["tiles_n"], p["grid"]) == \
            (tg.TG_CFG_288x160, 288, 160, 1, 1, 512)
     assert (p["interior_blocks"], p["fringe_blocks"], p["strip_blocks"], p["lds_bytes"], p["per_cu"]) == \
@@ -488,6 +488,26 @@ def test_plan_one_block_per_small_problem():
     assert _plan_status(8, 257, 129, 100, "bf16", config=tg.TG_CFG_288x160, swizzle=tg.SWZ_PAD) == \
         tg.TG_ERR_UNSUPPORTED
     assert _plan_status(8, 257, 129, 100, "f32", config=tg.TG_CFG_288x160) == tg.TG_ERR_UNSUPPORTED
+
+
+def test_plan_two_problems_per_workgroup():
+    """Single-block problems on the 288 x 160 tile in more than one round and at most two run two
+    per workgroup (256 workgroups), unless persistent = 1 asks for the plain grid; the plan is
+    otherwise the plain grid's."""
+    c4 = (512, 257, 129, 1000, "f16")
+    chained, plain = tg.tile_gemm_plan(*c4), tg.tile_gemm_plan(*c4, persistent=1)
+    assert (chained["config"], chained["persistent"], chained["grid"]) == (tg.TG_CFG_288x160, 1, 256)
+    assert (plain["persistent"], plain["grid"]) == (0, 512)
+    assert {k: v for k, v in chained.items() if k not in ("persistent", "grid")} == \
+           {k: v for k, v in plain.items() if k not in ("persistent", "grid")}
+    assert tg.tile_gemm_plan(*c4, persistent=2)["persistent"] == 1
+    assert tg.tile_gemm_plan(*c4, bias_mode=1, activation=2)["persistent"] == 1      # with the fused tail too
+    assert tg.tile_gemm_plan(257, 257, 129, 1000, "bf16")["grid"] == 256
+    # one round, more than two, fewer than four K tiles, another depth or placement: the plain grid
+    for args, kw in [((256, 257, 129, 1000, "f16"), {}), ((513, 257, 129, 1000, "f16"), {}),
+                     ((512, 257, 129, 96, "f16"), {}), (c4, dict(pipeline_depth=2)), (c4, dict(swizzle=tg.SWZ_NONE))]:
+        p = tg.tile_gemm_plan(*args, **kw)
+        assert p["config"] == tg.TG_CFG_288x160 and p["persistent"] == 0 and p["grid"] == args[0], (args, kw, p)
 
 
 def test_plan_b_repack_and_split_strips():

@@ -25,7 +25,7 @@ DTYPES = {"f32": TG_F32, "bf16": TG_BF16, "f16": TG_F16}
 TG_OK, TG_ERR_INVALID_ARG, TG_ERR_UNSUPPORTED, TG_ERR_LAUNCH, TG_ERR_INTERNAL, TG_ERR_SCRATCH_LIMIT = range(6)
 STATUS_NAMES = {0: "TG_OK", 1: "TG_ERR_INVALID_ARG", 2: "TG_ERR_UNSUPPORTED", 3: "TG_ERR_LAUNCH",
                 4: "TG_ERR_INTERNAL", 5: "TG_ERR_SCRATCH_LIMIT"}
-ABI_VERSION = 10
+ABI_VERSION = 11
 # bytes of the library's own scratch that tile_gemm_ex_noalloc works in (TILE_GEMM_NOALLOC_SCRATCH_BYTES)
 NOALLOC_SCRATCH_BYTES = 64 << 20
 

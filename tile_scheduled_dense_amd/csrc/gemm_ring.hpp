@@ -821,6 +821,85 @@ __device__ __forceinline__ void ring_persistent(const GemmParams &p, char *smem)
     wait_vmcnt<0>();
 }
 
+// Two batch entries per workgroup on one ring, for batches of single-tile
+// problems (each entry one fringe block) of more than one round and at most
+// two: workgroup w takes entry w, then entry w + G when it exists (G =
+// gridDim.x).  The first entry's last iterations copy the second entry's first
+// K tiles into the LDS copies its own last tiles release, so the second starts
+// with them landed or in flight while the first stores C, where a fresh
+// workgroup of the plain grid starts cold.  Each entry's MFMA sequence is the
+// plain ring's, so the result is bitwise the plain grid's.  The entries are
+// straight-line code: a loop over entries kept neither the accumulators nor
+// the copy state in registers.  The waits count copies only; loads and stores
+// share one in-order completion count, so ignoring the C stores and register
+// loads issued after some copies only makes a wait longer than it must be.
+template <class C, int STAGES, int SWZ, bool TAIL, bool NEXT>
+__device__ __forceinline__ void chain_entry(const GemmParams &p, RingBlock<C, STAGES, SWZ, true, true> &blk,
+                                            int64_t v, int64_t vn, int &cur, int &nxt) {
+    using Blk = RingBlock<C, STAGES, SWZ, true, true>;
+    static_assert(STAGES == 4, "waits written for four LDS copies");
+    const int64_t nk = blk.nk, ndma = blk.ndma;
+    // copy tiles in issue order: this entry's 0 .. ndma - 1 (its last K tile goes
+    // through registers), then the next entry's, numbered from nk
+    auto copied = [&](int64_t g) { return g < ndma || (NEXT && g >= nk); };
+    for (int64_t kt = 0; kt < nk; ++kt) {
+        if (kt < ndma) {
+            const int later = (copied(kt + 1) ? 1 : 0) + (copied(kt + 2) ? 1 : 0);
+            if (later >= 2) wait_vmcnt<2 * Blk::COPIES>();
+            else if (later == 1) wait_vmcnt<Blk::COPIES>();
+            else wait_vmcnt<0>();
+        } else {
+            // the register tail is older than the next entry's two copies issued so far
+            if (NEXT) wait_vmcnt<2 * Blk::COPIES>();
+            else wait_vmcnt<0>();
+            blk.tail_store(cur);
+        }
+        wait_lds();
+        block_barrier();            // tile kt visible; the copy of tile kt - 1 released
+        const int64_t g = kt + STAGES - 1;
+        if (g < ndma) {
+            blk.dma(g, nxt);
+        } else if (NEXT && g >= nk) {
+            if (g == nk) {          // this entry's copies are all issued: point the copies at the next
+                blk.b = vn;
+                blk.Ablk = p.A + vn * p.sA * C::ELEM;
+                blk.Bblk = p.B + vn * p.sB * C::ELEM;
+                blk.a_base = uniform_u64((uint64_t)blk.Ablk);
+                blk.b_base = uniform_u64((uint64_t)blk.Bblk);
+            }
+            blk.dma(g - nk, nxt);
+        }
+        if (kt == 0) blk.template compute<true>(cur);
+        else blk.template compute<false>(cur);
+        cur = cur + 1 == STAGES ? 0 : cur + 1;
+        nxt = nxt + 1 == STAGES ? 0 : nxt + 1;
+    }
+    blk.acc.settle();
+    auto get = [&](int i, int j, int w) { return blk.acc.get(i, j, w); };
+    store_tile_epilogue<C, true, decltype(get), chunk_values<C, TAIL>(), TAIL>(p, get, v, 0, 0, blk.wave, blk.lane);
+}
+
+// The host launches it for the 288 x 160 tile with G < batch <= 2 G and at
+// least STAGES K tiles per entry.
+template <class C, int STAGES, int SWZ, bool TAIL = false>
+__global__ __launch_bounds__(C::THREADS, C::OCCUPANCY) void gemm_ring_chain_kernel(GemmParams p) {
+    __shared__ __attribute__((aligned(1024))) char smem[STAGES * ring_stage_bytes<C, SWZ>()];
+    const int64_t v = blockIdx.x, vn = v + gridDim.x;
+    RingBlock<C, STAGES, SWZ, true, true> blk(p, smem, v, 0, 0);
+    blk.tail_load();
+#pragma unroll
+    for (int t = 0; t < STAGES - 1; ++t) blk.dma(t, t);
+    int cur = 0, nxt = STAGES - 1;
+    if (vn < p.batch) {
+        chain_entry<C, STAGES, SWZ, TAIL, true>(p, blk, v, vn, cur, nxt);
+        blk.acc.settle();       // the store-back's accumulator reads before the next entry's first MFMAs
+        blk.tail_load();
+        chain_entry<C, STAGES, SWZ, TAIL, false>(p, blk, vn, vn, cur, nxt);
+    } else {
+        chain_entry<C, STAGES, SWZ, TAIL, false>(p, blk, v, v, cur, nxt);
+    }
+}
+
 template <class C, int STAGES, int SWZ, bool TAIL = false>
 __global__ __launch_bounds__(C::THREADS, C::OCCUPANCY) void gemm_ring_persistent_kernel(GemmParams p) {
     __shared__ __attribute__((aligned(1024))) char smem[STAGES * ring_stage_bytes<C, SWZ>()];

@@ -71,6 +71,17 @@ tg_status launch_ring(const GemmParams &gp, const tg_plan_info &p, hipStream_t s
 
 template <int DT>
 tg_status launch_dtype(const GemmParams &gp, const tg_plan_info &p, hipStream_t s, bool tail) {
+    if (p.persistent && p.config == TG_CFG_288x160) {     // two batch entries per workgroup
+        if (p.pipeline_depth != 4 || p.swizzle != SWZ_XOR) return TG_ERR_INTERNAL;
+        using C = Ring288x160<DT>;
+        if (tail)
+            hipLaunchKernelGGL((gemm_ring_chain_kernel<C, 4, SWZ_XOR, true>), dim3((unsigned)p.grid), dim3(C::THREADS),
+                               0, s, gp);
+        else
+            hipLaunchKernelGGL((gemm_ring_chain_kernel<C, 4, SWZ_XOR>), dim3((unsigned)p.grid), dim3(C::THREADS), 0, s,
+                               gp);
+        return hipGetLastError() == hipSuccess ? TG_OK : TG_ERR_LAUNCH;
+    }
     if (p.persistent) {
         if (p.config != TG_CFG_256x256 || p.pipeline_depth != 4 || p.swizzle != SWZ_XOR) return TG_ERR_INTERNAL;
         using C = Ring256<DT>;

@@ -597,6 +597,17 @@ tg_status make_plan(int64_t batch, int64_t M, int64_t N, int64_t K, tg_dtype dty
         p.persistent = 1;
         p.grid = kPersistentBlocks;
     }
+    // Two batch entries per workgroup (tile_gemm.h): single-tile problems on the
+    // 288 x 160 tile in more than one round and at most two, unless the caller
+    // asks for the plain grid (512 x 257x129x1000 f16: 114.9 against 111.8 us
+    // in a standalone copy of the kernel, the same result bit for bit).
+    const int64_t chain_blocks = cfg_slots(TG_CFG_288x160);
+    if (sixteen && some && o.persistent != 1 && config == TG_CFG_288x160 && depth == 4 && swz == SWZ_XOR &&
+        splits == 1 && p.tiles_m == 1 && p.tiles_n == 1 && p.strip_blocks == 0 && !p.pack_a && !p.pack_b &&
+        batch > chain_blocks && batch <= 2 * chain_blocks && cdiv(K, d.bk) >= depth) {
+        p.persistent = 1;
+        p.grid = chain_blocks;
+    }
     return TG_OK;
 }
 
