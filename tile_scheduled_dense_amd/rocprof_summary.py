@@ -37,7 +37,7 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-GEMM_KERNEL_TAG = "tg::gemm"     # gemm_kernel (fp32) and gemm_ring_kernel (16-bit)
+GEMM_KERNEL_TAG = "tg::gemm"     # gemm_kernel (fp32), gemm_ring_kernel, gemm_ring_chain_kernel and gemm_ring_persistent_kernel
 
 
 def kernel_source_hash() -> str:
