@@ -53,6 +53,9 @@ PAIRS = [
     # the automatic choice: the deep-K workload's split (64 planes, all 64 MiB), then a batch
     (dict(dt="bf16", M=512, N=512, K=131072, batch=1, alpha=1.0, beta=0.0, opts={}),
      dict(dt="f16", M=130, N=97, K=5000, batch=2, alpha=1.0, beta=0.5, opts={})),
+    # two batch entries per workgroup on the 288 x 160 tile (no scratch), then a split into it
+    (dict(dt="bf16", M=150, N=100, K=200, batch=260, alpha=1.5, beta=0.5, opts=dict(config=tg.TG_CFG_288x160)),
+     dict(dt="bf16", M=300, N=260, K=4000, batch=1, alpha=1.0, beta=0.0, opts=dict(split_k=4))),
     # the aligned copy of A (lda = K + 3) in the scratch, then a split call of another config
     (dict(dt="bf16", M=2048, N=2300, K=1000, batch=1, alpha=1.5, beta=0.5, lda_pad=3, opts=dict(pack_a=2)),
      dict(dt="f16", M=257, N=129, K=1000, batch=3, alpha=1.0, beta=0.0, opts=dict(config=tg.TG_CFG_64x64,
